@@ -1,0 +1,212 @@
+"""Benchmark of the gated delta-rule hot path on one MI355X.
+
+A step is one chunkwise-parallel prefill (dr_chunk_fwd) over the KDA prefill
+workload: B=4, T=4096, H=16, d_k=d_v=128, bf16 q/k/v, fp32 gates and states,
+inputs resident in HBM. Two full input sets alternate so the 256 MB Infinity
+Cache cannot hold a step's inputs from the previous one. `value` is tokens/s
+(B*T tokens per step). The decode step (dr_decode_step) is timed in its own loop
+on 512 sequences x 32 heads with the 1 GiB fp32 state updated in place, and is
+reported as state GB/s under "decode".
+
+Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+
+
+def prefill_work(B, T, H, dk, dv, C=64, in_bytes=2, gate_bytes=4, n_states=None):
+    """Algorithmic bytes and useful FLOPs of one prefill call.
+    Bytes per token-head: q, k, v inputs + alpha (fp32) + gates + o (fp32); plus the
+    initial and final state of every (sequence, head). FLOPs: the chunkwise form's
+    useful (triangular) work per full chunk-head, pro rata per token."""
+    th = B * T * H
+    per_th = (2 * dk + dv) * in_bytes + 4 * dk + gate_bytes + 4 * dv
+    n_states = B if n_states is None else n_states
+    bytes_ = th * per_th + 2 * n_states * H * dk * dv * 4
+    f_chunk = 2 * (C * (C - 1) // 2 * dk + C * (C + 1) // 2 * dk + C * (C - 1) * (C - 2) // 6
+                   + C * (C - 1) // 2 * dk + C * (C - 1) // 2 * dv + 3 * C * dk * dv + C * (C + 1) // 2 * dv)
+    flops = th * f_chunk / C
+    return bytes_, flops
+
+
+def decode_bytes(N, H, dk, dv, in_bytes=2, gate_bytes=4):
+    """State read + write, plus the token's q, k, v, alpha, gates and o, per step."""
+    return N * H * (8 * dk * dv + (2 * dk + dv) * in_bytes + 4 * dk + gate_bytes + 4 * dv)
+
+
+def cpu_baseline():
+    """The fp64 oracle, as it is, on one batch row of the prefill workload (16 heads x
+    4096 tokens = a quarter of it) on one host core; scaled to tokens/s."""
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    import oracle
+    import synth
+    wl = synth.make_prefill("kda", 1, 4096, 16, 128, 128, in_dtype="bf16", seed=1002)
+    ctx = threadpool_limits(1) if threadpool_limits else None
+    t0 = time.perf_counter()
+    oracle.step_recurrence(wl.q, wl.k, wl.v, wl.alpha, wl.erase, None, "kda", S0=wl.S0)
+    dt = time.perf_counter() - t0
+    if ctx is not None:
+        ctx.__exit__(None, None, None)
+    return {"value": 4096 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"batch row 0 of the KDA prefill workload (16 heads x 4096 tokens, fp64 step "
+                      f"recurrence) in {dt:.1f} s on one core of {platform.processor() or platform.machine()}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=200)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only; --gpus must be 1 (the path runs per GPU with no "
+              "communication, see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import delta_rule_linear_chunked_amd as drl
+    import synth
+
+    dev = torch.device("cuda:0")
+    drl.load_library()
+
+    def t(x, bf16=False):
+        if x is None:
+            return None
+        y = torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+        return y.to(torch.bfloat16) if bf16 else y
+
+    # ------------------------------------------------------------------ prefill
+    B, T, H, D = 4, 4096, 16, 128
+    sets = []
+    for seed in (1002, 2002):
+        wl = synth.make_prefill("kda", B, T, H, D, D, in_dtype="bf16", seed=seed)
+        sets.append(dict(q=t(wl.q, True), k=t(wl.k, True), v=t(wl.v, True), alpha=t(wl.alpha),
+                         erase=t(wl.erase), S0=t(wl.S0)))
+        del wl
+    o = torch.empty((B, T, H, D), dtype=torch.float32, device=dev)
+    S_T = torch.empty((B, H, D, D), dtype=torch.float32, device=dev)
+
+    def step(i):
+        s = sets[i % 2]
+        drl.dr_chunk_fwd(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "kda", s["S0"], None, o, S_T)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    wall0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(args.steps):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])  # ms per launch
+    total_ms = evs[0].elapsed_time(evs[-1])
+    ms_step = total_ms / args.steps
+    tokens = B * T
+    value = tokens / (ms_step * 1e-3)
+    alg_bytes, flops = prefill_work(B, T, H, D, D)
+    achieved_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
+    plan = drl.chunk_fwd_plan(B, T, H, D, D)
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "prefill_kda_B4_T4096_H16_d128_traffic.json")
+    if os.path.exists(tfile):
+        tj = json.load(open(tfile))
+        traffic = tj.get("bytes_per_launch")
+
+    # ------------------------------------------------------------------ decode
+    decode = None
+    if not args.no_decode:
+        del sets
+        torch.cuda.empty_cache()
+        N, HD = 512, 32
+        pool = 16
+        wd = synth.make_decode("kda", N, HD, D, D, steps=pool, in_dtype="bf16", seed=1005)
+        toks = [dict(q=t(wd.q[i], True), k=t(wd.k[i], True), v=t(wd.v[i], True), alpha=t(wd.alpha[i]),
+                     erase=t(wd.erase[i])) for i in range(pool)]
+        S = t(wd.S0)
+        od = torch.empty((N, HD, D), dtype=torch.float32, device=dev)
+        del wd
+
+        def dstep(i):
+            s = toks[i % pool]
+            drl.dr_decode_step(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "kda", S, od)
+
+        for i in range(10):
+            dstep(i)
+        torch.cuda.synchronize()
+        dev_ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.decode_steps + 1)]
+        dev_ev[0].record(stream)
+        for i in range(args.decode_steps):
+            dstep(i)
+            dev_ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        dper = np.array([dev_ev[i].elapsed_time(dev_ev[i + 1]) for i in range(args.decode_steps)])
+        dms = dev_ev[0].elapsed_time(dev_ev[-1]) / args.decode_steps
+        dbytes = decode_bytes(N, HD, D, D)
+        decode = {
+            "workload": "decode KDA, 512 sequences x 32 heads, d_k=d_v=128, fp32 state 1 GiB in place, bf16 q/k/v",
+            "us_per_step": dms * 1e3,
+            "p50_us": float(np.percentile(dper, 50) * 1e3), "p95_us": float(np.percentile(dper, 95) * 1e3),
+            "p99_us": float(np.percentile(dper, 99) * 1e3),
+            "state_GBps": dbytes / (dms * 1e-3) / 1e9,
+            "tokens_per_s": N / (dms * 1e-3),
+            "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_step": dbytes, "steps": args.decode_steps,
+        }
+
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": "chunked fwd tokens/s (H=16,d=128,T=4096) + decode state GB/s, 1xMI355X",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "KDA chunked prefill B=4 T=4096 H=16 d_k=d_v=128, bf16 q/k/v, fp32 "
+                               "gates/state/output, random S0, chunk 64",
+                   "global_batch": B, "seq_len": T, "heads": H, "head_dim": D,
+                   "dv_block": plan[1], "workgroups": plan[2]},
+        "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved_gbs / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "chunk_fwd_kernel<128,32,bf16>", "alg_bytes_per_launch": alg_bytes},
+        "mfma": {"useful_tflops": flops / (ms_step * 1e-3) / 1e12,
+                 "frac_of_bf16_peak": flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                 "useful_flop_per_launch": flops},
+        "latency_ms": {"p50": float(np.percentile(per, 50)), "p95": float(np.percentile(per, 95)),
+                       "p99": float(np.percentile(per, 99)), "mean": float(per.mean())},
+        "decode": decode,
+        "run": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
+                "cus": props.multi_processor_count, "torch": torch.__version__,
+                "hip": getattr(torch.version, "hip", None), "host_cpu": platform.processor(),
+                "wall_s_timed": wall},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,203 @@
+"""Python binding of libdeltarule (gated delta-rule prefill and decode on MI355X).
+
+Argument marshalling only: the functions check that the torch tensors have the
+shapes, dtypes and layout the C ABI expects, pass raw device pointers and the
+current HIP stream, and raise on a non-zero status. Every step of the
+computation runs in the HIP kernels of ``lib/libdeltarule.so``; there is no
+fallback. If the library has not been built the first call raises.
+
+The names mirror the C entry points (``dr_chunk_fwd``, ``dr_decode_step``);
+``chunk_fwd`` and ``decode_step`` additionally allocate the outputs.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["dr_chunk_fwd", "dr_decode_step", "chunk_fwd", "decode_step", "chunk_fwd_plan",
+           "library_path", "load_library", "VARIANTS", "DeltaRuleError"]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "lib", "libdeltarule.so")
+VARIANTS = {"kda": 0, "rda": 1, "gdn2": 2, "ckda": 3}
+_DT = {torch.float32: 0, torch.bfloat16: 1}
+_lib = None
+
+
+class DeltaRuleError(RuntimeError):
+    pass
+
+
+class _Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("num_heads", ctypes.c_int64),
+                ("head_dim_k", ctypes.c_int64), ("head_dim_v", ctypes.c_int64),
+                ("num_seqs", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library(path: Optional[str] = None):
+    """Load libdeltarule.so once and declare its signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or _LIB_PATH
+    if not os.path.exists(p):
+        raise DeltaRuleError(f"{p} is missing: build it with `python -m delta_rule_linear_chunked_amd._build`")
+    lib = ctypes.CDLL(p)
+    vp, fp, ip = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int
+    lib.dr_chunk_fwd.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, vp, fp, fp, ctypes.POINTER(_Dims), vp]
+    lib.dr_chunk_fwd.restype = ip
+    lib.dr_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, fp, ctypes.POINTER(_Dims), vp]
+    lib.dr_decode_step.restype = ip
+    lib.dr_status_string.argtypes = [ip]
+    lib.dr_status_string.restype = ctypes.c_char_p
+    lib.dr_last_error.argtypes = []
+    lib.dr_last_error.restype = ctypes.c_char_p
+    lib.dr_version.restype = ip
+    lib.dr_chunk_fwd_plan.argtypes = [ctypes.POINTER(_Dims), ip, ctypes.POINTER(ctypes.c_int32),
+                                      ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
+    lib.dr_chunk_fwd_plan.restype = ip
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(lib, status: int, what: str):
+    if status != 0:
+        msg = lib.dr_last_error().decode()
+        raise DeltaRuleError(f"{what}: {lib.dr_status_string(status).decode()}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: Optional[torch.Tensor], name: str, shape, dtype=None, device=None):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _gate_shapes(variant: str, lead, dk, dv):
+    if variant in ("kda", "ckda"):
+        return tuple(lead), None
+    if variant == "rda":
+        return tuple(lead), tuple(lead)
+    if variant == "gdn2":
+        return tuple(lead) + (dk,), tuple(lead) + (dv,)
+    raise ValueError(f"unknown variant {variant!r}")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def chunk_fwd_plan(B: int, T: int, H: int, dk: int, dv: int, num_seqs: Optional[int] = None,
+                   variant: str = "kda", in_dtype: torch.dtype = torch.bfloat16):
+    """(chunk, dv_block, workgroups) the prefill launches for these sizes."""
+    lib = load_library()
+    d = _Dims(B, T, H, dk, dv, B if num_seqs is None else num_seqs, _DT[in_dtype], 0)
+    c, b, w = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int64()
+    _check(lib, lib.dr_chunk_fwd_plan(ctypes.byref(d), VARIANTS[variant], ctypes.byref(c),
+                                      ctypes.byref(b), ctypes.byref(w)), "dr_chunk_fwd_plan")
+    return c.value, b.value, w.value
+
+
+def dr_chunk_fwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, o, S_T) -> None:
+    """Chunkwise prefill into caller-provided ``o`` (and ``S_T``). Shapes as in
+    include/deltarule.h: q,k [B,T,H,dk]; v [B,T,H,dv]; alpha [B,T,H,dk] fp32; gates per
+    variant (fp32); S0/S_T [N,H,dk,dv] fp32 or None; cu_seqlens [N+1] int32 or None;
+    o [B,T,H,dv] fp32."""
+    lib = load_library()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"q dtype {q.dtype} is not float32 or bfloat16")
+    _need(q, "q", (B, T, H, dk), q.dtype, dev)
+    _need(k, "k", (B, T, H, dk), q.dtype, dev)
+    _need(v, "v", (B, T, H, dv), q.dtype, dev)
+    _need(alpha, "alpha", (B, T, H, dk), torch.float32, dev)
+    es, ws = _gate_shapes(variant, (B, T, H), dk, dv)
+    _need(erase, "erase", es, torch.float32, dev)
+    if ws is None:
+        if write is not None:
+            raise ValueError(f"{variant} takes no write gate")
+    else:
+        _need(write, "write", ws, torch.float32, dev)
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (cu_seqlens.shape[0],), torch.int32, dev)
+        N = cu_seqlens.shape[0] - 1
+    else:
+        N = B
+    if S0 is not None:
+        _need(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+    if S_T is not None:
+        _need(S_T, "S_T", (N, H, dk, dv), torch.float32, dev)
+    _need(o, "o", (B, T, H, dv), torch.float32, dev)
+    d = _Dims(B, T, H, dk, dv, N, _DT[q.dtype], 0)
+    st = lib.dr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
+                          VARIANTS[variant], _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
+                          ctypes.byref(d), _stream(dev))
+    _check(lib, st, "dr_chunk_fwd")
+
+
+def dr_decode_step(q, k, v, alpha, erase, write, variant: str, S, o) -> None:
+    """One decode step in place on ``S`` [N,H,dk,dv] fp32; writes ``o`` [N,H,dv] fp32.
+    q,k [N,H,dk]; v [N,H,dv]; alpha [N,H,dk]; gates per variant."""
+    lib = load_library()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"q dtype {q.dtype} is not float32 or bfloat16")
+    _need(q, "q", (N, H, dk), q.dtype, dev)
+    _need(k, "k", (N, H, dk), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(alpha, "alpha", (N, H, dk), torch.float32, dev)
+    es, ws = _gate_shapes(variant, (N, H), dk, dv)
+    _need(erase, "erase", es, torch.float32, dev)
+    if ws is None:
+        if write is not None:
+            raise ValueError(f"{variant} takes no write gate")
+    else:
+        _need(write, "write", ws, torch.float32, dev)
+    _need(S, "S", (N, H, dk, dv), torch.float32, dev)
+    _need(o, "o", (N, H, dv), torch.float32, dev)
+    d = _Dims(N, 1, H, dk, dv, N, _DT[q.dtype], 0)
+    st = lib.dr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
+                            VARIANTS[variant], _ptr(S), _ptr(o), ctypes.byref(d), _stream(dev))
+    _check(lib, st, "dr_decode_step")
+
+
+def chunk_fwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, cu_seqlens=None,
+              output_final_state: bool = True):
+    """Allocate o (and S_T) and run ``dr_chunk_fwd``. Returns (o, S_T or None)."""
+    B, T, H, _ = q.shape
+    dv = v.shape[-1]
+    N = B if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    S_T = (torch.empty((N, H, q.shape[-1], dv), dtype=torch.float32, device=q.device)
+           if output_final_state else None)
+    dr_chunk_fwd(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T)
+    return o, S_T
+
+
+def decode_step(q, k, v, alpha, erase, write, variant: str, S):
+    """Allocate o and run ``dr_decode_step`` (S is updated in place). Returns o."""
+    o = torch.empty((q.shape[0], q.shape[1], v.shape[-1]), dtype=torch.float32, device=q.device)
+    dr_decode_step(q, k, v, alpha, erase, write, variant, S, o)
+    return o

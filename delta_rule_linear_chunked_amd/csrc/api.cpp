@@ -1,0 +1,207 @@
+// C ABI of the gated delta-rule library: argument validation and kernel dispatch.
+// Every check runs on the host before any launch; no device memory is read here.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdint>
+#include <string>
+
+#include "../../include/deltarule.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+bool head_dim_ok(int64_t d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared checks of the variant's gate pointers. scalar_lead / vector shapes are implied by the
+// variant; the library cannot see extents of device buffers, so it checks presence only.
+int check_variant(int variant, const float* erase, const float* write, bool* vec) {
+  switch (variant) {
+    case DR_KDA:
+    case DR_CKDA:
+      if (write != nullptr)
+        return fail(DR_ERR_VARIANT, "variant %s takes beta as `erase` and no `write` gate",
+                    variant == DR_KDA ? "KDA" : "CKDA");
+      *vec = false;
+      break;
+    case DR_RDA:
+      if (write == nullptr) return fail(DR_ERR_VARIANT, "variant RDA needs a per-head `write` gate");
+      *vec = false;
+      break;
+    case DR_GDN2:
+      if (write == nullptr) return fail(DR_ERR_VARIANT, "variant GDN-2 needs a channel-wise `write` gate");
+      *vec = true;
+      break;
+    default:
+      return fail(DR_ERR_VARIANT, "unknown variant %d", variant);
+  }
+  if (erase == nullptr) return fail(DR_ERR_NULL, "`erase` gate is NULL");
+  return DR_OK;
+}
+
+int check_dims_common(const dr_dims* d) {
+  if (d == nullptr) return fail(DR_ERR_NULL, "dims is NULL");
+  if (d->reserved != 0) return fail(DR_ERR_SHAPE, "dims.reserved must be 0");
+  if (d->in_dtype != DR_F32 && d->in_dtype != DR_BF16)
+    return fail(DR_ERR_DTYPE, "in_dtype %d is neither DR_F32 nor DR_BF16", d->in_dtype);
+  if (d->batch < 0 || d->seqlen < 0 || d->num_heads < 1 || d->num_seqs < 0)
+    return fail(DR_ERR_SHAPE, "bad sizes: batch=%lld seqlen=%lld heads=%lld seqs=%lld",
+                (long long)d->batch, (long long)d->seqlen, (long long)d->num_heads,
+                (long long)d->num_seqs);
+  if (!head_dim_ok(d->head_dim_k) || !head_dim_ok(d->head_dim_v))
+    return fail(DR_ERR_UNSUPPORTED, "head sizes d_k=%lld d_v=%lld: each must be 16, 32, 64 or 128",
+                (long long)d->head_dim_k, (long long)d->head_dim_v);
+  // Kernels index with 64-bit offsets but keep (sequence, head) and token counts in 32 bits.
+  const int64_t lim = (int64_t)1 << 31;
+  if (d->num_heads >= lim || d->num_seqs * d->num_heads >= lim || d->batch * d->seqlen >= lim)
+    return fail(DR_ERR_SHAPE, "problem too large for 32-bit token or head counts");
+  return DR_OK;
+}
+
+int check_ptrs(std::initializer_list<std::pair<const void*, const char*>> req,
+               std::initializer_list<std::pair<const void*, const char*>> opt) {
+  for (auto& pr : req) {
+    if (pr.first == nullptr) return fail(DR_ERR_NULL, "`%s` is NULL", pr.second);
+    if (!aligned16(pr.first)) return fail(DR_ERR_ALIGN, "`%s` is not 16-byte aligned", pr.second);
+  }
+  for (auto& pr : opt)
+    if (pr.first != nullptr && !aligned16(pr.first))
+      return fail(DR_ERR_ALIGN, "`%s` is not 16-byte aligned", pr.second);
+  return DR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dr_status_string(int status) {
+  switch (status) {
+    case DR_OK: return "DR_OK";
+    case DR_ERR_NULL: return "DR_ERR_NULL: a required pointer is NULL";
+    case DR_ERR_SHAPE: return "DR_ERR_SHAPE: negative or inconsistent sizes";
+    case DR_ERR_DTYPE: return "DR_ERR_DTYPE: unsupported input dtype";
+    case DR_ERR_ALIGN: return "DR_ERR_ALIGN: pointer not 16-byte aligned";
+    case DR_ERR_UNSUPPORTED: return "DR_ERR_UNSUPPORTED: head size not in {16, 32, 64, 128}";
+    case DR_ERR_VARIANT: return "DR_ERR_VARIANT: unknown variant or gates that do not fit it";
+    case DR_ERR_HIP: return "DR_ERR_HIP: HIP runtime or launch failure";
+  }
+  return "unknown status";
+}
+
+const char* dr_last_error(void) { return g_last_error.c_str(); }
+
+int dr_version(void) { return 100; }
+
+static int prefill_checks(const dr_dims* dims, int variant, const float* erase, const float* write,
+                          const int32_t* cu_seqlens, bool* vec) {
+  int st = check_dims_common(dims);
+  if (st) return st;
+  st = check_variant(variant, erase, write, vec);
+  if (st) return st;
+  if (cu_seqlens != nullptr) {
+    if (dims->batch != 1)
+      return fail(DR_ERR_SHAPE, "packed sequences (cu_seqlens) need batch == 1, got %lld",
+                  (long long)dims->batch);
+  } else if (dims->num_seqs != dims->batch) {
+    return fail(DR_ERR_SHAPE, "num_seqs (%lld) must equal batch (%lld) without cu_seqlens",
+                (long long)dims->num_seqs, (long long)dims->batch);
+  }
+  return DR_OK;
+}
+
+int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t* dv_block,
+                      int64_t* workgroups) {
+  g_last_error.clear();
+  int st = check_dims_common(dims);
+  if (st) return st;
+  if (variant < DR_KDA || variant > DR_CKDA) return fail(DR_ERR_VARIANT, "unknown variant %d", variant);
+  const dr::PrefillPlan pl = dr::plan_prefill(dims->num_seqs * dims->num_heads,
+                                              (int)dims->head_dim_k, (int)dims->head_dim_v);
+  if (chunk) *chunk = pl.chunk;
+  if (dv_block) *dv_block = pl.dv_block;
+  if (workgroups) *workgroups = pl.workgroups;
+  return DR_OK;
+}
+
+int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                 const float* erase, const float* write, int variant,
+                 const float* S0, const int32_t* cu_seqlens,
+                 float* o, float* S_T, const dr_dims* dims, hipStream_t stream) {
+  g_last_error.clear();
+  bool vec = false;
+  int st = prefill_checks(dims, variant, erase, write, cu_seqlens, &vec);
+  if (st) return st;
+  const int64_t tokens = dims->batch * dims->seqlen;
+  if (tokens > 0) {
+    st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {alpha, "alpha"}, {erase, "erase"}, {o, "o"}},
+                    {{write, "write"}});
+    if (st) return st;
+  }
+  st = check_ptrs({}, {{S0, "S0"}, {S_T, "S_T"}, {cu_seqlens, "cu_seqlens"}});
+  if (st) return st;
+  if (cu_seqlens == nullptr && dims->num_seqs > 0 && dims->seqlen == 0 && S_T == nullptr)
+    return DR_OK;  // nothing to compute and nothing to write
+  if (dims->num_seqs == 0) return DR_OK;
+
+  dr::Params p{};
+  p.q = q; p.k = k; p.v = v; p.alpha = alpha;
+  p.erase = erase;
+  p.write = (variant == DR_KDA || variant == DR_CKDA) ? erase : write;
+  p.S0 = S0; p.cu = cu_seqlens; p.o = o; p.S = S_T;
+  p.T = dims->seqlen;
+  p.H = (int32_t)dims->num_heads;
+  p.DV = (int32_t)dims->head_dim_v;
+  const int64_t pairs = dims->num_seqs * dims->num_heads;
+  const dr::PrefillPlan pl = dr::plan_prefill(pairs, (int)dims->head_dim_k, (int)dims->head_dim_v);
+  p.num_pairs = (int32_t)pairs;
+  p.ndvb = pl.ndvb;
+  p.grid_logical = (int32_t)(pairs * pl.ndvb);
+  hipError_t e = dr::launch_prefill(p, pl, (int)dims->head_dim_k, dims->in_dtype == DR_BF16, vec, stream);
+  if (e != hipSuccess) return fail(DR_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  return DR_OK;
+}
+
+int dr_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                   const float* erase, const float* write, int variant,
+                   float* S, float* o, const dr_dims* dims, hipStream_t stream) {
+  g_last_error.clear();
+  int st = check_dims_common(dims);
+  if (st) return st;
+  bool vec = false;
+  st = check_variant(variant, erase, write, &vec);
+  if (st) return st;
+  if (dims->num_seqs != dims->batch)
+    return fail(DR_ERR_SHAPE, "decode: num_seqs (%lld) must equal batch (%lld)",
+                (long long)dims->num_seqs, (long long)dims->batch);
+  const int64_t nheads = dims->num_seqs * dims->num_heads;
+  if (nheads == 0) return DR_OK;
+  st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {alpha, "alpha"}, {erase, "erase"}, {S, "S"}, {o, "o"}},
+                  {{write, "write"}});
+  if (st) return st;
+  dr::Params p{};
+  p.q = q; p.k = k; p.v = v; p.alpha = alpha;
+  p.erase = erase;
+  p.write = (variant == DR_KDA || variant == DR_CKDA) ? erase : write;
+  p.o = o; p.S = S;
+  p.H = (int32_t)dims->num_heads;
+  p.DV = (int32_t)dims->head_dim_v;
+  hipError_t e = dr::launch_decode(p, nheads, (int)dims->head_dim_k, (int)dims->head_dim_v,
+                                   dims->in_dtype == DR_BF16, vec, stream);
+  if (e != hipSuccess) return fail(DR_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
+  return DR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,153 @@
+// Device-side building blocks shared by the decode and prefill kernels (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Kernel parameter block. Pointers are device memory; sizes are element counts.
+struct Params {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* erase;   // beta (KDA/CKDA), e (RDA) or b (GDN-2)
+  const float* write;   // == erase for KDA/CKDA, w (RDA) or w (GDN-2)
+  const float* S0;      // prefill initial states (may be null); decode: unused
+  const int32_t* cu;    // packed sequence offsets (may be null)
+  float* o;
+  float* S;             // prefill: final states (may be null); decode: state in/out
+  int64_t T;            // tokens per batch row (prefill)
+  int32_t H;
+  int32_t DV;           // full value width (the kernel handles a column block of it)
+  int32_t num_pairs;    // sequences x heads
+  int32_t ndvb;         // value-column blocks per (sequence, head)
+  int32_t grid_logical; // num_pairs * ndvb
+};
+
+__device__ __forceinline__ float ld_f32(const float* p) { return *p; }
+__device__ __forceinline__ float ld_f32(const __bf16* p) { return (float)*p; }
+
+// Eight consecutive elements (16-byte aligned for float pairs of f32x4, 16 bytes for bf16).
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+  x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
+}
+__device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
+  const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 16x16 tiles with a 32-deep reduction per call.
+//
+// Fragment convention (both precisions): lane l supplies row (A operand) or
+// column (B operand) l % 16 and the eight reduction indices 8*(l/16) + j,
+// j = 0..7, of the 32-deep slice. The accumulator holds column l % 16 and rows
+// 4*(l/16) + i, i = 0..3. A and B use the same reduction-index assignment, so
+// the sum over all four lane groups and eight items covers the slice exactly
+// once.
+//
+// PolF32: eight v_mfma_f32_16x16x4_f32, instruction j taking item j of every
+//         lane group (exact fp32 products).
+// PolBF3: operands split x = hi + lo (hi = bf16(x), lo = bf16(x - hi)) and
+//         hi*hi + hi*lo + lo*hi accumulated with v_mfma_f32_16x16x32_bf16;
+//         the dropped lo*lo term and the rounding of lo leave a relative error
+//         of about 2^-16 per product.
+// ---------------------------------------------------------------------------
+struct PolF32 {
+  struct Frag { float v[8]; };
+  static __device__ __forceinline__ Frag make(const float (&x)[8]) {
+    Frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = x[j];
+    return f;
+  }
+  static __device__ __forceinline__ Frag zero() {
+    Frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) f.v[j] = 0.f;
+    return f;
+  }
+  static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+  }
+};
+
+struct PolBF3 {
+  struct Frag { bf16x8 hi, lo; };
+  static __device__ __forceinline__ Frag make(const float (&x)[8]) {
+    Frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const __bf16 h = (__bf16)x[j];
+      f.hi[j] = h;
+      f.lo[j] = (__bf16)(x[j] - (float)h);
+    }
+    return f;
+  }
+  static __device__ __forceinline__ Frag zero() {
+    Frag f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { f.hi[j] = (__bf16)0.f; f.lo[j] = (__bf16)0.f; }
+    return f;
+  }
+  static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.lo, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.hi, b.hi, acc, 0, 0, 0);
+  }
+};
+
+template <typename InT> struct PolicyFor;
+template <> struct PolicyFor<float> { using type = PolF32; };
+template <> struct PolicyFor<__bf16> { using type = PolBF3; };
+
+// ---------------------------------------------------------------------------
+// Scans across the 16 lanes of a DPP row (rows are lanes 0-15, 16-31, 32-47, 48-63).
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_or(float old, float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                               __builtin_bit_cast(int, x), CTRL,
+                                                               0xf, 0xf, false));
+}
+constexpr int ROW_SHL1 = 0x101, ROW_SHL2 = 0x102, ROW_SHL4 = 0x104, ROW_SHL8 = 0x108;
+constexpr int ROW_SHR1 = 0x111, ROW_SHR2 = 0x112, ROW_SHR4 = 0x114, ROW_SHR8 = 0x118;
+
+// Inclusive prefix product over lanes 0..r of the row (lane r receives x_0 * ... * x_r).
+__device__ __forceinline__ float row_prefix_prod(float x) {
+  x *= dpp_or<ROW_SHR1>(1.f, x);
+  x *= dpp_or<ROW_SHR2>(1.f, x);
+  x *= dpp_or<ROW_SHR4>(1.f, x);
+  x *= dpp_or<ROW_SHR8>(1.f, x);
+  return x;
+}
+// Exclusive suffix product (lane r receives x_{r+1} * ... * x_15; lane 15 receives 1).
+__device__ __forceinline__ float row_suffix_prod_excl(float x) {
+  x *= dpp_or<ROW_SHL1>(1.f, x);
+  x *= dpp_or<ROW_SHL2>(1.f, x);
+  x *= dpp_or<ROW_SHL4>(1.f, x);
+  x *= dpp_or<ROW_SHL8>(1.f, x);
+  return dpp_or<ROW_SHL1>(1.f, x);
+}
+
+// Map a dispatched workgroup id to a logical work item so that consecutive
+// logical items (the value-column blocks of one sequence-head pair, which read
+// the same keys, queries and gates) land on the same XCD and share its L2.
+// Workgroups are dispatched round-robin over the 8 XCDs.
+__device__ __forceinline__ int xcd_remap(int b, int grid) {
+  constexpr int NXCD = 8;
+  const int per = grid / NXCD;  // grid is padded to a multiple of 8
+  return (b % NXCD) * per + (b / NXCD);
+}
+
+}  // namespace dr

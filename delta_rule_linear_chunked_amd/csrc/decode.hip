@@ -1,0 +1,162 @@
+// Single-token decode step of the gated delta rule on gfx950.
+//
+// One workgroup per (sequence, head). The d_k x d_v fp32 state is streamed
+// from HBM once with 128-bit non-temporal loads, kept in registers, reduced
+// over key rows, updated and streamed back in place, so each state byte is
+// read once and written once:
+//
+//   r_u = S^T (alpha . u),   r_q = S^T (alpha . q)        (one pass over S)
+//   delta = m - r_u                                        (delta-rule error)
+//   S <- Diag(alpha) S + k delta^T                         (in place)
+//   o = S_new^T q = r_q + (q . k) delta
+//
+// The update is the rule S_t = (I - k u^T) Diag(alpha) S + k m^T with the
+// erase/write vectors u, m of the KDA, RDA and GDN-2 rules (Hugging Face
+// discussion "KRAFTON/Raon-1-mini-preview" #1, the three state updates); the
+// last identity follows from S_new^T q = Diag(alpha)S^T q + delta (k . q).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace dr {
+
+template <int DK, int DV>
+struct DecodeShape {
+  static constexpr int COLS4 = DV / 4;                                 // float4 columns
+  static constexpr int RG = (DK < 256 / COLS4) ? DK : 256 / COLS4;     // row groups
+  static constexpr int RPT = DK / RG;                                  // rows per thread
+  static constexpr int NT = RG * COLS4;                                // threads
+  static_assert(RG * RPT == DK, "row split");
+  static_assert(NT <= 256 && NT % 64 == 0, "thread count");
+};
+
+template <int DK, int DV, typename InT, bool VEC>
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const Params p) {
+  using Sh = DecodeShape<DK, DV>;
+  constexpr int COLS4 = Sh::COLS4, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
+  __shared__ float s_q[DK], s_k[DK], s_au[DK], s_aq[DK], s_a[DK], s_m[DV];
+  __shared__ float s_red[2][RG][DV + 4];
+  __shared__ float s_qk[RG];
+  __shared__ float s_delta[DV];
+
+  const int tid = threadIdx.x;
+  const int c4 = tid % COLS4;
+  const int rg = tid / COLS4;
+  const int64_t nh = blockIdx.x;  // sequence * H + head
+  float* S = p.S + nh * (int64_t)DK * DV;
+
+  // Issue the state loads first: they do not depend on the token's vectors.
+  f32x4 st[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = rg + RG * i;
+    st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + row * DV) + c4);
+  }
+
+  // Stage the token's vectors.
+  const InT* q = static_cast<const InT*>(p.q) + nh * DK;
+  const InT* k = static_cast<const InT*>(p.k) + nh * DK;
+  const InT* v = static_cast<const InT*>(p.v) + nh * DV;
+  const float* al = p.alpha + nh * DK;
+  for (int i = tid; i < DK; i += NT) {
+    const float a = al[i], qi = ld_f32(q + i), ki = ld_f32(k + i);
+    const float ui = (VEC ? p.erase[nh * DK + i] : p.erase[nh]) * ki;
+    s_q[i] = qi;
+    s_k[i] = ki;
+    s_a[i] = a;
+    s_au[i] = a * ui;
+    s_aq[i] = a * qi;
+  }
+  for (int j = tid; j < DV; j += NT) {
+    const float wj = VEC ? p.write[nh * DV + j] : p.write[nh];
+    s_m[j] = wj * ld_f32(v + j);
+  }
+  __syncthreads();
+
+  // Partial reductions over this thread's rows.
+  float ru[4] = {0.f, 0.f, 0.f, 0.f}, rq[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = rg + RG * i;
+    const float au = s_au[row], aq = s_aq[row];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      ru[c] = fmaf(st[i][c], au, ru[c]);
+      rq[c] = fmaf(st[i][c], aq, rq[c]);
+    }
+    qk = fmaf(s_q[row], s_k[row], qk);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    s_red[0][rg][4 * c4 + c] = ru[c];
+    s_red[1][rg][4 * c4 + c] = rq[c];
+  }
+  if (c4 == 0) s_qk[rg] = qk;
+  __syncthreads();
+
+  if (tid < DV) {
+    float u_sum = 0.f, q_sum = 0.f, qk_sum = 0.f;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      u_sum += s_red[0][g][tid];
+      q_sum += s_red[1][g][tid];
+      qk_sum += s_qk[g];
+    }
+    const float delta = s_m[tid] - u_sum;
+    s_delta[tid] = delta;
+    p.o[nh * DV + tid] = fmaf(qk_sum, delta, q_sum);
+  }
+  __syncthreads();
+
+  float d[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) d[c] = s_delta[4 * c4 + c];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = rg + RG * i;
+    const float a = s_a[row], kr = s_k[row];
+    f32x4 nv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) nv[c] = fmaf(a, st[i][c], kr * d[c]);
+    __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(S + row * DV) + c4);
+  }
+}
+
+template <int DK, int DV, typename InT, bool VEC>
+static hipError_t launch_decode_t(const Params& p, int64_t nheads, hipStream_t s) {
+  constexpr int NT = DecodeShape<DK, DV>::NT;
+  hipLaunchKernelGGL((decode_kernel<DK, DV, InT, VEC>), dim3((unsigned)nheads), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DK, int DV>
+static hipError_t dispatch_gate(const Params& p, int64_t nheads, bool bf16, bool vec, hipStream_t s) {
+  if (bf16) return vec ? launch_decode_t<DK, DV, __bf16, true>(p, nheads, s)
+                       : launch_decode_t<DK, DV, __bf16, false>(p, nheads, s);
+  return vec ? launch_decode_t<DK, DV, float, true>(p, nheads, s)
+             : launch_decode_t<DK, DV, float, false>(p, nheads, s);
+}
+
+template <int DK>
+static hipError_t dispatch_dv(const Params& p, int64_t nheads, int dv, bool bf16, bool vec, hipStream_t s) {
+  switch (dv) {
+    case 16: return dispatch_gate<DK, 16>(p, nheads, bf16, vec, s);
+    case 32: return dispatch_gate<DK, 32>(p, nheads, bf16, vec, s);
+    case 64: return dispatch_gate<DK, 64>(p, nheads, bf16, vec, s);
+    case 128: return dispatch_gate<DK, 128>(p, nheads, bf16, vec, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const Params& p, int64_t nheads, int dk, int dv, bool bf16, bool vec,
+                         hipStream_t s) {
+  if (nheads == 0) return hipSuccess;
+  switch (dk) {
+    case 16: return dispatch_dv<16>(p, nheads, dv, bf16, vec, s);
+    case 32: return dispatch_dv<32>(p, nheads, dv, bf16, vec, s);
+    case 64: return dispatch_dv<64>(p, nheads, dv, bf16, vec, s);
+    case 128: return dispatch_dv<128>(p, nheads, dv, bf16, vec, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dr

@@ -1,0 +1,150 @@
+/*
+ * deltarule.h — C ABI of the MI355X (gfx950) gated delta-rule library.
+ *
+ * The library computes the recurrence
+ *
+ *     S_t = (I - k_t u_t^T) Diag(alpha_t) S_{t-1} + k_t m_t^T,      o_t = S_t^T q_t
+ *
+ * whose three instances are the KDA, RDA and GDN-2 update rules listed in the
+ * Hugging Face discussion "KRAFTON/Raon-1-mini-preview" #1 (the reply giving
+ * "the three state updates"), plus Complex KDA, which keeps KDA's formula with
+ * alpha in [-1, 1] and beta in [0, 2] (abstract of "Complex KDA: Understanding
+ * and Enhancing the Expressivity of Kimi Delta Attention", arXiv 2609.24797):
+ *
+ *     variant      erase gate (u_t)            write gate (m_t)
+ *     DR_KDA       beta_t  [.., H]   u = beta k   write == NULL, m = beta v
+ *     DR_CKDA      beta_t  [.., H]   u = beta k   write == NULL, m = beta v
+ *     DR_RDA       e_t     [.., H]   u = e k      w_t [.., H],    m = w v
+ *     DR_GDN2      b_t     [.., H, d_k] u = b.k   w_t [.., H, d_v], m = w.v
+ *
+ * The state S has d_k rows (key channels) and d_v columns; Diag(alpha_t) scales
+ * its rows. The readout uses the updated state and no 1/sqrt(d_k) factor.
+ * Gate values are not range-checked: CKDA differs from KDA only in the values
+ * the caller passes.
+ *
+ * Memory and layout. Every pointer argument is DEVICE memory on the current HIP
+ * device, row-major and densely packed in the shapes given below, and 16-byte
+ * aligned. The caller owns every buffer; the library keeps no pointer after a
+ * call returns, allocates nothing and holds no global state except a
+ * thread-local error message. Work is enqueued on `stream` and runs
+ * asynchronously; outputs are valid once the stream reaches that point.
+ *
+ * Errors. Argument errors are detected on the host before anything is launched
+ * and return a negative status (nothing is written). A failed kernel launch
+ * returns DR_ERR_HIP. dr_last_error() describes the most recent failure on the
+ * calling thread. The contents of cu_seqlens (device memory) are not read on
+ * the host: a cu_seqlens that is not non-decreasing from 0 to T is undefined
+ * behaviour.
+ */
+#ifndef DELTARULE_H
+#define DELTARULE_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dr_variant { DR_KDA = 0, DR_RDA = 1, DR_GDN2 = 2, DR_CKDA = 3 } dr_variant;
+
+/* Element type of q, k and v. Gates, states and outputs are always float32. */
+typedef enum dr_dtype { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;
+
+typedef enum dr_status {
+  DR_OK = 0,
+  DR_ERR_NULL = -1,        /* a required pointer is NULL */
+  DR_ERR_SHAPE = -2,       /* negative or inconsistent sizes */
+  DR_ERR_DTYPE = -3,       /* in_dtype is not DR_F32 / DR_BF16 */
+  DR_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  DR_ERR_UNSUPPORTED = -5, /* head size outside {16, 32, 64, 128} */
+  DR_ERR_VARIANT = -6,     /* unknown variant, or gate pointers that do not fit it */
+  DR_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed */
+} dr_status;
+
+/* Sizes of one call.
+ *   batch      B: rows of the [B, T, ...] token layout (1 when cu_seqlens is given)
+ *   seqlen     T: tokens per row (the total packed length when cu_seqlens is given)
+ *   num_heads  H
+ *   head_dim_k d_k, head_dim_v d_v: each one of 16, 32, 64, 128
+ *   num_seqs   N: number of sequences (= B without cu_seqlens, len(cu_seqlens) - 1 with it)
+ *   in_dtype   element type of q, k, v (dr_dtype)
+ */
+typedef struct dr_dims {
+  int64_t batch;
+  int64_t seqlen;
+  int64_t num_heads;
+  int64_t head_dim_k;
+  int64_t head_dim_v;
+  int64_t num_seqs;
+  int32_t in_dtype;
+  int32_t reserved; /* must be 0 */
+} dr_dims;
+
+/*
+ * Chunkwise-parallel prefill (the "scan/chunked" form of the recurrence that the
+ * course page "GDN, KDA và Mamba-2 · cập nhật state trong hybrid", section 3,
+ * says must match the step recurrence in the same dtype).
+ *
+ *   q, k       [B, T, H, d_k]  in_dtype
+ *   v          [B, T, H, d_v]  in_dtype
+ *   alpha      [B, T, H, d_k]  float32, channel-wise decay
+ *   erase      [B, T, H] float32 (KDA/CKDA beta, RDA e) or [B, T, H, d_k] (GDN-2 b)
+ *   write      NULL (KDA/CKDA), [B, T, H] (RDA w) or [B, T, H, d_v] (GDN-2 w)
+ *   S0         [N, H, d_k, d_v] float32 initial states, or NULL for zero states
+ *   cu_seqlens [N + 1] int32 or NULL. When given, B must be 1 and sequence n is
+ *              tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the packed row; each
+ *              sequence starts from its own S0[n] and no state crosses a boundary
+ *              (the same course page, section 3: document reset). Without it,
+ *              sequence n is batch row n.
+ *   o          [B, T, H, d_v] float32 output (written)
+ *   S_T        [N, H, d_k, d_v] float32 final states, or NULL to skip; may alias S0
+ *              for an in-place update.
+ * o must not alias any input. Results do not depend on how the library chunks
+ * the sequence, up to rounding.
+ */
+int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
+                 const float* erase, const float* write, int variant,
+                 const float* S0, const int32_t* cu_seqlens,
+                 float* o, float* S_T, const dr_dims* dims, hipStream_t stream);
+
+/*
+ * One recurrent decode step for N sequences x H heads, one token each: the
+ * fixed-size state is read once, updated in place and the token's output
+ * written (the course page above, section 1: the state's size does not grow
+ * with T at decode).
+ *
+ *   q, k       [N, H, d_k]  in_dtype;   v [N, H, d_v] in_dtype
+ *   alpha      [N, H, d_k]  float32
+ *   erase      [N, H] or [N, H, d_k] (GDN-2);  write NULL, [N, H] or [N, H, d_v]
+ *   S          [N, H, d_k, d_v] float32, read and overwritten with S_t
+ *   o          [N, H, d_v] float32 (written)
+ * dims: batch = num_seqs = N, seqlen = 1.
+ */
+int dr_decode_step(const void* q, const void* k, const void* v, const float* alpha,
+                   const float* erase, const float* write, int variant,
+                   float* S, float* o, const dr_dims* dims, hipStream_t stream);
+
+/* Static description of a status code. Never NULL. */
+const char* dr_status_string(int status);
+
+/* Message for the last failing call on this thread ("" if none). Valid until the
+ * next library call on the same thread. */
+const char* dr_last_error(void);
+
+/* Library ABI version: major * 10000 + minor * 100 + patch. */
+int dr_version(void);
+
+/*
+ * Launch shape the prefill would use for `dims` (for tests and profiling):
+ * chunk length, value columns per workgroup, and the number of workgroups.
+ * Returns DR_OK or an argument error.
+ */
+int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t* dv_block,
+                      int64_t* workgroups);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DELTARULE_H */

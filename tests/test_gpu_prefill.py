@@ -1,0 +1,181 @@
+"""GPU parity of the chunkwise prefill (dr_chunk_fwd) against the fp64 oracle.
+
+Tolerance (max |err| / RMS(ref), per tensor, for o and S_T separately): 1e-4 for fp32
+inputs, 1e-2 for bf16 inputs with fp32 state."""
+import numpy as np
+import pytest
+import torch
+
+import delta_rule_linear_chunked_amd as drl
+import oracle
+import synth
+from gpu_util import TOL, gpu_pairs, oracle_prefill, prefill_inputs, run_prefill, to_dev
+
+pytestmark = pytest.mark.gpu
+
+RECIPE = {"kda": "kda", "rda": "rda", "gdn2": "gdn2", "ckda": "ckda"}
+
+
+def check(wl, tag="", pairs=None):
+    o, S_T = run_prefill(wl)
+    tol = TOL[wl.in_dtype]
+    if pairs is None:
+        o_ref, S_ref = oracle_prefill(wl)
+        eo, es = oracle.rel_err(o, o_ref), oracle.rel_err(S_T, S_ref)
+    else:
+        o_ref, S_ref = oracle_prefill(wl, pairs)
+        o_g, S_g = gpu_pairs(wl, o, S_T, pairs)
+        eo = oracle.rel_err(np.concatenate(o_g), np.concatenate(o_ref))
+        es = oracle.rel_err(S_g, S_ref)
+    print(f"[prefill {wl.name} {tag}] err o={eo:.3e} S_T={es:.3e} tol={tol}", flush=True)
+    assert eo <= tol and es <= tol, (eo, es)
+    return eo, es
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["kda", "rda", "gdn2", "ckda"])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (32, 64), (64, 32), (128, 128), (128, 16)])
+def test_small_all_variants(variant, dk, dv, in_dtype):
+    wl = synth.make_prefill(RECIPE[variant], 2, 150, 2, dk, dv, in_dtype=in_dtype,
+                            seed=hash((variant, dk, dv, in_dtype)) % 2**31)
+    check(wl)
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 128, 200])
+def test_ragged_lengths(T):
+    wl = synth.make_prefill("ckda", 2, T, 3, 64, 64, in_dtype="bf16", seed=T)
+    check(wl, f"T={T}")
+
+
+def test_config1_kda_tiny_fp32():
+    check(synth.preset("kda_tiny"))
+
+
+def test_packed_varlen_with_empty_and_short_sequences():
+    lens = [70, 0, 1, 64, 129, 5, 0, 200]
+    for recipe in ("rda", "gdn2", "ckda"):
+        wl = synth.make_prefill(recipe, 1, 0, 3, 128, 64, in_dtype="bf16", seed=5, lengths=lens)
+        o, S_T = run_prefill(wl)
+        check(wl, "varlen")
+        # an empty sequence returns its initial state untouched
+        assert np.array_equal(S_T[1], wl.S0[1].astype(np.float64))
+
+
+def test_exact_zero_and_unit_gates():
+    """alpha = 0 exactly, alpha = +-1 and beta = 2 (Complex KDA ranges); zeros force the
+    exact running-product path for the block's diagonal tile."""
+    wl = synth.make_prefill("ckda", 2, 300, 2, 128, 128, in_dtype="bf16", seed=77)
+    rng = np.random.default_rng(1)
+    a = wl.alpha.copy()
+    a[rng.random(a.shape) < 0.003] = 0.0
+    a[:, 40:42] = 0.0            # whole tokens with every channel at zero
+    a[:, 100:116] = -1.0         # a full block of sign flips
+    wl.alpha = a
+    wl.erase[:, 50:60] = 2.0
+    check(wl, "zeros")
+    wl32 = synth.make_prefill("ckda", 1, 130, 2, 32, 32, in_dtype="f32", seed=78)
+    wl32.alpha[:, ::7] = 0.0
+    check(wl32, "zeros-fp32")
+
+
+def test_tiny_gates_underflow_gracefully():
+    wl = synth.make_prefill("kda", 1, 200, 2, 64, 64, in_dtype="bf16", seed=79)
+    wl.alpha[:, 20:40] = 1e-20   # products underflow inside a block
+    check(wl, "tiny")
+
+
+def test_kda_is_rda_with_equal_gates_bitwise():
+    wl = synth.make_prefill("kda", 2, 190, 2, 128, 128, in_dtype="bf16", seed=80)
+    a = prefill_inputs(wl)
+    o1, s1 = drl.chunk_fwd(**a)
+    a2 = dict(a, variant="rda", write=a["erase"].clone())
+    o2, s2 = drl.chunk_fwd(**a2)
+    a3 = dict(a, variant="ckda")
+    o3, s3 = drl.chunk_fwd(**a3)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    assert torch.equal(o1, o3) and torch.equal(s1, s3)
+
+
+def test_gdn2_uniform_gates_match_rda():
+    wl = synth.make_prefill("rda", 2, 150, 2, 64, 64, in_dtype="bf16", seed=81)
+    a = prefill_inputs(wl)
+    o1, s1 = drl.chunk_fwd(**a)
+    b = a["erase"][..., None].expand(*a["erase"].shape, 64).contiguous()
+    w = a["write"][..., None].expand(*a["write"].shape, 64).contiguous()
+    o2, s2 = drl.chunk_fwd(**dict(a, variant="gdn2", erase=b, write=w))
+    torch.cuda.synchronize()
+    assert oracle.rel_err(o2.cpu().numpy(), o1.cpu().numpy()) < 1e-5
+    assert oracle.rel_err(s2.cpu().numpy(), s1.cpu().numpy()) < 1e-5
+
+
+def test_deterministic():
+    wl = synth.make_prefill("gdn2", 2, 300, 4, 128, 128, in_dtype="bf16", seed=82)
+    a = prefill_inputs(wl)
+    o1, s1 = drl.chunk_fwd(**a)
+    o2, s2 = drl.chunk_fwd(**a)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+
+
+def test_state_in_place_and_optional_states():
+    wl = synth.make_prefill("rda", 2, 100, 2, 64, 64, in_dtype="bf16", seed=83)
+    a = prefill_inputs(wl)
+    o_ref, S_ref = drl.chunk_fwd(**a)
+    S = a["S0"].clone()
+    o = torch.empty_like(o_ref)
+    drl.dr_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["erase"], a["write"], "rda", S, None, o, S)
+    torch.cuda.synchronize()
+    assert torch.equal(S, S_ref) and torch.equal(o, o_ref)
+    # no initial state == zero initial state; no final state requested
+    o0, _ = drl.chunk_fwd(**dict(a, S0=None), output_final_state=False)
+    oz, _ = drl.chunk_fwd(**dict(a, S0=torch.zeros_like(a["S0"])))
+    torch.cuda.synchronize()
+    assert torch.equal(o0, oz)
+
+
+def test_split_and_resume():
+    """prefill(T) equals prefill(T1) followed by prefill(T - T1) started from its S_T."""
+    wl = synth.make_prefill("ckda", 2, 250, 2, 128, 64, in_dtype="bf16", seed=84)
+    a = prefill_inputs(wl)
+    o, S = drl.chunk_fwd(**a)
+    sl = lambda x, s: None if x is None else x[:, s].contiguous()  # noqa: E731
+    p1 = {**a, **{key: sl(a[key], slice(0, 90)) for key in ("q", "k", "v", "alpha", "erase", "write")}}
+    o1, S1 = drl.chunk_fwd(**p1)
+    p2 = {**a, **{key: sl(a[key], slice(90, 250)) for key in ("q", "k", "v", "alpha", "erase", "write")}}
+    p2["S0"] = S1
+    o2, S2 = drl.chunk_fwd(**p2)
+    torch.cuda.synchronize()
+    assert oracle.rel_err(torch.cat([o1, o2], 1).cpu().numpy(), o.cpu().numpy()) < 1e-4
+    assert oracle.rel_err(S2.cpu().numpy(), S.cpu().numpy()) < 1e-4
+
+
+def test_zero_length_batch_copies_state():
+    wl = synth.make_prefill("kda", 3, 0, 2, 64, 64, in_dtype="bf16", seed=85)
+    o, S_T = run_prefill(wl)
+    assert o.shape == (3, 0, 2, 64)
+    assert np.array_equal(S_T, wl.S0.astype(np.float64))
+
+
+# ----------------------------------------------------------------- the measured workloads, scaled
+@pytest.mark.parametrize("name,over", [
+    ("kda_prefill", dict(B=2, T=700, H=3)),
+    ("ckda_long", dict(B=1, T=1500, H=2)),
+    ("rda_varlen", dict(total=3000, nseq=5, lo=100, hi=1200, H=2)),
+    ("gdn2_varlen", dict(total=3000, nseq=5, lo=100, hi=1200, H=2)),
+])
+def test_scaled_workloads_full_compare(name, over):
+    check(synth.preset(name, **over), "scaled")
+
+
+# ----------------------------------------------------------------- full sizes, sampled (sequence, head) pairs
+@pytest.mark.parametrize("name", ["kda_prefill", "rda_varlen", "gdn2_varlen", "ckda_long"])
+def test_full_size_sampled_pairs(name):
+    wl = synth.preset(name)
+    rng = np.random.default_rng(99)
+    N, H = wl.num_seqs, wl.q.shape[2]
+    idx = rng.choice(N * H, size=3, replace=False)
+    pairs = [(int(i) // H, int(i) % H) for i in idx]
+    if wl.cu_seqlens is not None:   # always include the longest sequence
+        pairs[0] = (int(np.argmax(np.diff(wl.cu_seqlens))), pairs[0][1])
+    check(wl, "full-sampled", pairs=pairs)
