@@ -28,7 +28,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Shared checks of the variant's gate pointers. scalar_lead / vector shapes are implied by the
 // variant; the library cannot see extents of device buffers, so it checks presence only.
-int check_variant(int variant, const float* erase, const float* write, bool* vec) {
+int check_variant(int variant, const float* erase, const float* write, bool has_tokens, bool* vec) {
   switch (variant) {
     case DR_KDA:
     case DR_CKDA:
@@ -38,17 +38,19 @@ int check_variant(int variant, const float* erase, const float* write, bool* vec
       *vec = false;
       break;
     case DR_RDA:
-      if (write == nullptr) return fail(DR_ERR_VARIANT, "variant RDA needs a per-head `write` gate");
+      if (write == nullptr && has_tokens)
+        return fail(DR_ERR_VARIANT, "variant RDA needs a per-head `write` gate");
       *vec = false;
       break;
     case DR_GDN2:
-      if (write == nullptr) return fail(DR_ERR_VARIANT, "variant GDN-2 needs a channel-wise `write` gate");
+      if (write == nullptr && has_tokens)
+        return fail(DR_ERR_VARIANT, "variant GDN-2 needs a channel-wise `write` gate");
       *vec = true;
       break;
     default:
       return fail(DR_ERR_VARIANT, "unknown variant %d", variant);
   }
-  if (erase == nullptr) return fail(DR_ERR_NULL, "`erase` gate is NULL");
+  (void)erase;  // presence is checked with the other token pointers when there are tokens
   return DR_OK;
 }
 
@@ -109,7 +111,7 @@ static int prefill_checks(const dr_dims* dims, int variant, const float* erase, 
                           const int32_t* cu_seqlens, bool* vec) {
   int st = check_dims_common(dims);
   if (st) return st;
-  st = check_variant(variant, erase, write, vec);
+  st = check_variant(variant, erase, write, dims->batch * dims->seqlen > 0, vec);
   if (st) return st;
   if (cu_seqlens != nullptr) {
     if (dims->batch != 1)
@@ -181,7 +183,7 @@ int dr_decode_step(const void* q, const void* k, const void* v, const float* alp
   int st = check_dims_common(dims);
   if (st) return st;
   bool vec = false;
-  st = check_variant(variant, erase, write, &vec);
+  st = check_variant(variant, erase, write, dims->num_seqs > 0, &vec);
   if (st) return st;
   if (dims->num_seqs != dims->batch)
     return fail(DR_ERR_SHAPE, "decode: num_seqs (%lld) must equal batch (%lld)",
