@@ -7,6 +7,7 @@
 namespace dr {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Kernel parameter block. Pointers are device memory; sizes are element counts.
@@ -39,6 +40,28 @@ __device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
   x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
   x[4] = b[0]; x[5] = b[1]; x[6] = b[2]; x[7] = b[3];
 }
+__device__ __forceinline__ void load4(const float* p, float (&x)[4]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+  x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
+}
+__device__ __forceinline__ void store4(float* p, const f32x4& a) { *reinterpret_cast<f32x4*>(p) = a; }
+
+// Eight raw input elements kept in their storage type (prefetch registers).
+template <typename InT> struct Raw8;
+template <> struct Raw8<__bf16> {
+  bf16x8 v;
+  __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
+  __device__ __forceinline__ float get(int j) const { return (float)v[j]; }
+};
+template <> struct Raw8<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = *reinterpret_cast<const f32x4*>(p);
+    b = *reinterpret_cast<const f32x4*>(p + 4);
+  }
+  __device__ __forceinline__ float get(int j) const { return j < 4 ? a[j] : b[j - 4]; }
+};
+
 __device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
   const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
@@ -55,15 +78,30 @@ __device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
 // the sum over all four lane groups and eight items covers the slice exactly
 // once.
 //
+// A 16-deep variant (mma16) takes four items per lane, reduction indices
+// 4*(l/16) + j: the same assignment as the accumulator's rows, so an
+// accumulator can be fed back as the B operand of the next product unchanged.
+//
 // PolF32: eight v_mfma_f32_16x16x4_f32, instruction j taking item j of every
-//         lane group (exact fp32 products).
+//         lane group (exact fp32 products); four for mma16.
 // PolBF3: operands split x = hi + lo (hi = bf16(x), lo = bf16(x - hi)) and
 //         hi*hi + hi*lo + lo*hi accumulated with v_mfma_f32_16x16x32_bf16;
 //         the dropped lo*lo term and the rounding of lo leave a relative error
-//         of about 2^-16 per product.
+//         of about 2^-16 per product. mma16 uses v_mfma_f32_16x16x16_bf16.
 // ---------------------------------------------------------------------------
 struct PolF32 {
   struct Frag { float v[8]; };
+  struct Frag4 { float v[4]; };
+  static __device__ __forceinline__ Frag4 make4(const float (&x)[4]) {
+    Frag4 f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.v[j] = x[j];
+    return f;
+  }
+  static __device__ __forceinline__ void mma16(f32x4& acc, const Frag4& a, const Frag4& b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+  }
   static __device__ __forceinline__ Frag make(const float (&x)[8]) {
     Frag f;
 #pragma unroll
@@ -84,6 +122,22 @@ struct PolF32 {
 
 struct PolBF3 {
   struct Frag { bf16x8 hi, lo; };
+  struct Frag4 { bf16x4 hi, lo; };
+  static __device__ __forceinline__ Frag4 make4(const float (&x)[4]) {
+    Frag4 f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const __bf16 h = (__bf16)x[j];
+      f.hi[j] = h;
+      f.lo[j] = (__bf16)(x[j] - (float)h);
+    }
+    return f;
+  }
+  static __device__ __forceinline__ void mma16(f32x4& acc, const Frag4& a, const Frag4& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
+  }
   static __device__ __forceinline__ Frag make(const float (&x)[8]) {
     Frag f;
 #pragma unroll
@@ -122,6 +176,7 @@ __device__ __forceinline__ float dpp_or(float old, float x) {
 }
 constexpr int ROW_SHL1 = 0x101, ROW_SHL2 = 0x102, ROW_SHL4 = 0x104, ROW_SHL8 = 0x108;
 constexpr int ROW_SHR1 = 0x111, ROW_SHR2 = 0x112, ROW_SHR4 = 0x114, ROW_SHR8 = 0x118;
+constexpr int ROW_BCAST15 = 0x15F;  // gfx950 row_newbcast:15: every lane reads lane 15 of its row
 
 // Inclusive prefix product over lanes 0..r of the row (lane r receives x_0 * ... * x_r).
 __device__ __forceinline__ float row_prefix_prod(float x) {
@@ -131,6 +186,27 @@ __device__ __forceinline__ float row_prefix_prod(float x) {
   x *= dpp_or<ROW_SHR8>(1.f, x);
   return x;
 }
+// Eight independent inclusive prefix products across the row, one VOP2 DPP multiply
+// per element and step: v_mul_f32_dpp x, x, x row_shr:d writes x_{r-d} * x_r, and the
+// lanes r < d, whose source lies outside the row, are not written (bound_ctrl off), so
+// they keep x_r. The eight chains are interleaved, so each DPP read comes 8 VALU
+// instructions after the write it depends on; the s_nop pairs cover the instructions
+// just before and after the block. Needs every lane of the wave active.
+__device__ __forceinline__ void row_prefix_prod8(float (&x)[8]) {
+#define DR_STEP(D)                                                           \
+  "v_mul_f32_dpp %0, %0, %0 row_shr:" #D " row_mask:0xf bank_mask:0xf\n"    \
+  "v_mul_f32_dpp %1, %1, %1 row_shr:" #D " row_mask:0xf bank_mask:0xf\n"    \
+  "v_mul_f32_dpp %2, %2, %2 row_shr:" #D " row_mask:0xf bank_mask:0xf\n"    \
+  "v_mul_f32_dpp %3, %3, %3 row_shr:" #D " row_mask:0xf bank_mask:0xf\n"    \
+  "v_mul_f32_dpp %4, %4, %4 row_shr:" #D " row_mask:0xf bank_mask:0xf\n"    \
+  "v_mul_f32_dpp %5, %5, %5 row_shr:" #D " row_mask:0xf bank_mask:0xf\n"    \
+  "v_mul_f32_dpp %6, %6, %6 row_shr:" #D " row_mask:0xf bank_mask:0xf\n"    \
+  "v_mul_f32_dpp %7, %7, %7 row_shr:" #D " row_mask:0xf bank_mask:0xf\n"
+  asm("s_nop 1\n" DR_STEP(1) DR_STEP(2) DR_STEP(4) DR_STEP(8) "s_nop 1\n"
+      : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]));
+#undef DR_STEP
+}
+
 // Exclusive suffix product (lane r receives x_{r+1} * ... * x_15; lane 15 receives 1).
 __device__ __forceinline__ float row_suffix_prod_excl(float x) {
   x *= dpp_or<ROW_SHL1>(1.f, x);

@@ -48,27 +48,27 @@ template <int DK, int DVB>
 struct PrefillSmem {
   float kg[CH][DK + 4];     // k_s . g_s
   float tot[NBLK][DK];      // t_J
-  float A[CH][LDT];         // strictly lower A
-  float At[CH][LDT];        // T_II A_IK for K < I
-  float Ti[CH][LDT];        // T = (I + A)^-1, lower blocks; upper blocks stay zero
-  float P[CH][LDT];         // lower P; upper blocks stay zero
+  float A[CH][LDT];         // A: strictly lower diagonal blocks and the blocks below them
+  float P[CH][LDT];         // P: lower blocks; blocks above the diagonal stay zero
+  float Td[NBLK][16][20];   // (I + A_JJ)^-1 of each diagonal block
   float S[DVB][DK + 4];     // state block, transposed: [value column][key channel]
-  float R[DVB][LDT];        // (M - Utilde S0)^T
   float D[DVB][LDT];        // delta^T
 };
 
-template <int N>
-__device__ __forceinline__ void mul8(float (&x)[8], const float* p) {
-  float t[8];
-  load8(p, t);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) x[j] *= t[j];
+// Orders this wave's LDS writes before its later LDS reads by other lanes of the
+// same wave (LDS executes a wave's instructions in order; this stops the compiler
+// from reordering across the point).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
 template <int DKR, int DVB, typename InT, bool VEC>
 __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(const Params p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
+  using Frag4 = typename Pol::Frag4;
   constexpr int DK = DKR < 32 ? 32 : DKR;  // key width padded to the 32-deep MFMA slice
   constexpr int KS = DK / 32;              // reduction slices over key channels
   constexpr int NCT = DVB / 16;            // 16-wide value-column tiles
@@ -93,141 +93,172 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(const Params p) {
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
-  const int I = w;  // this wave's 16-token block
   const InT* qp = static_cast<const InT*>(p.q);
   const InT* kp = static_cast<const InT*>(p.k);
   const InT* vp = static_cast<const InT*>(p.v);
   const int DV = p.DV;
 
-  // ---- state block in, upper tiles of P and T zeroed
-  for (int i = tid; i < CH * LDT; i += 256) {
-    (&sm.P[0][0])[i] = 0.f;
-    (&sm.Ti[0][0])[i] = 0.f;
-  }
+  // ---- state block in; P's upper blocks zeroed once (never written)
+  for (int i = tid; i < CH * LDT; i += 256) (&sm.P[0][0])[i] = 0.f;
   for (int i = tid; i < DK * DVB; i += 256) {
     const int ch = i / DVB, c = i % DVB;
     float s0 = 0.f;
     if (p.S0 && ch < DKR) s0 = p.S0[(((int64_t)n * H + h) * DKR + ch) * DV + dv0 + c];
     sm.S[c][ch] = s0;
   }
+
+  // ---- prefetch registers: this lane's token row of the next chunk (lane layout of the
+  // 32-deep fragments: row r of block w, channels 32*ks + 8*g + j), and the value/write
+  // entries it needs in accumulator layout (rows 4*g + i of block w, column 16*ct + r).
+  Raw8<InT> pk[KS], pq[KS];
+  float pa[KS][8], pb[VEC ? KS : 1][8];
+  float pe = 0.f;
+  InT pv[NCT][4];  // raw: converting at load time would make the load synchronous
+  float pw[VEC ? NCT : 1][4];
+  auto prefetch = [&](int64_t c0n) {
+    const int64_t last = bos + len - 1;  // a valid token: rows past the end are clamped, then masked
+    int64_t tk = bos + c0n + 16 * w + r;
+    tk = tk > last ? last : tk;
+    const int64_t th = tk * H + h;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = (32 * ks + 8 * g) < DKR ? (32 * ks + 8 * g) : 0;
+      pk[ks].load(kp + th * DKR + ch0);
+      pq[ks].load(qp + th * DKR + ch0);
+      load8(p.alpha + th * DKR + ch0, pa[ks]);
+      if constexpr (VEC) load8(p.erase + th * DKR + ch0, pb[ks]);
+    }
+    if constexpr (!VEC) pe = p.erase[th];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t tv = bos + c0n + 16 * w + 4 * g + i;
+      tv = tv > last ? last : tv;
+      const int64_t thv = tv * H + h;
+      if constexpr (!VEC) pw[0][i] = p.write[thv];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int col = dv0 + 16 * ct + r;
+        pv[ct][i] = vp[thv * DV + col];
+        if constexpr (VEC) pw[ct][i] = p.write[thv * DV + col];
+      }
+    }
+  };
+  if (len > 0) prefetch(0);
   __syncthreads();
 
   for (int64_t c0 = 0; c0 < len; c0 += CH) {
-    const int nrows = (int)((len - c0) < CH ? (len - c0) : CH);
-    const int row = 16 * I + r;
-    const bool valid = row < nrows;
-    const int64_t th = (bos + c0 + row) * H + h;  // token-head index of this lane's row
+    const int row = 16 * w + r;
+    const bool valid = c0 + row < len;
 
-    // ================= gate preparation and operands of this wave's rows
-    Frag UF[KS], QF[KS], KD[KS];
-    bool ok = true;
+    // ================= gate preparation, operands and the diagonal tiles of block w
+    Frag UF[KS], QF[KS];
+    float mv[NCT][4];  // write vectors m of rows 4g+i (accumulator layout)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bool vi = c0 + 16 * w + 4 * g + i < len;
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        mv[ct][i] = vi ? pw[VEC ? ct : 0][i] * (float)pv[ct][i] : 0.f;
+        // Materialise here: if the product sinks past the next prefetch, the old and new
+        // prefetch registers overlap and the compiler copies them with waiting moves.
+        asm volatile("" : "+v"(mv[ct][i]));
+      }
+    }
     {
-      const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
+      bool ok = true;
+      f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f}, pd = ad;
+      float fr[KS][8], rf[KS][8];  // f_r and 1 / f_r of this lane's row
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int ch0 = 32 * ks + 8 * g;
-        float a8[8], k8[8], q8[8], b8[8];
-        if (valid && ch0 < DKR) {
-          load8(kp + th * DKR + ch0, k8);
-          load8(qp + th * DKR + ch0, q8);
-          load8(p.alpha + th * DKR + ch0, a8);
-          if (VEC) load8(p.erase + th * DKR + ch0, b8);
-        } else {
+        const bool live = valid && ch0 < DKR;
+        float uf[8], qf[8], kd[8], f8[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) { k8[j] = 0.f; q8[j] = 0.f; a8[j] = 1.f; b8[j] = 0.f; }
-        }
-        float uf[8], qf[8], kd[8], kgv[8];
+        for (int j = 0; j < 8; ++j) f8[j] = live ? pa[ks][j] : 1.f;
+        row_prefix_prod8(f8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float f = row_prefix_prod(a8[j]);
-          const float gx = row_suffix_prod_excl(a8[j]);
-          const float u = (VEC ? b8[j] : esc) * k8[j];
+          const float kk = live ? pk[ks].get(j) : 0.f;
+          const float qq = live ? pq[ks].get(j) : 0.f;
+          const float ee = VEC ? pb[VEC ? ks : 0][j] : pe;
+          const float f = f8[j];
           const float af = fabsf(f);
           ok = ok && (af >= FAST_LO) && (af <= FAST_HI);
-          uf[j] = u * f;
-          qf[j] = q8[j] * f;
-          kd[j] = k8[j] * __builtin_amdgcn_rcpf(f);
-          kgv[j] = k8[j] * gx;
-          if (r == 15) sm.tot[I][ch0 + j] = f;
+          fr[ks][j] = f;
+          rf[ks][j] = __builtin_amdgcn_rcpf(f);
+          uf[j] = ee * kk * f;
+          qf[j] = qq * f;
+          kd[j] = kk * rf[ks][j];
         }
-        *reinterpret_cast<f32x4*>(&sm.kg[row][ch0]) = f32x4{kgv[0], kgv[1], kgv[2], kgv[3]};
-        *reinterpret_cast<f32x4*>(&sm.kg[row][ch0 + 4]) = f32x4{kgv[4], kgv[5], kgv[6], kgv[7]};
+        if (r == 15) {
+          store4(&sm.tot[w][ch0], f32x4{fr[ks][0], fr[ks][1], fr[ks][2], fr[ks][3]});
+          store4(&sm.tot[w][ch0 + 4], f32x4{fr[ks][4], fr[ks][5], fr[ks][6], fr[ks][7]});
+        }
         UF[ks] = Pol::make(uf);
         QF[ks] = Pol::make(qf);
-        KD[ks] = Pol::make(kd);
+        const Frag KD = Pol::make(kd);
+        Pol::mma(ad, UF[ks], KD);
+        Pol::mma(pd, QF[ks], KD);
       }
-    }
-    const bool fast = __all(ok);
-    __syncthreads();
-
-    // ================= A and P tiles of block row I
-    {
-      f32x4 accA[NBLK], accP[NBLK];
+      const bool fast = __all(ok);
+      // k_s . g_s, g_s = prod of alpha over s+1 .. block end: t / f_s while every |f| is in
+      // range, else an exact suffix scan.
 #pragma unroll
-      for (int J = 0; J < NBLK; ++J) { accA[J] = f32x4{0.f, 0.f, 0.f, 0.f}; accP[J] = accA[J]; }
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch0 = 32 * ks + 8 * g;
+        const bool live = valid && ch0 < DKR;
+        float kgv[8];
+        if (fast) {
 #pragma unroll
-      for (int J = 0; J < NBLK - 1; ++J) {
-        if (J < I) {
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const int ch0 = 32 * ks + 8 * g;
-            float x[8];
-            load8(&sm.kg[16 * J + r][ch0], x);
-            for (int Jp = J + 1; Jp < I; ++Jp) mul8<8>(x, &sm.tot[Jp][ch0]);
-            const Frag B = Pol::make(x);
-            Pol::mma(accA[J], UF[ks], B);
-            Pol::mma(accP[J], QF[ks], B);
+          for (int j = 0; j < 8; ++j) {
+            const float t = dpp_or<ROW_BCAST15>(0.f, fr[ks][j]);
+            kgv[j] = (live ? pk[ks].get(j) : 0.f) * (t * rf[ks][j]);
           }
+        } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sm.A[16 * I + 4 * g + i][16 * J + r] = accA[J][i];
-            sm.P[16 * I + 4 * g + i][16 * J + r] = accP[J][i];
+          for (int j = 0; j < 8; ++j) {
+            const float a = live ? pa[ks][j] : 1.f;
+            kgv[j] = (live ? pk[ks].get(j) : 0.f) * row_suffix_prod_excl(a);
           }
         }
+        store4(&sm.kg[row][ch0], f32x4{kgv[0], kgv[1], kgv[2], kgv[3]});
+        store4(&sm.kg[row][ch0 + 4], f32x4{kgv[4], kgv[5], kgv[6], kgv[7]});
       }
       if (fast) {
-        f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f}, pd = ad;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          Pol::mma(ad, UF[ks], KD[ks]);
-          Pol::mma(pd, QF[ks], KD[ks]);
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = 4 * g + i;  // row within the block; r is the column
-          sm.A[16 * I + rr][16 * I + r] = (r < rr) ? ad[i] : 0.f;
-          sm.P[16 * I + rr][16 * I + r] = (r <= rr) ? pd[i] : 0.f;
+          sm.A[16 * w + rr][16 * w + r] = (r < rr) ? ad[i] : 0.f;
+          sm.P[16 * w + rr][16 * w + r] = (r <= rr) ? pd[i] : 0.f;
         }
       } else {
-        // Diagonal tile from running products of the gates (exact for any gate value).
-        const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
-        float a2[KS][8], k2[KS][8], q2[KS][8], u2[KS][8];
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int ch0 = 32 * ks + 8 * g;
-          float b8[8];
-          if (valid && ch0 < DKR) {
-            load8(kp + th * DKR + ch0, k2[ks]);
-            load8(qp + th * DKR + ch0, q2[ks]);
-            load8(p.alpha + th * DKR + ch0, a2[ks]);
-            if (VEC) load8(p.erase + th * DKR + ch0, b8);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) { k2[ks][j] = 0.f; q2[ks][j] = 0.f; a2[ks][j] = 1.f; b8[j] = 0.f; }
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) u2[ks][j] = (VEC ? b8[j] : esc) * k2[ks][j];
-        }
+        // Diagonal tile from running products of the gates (exact for any gate value,
+        // including zero), reloading this lane's row of the chunk.
+        const int64_t last = bos + len - 1;
+        int64_t tk = bos + c0 + row;
+        tk = tk > last ? last : tk;
+        const int64_t th = tk * H + h;
         for (int s = 0; s < 16; ++s) {
           float ap = 0.f, pp = 0.f;
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
+            const int ch0 = 32 * ks + 8 * g;
+            const bool live = valid && ch0 < DKR;
+            float a2[8], k2[8], q2[8], b2[8];
+            load8(p.alpha + th * DKR + (live ? ch0 : 0), a2);
+            load8(kp + th * DKR + (live ? ch0 : 0), k2);
+            load8(qp + th * DKR + (live ? ch0 : 0), q2);
+            if constexpr (VEC) load8(p.erase + th * DKR + (live ? ch0 : 0), b2);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-              const float rho = row_prefix_prod(r > s ? a2[ks][j] : 1.f);
-              const float kv = __shfl(k2[ks][j], 16 * g + s);
-              ap = fmaf(u2[ks][j] * kv, rho, ap);
-              pp = fmaf(q2[ks][j] * kv, rho, pp);
+              const float a = live ? a2[j] : 1.f;
+              const float kk = live ? k2[j] : 0.f;
+              const float qq = live ? q2[j] : 0.f;
+              const float uu = (VEC ? b2[j] : pe) * kk;
+              const float rho = row_prefix_prod(r > s ? a : 1.f);
+              const float kv = __shfl(kk, 16 * g + s);
+              ap = fmaf(uu * kv, rho, ap);
+              pp = fmaf(qq * kv, rho, pp);
             }
           }
           ap += __shfl_xor(ap, 16);
@@ -235,158 +266,144 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(const Params p) {
           pp += __shfl_xor(pp, 16);
           pp += __shfl_xor(pp, 32);
           if (g == 0) {
-            sm.A[16 * I + r][16 * I + s] = (r > s) ? ap : 0.f;
-            sm.P[16 * I + r][16 * I + s] = (r >= s) ? pp : 0.f;
+            sm.A[16 * w + r][16 * w + s] = (r > s) ? ap : 0.f;
+            sm.P[16 * w + r][16 * w + s] = (r >= s) ? pp : 0.f;
           }
         }
       }
     }
-    __syncthreads();
-
-    // ================= T = (I + A)^-1
-    // (a) diagonal blocks by forward substitution, one lane per column
+    wave_lds_sync();
+    // (I + A_ww)^-1 by forward substitution, one lane per column
     if (l < 16) {
       float t[16];
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
+        float ar[16];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) load4(&sm.A[16 * w + rr][16 * w + 4 * q4], *reinterpret_cast<float(*)[4]>(&ar[4 * q4]));
         float acc = (rr == l) ? 1.f : 0.f;
 #pragma unroll
-        for (int s = 0; s < rr; ++s) acc = fmaf(-sm.A[16 * I + rr][16 * I + s], t[s], acc);
+        for (int s = 0; s < rr; ++s) acc = fmaf(-ar[s], t[s], acc);
         t[rr] = acc;
       }
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sm.Ti[16 * I + rr][16 * I + l] = t[rr];
+      for (int rr = 0; rr < 16; ++rr) sm.Td[w][rr][l] = t[rr];
     }
+    // Unconditional (rows past the end are clamped): a conditional prefetch makes the
+    // compiler copy the in-flight registers at the loop latch, which waits for the loads.
+    prefetch(c0 + CH);
     __syncthreads();
-    // (b) At_IK = T_II A_IK
-    {
-      float x[8];
-      if (g < 2) load8(&sm.Ti[16 * I + r][16 * I + 8 * g], x);
-      else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = 0.f;
-      }
-      const Frag Tii = Pol::make(x);
-#pragma unroll
-      for (int K = 0; K < NBLK - 1; ++K) {
-        if (K < I) {
-          float y[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) y[j] = (g < 2) ? sm.A[16 * I + 8 * g + j][16 * K + r] : 0.f;
-          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-          Pol::mma(acc, Tii, Pol::make(y));
-#pragma unroll
-          for (int i = 0; i < 4; ++i) sm.At[16 * I + 4 * g + i][16 * K + r] = acc[i];
-        }
-      }
-    }
-    __syncthreads();
-    // (c) T_IJ = -sum_{K=J..I-1} At_IK T_KJ, by increasing distance I - J
-#pragma unroll
-    for (int d = 1; d < NBLK; ++d) {
-      if (I >= d) {
-        const int J = I - d;
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          if (st < (d + 1) / 2) {
-            const int k0 = 16 * J + 32 * st + 8 * g;
-            float a8[8], b8[8];
-            if (k0 < 16 * I) {
-              load8(&sm.At[16 * I + r][k0], a8);
-#pragma unroll
-              for (int j = 0; j < 8; ++j) b8[j] = sm.Ti[k0 + j][16 * J + r];
-            } else {
-#pragma unroll
-              for (int j = 0; j < 8; ++j) { a8[j] = 0.f; b8[j] = 0.f; }
-            }
-            Pol::mma(acc, Pol::make(a8), Pol::make(b8));
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.Ti[16 * I + 4 * g + i][16 * J + r] = -acc[i];
-      }
-      __syncthreads();
-    }
 
-    // ================= X = Utilde S0, Y = Qtilde S0, R = M - X   (block row I)
-    f32x4 accY[NCT];
+    // ================= off-diagonal tiles of block row w, and X = Utilde S0, Y = Qtilde S0
+    f32x4 accY[NCT], Rm[NCT];
     {
-      f32x4 accX[NCT];
+      f32x4 accA[NBLK - 1], accP[NBLK - 1], accX[NCT];
+#pragma unroll
+      for (int J = 0; J < NBLK - 1; ++J) { accA[J] = f32x4{0.f, 0.f, 0.f, 0.f}; accP[J] = accA[J]; }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) { accX[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; accY[ct] = accX[ct]; }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int ch0 = 32 * ks + 8 * g;
-        float pre[8];
+        // running product over earlier blocks: mid[J] = prod_{J<J'<w} t_J', pre = prod_{J<w} t_J
+        float run[8], mid[NBLK - 1][8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pre[j] = 1.f;
-        for (int Jp = 0; Jp < I; ++Jp) mul8<8>(pre, &sm.tot[Jp][ch0]);
+        for (int j = 0; j < 8; ++j) run[j] = 1.f;
+#pragma unroll
+        for (int J = NBLK - 2; J >= 0; --J) {
+          if (J < w) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) mid[J][j] = run[j];
+            float t8[8];
+            load8(&sm.tot[J][ch0], t8);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) run[j] *= t8[j];
+          }
+        }
+#pragma unroll
+        for (int J = 0; J < NBLK - 1; ++J) {
+          if (J < w) {
+            float x[8];
+            load8(&sm.kg[16 * J + r][ch0], x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[j] *= mid[J][j];
+            const Frag B = Pol::make(x);
+            Pol::mma(accA[J], UF[ks], B);
+            Pol::mma(accP[J], QF[ks], B);
+          }
+        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           float x[8];
           load8(&sm.S[16 * ct + r][ch0], x);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] *= pre[j];
+          for (int j = 0; j < 8; ++j) x[j] *= run[j];
           const Frag B = Pol::make(x);
           Pol::mma(accX[ct], UF[ks], B);
           Pol::mma(accY[ct], QF[ks], B);
         }
       }
 #pragma unroll
+      for (int J = 0; J < NBLK - 1; ++J) {
+        if (J < w) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sm.A[16 * w + 4 * g + i][16 * J + r] = accA[J][i];
+            sm.P[16 * w + 4 * g + i][16 * J + r] = accP[J][i];
+          }
+        }
+      }
+#pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const int col = dv0 + 16 * ct + r;
-        f32x4 rv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rw = 16 * I + 4 * g + i;
-          float m = 0.f;
-          if (rw < nrows) {
-            const int64_t tht = (bos + c0 + rw) * H + h;
-            const float wg = VEC ? p.write[tht * DV + col] : p.write[tht];
-            m = wg * ld_f32(vp + tht * DV + col);
-          }
-          rv[i] = m - accX[ct][i];
-        }
-        *reinterpret_cast<f32x4*>(&sm.R[16 * ct + r][16 * I + 4 * g]) = rv;
+        for (int i = 0; i < 4; ++i) Rm[ct][i] = mv[ct][i] - accX[ct][i];
       }
     }
     __syncthreads();
 
-    // ================= delta = T R   (block row I)
-    const int nst = (I + 2) / 2;
-    {
-      f32x4 accD[NCT];
+    // ================= delta by blocked forward substitution:
+    //   delta_J = (I + A_JJ)^-1 (R_J - sum_{K<J} A_JK delta_K)
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) accD[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int J = 0; J < NBLK; ++J) {
+      if (w == J) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (st < nst) {
-          const int k0 = 32 * st + 8 * g;
-          float a8[8];
-          load8(&sm.Ti[16 * I + r][k0], a8);
-          const Frag Af = Pol::make(a8);
+        for (int K = 0; K < NBLK - 1; ++K) {
+          if (K < J) {
+            float a4[4];
+            load4(&sm.A[16 * J + r][16 * K + 4 * g], a4);
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            float b8[8];
-            load8(&sm.R[16 * ct + r][k0], b8);
-            Pol::mma(accD[ct], Af, Pol::make(b8));
+            for (int j = 0; j < 4; ++j) a4[j] = -a4[j];
+            const Frag4 Af = Pol::make4(a4);
+#pragma unroll
+            for (int ct = 0; ct < NCT; ++ct) {
+              float b4[4];
+              load4(&sm.D[16 * ct + r][16 * K + 4 * g], b4);
+              Pol::mma16(Rm[ct], Af, Pol::make4(b4));
+            }
           }
         }
-      }
+        float t4[4];
+        load4(&sm.Td[J][r][4 * g], t4);
+        const Frag4 Tf = Pol::make4(t4);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        *reinterpret_cast<f32x4*>(&sm.D[16 * ct + r][16 * I + 4 * g]) = accD[ct];
+        for (int ct = 0; ct < NCT; ++ct) {
+          float b4[4] = {Rm[ct][0], Rm[ct][1], Rm[ct][2], Rm[ct][3]};
+          f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
+          Pol::mma16(d, Tf, Pol::make4(b4));
+          store4(&sm.D[16 * ct + r][16 * J + 4 * g], d);
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
 
-    // ================= O = Y + P delta   (block row I)
+    // ================= O = Y + P delta   (block row w)
+    const int nst = (w + 2) / 2;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       if (st < nst) {
         const int k0 = 32 * st + 8 * g;
         float a8[8];
-        load8(&sm.P[16 * I + r][k0], a8);
+        load8(&sm.P[16 * w + r][k0], a8);
         const Frag Af = Pol::make(a8);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
@@ -400,45 +417,55 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(const Params p) {
     for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int rw = 16 * I + 4 * g + i;
-        if (rw < nrows) p.o[((bos + c0 + rw) * H + h) * DV + dv0 + 16 * ct + r] = accY[ct][i];
+        const int rw = 16 * w + 4 * g + i;
+        if (c0 + rw < len) p.o[((bos + c0 + rw) * H + h) * DV + dv0 + 16 * ct + r] = accY[ct][i];
       }
     }
 
     // ================= S <- Diag(Gamma_C) S0 + Kbar^T delta   (key-channel tiles of this wave)
-    for (int rt = w; rt < DK / 16; rt += 4) {
-      const int chA = 16 * rt + r;
-      Frag KB[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int k0 = 32 * st + 8 * g;
-        const int blk = k0 >> 4;
-        float suf = 1.f;
-        for (int Jp = blk + 1; Jp < NBLK; ++Jp) suf *= sm.tot[Jp][chA];
-        float x[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[j] = sm.kg[k0 + j][chA] * suf;
-        KB[st] = Pol::make(x);
-      }
-      float gC[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int ch = 16 * rt + 4 * g + i;
-        gC[i] = sm.tot[0][ch] * sm.tot[1][ch] * sm.tot[2][ch] * sm.tot[3][ch];
-      }
+    {
+      Frag DF[NCT][2];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 s4 = *reinterpret_cast<const f32x4*>(&sm.S[16 * ct + r][16 * rt + 4 * g]);
-        f32x4 acc;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = gC[i] * s4[i];
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           float b8[8];
           load8(&sm.D[16 * ct + r][32 * st + 8 * g], b8);
-          Pol::mma(acc, KB[st], Pol::make(b8));
+          DF[ct][st] = Pol::make(b8);
         }
-        *reinterpret_cast<f32x4*>(&sm.S[16 * ct + r][16 * rt + 4 * g]) = acc;
+      }
+      for (int rt = w; rt < DK / 16; rt += 4) {
+        const int chA = 16 * rt + r;
+        float tA[NBLK];
+#pragma unroll
+        for (int J = 0; J < NBLK; ++J) tA[J] = sm.tot[J][chA];
+        Frag KB[2];
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const int k0 = 32 * st + 8 * g;
+          const int blk = 2 * st + (g >> 1);
+          float suf = 1.f;
+#pragma unroll
+          for (int J = 1; J < NBLK; ++J) suf *= (J > blk) ? tA[J] : 1.f;
+          float x[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] = sm.kg[k0 + j][chA] * suf;
+          KB[st] = Pol::make(x);
+        }
+        float tt[NBLK][4];
+#pragma unroll
+        for (int J = 0; J < NBLK; ++J) load4(&sm.tot[J][16 * rt + 4 * g], tt[J]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          float s4[4];
+          load4(&sm.S[16 * ct + r][16 * rt + 4 * g], s4);
+          f32x4 acc;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[i] = tt[0][i] * tt[1][i] * tt[2][i] * tt[3][i] * s4[i];
+#pragma unroll
+          for (int st = 0; st < 2; ++st) Pol::mma(acc, KB[st], DF[ct][st]);
+          store4(&sm.S[16 * ct + r][16 * rt + 4 * g], acc);
+        }
       }
     }
     __syncthreads();
