@@ -48,6 +48,37 @@ def decode_bytes(N, H, dk, dv, in_bytes=2, gate_bytes=4):
     return N * H * (8 * dk * dv + (2 * dk + dv) * in_bytes + 4 * dk + gate_bytes + 4 * dv)
 
 
+def kernel_source_digest():
+    """sha256 of the prefill kernel's sources: a stored traffic measurement is used only while
+    it matches the code that is being timed."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("prefill.hip", "common.hpp"):
+        with open(os.path.join(ROOT, "delta_rule_linear_chunked_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def copy_calibration(dev, mib=512, reps=5):
+    """A plain device-to-device copy of known size (the reference for HBM counters and the
+    measured copy bandwidth)."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.randn(n, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    return {"bytes_read_per_copy": n * 4, "bytes_written_per_copy": n * 4, "copies": reps + 1,
+            "ms_per_copy": ms, "copy_GBps": 2 * n * 4 / (ms * 1e-3) / 1e9}
+
+
 def cpu_baseline():
     """The fp64 oracle, as it is, on the whole prefill workload (4 sequences x 16 heads x
     4096 tokens, a few seconds of host time) on one host core."""
@@ -77,6 +108,8 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run the plain copy used to scale the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only; --gpus must be 1 (the path runs per GPU with no "
@@ -88,6 +121,9 @@ def main():
     import synth
 
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        print(json.dumps({"copy_calibration": copy_calibration(dev)}))
+        return
     drl.load_library()
 
     def t(x, bf16=False):
@@ -133,10 +169,11 @@ def main():
     plan = drl.chunk_fwd_plan(B, T, H, D, D)
 
     traffic = None
-    tfile = os.path.join(ROOT, "profiles", "prefill_kda_B4_T4096_H16_d128_traffic.json")
+    tfile = os.path.join(ROOT, "profiles", "chunk_fwd_kda_B4_T4096_H16_d128_traffic.json")
     if os.path.exists(tfile):
         tj = json.load(open(tfile))
-        traffic = tj.get("bytes_per_launch")
+        if tj.get("kernel_source_sha256") == kernel_source_digest():
+            traffic = tj.get("bytes_per_launch")
 
     # ------------------------------------------------------------------ decode
     decode = None
@@ -179,6 +216,7 @@ def main():
             "bytes_per_step": dbytes, "steps": args.decode_steps,
         }
 
+    copy = copy_calibration(dev, mib=256, reps=3)
     props = torch.cuda.get_device_properties(dev)
     line = {
         "metric": "chunked fwd tokens/s (H=16,d=128,T=4096) + decode state GB/s, 1xMI355X",
@@ -198,6 +236,7 @@ def main():
         "latency_ms": {"p50": float(np.percentile(per, 50)), "p95": float(np.percentile(per, 95)),
                        "p99": float(np.percentile(per, 99)), "mean": float(per.mean())},
         "decode": decode,
+        "measured_copy_GBps": copy["copy_GBps"],
         "run": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count, "torch": torch.__version__,
                 "hip": getattr(torch.version, "hip", None), "host_cpu": platform.processor(),
