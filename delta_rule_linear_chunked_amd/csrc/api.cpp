@@ -1,8 +1,9 @@
 // C ABI of the gated delta-rule library: argument validation and kernel dispatch.
 // Every check runs on the host before any launch; no device memory is read here.
 #include <cstdarg>
-#include <cstdio>
 #include <cstdint>
+#include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/deltarule.h"
@@ -85,6 +86,37 @@ int check_ptrs(std::initializer_list<std::pair<const void*, const char*>> req,
   return DR_OK;
 }
 
+// Workspace pool of the prefill (per device): stream-ordered allocations that stay cached in
+// the pool between calls, so steady-state calls do not reach the device allocator.
+hipError_t workspace_alloc(size_t bytes, hipStream_t stream, void** ptr) {
+  static std::mutex mu;
+  static hipMemPool_t pools[256] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 256) return hipErrorInvalidDevice;
+  hipMemPool_t pool;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    if (!pools[dev]) {
+      hipMemPoolProps props = {};
+      props.allocType = hipMemAllocationTypePinned;
+      props.location.type = hipMemLocationTypeDevice;
+      props.location.id = dev;
+      e = hipMemPoolCreate(&pools[dev], &props);
+      if (e != hipSuccess) {
+        pools[dev] = nullptr;
+        return e;
+      }
+      uint64_t keep = UINT64_MAX;
+      e = hipMemPoolSetAttribute(pools[dev], hipMemPoolAttrReleaseThreshold, &keep);
+      if (e != hipSuccess) return e;
+    }
+    pool = pools[dev];
+  }
+  return hipMallocFromPoolAsync(ptr, bytes, pool, stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -130,8 +162,9 @@ int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t*
   int st = check_dims_common(dims);
   if (st) return st;
   if (variant < DR_KDA || variant > DR_CKDA) return fail(DR_ERR_VARIANT, "unknown variant %d", variant);
-  const dr::PrefillPlan pl = dr::plan_prefill(dims->num_seqs * dims->num_heads,
-                                              (int)dims->head_dim_k, (int)dims->head_dim_v);
+  const dr::PrefillPlan pl = dr::plan_prefill(dims->num_seqs * dims->num_heads, dims->num_seqs, dims->batch,
+                                              dims->seqlen, dims->num_heads, (int)dims->head_dim_k,
+                                              (int)dims->head_dim_v, dims->batch == 1 && dims->num_seqs != 1);
   if (chunk) *chunk = pl.chunk;
   if (dv_block) *dv_block = pl.dv_block;
   if (workgroups) *workgroups = pl.workgroups;
@@ -167,12 +200,24 @@ int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha
   p.H = (int32_t)dims->num_heads;
   p.DV = (int32_t)dims->head_dim_v;
   const int64_t pairs = dims->num_seqs * dims->num_heads;
-  const dr::PrefillPlan pl = dr::plan_prefill(pairs, (int)dims->head_dim_k, (int)dims->head_dim_v);
+  const dr::PrefillPlan pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen, dims->num_heads,
+                                              (int)dims->head_dim_k, (int)dims->head_dim_v, cu_seqlens != nullptr);
   p.num_pairs = (int32_t)pairs;
   p.ndvb = pl.ndvb;
   p.grid_logical = (int32_t)(pairs * pl.ndvb);
-  hipError_t e = dr::launch_prefill(p, pl, (int)dims->head_dim_k, dims->in_dtype == DR_BF16, vec, stream);
+  p.nseq = (int32_t)dims->num_seqs;
+  void* ws = nullptr;
+  hipError_t e = hipSuccess;
+  if (pl.workspace > 0) {
+    e = workspace_alloc((size_t)pl.workspace, stream, &ws);
+    if (e != hipSuccess)
+      return fail(DR_ERR_HIP, "prefill workspace (%lld bytes) allocation failed: %s", (long long)pl.workspace,
+                  hipGetErrorString(e));
+  }
+  e = dr::launch_prefill(p, pl, ws, (int)dims->head_dim_k, dims->in_dtype == DR_BF16, vec, stream);
+  hipError_t ef = ws ? hipFreeAsync(ws, stream) : hipSuccess;
   if (e != hipSuccess) return fail(DR_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
+  if (ef != hipSuccess) return fail(DR_ERR_HIP, "prefill workspace release failed: %s", hipGetErrorString(ef));
   return DR_OK;
 }
 

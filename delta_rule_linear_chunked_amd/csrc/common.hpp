@@ -28,6 +28,15 @@ struct Params {
   int32_t num_pairs;    // sequences x heads
   int32_t ndvb;         // value-column blocks per (sequence, head)
   int32_t grid_logical; // num_pairs * ndvb
+  // prefill workspace: one record of per-chunk operands per (chunk slot, head)
+  unsigned char* rec;
+  int64_t rec_size;
+  int32_t* chunk_seq;   // packed: sequence of each chunk slot (-1: unused slot)
+  int32_t* chunk_c0;    // packed: first token of the chunk within its sequence
+  int32_t* seq_first;   // packed: first chunk slot of each sequence
+  int32_t slots;        // chunk slots
+  int32_t cps;          // fixed length: chunks per sequence
+  int32_t nseq;         // sequences
 };
 
 __device__ __forceinline__ float ld_f32(const float* p) { return *p; }

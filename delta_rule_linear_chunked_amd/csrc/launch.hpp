@@ -12,17 +12,22 @@ struct Params;
 hipError_t launch_decode(const Params& p, int64_t nheads, int dk, int dv, bool bf16, bool vec,
                          hipStream_t s);
 
-// Prefill launch shape for a problem: value columns per workgroup and grid size.
+// Prefill launch shape for a problem.
 struct PrefillPlan {
   int chunk;
   int dv_block;
   int ndvb;
-  int64_t workgroups;  // padded to a multiple of 8 (XCD count)
+  int64_t workgroups;  // state pass: padded to a multiple of 8 (XCD count)
+  int64_t slots;       // chunk slots (an upper bound for packed sequences)
+  int64_t rec_size;    // bytes of one (chunk slot, head) operand record
+  int64_t workspace;   // bytes of workspace (records + packed-sequence tables)
 };
-PrefillPlan plan_prefill(int64_t num_pairs, int dk, int dv);
+PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int64_t seqlen,
+                         int64_t heads, int dk, int dv, bool packed);
 
-// Prefill: chunkwise-parallel forward over every (sequence, head, value block).
-hipError_t launch_prefill(const Params& p, const PrefillPlan& plan, int dk, bool bf16, bool vec,
+// Prefill: chunk preparation over every (chunk, head), then the state pass over every
+// (sequence, head, value block). `ws` is a workspace of plan.workspace bytes.
+hipError_t launch_prefill(Params p, const PrefillPlan& plan, void* ws, int dk, bool bf16, bool vec,
                           hipStream_t s);
 
 }  // namespace dr

@@ -8,13 +8,21 @@
 // start state S0 and ratio(r, s) = prod_{j=s+1..r} alpha_j:
 //
 //   A[r,s] = sum_i u_ri k_si ratio(r,s)_i   (s < r)        P[r,s] likewise with q (s <= r)
-//   delta  = (I + A)^-1 (M - Utilde S0),     Utilde_r = Gamma_r . u_r
+//   T      = (I + A)^-1
+//   delta  = T (M - Utilde S0),              Utilde_r = Gamma_r . u_r
 //   O      = Qtilde S0 + P delta,            Qtilde_r = Gamma_r . q_r
 //   S_C    = Diag(Gamma_C) S0 + Kbar^T delta, Kbar_s = ratio(C, s) . k_s
 //
 // (derived by unrolling the step rule; the course page "GDN, KDA và Mamba-2",
 // section 3, asks for such a chunked kernel to be checked against the step
 // recurrence).
+//
+// Two passes. chunk_prep_kernel (one workgroup per chunk and head, all chunks in
+// parallel) computes everything that does not depend on the state — gate
+// products, A, P, T, Utilde, Qtilde, Kbar, Gamma_C — and writes it to a
+// workspace record as MFMA operand fragments. chunk_state_kernel (one workgroup
+// per sequence, head and block of value columns) then walks the chunks in order
+// with the state held in registers, doing only the state-dependent products.
 //
 // Gate preparation uses signed products, never logarithms, because Complex KDA
 // gates may be negative or zero. Each chunk is split into four 16-token blocks;
@@ -25,14 +33,10 @@
 //   t_J = total product of block J
 // so that for r in block I and s in block J < I
 //   ratio(r, s) = f_r * (prod_{J<J'<I} t_J') * g_s     (every factor in [-1, 1] when |alpha| <= 1)
-// and inside a block ratio(r, s) = f_r * (1 / f_s). The in-block factorisation
-// is used only while every |f| of the block lies in [2^-100, 2^100]; otherwise
-// (gates at or extremely close to zero) the block's diagonal tile is computed
-// directly from running products, which is exact for any gate value.
-//
-// Work split: one workgroup of four waves per (sequence, head, block of value
-// columns); the d_k x DVB state block stays in LDS across the whole sequence.
-// Wave w owns token rows 16w..16w+15 of each chunk.
+// and inside a block ratio(r, s) = f_r * (1 / f_s), g_s = t_J / f_s. The in-block
+// factorisation is used only while every |f| of the block lies in [2^-100, 2^100];
+// otherwise (gates at or extremely close to zero) the block's diagonal tiles and
+// g come from running products, which are exact for any gate value.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -40,20 +44,35 @@ namespace dr {
 
 constexpr int CH = 64;    // chunk length
 constexpr int NBLK = 4;   // 16-token blocks per chunk
-constexpr int LDT = 68;   // padded row stride of 64-wide tiles (floats)
+constexpr int LDT = 68;   // padded row stride of 64-wide fp32 tiles
 constexpr float FAST_LO = 0x1p-100f;
 constexpr float FAST_HI = 0x1p100f;
 
-template <int DK, int DVB>
-struct PrefillSmem {
-  float kg[CH][DK + 4];     // k_s . g_s
-  float tot[NBLK][DK];      // t_J
-  float A[CH][LDT];         // A: strictly lower diagonal blocks and the blocks below them
-  float P[CH][LDT];         // P: lower blocks; blocks above the diagonal stay zero
-  float Td[NBLK][16][20];   // (I + A_JJ)^-1 of each diagonal block
-  float S[DVB][DK + 4];     // state block, transposed: [value column][key channel]
-  float D[DVB][LDT];        // delta^T
+// Operand record of one (chunk slot, head). Every fragment is 32 bytes per lane
+// (bf16 hi + lo, or eight fp32 values), stored lane-contiguously, so a wave moves a
+// fragment with two fully coalesced 16-byte accesses per lane.
+template <int DK>
+struct Rec {
+  static constexpr int KS = DK / 32;
+  static constexpr int64_t FR = 64 * 32;                        // bytes of one fragment
+  static constexpr int64_t UT = 0;                              // Utilde  [block][ks]
+  static constexpr int64_t QT = UT + NBLK * KS * FR;            // Qtilde  [block][ks]
+  static constexpr int64_t KB = QT + NBLK * KS * FR;            // Kbar^T  [key tile][token step]
+  static constexpr int64_t TT = KB + (DK / 16) * 2 * FR;        // T       [block][token step]
+  static constexpr int64_t PP = TT + NBLK * 2 * FR;             // P       [block][token step]
+  static constexpr int64_t GC = PP + NBLK * 2 * FR;             // Gamma_C [DK] fp32
+  static constexpr int64_t SIZE = (GC + DK * 4 + 255) / 256 * 256;
 };
+
+template <class Frag>
+__device__ __forceinline__ void st_frag(unsigned char* base, int64_t idx, int lane, const Frag& f) {
+  static_assert(sizeof(Frag) == 32, "fragment size");
+  *reinterpret_cast<Frag*>(base + (idx * 64 + lane) * 32) = f;
+}
+template <class Frag>
+__device__ __forceinline__ Frag ld_frag(const unsigned char* base, int64_t idx, int lane) {
+  return *reinterpret_cast<const Frag*>(base + (idx * 64 + lane) * 32);
+}
 
 // Orders this wave's LDS writes before its later LDS reads by other lanes of the
 // same wave (LDS executes a wave's instructions in order; this stops the compiler
@@ -64,17 +83,435 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-template <int DKR, int DVB, typename InT, bool VEC>
-__global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(const Params p) {
+// Sequence, first token and length of a chunk slot. Returns false for an unused slot.
+__device__ __forceinline__ bool resolve_slot(const Params& p, int slot, int& n, int64_t& bos, int64_t& len,
+                                             int64_t& c0) {
+  if (p.cu) {
+    n = p.chunk_seq[slot];
+    if (n < 0) return false;
+    bos = p.cu[n];
+    len = (int64_t)p.cu[n + 1] - bos;
+    c0 = p.chunk_c0[slot];
+  } else {
+    n = slot / p.cps;
+    bos = (int64_t)n * p.T;
+    len = p.T;
+    c0 = (int64_t)(slot % p.cps) * CH;
+  }
+  return true;
+}
+
+// ============================================================================ pass 0
+// Packed sequences: first chunk slot of each sequence (exclusive scan of the chunk
+// counts) and, for every slot, its sequence and first token. One workgroup.
+__global__ __launch_bounds__(256) void chunk_plan_kernel(const Params p) {
+  __shared__ int s_scan[256];
+  __shared__ int s_carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) s_carry = 0;
+  __syncthreads();
+  for (int base = 0; base < p.nseq; base += 256) {
+    const int n = base + tid;
+    const int nc = n < p.nseq ? (p.cu[n + 1] - p.cu[n] + CH - 1) / CH : 0;
+    s_scan[tid] = nc;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int x = tid >= d ? s_scan[tid - d] : 0;
+      __syncthreads();
+      s_scan[tid] += x;
+      __syncthreads();
+    }
+    if (n < p.nseq) p.seq_first[n] = s_carry + s_scan[tid] - nc;
+    __syncthreads();
+    if (tid == 255) s_carry += s_scan[255];
+    __syncthreads();
+  }
+  const int total = s_carry;
+  if (tid == 0) p.seq_first[p.nseq] = total;
+  __syncthreads();  // seq_first complete (the workgroup-scope fence covers global memory)
+  for (int slot = tid; slot < p.slots; slot += 256) {
+    int n = -1, c0 = 0;
+    if (slot < total) {
+      int lo = 0, hi = p.nseq;  // last sequence whose first slot is <= slot
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.seq_first[mid] <= slot) lo = mid; else hi = mid;
+      }
+      n = lo;
+      c0 = (slot - p.seq_first[lo]) * CH;
+    }
+    p.chunk_seq[slot] = n;
+    p.chunk_c0[slot] = c0;
+  }
+}
+
+// ============================================================================ pass 1
+template <int DK>
+struct PrepSmem {
+  float tot[NBLK][DK];      // t_J
+  float A[CH][LDT];         // A (strictly lower)
+  float Td[NBLK][16][20];   // (I + A_JJ)^-1
+  union { float P[CH][LDT]; float At[CH][LDT]; } u1;      // P, later T_II A_IK
+  union { float kg[CH][DK + 4]; float T[CH][LDT]; } u2;   // k . g, later T
+};
+
+template <int DKR, typename InT, bool VEC>
+__global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
-  using Frag4 = typename Pol::Frag4;
   constexpr int DK = DKR < 32 ? 32 : DKR;  // key width padded to the 32-deep MFMA slice
-  constexpr int KS = DK / 32;              // reduction slices over key channels
-  constexpr int NCT = DVB / 16;            // 16-wide value-column tiles
+  constexpr int KS = DK / 32;
+  using R = Rec<DK>;
+
+  __shared__ __align__(16) PrepSmem<DK> sm;
+
+  const int slot = blockIdx.x / p.H;
+  const int h = blockIdx.x % p.H;
+  int n;
+  int64_t bos, len, c0;
+  if (!resolve_slot(p, slot, n, bos, len, c0)) return;
+  unsigned char* rec = p.rec + ((int64_t)slot * p.H + h) * p.rec_size;
+  const int H = p.H;
+  const int tid = threadIdx.x;
+  const int w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  const InT* qp = static_cast<const InT*>(p.q);
+  const InT* kp = static_cast<const InT*>(p.k);
+
+  // upper blocks of P are read (as zeros) by the state pass's 32-deep steps
+  for (int i = tid; i < CH * LDT; i += 256) (&sm.u1.P[0][0])[i] = 0.f;
+
+  const int row = 16 * w + r;
+  const bool valid = c0 + row < len;
+  const int64_t th = (bos + c0 + (valid ? row : 0)) * H + h;
+
+  // ---------------------------------------------------------------- gate preparation
+  float uf[KS][8], qf[KS][8];  // u . f and q . f of this lane's row
+  {
+    bool ok = true;
+    f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f}, pd = ad;
+    float fr[KS][8], rf[KS][8];
+    const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * g;
+      const bool live = valid && ch0 < DKR;
+      float a8[8], k8[8], q8[8], b8[8];
+      if (live) {
+        load8(kp + th * DKR + ch0, k8);
+        load8(qp + th * DKR + ch0, q8);
+        load8(p.alpha + th * DKR + ch0, a8);
+        if constexpr (VEC) load8(p.erase + th * DKR + ch0, b8);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { k8[j] = 0.f; q8[j] = 0.f; a8[j] = 1.f; b8[j] = 0.f; }
+      }
+      float f8[8], kd[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) f8[j] = a8[j];
+      row_prefix_prod8(f8);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float f = f8[j];
+        const float af = fabsf(f);
+        ok = ok && (af >= FAST_LO) && (af <= FAST_HI);
+        fr[ks][j] = f;
+        rf[ks][j] = __builtin_amdgcn_rcpf(f);
+        uf[ks][j] = (VEC ? b8[j] : esc) * k8[j] * f;
+        qf[ks][j] = q8[j] * f;
+        kd[j] = k8[j] * rf[ks][j];
+      }
+      if (r == 15) {
+        store4(&sm.tot[w][ch0], f32x4{fr[ks][0], fr[ks][1], fr[ks][2], fr[ks][3]});
+        store4(&sm.tot[w][ch0 + 4], f32x4{fr[ks][4], fr[ks][5], fr[ks][6], fr[ks][7]});
+      }
+      const Frag KD = Pol::make(kd);
+      Pol::mma(ad, Pol::make(uf[ks]), KD);
+      Pol::mma(pd, Pol::make(qf[ks]), KD);
+      // k_s . g_s with g_s = t / f_s (replaced below if some |f| is out of range)
+      float kgv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kgv[j] = k8[j] * (dpp_or<ROW_BCAST15>(0.f, fr[ks][j]) * rf[ks][j]);
+      store4(&sm.u2.kg[row][ch0], f32x4{kgv[0], kgv[1], kgv[2], kgv[3]});
+      store4(&sm.u2.kg[row][ch0 + 4], f32x4{kgv[4], kgv[5], kgv[6], kgv[7]});
+    }
+    if (__all(ok)) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int rr = 4 * g + i;  // row within the block; r is the column
+        sm.A[16 * w + rr][16 * w + r] = (r < rr) ? ad[i] : 0.f;
+        sm.u1.P[16 * w + rr][16 * w + r] = (r <= rr) ? pd[i] : 0.f;
+      }
+    } else {
+      // Some gate of this block is zero or nearly so: exact suffix products for k . g and
+      // the diagonal tiles from running products of the gates.
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch0 = 32 * ks + 8 * g;
+        const bool live = valid && ch0 < DKR;
+        float a8[8], k8[8];
+        load8(p.alpha + th * DKR + (live ? ch0 : 0), a8);
+        load8(kp + th * DKR + (live ? ch0 : 0), k8);
+        float kgv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kgv[j] = (live ? k8[j] : 0.f) * row_suffix_prod_excl(live ? a8[j] : 1.f);
+        store4(&sm.u2.kg[row][ch0], f32x4{kgv[0], kgv[1], kgv[2], kgv[3]});
+        store4(&sm.u2.kg[row][ch0 + 4], f32x4{kgv[4], kgv[5], kgv[6], kgv[7]});
+      }
+      for (int s = 0; s < 16; ++s) {
+        float ap = 0.f, pp = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const int ch0 = 32 * ks + 8 * g;
+          const bool live = valid && ch0 < DKR;
+          float a2[8], k2[8], q2[8], b2[8];
+          load8(p.alpha + th * DKR + (live ? ch0 : 0), a2);
+          load8(kp + th * DKR + (live ? ch0 : 0), k2);
+          load8(qp + th * DKR + (live ? ch0 : 0), q2);
+          if constexpr (VEC) load8(p.erase + th * DKR + (live ? ch0 : 0), b2);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float a = live ? a2[j] : 1.f;
+            const float kk = live ? k2[j] : 0.f;
+            const float qq = live ? q2[j] : 0.f;
+            const float uu = (VEC ? b2[j] : esc) * kk;
+            const float rho = row_prefix_prod(r > s ? a : 1.f);
+            const float kv = __shfl(kk, 16 * g + s);
+            ap = fmaf(uu * kv, rho, ap);
+            pp = fmaf(qq * kv, rho, pp);
+          }
+        }
+        ap += __shfl_xor(ap, 16);
+        ap += __shfl_xor(ap, 32);
+        pp += __shfl_xor(pp, 16);
+        pp += __shfl_xor(pp, 32);
+        if (g == 0) {
+          sm.A[16 * w + r][16 * w + s] = (r > s) ? ap : 0.f;
+          sm.u1.P[16 * w + r][16 * w + s] = (r >= s) ? pp : 0.f;
+        }
+      }
+    }
+  }
+  wave_lds_sync();
+  // (I + A_ww)^-1 by forward substitution, one lane per column
+  if (l < 16) {
+    float t[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      float ar[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) load4(&sm.A[16 * w + rr][16 * w + 4 * q4], *reinterpret_cast<float(*)[4]>(&ar[4 * q4]));
+      float acc = (rr == l) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < rr; ++s) acc = fmaf(-ar[s], t[s], acc);
+      t[rr] = acc;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sm.Td[w][rr][l] = t[rr];
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- off-diagonal tiles, Utilde, Qtilde
+  {
+    f32x4 accA[NBLK - 1], accP[NBLK - 1];
+#pragma unroll
+    for (int J = 0; J < NBLK - 1; ++J) { accA[J] = f32x4{0.f, 0.f, 0.f, 0.f}; accP[J] = accA[J]; }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * g;
+      // mid[J] = prod_{J<J'<w} t_J', run = prod_{J<w} t_J (Gamma at the block start)
+      float run[8], mid[NBLK - 1][8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) run[j] = 1.f;
+#pragma unroll
+      for (int J = NBLK - 2; J >= 0; --J) {
+        if (J < w) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) mid[J][j] = run[j];
+          float t8[8];
+          load8(&sm.tot[J][ch0], t8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) run[j] *= t8[j];
+        }
+      }
+      const Frag UF = Pol::make(uf[ks]);
+      const Frag QF = Pol::make(qf[ks]);
+#pragma unroll
+      for (int J = 0; J < NBLK - 1; ++J) {
+        if (J < w) {
+          float x[8];
+          load8(&sm.u2.kg[16 * J + r][ch0], x);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[j] *= mid[J][j];
+          const Frag B = Pol::make(x);
+          Pol::mma(accA[J], UF, B);
+          Pol::mma(accP[J], QF, B);
+        }
+      }
+      float ut[8], qt[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { ut[j] = uf[ks][j] * run[j]; qt[j] = qf[ks][j] * run[j]; }
+      st_frag(rec + R::UT, w * KS + ks, l, Pol::make(ut));
+      st_frag(rec + R::QT, w * KS + ks, l, Pol::make(qt));
+    }
+#pragma unroll
+    for (int J = 0; J < NBLK - 1; ++J) {
+      if (J < w) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sm.A[16 * w + 4 * g + i][16 * J + r] = accA[J][i];
+          sm.u1.P[16 * w + 4 * g + i][16 * J + r] = accP[J][i];
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- P, Kbar^T and Gamma_C out
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    float a8[8];
+    load8(&sm.u1.P[16 * w + r][32 * st + 8 * g], a8);
+    st_frag(rec + R::PP, w * 2 + st, l, Pol::make(a8));
+  }
+  for (int rt = w; rt < DK / 16; rt += 4) {
+    const int chA = 16 * rt + r;
+    float tA[NBLK];
+#pragma unroll
+    for (int J = 0; J < NBLK; ++J) tA[J] = sm.tot[J][chA];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int k0 = 32 * st + 8 * g;
+      const int blk = 2 * st + (g >> 1);
+      float suf = 1.f;
+#pragma unroll
+      for (int J = 1; J < NBLK; ++J) suf *= (J > blk) ? tA[J] : 1.f;
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = sm.u2.kg[k0 + j][chA] * suf;
+      st_frag(rec + R::KB, rt * 2 + st, l, Pol::make(x));
+    }
+  }
+  if (tid < DK) {
+    reinterpret_cast<float*>(rec + R::GC)[tid] = sm.tot[0][tid] * sm.tot[1][tid] * sm.tot[2][tid] * sm.tot[3][tid];
+  }
+  __syncthreads();
+
+  // ---------------------------------------------------------------- T = (I + A)^-1
+  for (int i = tid; i < CH * LDT; i += 256) {
+    const int rr = i / LDT, cc = i % LDT;
+    (&sm.u2.T[0][0])[i] = (cc < CH && (rr >> 4) == (cc >> 4)) ? sm.Td[rr >> 4][rr & 15][cc & 15] : 0.f;
+  }
+  {  // At_IK = T_II A_IK (K < I)
+    float x[8];
+    if (g < 2) {
+      load8(&sm.Td[w][r][8 * g], x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = 0.f;
+    }
+    const Frag Tii = Pol::make(x);
+#pragma unroll
+    for (int K = 0; K < NBLK - 1; ++K) {
+      if (K < w) {
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = (g < 2) ? sm.A[16 * w + 8 * g + j][16 * K + r] : 0.f;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        Pol::mma(acc, Tii, Pol::make(y));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.u1.At[16 * w + 4 * g + i][16 * K + r] = acc[i];
+      }
+    }
+  }
+  __syncthreads();
+  // T_IJ = -sum_{K=J..I-1} At_IK T_KJ, by increasing distance I - J
+#pragma unroll
+  for (int d = 1; d < NBLK; ++d) {
+    if (w >= d) {
+      const int J = w - d;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (st < (d + 1) / 2) {
+          const int k0 = 16 * J + 32 * st + 8 * g;
+          float a8[8], b8[8];
+          if (k0 < 16 * w) {
+            load8(&sm.u1.At[16 * w + r][k0], a8);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b8[j] = sm.u2.T[k0 + j][16 * J + r];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { a8[j] = 0.f; b8[j] = 0.f; }
+          }
+          Pol::mma(acc, Pol::make(a8), Pol::make(b8));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sm.u2.T[16 * w + 4 * g + i][16 * J + r] = -acc[i];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    float a8[8];
+    load8(&sm.u2.T[16 * w + r][32 * st + 8 * g], a8);
+    st_frag(rec + R::TT, w * 2 + st, l, Pol::make(a8));
+  }
+}
+
+// ============================================================================ pass 2
+// Split-operand tile in LDS: a row-major matrix whose fragments are 8 consecutive
+// columns of a row (the reduction index), written 4 columns at a time from an
+// accumulator.
+template <class Pol, int ROWS, int COLS> struct OpTile;
+template <int ROWS, int COLS> struct OpTile<PolBF3, ROWS, COLS> {
+  __bf16 hi[ROWS][COLS + 8], lo[ROWS][COLS + 8];
+  __device__ __forceinline__ void put4(int row, int col, const f32x4& x) {
+    bf16x4 h, o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[i] = (__bf16)x[i];
+      o[i] = (__bf16)(x[i] - (float)h[i]);
+    }
+    *reinterpret_cast<bf16x4*>(&hi[row][col]) = h;
+    *reinterpret_cast<bf16x4*>(&lo[row][col]) = o;
+  }
+  __device__ __forceinline__ PolBF3::Frag get8(int row, int col) const {
+    PolBF3::Frag f;
+    f.hi = *reinterpret_cast<const bf16x8*>(&hi[row][col]);
+    f.lo = *reinterpret_cast<const bf16x8*>(&lo[row][col]);
+    return f;
+  }
+};
+template <int ROWS, int COLS> struct OpTile<PolF32, ROWS, COLS> {
+  float v[ROWS][COLS + 4];
+  __device__ __forceinline__ void put4(int row, int col, const f32x4& x) { store4(&v[row][col], x); }
+  __device__ __forceinline__ PolF32::Frag get8(int row, int col) const {
+    PolF32::Frag f;
+    load8(&v[row][col], f.v);
+    return f;
+  }
+};
+
+template <class Pol, int DK, int DVB>
+struct StateSmem {
+  OpTile<Pol, DVB, DK> S;   // state, transposed: [value column][key channel]
+  OpTile<Pol, DVB, CH> R;   // (M - Utilde S0)^T: [value column][token]
+  OpTile<Pol, DVB, CH> D;   // delta^T
+};
+
+template <int DKR, int DVB, typename InT, bool VEC>
+__global__ __launch_bounds__(256, 2) void chunk_state_kernel(const Params p) {
+  using Pol = typename PolicyFor<InT>::type;
+  using Frag = typename Pol::Frag;
+  constexpr int DK = DKR < 32 ? 32 : DKR;
+  constexpr int KS = DK / 32;
+  constexpr int NCT = DVB / 16;
+  constexpr int NRT = (DK / 16 + 3) / 4;  // key-channel tiles per wave (rounded up)
+  using R = Rec<DK>;
   static_assert(DVB % 16 == 0 && DVB <= 64, "value block");
 
-  __shared__ __align__(16) PrefillSmem<DK, DVB> sm;
+  __shared__ __align__(16) StateSmem<Pol, DK, DVB> sm;
 
   const int lid = xcd_remap(blockIdx.x, gridDim.x);
   if (lid >= p.grid_logical) return;
@@ -83,55 +520,81 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(const Params p) {
   const int H = p.H;
   const int n = pair / H, h = pair % H;
   int64_t bos, len;
+  int first;
   if (p.cu) {
     bos = p.cu[n];
     len = (int64_t)p.cu[n + 1] - bos;
+    first = p.seq_first[n];
   } else {
     bos = (int64_t)n * p.T;
     len = p.T;
+    first = n * p.cps;
   }
-
+  const int nch = (int)((len + CH - 1) / CH);
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
-  const InT* qp = static_cast<const InT*>(p.q);
-  const InT* kp = static_cast<const InT*>(p.k);
-  const InT* vp = static_cast<const InT*>(p.v);
   const int DV = p.DV;
+  const InT* vp = static_cast<const InT*>(p.v);
 
-  // ---- state block in; P's upper blocks zeroed once (never written)
-  for (int i = tid; i < CH * LDT; i += 256) (&sm.P[0][0])[i] = 0.f;
-  for (int i = tid; i < DK * DVB; i += 256) {
-    const int ch = i / DVB, c = i % DVB;
-    float s0 = 0.f;
-    if (p.S0 && ch < DKR) s0 = p.S0[(((int64_t)n * H + h) * DKR + ch) * DV + dv0 + c];
-    sm.S[c][ch] = s0;
+  // ---- state: fp32 master in registers (this wave's key-channel tiles), split copy in LDS
+  f32x4 Sm[NRT][NCT];
+#pragma unroll
+  for (int m = 0; m < NRT; ++m) {
+    const int rt = w + 4 * m;
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (rt < DK / 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 16 * rt + 4 * g + i;
+          if (p.S0 && ch < DKR) x[i] = p.S0[(((int64_t)n * H + h) * DKR + ch) * DV + dv0 + 16 * ct + r];
+        }
+        sm.S.put4(16 * ct + r, 16 * rt + 4 * g, x);
+      }
+      Sm[m][ct] = x;
+    }
   }
 
-  // ---- prefetch registers: this lane's token row of the next chunk (lane layout of the
-  // 32-deep fragments: row r of block w, channels 32*ks + 8*g + j), and the value/write
-  // entries it needs in accumulator layout (rows 4*g + i of block w, column 16*ct + r).
-  Raw8<InT> pk[KS], pq[KS];
-  float pa[KS][8], pb[VEC ? KS : 1][8];
-  float pe = 0.f;
-  InT pv[NCT][4];  // raw: converting at load time would make the load synchronous
+  // ---- prefetch registers for the next chunk, each group loaded right after the current
+  // values' last use (past the last chunk the last record is reloaded and left unused)
+  Frag fU[KS], fQ[KS], fT[2], fP[2], fK[NRT][2];
+  f32x4 gC[NRT];
+  InT pv[NCT][4];
   float pw[VEC ? NCT : 1][4];
-  auto prefetch = [&](int64_t c0n) {
-    const int64_t last = bos + len - 1;  // a valid token: rows past the end are clamped, then masked
-    int64_t tk = bos + c0n + 16 * w + r;
-    tk = tk > last ? last : tk;
-    const int64_t th = tk * H + h;
+  auto rec_of = [&](int c) -> const unsigned char* {
+    const int cc = c < nch ? c : nch - 1;
+    return p.rec + ((int64_t)(first + cc) * H + h) * p.rec_size;
+  };
+  auto pf_uq = [&](int c) {
+    const unsigned char* rc = rec_of(c);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int ch0 = (32 * ks + 8 * g) < DKR ? (32 * ks + 8 * g) : 0;
-      pk[ks].load(kp + th * DKR + ch0);
-      pq[ks].load(qp + th * DKR + ch0);
-      load8(p.alpha + th * DKR + ch0, pa[ks]);
-      if constexpr (VEC) load8(p.erase + th * DKR + ch0, pb[ks]);
+      fU[ks] = ld_frag<Frag>(rc + R::UT, w * KS + ks, l);
+      fQ[ks] = ld_frag<Frag>(rc + R::QT, w * KS + ks, l);
     }
-    if constexpr (!VEC) pe = p.erase[th];
+  };
+  auto pf_t = [&](int c) {
+    const unsigned char* rc = rec_of(c);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) fT[st] = ld_frag<Frag>(rc + R::TT, w * 2 + st, l);
+  };
+  auto pf_rest = [&](int c) {
+    const unsigned char* rc = rec_of(c);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) fP[st] = ld_frag<Frag>(rc + R::PP, w * 2 + st, l);
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+      const int rt = w + 4 * m < DK / 16 ? w + 4 * m : 0;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) fK[m][st] = ld_frag<Frag>(rc + R::KB, rt * 2 + st, l);
+      gC[m] = *reinterpret_cast<const f32x4*>(rc + R::GC + (16 * rt + 4 * g) * 4);
+    }
+    const int64_t cc = (int64_t)(c < nch ? c : nch - 1) * CH;
+    const int64_t last = bos + len - 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int64_t tv = bos + c0n + 16 * w + 4 * g + i;
+      int64_t tv = bos + cc + 16 * w + 4 * g + i;
       tv = tv > last ? last : tv;
       const int64_t thv = tv * H + h;
       if constexpr (!VEC) pw[0][i] = p.write[thv];
@@ -143,358 +606,174 @@ __global__ __launch_bounds__(256, 1) void chunk_fwd_kernel(const Params p) {
       }
     }
   };
-  if (len > 0) prefetch(0);
+  if (nch > 0) {
+    pf_uq(0);
+    pf_t(0);
+    pf_rest(0);
+  }
   __syncthreads();
 
-  for (int64_t c0 = 0; c0 < len; c0 += CH) {
-    const int row = 16 * w + r;
-    const bool valid = c0 + row < len;
-
-    // ================= gate preparation, operands and the diagonal tiles of block w
-    Frag UF[KS], QF[KS];
-    float mv[NCT][4];  // write vectors m of rows 4g+i (accumulator layout)
+  for (int c = 0; c < nch; ++c) {
+    const int64_t c0 = (int64_t)c * CH;
+    // write values m = w . v of rows 4g+i (accumulator layout), taken out of the prefetch
+    // registers now so that their next load does not wait on a late use
+    float mv[NCT][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool vi = c0 + 16 * w + 4 * g + i < len;
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         mv[ct][i] = vi ? pw[VEC ? ct : 0][i] * (float)pv[ct][i] : 0.f;
-        // Materialise here: if the product sinks past the next prefetch, the old and new
-        // prefetch registers overlap and the compiler copies them with waiting moves.
         asm volatile("" : "+v"(mv[ct][i]));
       }
     }
-    {
-      bool ok = true;
-      f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f}, pd = ad;
-      float fr[KS][8], rf[KS][8];  // f_r and 1 / f_r of this lane's row
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch0 = 32 * ks + 8 * g;
-        const bool live = valid && ch0 < DKR;
-        float uf[8], qf[8], kd[8], f8[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) f8[j] = live ? pa[ks][j] : 1.f;
-        row_prefix_prod8(f8);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float kk = live ? pk[ks].get(j) : 0.f;
-          const float qq = live ? pq[ks].get(j) : 0.f;
-          const float ee = VEC ? pb[VEC ? ks : 0][j] : pe;
-          const float f = f8[j];
-          const float af = fabsf(f);
-          ok = ok && (af >= FAST_LO) && (af <= FAST_HI);
-          fr[ks][j] = f;
-          rf[ks][j] = __builtin_amdgcn_rcpf(f);
-          uf[j] = ee * kk * f;
-          qf[j] = qq * f;
-          kd[j] = kk * rf[ks][j];
-        }
-        if (r == 15) {
-          store4(&sm.tot[w][ch0], f32x4{fr[ks][0], fr[ks][1], fr[ks][2], fr[ks][3]});
-          store4(&sm.tot[w][ch0 + 4], f32x4{fr[ks][4], fr[ks][5], fr[ks][6], fr[ks][7]});
-        }
-        UF[ks] = Pol::make(uf);
-        QF[ks] = Pol::make(qf);
-        const Frag KD = Pol::make(kd);
-        Pol::mma(ad, UF[ks], KD);
-        Pol::mma(pd, QF[ks], KD);
-      }
-      const bool fast = __all(ok);
-      // k_s . g_s, g_s = prod of alpha over s+1 .. block end: t / f_s while every |f| is in
-      // range, else an exact suffix scan.
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch0 = 32 * ks + 8 * g;
-        const bool live = valid && ch0 < DKR;
-        float kgv[8];
-        if (fast) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float t = dpp_or<ROW_BCAST15>(0.f, fr[ks][j]);
-            kgv[j] = (live ? pk[ks].get(j) : 0.f) * (t * rf[ks][j]);
-          }
-        } else {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float a = live ? pa[ks][j] : 1.f;
-            kgv[j] = (live ? pk[ks].get(j) : 0.f) * row_suffix_prod_excl(a);
-          }
-        }
-        store4(&sm.kg[row][ch0], f32x4{kgv[0], kgv[1], kgv[2], kgv[3]});
-        store4(&sm.kg[row][ch0 + 4], f32x4{kgv[4], kgv[5], kgv[6], kgv[7]});
-      }
-      if (fast) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = 4 * g + i;  // row within the block; r is the column
-          sm.A[16 * w + rr][16 * w + r] = (r < rr) ? ad[i] : 0.f;
-          sm.P[16 * w + rr][16 * w + r] = (r <= rr) ? pd[i] : 0.f;
-        }
-      } else {
-        // Diagonal tile from running products of the gates (exact for any gate value,
-        // including zero), reloading this lane's row of the chunk.
-        const int64_t last = bos + len - 1;
-        int64_t tk = bos + c0 + row;
-        tk = tk > last ? last : tk;
-        const int64_t th = tk * H + h;
-        for (int s = 0; s < 16; ++s) {
-          float ap = 0.f, pp = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const int ch0 = 32 * ks + 8 * g;
-            const bool live = valid && ch0 < DKR;
-            float a2[8], k2[8], q2[8], b2[8];
-            load8(p.alpha + th * DKR + (live ? ch0 : 0), a2);
-            load8(kp + th * DKR + (live ? ch0 : 0), k2);
-            load8(qp + th * DKR + (live ? ch0 : 0), q2);
-            if constexpr (VEC) load8(p.erase + th * DKR + (live ? ch0 : 0), b2);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-              const float a = live ? a2[j] : 1.f;
-              const float kk = live ? k2[j] : 0.f;
-              const float qq = live ? q2[j] : 0.f;
-              const float uu = (VEC ? b2[j] : pe) * kk;
-              const float rho = row_prefix_prod(r > s ? a : 1.f);
-              const float kv = __shfl(kk, 16 * g + s);
-              ap = fmaf(uu * kv, rho, ap);
-              pp = fmaf(qq * kv, rho, pp);
-            }
-          }
-          ap += __shfl_xor(ap, 16);
-          ap += __shfl_xor(ap, 32);
-          pp += __shfl_xor(pp, 16);
-          pp += __shfl_xor(pp, 32);
-          if (g == 0) {
-            sm.A[16 * w + r][16 * w + s] = (r > s) ? ap : 0.f;
-            sm.P[16 * w + r][16 * w + s] = (r >= s) ? pp : 0.f;
-          }
-        }
-      }
-    }
-    wave_lds_sync();
-    // (I + A_ww)^-1 by forward substitution, one lane per column
-    if (l < 16) {
-      float t[16];
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        float ar[16];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) load4(&sm.A[16 * w + rr][16 * w + 4 * q4], *reinterpret_cast<float(*)[4]>(&ar[4 * q4]));
-        float acc = (rr == l) ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < rr; ++s) acc = fmaf(-ar[s], t[s], acc);
-        t[rr] = acc;
-      }
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sm.Td[w][rr][l] = t[rr];
-    }
-    // Unconditional (rows past the end are clamped): a conditional prefetch makes the
-    // compiler copy the in-flight registers at the loop latch, which waits for the loads.
-    prefetch(c0 + CH);
-    __syncthreads();
 
-    // ================= off-diagonal tiles of block row w, and X = Utilde S0, Y = Qtilde S0
-    f32x4 accY[NCT], Rm[NCT];
+    // ================= X = Utilde S0, Y = Qtilde S0, R = M - X   (block row w)
+    f32x4 accY[NCT];
     {
-      f32x4 accA[NBLK - 1], accP[NBLK - 1], accX[NCT];
-#pragma unroll
-      for (int J = 0; J < NBLK - 1; ++J) { accA[J] = f32x4{0.f, 0.f, 0.f, 0.f}; accP[J] = accA[J]; }
+      f32x4 accX[NCT];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) { accX[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; accY[ct] = accX[ct]; }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int ch0 = 32 * ks + 8 * g;
-        // running product over earlier blocks: mid[J] = prod_{J<J'<w} t_J', pre = prod_{J<w} t_J
-        float run[8], mid[NBLK - 1][8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) run[j] = 1.f;
-#pragma unroll
-        for (int J = NBLK - 2; J >= 0; --J) {
-          if (J < w) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) mid[J][j] = run[j];
-            float t8[8];
-            load8(&sm.tot[J][ch0], t8);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) run[j] *= t8[j];
-          }
-        }
-#pragma unroll
-        for (int J = 0; J < NBLK - 1; ++J) {
-          if (J < w) {
-            float x[8];
-            load8(&sm.kg[16 * J + r][ch0], x);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[j] *= mid[J][j];
-            const Frag B = Pol::make(x);
-            Pol::mma(accA[J], UF[ks], B);
-            Pol::mma(accP[J], QF[ks], B);
-          }
-        }
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
-          float x[8];
-          load8(&sm.S[16 * ct + r][ch0], x);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] *= run[j];
-          const Frag B = Pol::make(x);
-          Pol::mma(accX[ct], UF[ks], B);
-          Pol::mma(accY[ct], QF[ks], B);
-        }
-      }
-#pragma unroll
-      for (int J = 0; J < NBLK - 1; ++J) {
-        if (J < w) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sm.A[16 * w + 4 * g + i][16 * J + r] = accA[J][i];
-            sm.P[16 * w + 4 * g + i][16 * J + r] = accP[J][i];
-          }
+          const Frag B = sm.S.get8(16 * ct + r, 32 * ks + 8 * g);
+          Pol::mma(accX[ct], fU[ks], B);
+          Pol::mma(accY[ct], fQ[ks], B);
         }
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
+        f32x4 rv;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Rm[ct][i] = mv[ct][i] - accX[ct][i];
+        for (int i = 0; i < 4; ++i) rv[i] = mv[ct][i] - accX[ct][i];
+        sm.R.put4(16 * ct + r, 16 * w + 4 * g, rv);
       }
     }
+    pf_uq(c + 1);
     __syncthreads();
 
-    // ================= delta by blocked forward substitution:
-    //   delta_J = (I + A_JJ)^-1 (R_J - sum_{K<J} A_JK delta_K)
-#pragma unroll
-    for (int J = 0; J < NBLK; ++J) {
-      if (w == J) {
-#pragma unroll
-        for (int K = 0; K < NBLK - 1; ++K) {
-          if (K < J) {
-            float a4[4];
-            load4(&sm.A[16 * J + r][16 * K + 4 * g], a4);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) a4[j] = -a4[j];
-            const Frag4 Af = Pol::make4(a4);
-#pragma unroll
-            for (int ct = 0; ct < NCT; ++ct) {
-              float b4[4];
-              load4(&sm.D[16 * ct + r][16 * K + 4 * g], b4);
-              Pol::mma16(Rm[ct], Af, Pol::make4(b4));
-            }
-          }
-        }
-        float t4[4];
-        load4(&sm.Td[J][r][4 * g], t4);
-        const Frag4 Tf = Pol::make4(t4);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          float b4[4] = {Rm[ct][0], Rm[ct][1], Rm[ct][2], Rm[ct][3]};
-          f32x4 d = f32x4{0.f, 0.f, 0.f, 0.f};
-          Pol::mma16(d, Tf, Pol::make4(b4));
-          store4(&sm.D[16 * ct + r][16 * J + 4 * g], d);
-        }
-      }
-      __syncthreads();
-    }
-
-    // ================= O = Y + P delta   (block row w)
+    // ================= delta = T R   (block row w)
     const int nst = (w + 2) / 2;
+    {
+      f32x4 accD[NCT];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      if (st < nst) {
-        const int k0 = 32 * st + 8 * g;
-        float a8[8];
-        load8(&sm.P[16 * w + r][k0], a8);
-        const Frag Af = Pol::make(a8);
+      for (int ct = 0; ct < NCT; ++ct) accD[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          float b8[8];
-          load8(&sm.D[16 * ct + r][k0], b8);
-          Pol::mma(accY[ct], Af, Pol::make(b8));
+      for (int st = 0; st < 2; ++st) {
+        if (st < nst) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) Pol::mma(accD[ct], fT[st], sm.R.get8(16 * ct + r, 32 * st + 8 * g));
         }
       }
-    }
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int rw = 16 * w + 4 * g + i;
-        if (c0 + rw < len) p.o[((bos + c0 + rw) * H + h) * DV + dv0 + 16 * ct + r] = accY[ct][i];
-      }
+      for (int ct = 0; ct < NCT; ++ct) sm.D.put4(16 * ct + r, 16 * w + 4 * g, accD[ct]);
     }
+    pf_t(c + 1);
+    __syncthreads();
 
-    // ================= S <- Diag(Gamma_C) S0 + Kbar^T delta   (key-channel tiles of this wave)
+    // ================= O = Y + P delta, and S <- Diag(Gamma_C) S0 + Kbar^T delta
     {
       Frag DF[NCT][2];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          float b8[8];
-          load8(&sm.D[16 * ct + r][32 * st + 8 * g], b8);
-          DF[ct][st] = Pol::make(b8);
+        for (int st = 0; st < 2; ++st) DF[ct][st] = sm.D.get8(16 * ct + r, 32 * st + 8 * g);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (st < nst) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) Pol::mma(accY[ct], fP[st], DF[ct][st]);
         }
       }
-      for (int rt = w; rt < DK / 16; rt += 4) {
-        const int chA = 16 * rt + r;
-        float tA[NBLK];
 #pragma unroll
-        for (int J = 0; J < NBLK; ++J) tA[J] = sm.tot[J][chA];
-        Frag KB[2];
+      for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const int k0 = 32 * st + 8 * g;
-          const int blk = 2 * st + (g >> 1);
-          float suf = 1.f;
-#pragma unroll
-          for (int J = 1; J < NBLK; ++J) suf *= (J > blk) ? tA[J] : 1.f;
-          float x[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[j] = sm.kg[k0 + j][chA] * suf;
-          KB[st] = Pol::make(x);
+        for (int i = 0; i < 4; ++i) {
+          const int64_t rw = c0 + 16 * w + 4 * g + i;
+          if (rw < len) p.o[((bos + rw) * H + h) * DV + dv0 + 16 * ct + r] = accY[ct][i];
         }
-        float tt[NBLK][4];
+      }
 #pragma unroll
-        for (int J = 0; J < NBLK; ++J) load4(&sm.tot[J][16 * rt + 4 * g], tt[J]);
+      for (int m = 0; m < NRT; ++m) {
+        const int rt = w + 4 * m;
+        if (rt < DK / 16) {
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          float s4[4];
-          load4(&sm.S[16 * ct + r][16 * rt + 4 * g], s4);
-          f32x4 acc;
+          for (int ct = 0; ct < NCT; ++ct) {
+            f32x4 acc;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] = tt[0][i] * tt[1][i] * tt[2][i] * tt[3][i] * s4[i];
+            for (int i = 0; i < 4; ++i) acc[i] = gC[m][i] * Sm[m][ct][i];
 #pragma unroll
-          for (int st = 0; st < 2; ++st) Pol::mma(acc, KB[st], DF[ct][st]);
-          store4(&sm.S[16 * ct + r][16 * rt + 4 * g], acc);
+            for (int st = 0; st < 2; ++st) Pol::mma(acc, fK[m][st], DF[ct][st]);
+            Sm[m][ct] = acc;
+            sm.S.put4(16 * ct + r, 16 * rt + 4 * g, acc);
+          }
         }
       }
     }
+    pf_rest(c + 1);
     __syncthreads();
   }
 
   // ---- final state out
   if (p.S) {
-    for (int i = tid; i < DKR * DVB; i += 256) {
-      const int ch = i / DVB, c = i % DVB;
-      p.S[(((int64_t)n * H + h) * DKR + ch) * DV + dv0 + c] = sm.S[c][ch];
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+      const int rt = w + 4 * m;
+      if (rt < DK / 16) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ch = 16 * rt + 4 * g + i;
+            if (ch < DKR) p.S[(((int64_t)n * H + h) * DKR + ch) * DV + dv0 + 16 * ct + r] = Sm[m][ct][i];
+          }
+        }
+      }
     }
   }
 }
 
-PrefillPlan plan_prefill(int64_t num_pairs, int dk, int dv) {
-  (void)dk;
+// ============================================================================ host
+static int64_t rec_size_for(int dk) {
+  switch (dk) {
+    case 16: case 32: return Rec<32>::SIZE;
+    case 64: return Rec<64>::SIZE;
+    default: return Rec<128>::SIZE;
+  }
+}
+
+PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int64_t seqlen,
+                         int64_t heads, int dk, int dv, bool packed) {
   PrefillPlan pl;
   pl.chunk = CH;
-  pl.dv_block = (dv >= 32 && num_pairs * (dv / 32) >= 256) ? 32 : 16;
+  pl.dv_block = (dv >= 32 && num_pairs * (dv / 32) >= 512) ? 32 : 16;
   pl.ndvb = dv / pl.dv_block;
   const int64_t logical = num_pairs * pl.ndvb;
   pl.workgroups = (logical + 7) / 8 * 8;
+  const int64_t cps = (seqlen + CH - 1) / CH;
+  pl.slots = packed ? cps + num_seqs : batch * cps;
+  pl.rec_size = rec_size_for(dk);
+  const int64_t tables = packed ? ((2 * pl.slots + num_seqs + 1) * 4 + 255) / 256 * 256 : 0;
+  pl.workspace = pl.slots * heads * pl.rec_size + tables;
   return pl;
 }
 
 template <int DKR, int DVB, typename InT, bool VEC>
 static hipError_t launch_t(const Params& p, const PrefillPlan& pl, hipStream_t s) {
-  hipLaunchKernelGGL((chunk_fwd_kernel<DKR, DVB, InT, VEC>), dim3((unsigned)pl.workgroups), dim3(256),
-                     0, s, p);
+  if (p.cu) {
+    hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (pl.slots > 0) {
+    hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC>), dim3((unsigned)(pl.slots * p.H)), dim3(256), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((chunk_state_kernel<DKR, DVB, InT, VEC>), dim3((unsigned)pl.workgroups), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
@@ -510,9 +789,19 @@ static hipError_t launch_dvb(const Params& p, const PrefillPlan& pl, bool bf16, 
   return launch_gate<DKR, 16>(p, pl, bf16, vec, s);
 }
 
-hipError_t launch_prefill(const Params& p, const PrefillPlan& pl, int dk, bool bf16, bool vec,
+hipError_t launch_prefill(Params p, const PrefillPlan& pl, void* ws, int dk, bool bf16, bool vec,
                           hipStream_t s) {
   if (pl.workgroups == 0) return hipSuccess;
+  p.rec = static_cast<unsigned char*>(ws);
+  p.rec_size = pl.rec_size;
+  p.slots = (int32_t)pl.slots;
+  p.cps = (int32_t)((p.T + CH - 1) / CH);
+  if (p.cu) {
+    int32_t* tables = reinterpret_cast<int32_t*>(p.rec + pl.slots * p.H * pl.rec_size);
+    p.chunk_seq = tables;
+    p.chunk_c0 = tables + pl.slots;
+    p.seq_first = tables + 2 * pl.slots;
+  }
   switch (dk) {
     case 16: return launch_dvb<16>(p, pl, bf16, vec, s);
     case 32: return launch_dvb<32>(p, pl, bf16, vec, s);

@@ -101,10 +101,10 @@ def test_empty_problems_launch_nothing(lib):
 
 
 def test_plan(lib):
-    # 64 (sequence, head) pairs of d = 128: four 32-wide value blocks -> 256 workgroups
+    # 64 (sequence, head) pairs of d = 128: eight 16-wide value blocks -> 512 state workgroups
     c, b, w = drl.chunk_fwd_plan(4, 4096, 16, 128, 128)
-    assert (c, b, w) == (64, 32, 256)
-    # 32 pairs: 16-wide blocks keep 256 workgroups busy
-    assert drl.chunk_fwd_plan(2, 16384, 16, 128, 128) == (64, 16, 256)
+    assert (c, b, w) == (64, 16, 512)
+    # 192 pairs: 32-wide blocks already give 768 workgroups
+    assert drl.chunk_fwd_plan(1, 32768, 16, 128, 128, num_seqs=12) == (64, 32, 768)
     # grid padded to a multiple of the 8 XCDs
     assert drl.chunk_fwd_plan(1, 64, 2, 16, 16)[2] == 8
