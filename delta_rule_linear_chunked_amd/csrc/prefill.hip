@@ -37,6 +37,8 @@
 // factorisation is used only while every |f| of the block lies in [2^-100, 2^100];
 // otherwise (gates at or extremely close to zero) the block's diagonal tiles and
 // g come from running products, which are exact for any gate value.
+#include <cstdlib>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -170,7 +172,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   int n;
   int64_t bos, len, c0;
   if (!resolve_slot(p, slot, n, bos, len, c0)) return;
-  unsigned char* rec = p.rec + ((int64_t)slot * p.H + h) * p.rec_size;
+  unsigned char* rec = p.rec + ((int64_t)h * p.slots + slot) * p.rec_size;  // a head's chunks are adjacent
   const int H = p.H;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
@@ -189,7 +191,6 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   {
     bool ok = true;
     f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f}, pd = ad;
-    float fr[KS][8], rf[KS][8];
     const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -205,32 +206,29 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) { k8[j] = 0.f; q8[j] = 0.f; a8[j] = 1.f; b8[j] = 0.f; }
       }
-      float f8[8], kd[8];
+      float f8[8], kd[8], kgv[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) f8[j] = a8[j];
       row_prefix_prod8(f8);
+      if (r == 15) {
+        store4(&sm.tot[w][ch0], f32x4{f8[0], f8[1], f8[2], f8[3]});
+        store4(&sm.tot[w][ch0 + 4], f32x4{f8[4], f8[5], f8[6], f8[7]});
+      }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float f = f8[j];
         const float af = fabsf(f);
         ok = ok && (af >= FAST_LO) && (af <= FAST_HI);
-        fr[ks][j] = f;
-        rf[ks][j] = __builtin_amdgcn_rcpf(f);
+        const float rf = __builtin_amdgcn_rcpf(f);
         uf[ks][j] = (VEC ? b8[j] : esc) * k8[j] * f;
         qf[ks][j] = q8[j] * f;
-        kd[j] = k8[j] * rf[ks][j];
-      }
-      if (r == 15) {
-        store4(&sm.tot[w][ch0], f32x4{fr[ks][0], fr[ks][1], fr[ks][2], fr[ks][3]});
-        store4(&sm.tot[w][ch0 + 4], f32x4{fr[ks][4], fr[ks][5], fr[ks][6], fr[ks][7]});
+        kd[j] = k8[j] * rf;
+        // k_s . g_s with g_s = t / f_s (replaced below if some |f| is out of range)
+        kgv[j] = k8[j] * (dpp_or<ROW_BCAST15>(0.f, f) * rf);
       }
       const Frag KD = Pol::make(kd);
       Pol::mma(ad, Pol::make(uf[ks]), KD);
       Pol::mma(pd, Pol::make(qf[ks]), KD);
-      // k_s . g_s with g_s = t / f_s (replaced below if some |f| is out of range)
-      float kgv[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) kgv[j] = k8[j] * (dpp_or<ROW_BCAST15>(0.f, fr[ks][j]) * rf[ks][j]);
       store4(&sm.u2.kg[row][ch0], f32x4{kgv[0], kgv[1], kgv[2], kgv[3]});
       store4(&sm.u2.kg[row][ch0 + 4], f32x4{kgv[4], kgv[5], kgv[6], kgv[7]});
     }
@@ -501,7 +499,7 @@ struct StateSmem {
 };
 
 template <int DKR, int DVB, typename InT, bool VEC>
-__global__ __launch_bounds__(256, 2) void chunk_state_kernel(const Params p) {
+__global__ __launch_bounds__(256, DVB == 16 ? 2 : 1) void chunk_state_kernel(const Params p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
   constexpr int DK = DKR < 32 ? 32 : DKR;
@@ -564,32 +562,11 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(const Params p) {
   float pw[VEC ? NCT : 1][4];
   auto rec_of = [&](int c) -> const unsigned char* {
     const int cc = c < nch ? c : nch - 1;
-    return p.rec + ((int64_t)(first + cc) * H + h) * p.rec_size;
+    return p.rec + ((int64_t)h * p.slots + first + cc) * p.rec_size;
   };
+  // Utilde, Qtilde and the write values m = w . v (rows 4g+i, accumulator layout) of chunk c
   auto pf_uq = [&](int c) {
     const unsigned char* rc = rec_of(c);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      fU[ks] = ld_frag<Frag>(rc + R::UT, w * KS + ks, l);
-      fQ[ks] = ld_frag<Frag>(rc + R::QT, w * KS + ks, l);
-    }
-  };
-  auto pf_t = [&](int c) {
-    const unsigned char* rc = rec_of(c);
-#pragma unroll
-    for (int st = 0; st < 2; ++st) fT[st] = ld_frag<Frag>(rc + R::TT, w * 2 + st, l);
-  };
-  auto pf_rest = [&](int c) {
-    const unsigned char* rc = rec_of(c);
-#pragma unroll
-    for (int st = 0; st < 2; ++st) fP[st] = ld_frag<Frag>(rc + R::PP, w * 2 + st, l);
-#pragma unroll
-    for (int m = 0; m < NRT; ++m) {
-      const int rt = w + 4 * m < DK / 16 ? w + 4 * m : 0;
-#pragma unroll
-      for (int st = 0; st < 2; ++st) fK[m][st] = ld_frag<Frag>(rc + R::KB, rt * 2 + st, l);
-      gC[m] = *reinterpret_cast<const f32x4*>(rc + R::GC + (16 * rt + 4 * g) * 4);
-    }
     const int64_t cc = (int64_t)(c < nch ? c : nch - 1) * CH;
     const int64_t last = bos + len - 1;
 #pragma unroll
@@ -604,6 +581,29 @@ __global__ __launch_bounds__(256, 2) void chunk_state_kernel(const Params p) {
         pv[ct][i] = vp[thv * DV + col];
         if constexpr (VEC) pw[ct][i] = p.write[thv * DV + col];
       }
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      fU[ks] = ld_frag<Frag>(rc + R::UT, w * KS + ks, l);
+      fQ[ks] = ld_frag<Frag>(rc + R::QT, w * KS + ks, l);
+    }
+  };
+  // T and P rows of block w are zero past token 16w + 15: only (w + 2) / 2 steps are loaded
+  auto pf_t = [&](int c) {
+    const unsigned char* rc = rec_of(c);
+    fT[0] = ld_frag<Frag>(rc + R::TT, w * 2, l);
+    if (w >= 2) fT[1] = ld_frag<Frag>(rc + R::TT, w * 2 + 1, l);
+  };
+  auto pf_rest = [&](int c) {
+    const unsigned char* rc = rec_of(c);
+    fP[0] = ld_frag<Frag>(rc + R::PP, w * 2, l);
+    if (w >= 2) fP[1] = ld_frag<Frag>(rc + R::PP, w * 2 + 1, l);
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+      const int rt = w + 4 * m < DK / 16 ? w + 4 * m : 0;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) fK[m][st] = ld_frag<Frag>(rc + R::KB, rt * 2 + st, l);
+      gC[m] = *reinterpret_cast<const f32x4*>(rc + R::GC + (16 * rt + 4 * g) * 4);
     }
   };
   if (nch > 0) {
@@ -749,7 +749,15 @@ PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int
                          int64_t heads, int dk, int dv, bool packed) {
   PrefillPlan pl;
   pl.chunk = CH;
-  pl.dv_block = (dv >= 32 && num_pairs * (dv / 32) >= 512) ? 32 : 16;
+  // Value columns per state workgroup: every workgroup of a head reads the head's whole
+  // operand record each chunk, so wider blocks cut the load traffic per CU; narrower
+  // blocks are used only when wide ones would leave CUs idle. DR_DV_BLOCK overrides
+  // (16, 32 or 64) for tuning.
+  pl.dv_block = (dv >= 32 && num_pairs * (dv / 32) >= 256) ? 32 : 16;
+  if (const char* e = getenv("DR_DV_BLOCK")) {
+    const int b = atoi(e);
+    if ((b == 16 || b == 32 || b == 64) && b <= dv) pl.dv_block = b;
+  }
   pl.ndvb = dv / pl.dv_block;
   const int64_t logical = num_pairs * pl.ndvb;
   pl.workgroups = (logical + 7) / 8 * 8;
@@ -785,6 +793,7 @@ static hipError_t launch_gate(const Params& p, const PrefillPlan& pl, bool bf16,
 
 template <int DKR>
 static hipError_t launch_dvb(const Params& p, const PrefillPlan& pl, bool bf16, bool vec, hipStream_t s) {
+  if (pl.dv_block == 64) return launch_gate<DKR, 64>(p, pl, bf16, vec, s);
   if (pl.dv_block == 32) return launch_gate<DKR, 32>(p, pl, bf16, vec, s);
   return launch_gate<DKR, 16>(p, pl, bf16, vec, s);
 }
