@@ -499,7 +499,7 @@ struct StateSmem {
 };
 
 template <int DKR, int DVB, typename InT, bool VEC>
-__global__ __launch_bounds__(256, DVB == 16 ? 2 : 1) void chunk_state_kernel(const Params p) {
+__global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
   constexpr int DK = DKR < 32 ? 32 : DKR;
