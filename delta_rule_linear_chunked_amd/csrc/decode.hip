@@ -1,9 +1,11 @@
 // Single-token decode step of the gated delta rule on gfx950.
 //
-// One workgroup per (sequence, head). The d_k x d_v fp32 state is streamed
-// from HBM once with 128-bit non-temporal loads, kept in registers, reduced
-// over key rows, updated and streamed back in place, so each state byte is
-// read once and written once:
+// One workgroup per (sequence, head, slice of DVS value columns): every value
+// column of the update is independent (delta_j needs only column j of S), so a
+// head splits into d_v / DVS workgroups with no exchange between them. The slice
+// of the fp32 state is streamed from HBM once with 128-bit non-temporal loads,
+// kept in registers, reduced over key rows, updated and streamed back in place,
+// so each state byte is read once and written once:
 //
 //   r_u = S^T (alpha . u),   r_q = S^T (alpha . q)        (one pass over S)
 //   delta = m - r_u                                        (delta-rule error)
@@ -17,32 +19,42 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#ifndef DECODE_DVS
+#define DECODE_DVS 128
+#endif
+#ifndef DECODE_NT
+#define DECODE_NT 256
+#endif
+
 namespace dr {
 
 template <int DK, int DV>
 struct DecodeShape {
-  static constexpr int COLS4 = DV / 4;                                 // float4 columns
-  static constexpr int RG = (DK < 256 / COLS4) ? DK : 256 / COLS4;     // row groups
+  static constexpr int DVS = DECODE_DVS < DV ? DECODE_DVS : DV;       // value columns per workgroup
+  static constexpr int NSPLIT = DV / DVS;
+  static constexpr int COLS4 = DVS / 4;                                // float4 columns
+  static constexpr int RG = (DK < DECODE_NT / COLS4) ? DK : DECODE_NT / COLS4;  // row groups
   static constexpr int RPT = DK / RG;                                  // rows per thread
   static constexpr int NT = RG * COLS4;                                // threads
   static_assert(RG * RPT == DK, "row split");
-  static_assert(NT <= 256 && NT % 64 == 0, "thread count");
+  static_assert(NT <= 512 && NT % 64 == 0, "thread count");
 };
 
 template <int DK, int DV, typename InT, bool VEC>
 __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const Params p) {
   using Sh = DecodeShape<DK, DV>;
-  constexpr int COLS4 = Sh::COLS4, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
-  __shared__ float s_q[DK], s_k[DK], s_au[DK], s_aq[DK], s_a[DK], s_m[DV];
-  __shared__ float s_red[2][RG][DV + 4];
+  constexpr int DVS = Sh::DVS, COLS4 = Sh::COLS4, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
+  __shared__ float s_q[DK], s_k[DK], s_au[DK], s_aq[DK], s_a[DK], s_m[DVS];
+  __shared__ float s_red[2][RG][DVS + 4];
   __shared__ float s_qk[RG];
-  __shared__ float s_delta[DV];
+  __shared__ float s_delta[DVS];
 
   const int tid = threadIdx.x;
   const int c4 = tid % COLS4;
   const int rg = tid / COLS4;
-  const int64_t nh = blockIdx.x;  // sequence * H + head
-  float* S = p.S + nh * (int64_t)DK * DV;
+  const int64_t nh = blockIdx.x / Sh::NSPLIT;          // sequence * H + head
+  const int col0 = (blockIdx.x % Sh::NSPLIT) * DVS;    // first value column of the slice
+  float* S = p.S + nh * (int64_t)DK * DV + col0;
 
   // Issue the state loads first: they do not depend on the token's vectors.
   f32x4 st[RPT];
@@ -55,7 +67,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
   // Stage the token's vectors.
   const InT* q = static_cast<const InT*>(p.q) + nh * DK;
   const InT* k = static_cast<const InT*>(p.k) + nh * DK;
-  const InT* v = static_cast<const InT*>(p.v) + nh * DV;
+  const InT* v = static_cast<const InT*>(p.v) + nh * DV + col0;
   const float* al = p.alpha + nh * DK;
   for (int i = tid; i < DK; i += NT) {
     const float a = al[i], qi = ld_f32(q + i), ki = ld_f32(k + i);
@@ -66,8 +78,8 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
     s_au[i] = a * ui;
     s_aq[i] = a * qi;
   }
-  for (int j = tid; j < DV; j += NT) {
-    const float wj = VEC ? p.write[nh * DV + j] : p.write[nh];
+  for (int j = tid; j < DVS; j += NT) {
+    const float wj = VEC ? p.write[nh * DV + col0 + j] : p.write[nh];
     s_m[j] = wj * ld_f32(v + j);
   }
   __syncthreads();
@@ -93,7 +105,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
   if (c4 == 0) s_qk[rg] = qk;
   __syncthreads();
 
-  if (tid < DV) {
+  if (tid < DVS) {
     float u_sum = 0.f, q_sum = 0.f, qk_sum = 0.f;
 #pragma unroll
     for (int g = 0; g < RG; ++g) {
@@ -103,7 +115,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
     }
     const float delta = s_m[tid] - u_sum;
     s_delta[tid] = delta;
-    p.o[nh * DV + tid] = fmaf(qk_sum, delta, q_sum);
+    p.o[nh * DV + col0 + tid] = fmaf(qk_sum, delta, q_sum);
   }
   __syncthreads();
 
@@ -124,7 +136,8 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
 template <int DK, int DV, typename InT, bool VEC>
 static hipError_t launch_decode_t(const Params& p, int64_t nheads, hipStream_t s) {
   constexpr int NT = DecodeShape<DK, DV>::NT;
-  hipLaunchKernelGGL((decode_kernel<DK, DV, InT, VEC>), dim3((unsigned)nheads), dim3(NT), 0, s, p);
+  hipLaunchKernelGGL((decode_kernel<DK, DV, InT, VEC>), dim3((unsigned)(nheads * DecodeShape<DK, DV>::NSPLIT)),
+                     dim3(NT), 0, s, p);
   return hipGetLastError();
 }
 

@@ -554,79 +554,79 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     }
   }
 
-  // ---- prefetch registers for the next chunk, each group loaded right after the current
-  // values' last use (past the last chunk the last record is reloaded and left unused)
-  Frag fU[KS], fQ[KS], fT[2], fP[2], fK[NRT][2];
-  f32x4 gC[NRT];
-  InT pv[NCT][4];
-  float pw[VEC ? NCT : 1][4];
-  auto rec_of = [&](int c) -> const unsigned char* {
+  // ---- operands of a chunk, in registers. Two sets alternate: while chunk c is computed
+  // from one, the loads of chunk c + 1 stream into the other, so the load path works in
+  // parallel with the MFMAs (past the last chunk the last record is reloaded and unused).
+  struct Ops {
+    Frag fU[KS], fQ[KS], fT[2], fP[2], fK[NRT][2];
+    f32x4 gC[NRT];
+    InT pv[NCT][4];
+    float pw[VEC ? NCT : 1][4];
+  };
+  auto rec_ptr = [&](int c) -> const unsigned char* {
     const int cc = c < nch ? c : nch - 1;
     return p.rec + ((int64_t)h * p.slots + first + cc) * p.rec_size;
   };
-  // Utilde, Qtilde and the write values m = w . v (rows 4g+i, accumulator layout) of chunk c
-  auto pf_uq = [&](int c) {
-    const unsigned char* rc = rec_of(c);
-    const int64_t cc = (int64_t)(c < nch ? c : nch - 1) * CH;
+  auto load_uq = [&](Ops& op, const unsigned char* rc, int ks) {
+    op.fU[ks] = ld_frag<Frag>(rc + R::UT, w * KS + ks, l);
+    op.fQ[ks] = ld_frag<Frag>(rc + R::QT, w * KS + ks, l);
+  };
+  // T and P rows of block w are zero past token 16w + 15: only (w + 2) / 2 steps are loaded
+  auto load_tp = [&](Ops& op, const unsigned char* rc) {
+    op.fT[0] = ld_frag<Frag>(rc + R::TT, w * 2, l);
+    op.fP[0] = ld_frag<Frag>(rc + R::PP, w * 2, l);
+    if (w >= 2) {
+      op.fT[1] = ld_frag<Frag>(rc + R::TT, w * 2 + 1, l);
+      op.fP[1] = ld_frag<Frag>(rc + R::PP, w * 2 + 1, l);
+    }
+  };
+  auto load_k = [&](Ops& op, const unsigned char* rc, int m) {
+    const int rt = w + 4 * m < DK / 16 ? w + 4 * m : 0;
+#pragma unroll
+    for (int st = 0; st < 2; ++st) op.fK[m][st] = ld_frag<Frag>(rc + R::KB, rt * 2 + st, l);
+    op.gC[m] = *reinterpret_cast<const f32x4*>(rc + R::GC + (16 * rt + 4 * g) * 4);
+  };
+  auto load_vw = [&](Ops& op, int c) {
+    const int cc = c < nch ? c : nch - 1;
     const int64_t last = bos + len - 1;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int64_t tv = bos + cc + 16 * w + 4 * g + i;
+      int64_t tv = bos + (int64_t)cc * CH + 16 * w + 4 * g + i;
       tv = tv > last ? last : tv;
       const int64_t thv = tv * H + h;
-      if constexpr (!VEC) pw[0][i] = p.write[thv];
+      if constexpr (!VEC) op.pw[0][i] = p.write[thv];
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const int col = dv0 + 16 * ct + r;
-        pv[ct][i] = vp[thv * DV + col];
-        if constexpr (VEC) pw[ct][i] = p.write[thv * DV + col];
+        op.pv[ct][i] = vp[thv * DV + col];
+        if constexpr (VEC) op.pw[ct][i] = p.write[thv * DV + col];
       }
     }
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      fU[ks] = ld_frag<Frag>(rc + R::UT, w * KS + ks, l);
-      fQ[ks] = ld_frag<Frag>(rc + R::QT, w * KS + ks, l);
-    }
   };
-  // T and P rows of block w are zero past token 16w + 15: only (w + 2) / 2 steps are loaded
-  auto pf_t = [&](int c) {
-    const unsigned char* rc = rec_of(c);
-    fT[0] = ld_frag<Frag>(rc + R::TT, w * 2, l);
-    if (w >= 2) fT[1] = ld_frag<Frag>(rc + R::TT, w * 2 + 1, l);
-  };
-  auto pf_rest = [&](int c) {
-    const unsigned char* rc = rec_of(c);
-    fP[0] = ld_frag<Frag>(rc + R::PP, w * 2, l);
-    if (w >= 2) fP[1] = ld_frag<Frag>(rc + R::PP, w * 2 + 1, l);
+  auto load_ops = [&](Ops& op, int c) {
+    const unsigned char* rc = rec_ptr(c);
 #pragma unroll
-    for (int m = 0; m < NRT; ++m) {
-      const int rt = w + 4 * m < DK / 16 ? w + 4 * m : 0;
+    for (int ks = 0; ks < KS; ++ks) load_uq(op, rc, ks);
+    load_tp(op, rc);
 #pragma unroll
-      for (int st = 0; st < 2; ++st) fK[m][st] = ld_frag<Frag>(rc + R::KB, rt * 2 + st, l);
-      gC[m] = *reinterpret_cast<const f32x4*>(rc + R::GC + (16 * rt + 4 * g) * 4);
-    }
+    for (int m = 0; m < NRT; ++m) load_k(op, rc, m);
+    load_vw(op, c);
   };
-  if (nch > 0) {
-    pf_uq(0);
-    pf_t(0);
-    pf_rest(0);
-  }
-  __syncthreads();
 
-  for (int c = 0; c < nch; ++c) {
+  auto chunk = [&](int c, Ops& cur, Ops& nxt) {
     const int64_t c0 = (int64_t)c * CH;
-    // write values m = w . v of rows 4g+i (accumulator layout), taken out of the prefetch
-    // registers now so that their next load does not wait on a late use
+    // write values m = w . v of rows 4g+i (accumulator layout)
     float mv[NCT][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const bool vi = c0 + 16 * w + 4 * g + i < len;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        mv[ct][i] = vi ? pw[VEC ? ct : 0][i] * (float)pv[ct][i] : 0.f;
-        asm volatile("" : "+v"(mv[ct][i]));
-      }
+      for (int ct = 0; ct < NCT; ++ct) mv[ct][i] = vi ? cur.pw[VEC ? ct : 0][i] * (float)cur.pv[ct][i] : 0.f;
     }
+    // the next chunk's operands stream into `nxt` in small groups placed between the
+    // MFMA groups below, so the load path and the matrix cores work at the same time
+    const unsigned char* rn = rec_ptr(c + 1);
+    load_vw(nxt, c + 1);
 
     // ================= X = Utilde S0, Y = Qtilde S0, R = M - X   (block row w)
     f32x4 accY[NCT];
@@ -636,12 +636,15 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
       for (int ct = 0; ct < NCT; ++ct) { accX[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; accY[ct] = accX[ct]; }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
+        load_uq(nxt, rn, ks);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const Frag B = sm.S.get8(16 * ct + r, 32 * ks + 8 * g);
-          Pol::mma(accX[ct], fU[ks], B);
-          Pol::mma(accY[ct], fQ[ks], B);
+          Pol::mma(accX[ct], cur.fU[ks], B);
+          Pol::mma(accY[ct], cur.fQ[ks], B);
         }
+        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);        // 4 global loads
+        __builtin_amdgcn_sched_group_barrier(0x008, 6 * NCT, 0);  // then this slice's MFMAs
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -651,11 +654,11 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
         sm.R.put4(16 * ct + r, 16 * w + 4 * g, rv);
       }
     }
-    pf_uq(c + 1);
     __syncthreads();
 
     // ================= delta = T R   (block row w)
     const int nst = (w + 2) / 2;
+    load_tp(nxt, rn);
     {
       f32x4 accD[NCT];
 #pragma unroll
@@ -664,13 +667,12 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
       for (int st = 0; st < 2; ++st) {
         if (st < nst) {
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Pol::mma(accD[ct], fT[st], sm.R.get8(16 * ct + r, 32 * st + 8 * g));
+          for (int ct = 0; ct < NCT; ++ct) Pol::mma(accD[ct], cur.fT[st], sm.R.get8(16 * ct + r, 32 * st + 8 * g));
         }
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) sm.D.put4(16 * ct + r, 16 * w + 4 * g, accD[ct]);
     }
-    pf_t(c + 1);
     __syncthreads();
 
     // ================= O = Y + P delta, and S <- Diag(Gamma_C) S0 + Kbar^T delta
@@ -685,7 +687,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
       for (int st = 0; st < 2; ++st) {
         if (st < nst) {
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Pol::mma(accY[ct], fP[st], DF[ct][st]);
+          for (int ct = 0; ct < NCT; ++ct) Pol::mma(accY[ct], cur.fP[st], DF[ct][st]);
         }
       }
 #pragma unroll
@@ -699,22 +701,30 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 #pragma unroll
       for (int m = 0; m < NRT; ++m) {
         const int rt = w + 4 * m;
+        load_k(nxt, rn, m);
         if (rt < DK / 16) {
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
             f32x4 acc;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = gC[m][i] * Sm[m][ct][i];
+            for (int i = 0; i < 4; ++i) acc[i] = cur.gC[m][i] * Sm[m][ct][i];
 #pragma unroll
-            for (int st = 0; st < 2; ++st) Pol::mma(acc, fK[m][st], DF[ct][st]);
+            for (int st = 0; st < 2; ++st) Pol::mma(acc, cur.fK[m][st], DF[ct][st]);
             Sm[m][ct] = acc;
             sm.S.put4(16 * ct + r, 16 * rt + 4 * g, acc);
           }
         }
       }
     }
-    pf_rest(c + 1);
     __syncthreads();
+  };
+
+  Ops opA, opB;
+  if (nch > 0) load_ops(opA, 0);
+  __syncthreads();
+  for (int c = 0; c < nch; c += 2) {
+    chunk(c, opA, opB);
+    if (c + 1 < nch) chunk(c + 1, opB, opA);
   }
 
   // ---- final state out

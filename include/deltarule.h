@@ -24,10 +24,15 @@
  *
  * Memory and layout. Every pointer argument is DEVICE memory on the current HIP
  * device, row-major and densely packed in the shapes given below, and 16-byte
- * aligned. The caller owns every buffer; the library keeps no pointer after a
- * call returns, allocates nothing and holds no global state except a
- * thread-local error message. Work is enqueued on `stream` and runs
- * asynchronously; outputs are valid once the stream reaches that point.
+ * aligned. The caller owns every argument buffer; the library keeps no pointer
+ * to them after a call returns. dr_decode_step uses no other device memory.
+ * dr_chunk_fwd needs a workspace between its two kernels (about 128.5 KiB per
+ * 64-token chunk and head at d_k = 128); it takes it stream-ordered on `stream`
+ * from a per-device memory pool owned by the library, which keeps what it has
+ * reserved for later calls (a larger problem grows it once). Apart from that
+ * pool the library holds only a thread-local error message. Work is enqueued
+ * on `stream` and runs asynchronously; outputs are valid once the stream
+ * reaches that point.
  *
  * Errors. Argument errors are detected on the host before anything is launched
  * and return a negative status (nothing is written). A failed kernel launch
@@ -101,7 +106,8 @@ typedef struct dr_dims {
  *   S_T        [N, H, d_k, d_v] float32 final states, or NULL to skip; may alias S0
  *              for an in-place update.
  * o must not alias any input. Results do not depend on how the library chunks
- * the sequence, up to rounding.
+ * the sequence, up to rounding. Returns DR_ERR_HIP, with nothing launched, when
+ * the workspace cannot be reserved.
  */
 int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                  const float* erase, const float* write, int variant,
@@ -137,7 +143,8 @@ int dr_version(void);
 
 /*
  * Launch shape the prefill would use for `dims` (for tests and profiling):
- * chunk length, value columns per workgroup, and the number of workgroups.
+ * chunk length, value columns per workgroup of the sequential state pass, and
+ * that pass's number of workgroups.
  * Returns DR_OK or an argument error.
  */
 int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t* dv_block,

@@ -101,9 +101,11 @@ def test_empty_problems_launch_nothing(lib):
 
 
 def test_plan(lib):
-    # 64 (sequence, head) pairs of d = 128: eight 16-wide value blocks -> 512 state workgroups
+    # 64 (sequence, head) pairs of d = 128: four 32-wide value blocks fill the 256 CUs
     c, b, w = drl.chunk_fwd_plan(4, 4096, 16, 128, 128)
-    assert (c, b, w) == (64, 16, 512)
+    assert (c, b, w) == (64, 32, 256)
+    # too few pairs for 32-wide blocks to fill the chip: 16-wide blocks
+    assert drl.chunk_fwd_plan(1, 4096, 16, 128, 128)[1:] == (16, 128)
     # 192 pairs: 32-wide blocks already give 768 workgroups
     assert drl.chunk_fwd_plan(1, 32768, 16, 128, 128, num_seqs=12) == (64, 32, 768)
     # grid padded to a multiple of the 8 XCDs
