@@ -38,6 +38,7 @@
 // otherwise (gates at or extremely close to zero) the block's diagonal tiles and
 // g come from running products, which are exact for any gate value.
 #include <cstdlib>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -496,6 +497,7 @@ struct StateSmem {
   OpTile<Pol, DVB, DK> S;   // state, transposed: [value column][key channel]
   OpTile<Pol, DVB, CH> R;   // (M - Utilde S0)^T: [value column][token]
   OpTile<Pol, DVB, CH> D;   // delta^T
+  float X[NBLK][16][DVB + 4];  // per wave: m = w . v in, then O out, between row and accumulator layouts
 };
 
 template <int DKR, int DVB, typename InT, bool VEC>
@@ -557,11 +559,18 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
   // ---- operands of a chunk, in registers. Two sets alternate: while chunk c is computed
   // from one, the loads of chunk c + 1 stream into the other, so the load path works in
   // parallel with the MFMAs (past the last chunk the last record is reloaded and unused).
+  // v and the write gate move as row segments: lane l holds token 16w + l/4 of the wave's
+  // block, value columns (l % 4) * E .. + E - 1 of the block, with 16-byte accesses.
+  constexpr int E = DVB / 4;
+  typedef InT RowV __attribute__((ext_vector_type(E)));
+  typedef float RowF __attribute__((ext_vector_type(E)));
+  using WRow = typename std::conditional<VEC, RowF, float>::type;
+  const int lr = l >> 2, lc = (l & 3) * E;
   struct Ops {
     Frag fU[KS], fQ[KS], fT[2], fP[2], fK[NRT][2];
     f32x4 gC[NRT];
-    InT pv[NCT][4];
-    float pw[VEC ? NCT : 1][4];
+    RowV pv;
+    WRow pw;
   };
   auto rec_ptr = [&](int c) -> const unsigned char* {
     const int cc = c < nch ? c : nch - 1;
@@ -589,19 +598,12 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
   auto load_vw = [&](Ops& op, int c) {
     const int cc = c < nch ? c : nch - 1;
     const int64_t last = bos + len - 1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int64_t tv = bos + (int64_t)cc * CH + 16 * w + 4 * g + i;
-      tv = tv > last ? last : tv;
-      const int64_t thv = tv * H + h;
-      if constexpr (!VEC) op.pw[0][i] = p.write[thv];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int col = dv0 + 16 * ct + r;
-        op.pv[ct][i] = vp[thv * DV + col];
-        if constexpr (VEC) op.pw[ct][i] = p.write[thv * DV + col];
-      }
-    }
+    int64_t tv = bos + (int64_t)cc * CH + 16 * w + lr;
+    tv = tv > last ? last : tv;
+    const int64_t thv = tv * H + h;
+    op.pv = *reinterpret_cast<const RowV*>(vp + thv * DV + dv0 + lc);
+    if constexpr (VEC) op.pw = *reinterpret_cast<const RowF*>(p.write + thv * DV + dv0 + lc);
+    else op.pw = p.write[thv];
   };
   auto load_ops = [&](Ops& op, int c) {
     const unsigned char* rc = rec_ptr(c);
@@ -615,13 +617,29 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 
   auto chunk = [&](int c, Ops& cur, Ops& nxt) {
     const int64_t c0 = (int64_t)c * CH;
-    // write values m = w . v of rows 4g+i (accumulator layout)
+    // write values m = w . v (zero past the sequence end), row layout -> LDS -> rows 4g+i of
+    // the accumulator layout
+    {
+      const bool vi = c0 + 16 * w + lr < len;
+#pragma unroll
+      for (int j4 = 0; j4 < E / 4; ++j4) {
+        f32x4 x;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float wg;
+          if constexpr (VEC) wg = cur.pw[4 * j4 + u];
+          else wg = cur.pw;
+          x[u] = vi ? wg * (float)cur.pv[4 * j4 + u] : 0.f;
+        }
+        store4(&sm.X[w][lr][lc + 4 * j4], x);
+      }
+    }
+    wave_lds_sync();
     float mv[NCT][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const bool vi = c0 + 16 * w + 4 * g + i < len;
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) mv[ct][i] = vi ? cur.pw[VEC ? ct : 0][i] * (float)cur.pv[ct][i] : 0.f;
+      for (int ct = 0; ct < NCT; ++ct) mv[ct][i] = sm.X[w][4 * g + i][16 * ct + r];
     }
     // the next chunk's operands stream into `nxt` in small groups placed between the
     // MFMA groups below, so the load path and the matrix cores work at the same time
@@ -690,12 +708,19 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
           for (int ct = 0; ct < NCT; ++ct) Pol::mma(accY[ct], cur.fP[st], DF[ct][st]);
         }
       }
+      // O: accumulator layout -> LDS -> row segments, stored with 16-byte accesses
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t rw = c0 + 16 * w + 4 * g + i;
-          if (rw < len) p.o[((bos + rw) * H + h) * DV + dv0 + 16 * ct + r] = accY[ct][i];
+        for (int i = 0; i < 4; ++i) sm.X[w][4 * g + i][16 * ct + r] = accY[ct][i];
+      }
+      wave_lds_sync();
+      {
+        const int64_t rw = c0 + 16 * w + lr;
+        if (rw < len) {
+          float* orow = p.o + ((bos + rw) * H + h) * DV + dv0 + lc;
+#pragma unroll
+          for (int j4 = 0; j4 < E / 4; ++j4) store4(orow + 4 * j4, *reinterpret_cast<const f32x4*>(&sm.X[w][lr][lc + 4 * j4]));
         }
       }
 #pragma unroll
