@@ -366,11 +366,14 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   __syncthreads();
 
   // ---------------------------------------------------------------- P, Kbar^T and Gamma_C out
+  // (rows of blocks 0 and 1 are zero in tokens 32..63: that step is never read, nor written)
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    float a8[8];
-    load8(&sm.u1.P[16 * w + r][32 * st + 8 * g], a8);
-    st_frag(rec + R::PP, w * 2 + st, l, Pol::make(a8));
+    if (st == 0 || w >= 2) {
+      float a8[8];
+      load8(&sm.u1.P[16 * w + r][32 * st + 8 * g], a8);
+      st_frag(rec + R::PP, w * 2 + st, l, Pol::make(a8));
+    }
   }
   for (int rt = w; rt < DK / 16; rt += 4) {
     const int chA = 16 * rt + r;
@@ -452,9 +455,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   }
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    float a8[8];
-    load8(&sm.u2.T[16 * w + r][32 * st + 8 * g], a8);
-    st_frag(rec + R::TT, w * 2 + st, l, Pol::make(a8));
+    if (st == 0 || w >= 2) {
+      float a8[8];
+      load8(&sm.u2.T[16 * w + r][32 * st + 8 * g], a8);
+      st_frag(rec + R::TT, w * 2 + st, l, Pol::make(a8));
+    }
   }
 }
 
