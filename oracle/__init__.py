@@ -24,3 +24,4 @@ from .recurrence import (  # noqa: F401
     rel_err,
 )
 from .chunked import chunked_reference  # noqa: F401
+from . import states  # noqa: F401
