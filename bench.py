@@ -111,6 +111,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-states", action="store_true", help="skip the snapshot and slot-pool timings")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the plain copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -171,6 +172,33 @@ def main():
     achieved_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
     plan = drl.chunk_fwd_plan(B, T, H, D, D)
 
+    # stored-state options on the same workload: snapshots every 64 and every 1024 tokens
+    states = None
+    if not args.no_states:
+        states = {}
+        for every in (1024, 64):
+            snaps = torch.empty((B * (T // every), H, D, D), dtype=torch.float32, device=dev)
+
+            def sstep(i, every=every, snaps=snaps):
+                s = sets[i % 2]
+                drl.dr_chunk_fwd_ex(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "kda", s["S0"], None,
+                                    o, S_T, snapshots=snaps, snapshot_every=every)
+
+            for i in range(3):
+                sstep(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.steps):
+                sstep(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / args.steps
+            states[f"prefill_snapshot_every_{every}"] = {
+                "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
+                "snapshot_bytes": snaps.numel() * 4, "overhead_vs_plain": ms / ms_step - 1.0}
+            del snaps
+
     traffic, kernel_traffic = None, None
     tfile = os.path.join(ROOT, "profiles", "chunk_fwd_kda_B4_T4096_H16_d128_traffic.json")
     if os.path.exists(tfile):
@@ -218,6 +246,27 @@ def main():
         torch.cuda.synchronize()
         dper = np.array([dev_ev[i].elapsed_time(dev_ev[i + 1]) for i in range(args.decode_steps)])
         dbytes = decode_bytes(N, HD, D, D)
+        pooled = None
+        if not args.no_states:
+            # the same steps through a slot pool: sequence n owns a random slot of the 1 GiB state
+            perm = torch.from_numpy(np.random.default_rng(7).permutation(N).astype(np.int32)).to(dev)
+
+            def pstep(i):
+                s = toks[i % pool]
+                drl.dr_decode_step_ex(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "kda", S, od,
+                                      state_idx=perm)
+
+            for i in range(10):
+                pstep(i)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(args.decode_steps):
+                pstep(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            pms = e0.elapsed_time(e1) / args.decode_steps
+            pooled = {"us_per_step": pms * 1e3, "state_GBps": dbytes / (pms * 1e-3) / 1e9,
+                      "slots": N, "order": "random permutation"}
         decode = {
             "workload": "decode KDA, 512 sequences x 32 heads, d_k=d_v=128, fp32 state 1 GiB in place, bf16 q/k/v",
             "us_per_step": dms * 1e3,
@@ -227,6 +276,7 @@ def main():
             "tokens_per_s": N / (dms * 1e-3),
             "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "bytes_per_step": dbytes, "steps": args.decode_steps,
+            "slot_pool": pooled,
         }
 
     copy = copy_calibration(dev, mib=256, reps=3)
@@ -250,6 +300,7 @@ def main():
         "latency_ms": {"p50": float(np.percentile(per, 50)), "p95": float(np.percentile(per, 95)),
                        "p99": float(np.percentile(per, 99)), "mean": float(per.mean())},
         "decode": decode,
+        "stored_states": states,
         "measured_copy_GBps": copy["copy_GBps"],
         "run": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count, "torch": torch.__version__,

@@ -17,8 +17,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["dr_chunk_fwd", "dr_decode_step", "chunk_fwd", "decode_step", "chunk_fwd_plan",
-           "library_path", "load_library", "VARIANTS", "DeltaRuleError"]
+__all__ = ["dr_chunk_fwd", "dr_decode_step", "dr_chunk_fwd_ex", "dr_decode_step_ex", "chunk_fwd",
+           "decode_step", "chunk_fwd_plan", "snapshot_count", "library_path", "load_library", "VARIANTS",
+           "DeltaRuleError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "lib", "libdeltarule.so")
@@ -35,6 +36,11 @@ class _Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("num_heads", ctypes.c_int64),
                 ("head_dim_k", ctypes.c_int64), ("head_dim_v", ctypes.c_int64),
                 ("num_seqs", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class _StateOpts(ctypes.Structure):
+    _fields_ = [("state_idx", ctypes.c_void_p), ("num_slots", ctypes.c_int64),
+                ("snapshots", ctypes.c_void_p), ("snapshot_every", ctypes.c_int64)]
 
 
 def library_path() -> str:
@@ -55,6 +61,11 @@ def load_library(path: Optional[str] = None):
     lib.dr_chunk_fwd.restype = ip
     lib.dr_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, fp, ctypes.POINTER(_Dims), vp]
     lib.dr_decode_step.restype = ip
+    op = ctypes.POINTER(_StateOpts)
+    lib.dr_chunk_fwd_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, vp, fp, fp, ctypes.POINTER(_Dims), op, vp]
+    lib.dr_chunk_fwd_ex.restype = ip
+    lib.dr_decode_step_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, fp, ctypes.POINTER(_Dims), op, vp]
+    lib.dr_decode_step_ex.restype = ip
     lib.dr_status_string.argtypes = [ip]
     lib.dr_status_string.restype = ctypes.c_char_p
     lib.dr_last_error.argtypes = []
@@ -116,11 +127,25 @@ def chunk_fwd_plan(B: int, T: int, H: int, dk: int, dv: int, num_seqs: Optional[
     return c.value, b.value, w.value
 
 
+def snapshot_count(lengths, every: int) -> int:
+    """Rows of the snapshot buffer for sequences of these lengths: floor(len / every) each."""
+    return int(sum(int(n) // int(every) for n in lengths))
+
+
 def dr_chunk_fwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, o, S_T) -> None:
     """Chunkwise prefill into caller-provided ``o`` (and ``S_T``). Shapes as in
     include/deltarule.h: q,k [B,T,H,dk]; v [B,T,H,dv]; alpha [B,T,H,dk] fp32; gates per
     variant (fp32); S0/S_T [N,H,dk,dv] fp32 or None; cu_seqlens [N+1] int32 or None;
     o [B,T,H,dv] fp32."""
+    dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T)
+
+
+def dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, o, S_T,
+                    state_idx=None, snapshots=None, snapshot_every: int = 0) -> None:
+    """``dr_chunk_fwd`` with stored-state options. With ``state_idx`` [N] int32, S0 and S_T
+    are pools [P,H,dk,dv] whose row state_idx[n] belongs to sequence n. ``snapshots``
+    [num,H,dk,dv] fp32 receives the state after every ``snapshot_every`` tokens of each
+    sequence (rows ordered by sequence, see ``snapshot_count``)."""
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -143,21 +168,36 @@ def dr_chunk_fwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, o, 
         N = cu_seqlens.shape[0] - 1
     else:
         N = B
+    rows = N
+    if state_idx is not None:
+        _need(state_idx, "state_idx", (N,), torch.int32, dev)
+        pools = [t for t in (S0, S_T) if t is not None]
+        rows = pools[0].shape[0] if pools else 0
     if S0 is not None:
-        _need(S0, "S0", (N, H, dk, dv), torch.float32, dev)
+        _need(S0, "S0", (rows, H, dk, dv), torch.float32, dev)
     if S_T is not None:
-        _need(S_T, "S_T", (N, H, dk, dv), torch.float32, dev)
+        _need(S_T, "S_T", (rows, H, dk, dv), torch.float32, dev)
+    if snapshots is not None:
+        _need(snapshots, "snapshots", (snapshots.shape[0], H, dk, dv), torch.float32, dev)
     _need(o, "o", (B, T, H, dv), torch.float32, dev)
     d = _Dims(B, T, H, dk, dv, N, _DT[q.dtype], 0)
-    st = lib.dr_chunk_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
-                          VARIANTS[variant], _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
-                          ctypes.byref(d), _stream(dev))
+    opts = _StateOpts(None if state_idx is None else state_idx.data_ptr(), rows,
+                      None if snapshots is None else snapshots.data_ptr(), int(snapshot_every or 0))
+    st = lib.dr_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
+                             VARIANTS[variant], _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
+                             ctypes.byref(d), ctypes.byref(opts), _stream(dev))
     _check(lib, st, "dr_chunk_fwd")
 
 
 def dr_decode_step(q, k, v, alpha, erase, write, variant: str, S, o) -> None:
     """One decode step in place on ``S`` [N,H,dk,dv] fp32; writes ``o`` [N,H,dv] fp32.
     q,k [N,H,dk]; v [N,H,dv]; alpha [N,H,dk]; gates per variant."""
+    dr_decode_step_ex(q, k, v, alpha, erase, write, variant, S, o)
+
+
+def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_idx=None) -> None:
+    """``dr_decode_step`` on a pool: with ``state_idx`` [N] int32, ``S`` is [P,H,dk,dv] and
+    sequence n updates row state_idx[n] in place (a slot outside the pool: o = 0, no state)."""
     lib = load_library()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -175,29 +215,49 @@ def dr_decode_step(q, k, v, alpha, erase, write, variant: str, S, o) -> None:
             raise ValueError(f"{variant} takes no write gate")
     else:
         _need(write, "write", ws, torch.float32, dev)
-    _need(S, "S", (N, H, dk, dv), torch.float32, dev)
+    rows = N
+    if state_idx is not None:
+        _need(state_idx, "state_idx", (N,), torch.int32, dev)
+        rows = S.shape[0]
+    _need(S, "S", (rows, H, dk, dv), torch.float32, dev)
     _need(o, "o", (N, H, dv), torch.float32, dev)
     d = _Dims(N, 1, H, dk, dv, N, _DT[q.dtype], 0)
-    st = lib.dr_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
-                            VARIANTS[variant], _ptr(S), _ptr(o), ctypes.byref(d), _stream(dev))
+    opts = _StateOpts(None if state_idx is None else state_idx.data_ptr(), rows, None, 0)
+    st = lib.dr_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
+                               VARIANTS[variant], _ptr(S), _ptr(o), ctypes.byref(d), ctypes.byref(opts),
+                               _stream(dev))
     _check(lib, st, "dr_decode_step")
 
 
 def chunk_fwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, cu_seqlens=None,
-              output_final_state: bool = True):
-    """Allocate o (and S_T) and run ``dr_chunk_fwd``. Returns (o, S_T or None)."""
-    B, T, H, _ = q.shape
+              output_final_state: bool = True, state_idx=None, snapshot_every: Optional[int] = None):
+    """Allocate o (and S_T) and run the prefill. Returns (o, S_T or None), plus the snapshot
+    tensor when ``snapshot_every`` is given. With ``state_idx``, S0 is a pool of states that
+    is updated in place (and returned as S_T)."""
+    B, T, H, dk = q.shape
     dv = v.shape[-1]
     N = B if cu_seqlens is None else cu_seqlens.shape[0] - 1
     o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
-    S_T = (torch.empty((N, H, q.shape[-1], dv), dtype=torch.float32, device=q.device)
-           if output_final_state else None)
-    dr_chunk_fwd(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T)
-    return o, S_T
+    if state_idx is not None:
+        if S0 is None:
+            raise ValueError("state_idx needs the pool of states as S0")
+        S_T = S0
+    else:
+        S_T = (torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
+               if output_final_state else None)
+    snaps = None
+    if snapshot_every is not None:
+        lens = [T] * B if cu_seqlens is None else (cu_seqlens[1:] - cu_seqlens[:-1]).tolist()
+        snaps = torch.empty((snapshot_count(lens, snapshot_every), H, dk, dv), dtype=torch.float32,
+                            device=q.device)
+    dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T, state_idx, snaps,
+                    snapshot_every or 0)
+    return (o, S_T) if snapshot_every is None else (o, S_T, snaps)
 
 
-def decode_step(q, k, v, alpha, erase, write, variant: str, S):
-    """Allocate o and run ``dr_decode_step`` (S is updated in place). Returns o."""
+def decode_step(q, k, v, alpha, erase, write, variant: str, S, state_idx=None):
+    """Allocate o and run the decode step (S, or its rows state_idx, updated in place).
+    Returns o."""
     o = torch.empty((q.shape[0], q.shape[1], v.shape[-1]), dtype=torch.float32, device=q.device)
-    dr_decode_step(q, k, v, alpha, erase, write, variant, S, o)
+    dr_decode_step_ex(q, k, v, alpha, erase, write, variant, S, o, state_idx)
     return o

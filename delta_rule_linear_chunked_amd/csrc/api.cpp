@@ -171,10 +171,37 @@ int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t*
   return DR_OK;
 }
 
+// Checks of the state-pool and snapshot options shared by prefill and decode.
+static int state_opts_checks(const dr_state_opts* opts, bool prefill) {
+  if (!opts) return DR_OK;
+  if (opts->state_idx) {
+    if (!aligned16(opts->state_idx)) return fail(DR_ERR_ALIGN, "state_idx must be 16-byte aligned");
+    if (opts->num_slots < 0) return fail(DR_ERR_SHAPE, "num_slots (%lld) is negative", (long long)opts->num_slots);
+    if (opts->num_slots > INT32_MAX) return fail(DR_ERR_UNSUPPORTED, "num_slots above 2^31 - 1");
+  }
+  if (opts->snapshots) {
+    if (!prefill) return fail(DR_ERR_SHAPE, "snapshots are a prefill option");
+    if (!aligned16(opts->snapshots)) return fail(DR_ERR_ALIGN, "snapshots must be 16-byte aligned");
+    if (opts->snapshot_every <= 0 || opts->snapshot_every % 64 != 0)
+      return fail(DR_ERR_SHAPE, "snapshot_every (%lld) must be a positive multiple of 64",
+                  (long long)opts->snapshot_every);
+    if (opts->snapshot_every / 64 > INT32_MAX) return fail(DR_ERR_UNSUPPORTED, "snapshot_every too large");
+  }
+  return DR_OK;
+}
+
 int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                  const float* erase, const float* write, int variant,
                  const float* S0, const int32_t* cu_seqlens,
                  float* o, float* S_T, const dr_dims* dims, hipStream_t stream) {
+  return dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T, dims, nullptr, stream);
+}
+
+int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* alpha,
+                    const float* erase, const float* write, int variant,
+                    const float* S0, const int32_t* cu_seqlens,
+                    float* o, float* S_T, const dr_dims* dims, const dr_state_opts* opts,
+                    hipStream_t stream) {
   g_last_error.clear();
   bool vec = false;
   int st = prefill_checks(dims, variant, erase, write, cu_seqlens, &vec);
@@ -187,8 +214,10 @@ int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha
   }
   st = check_ptrs({}, {{S0, "S0"}, {S_T, "S_T"}, {cu_seqlens, "cu_seqlens"}});
   if (st) return st;
+  st = state_opts_checks(opts, true);
+  if (st) return st;
   if (cu_seqlens == nullptr && dims->num_seqs > 0 && dims->seqlen == 0 && S_T == nullptr)
-    return DR_OK;  // nothing to compute and nothing to write
+    return DR_OK;  // nothing to compute and nothing to write (no snapshot fits in zero tokens)
   if (dims->num_seqs == 0) return DR_OK;
 
   dr::Params p{};
@@ -206,6 +235,12 @@ int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha
   p.ndvb = pl.ndvb;
   p.grid_logical = (int32_t)(pairs * pl.ndvb);
   p.nseq = (int32_t)dims->num_seqs;
+  if (opts) {
+    p.sidx = opts->state_idx;
+    p.nslots = opts->num_slots;
+    p.snap = opts->snapshots;
+    p.snap_chunks = opts->snapshots ? (int32_t)(opts->snapshot_every / 64) : 0;
+  }
   void* ws = nullptr;
   hipError_t e = hipSuccess;
   if (pl.workspace > 0) {
@@ -224,6 +259,13 @@ int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha
 int dr_decode_step(const void* q, const void* k, const void* v, const float* alpha,
                    const float* erase, const float* write, int variant,
                    float* S, float* o, const dr_dims* dims, hipStream_t stream) {
+  return dr_decode_step_ex(q, k, v, alpha, erase, write, variant, S, o, dims, nullptr, stream);
+}
+
+int dr_decode_step_ex(const void* q, const void* k, const void* v, const float* alpha,
+                      const float* erase, const float* write, int variant,
+                      float* S, float* o, const dr_dims* dims, const dr_state_opts* opts,
+                      hipStream_t stream) {
   g_last_error.clear();
   int st = check_dims_common(dims);
   if (st) return st;
@@ -238,7 +280,13 @@ int dr_decode_step(const void* q, const void* k, const void* v, const float* alp
   st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {alpha, "alpha"}, {erase, "erase"}, {S, "S"}, {o, "o"}},
                   {{write, "write"}});
   if (st) return st;
+  st = state_opts_checks(opts, false);
+  if (st) return st;
   dr::Params p{};
+  if (opts) {
+    p.sidx = opts->state_idx;
+    p.nslots = opts->num_slots;
+  }
   p.q = q; p.k = k; p.v = v; p.alpha = alpha;
   p.erase = erase;
   p.write = (variant == DR_KDA || variant == DR_CKDA) ? erase : write;

@@ -37,6 +37,12 @@ struct Params {
   int32_t slots;        // chunk slots
   int32_t cps;          // fixed length: chunks per sequence
   int32_t nseq;         // sequences
+  // state pools and snapshots
+  const int32_t* sidx;  // slot of each sequence in the state buffers (null: slot n)
+  int64_t nslots;       // slots of the state buffers when sidx is set
+  float* snap;          // prefill: states after every snap_chunks chunks of each sequence (may be null)
+  int32_t snap_chunks;  // chunks between snapshots
+  int32_t* snap_first;  // packed: first snapshot row of each sequence
 };
 
 __device__ __forceinline__ float ld_f32(const float* p) { return *p; }

@@ -54,7 +54,19 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
   const int rg = tid / COLS4;
   const int64_t nh = blockIdx.x / Sh::NSPLIT;          // sequence * H + head
   const int col0 = (blockIdx.x % Sh::NSPLIT) * DVS;    // first value column of the slice
-  float* S = p.S + nh * (int64_t)DK * DV + col0;
+  // state row: the sequence's own, or slot state_idx[n] of a pool; a slot outside the
+  // pool has no state: the output is zero and nothing is read or written
+  int64_t srow = nh;
+  if (p.sidx) {
+    const int64_t n = nh / p.H;
+    const int32_t sl = p.sidx[n];
+    if (sl < 0 || sl >= p.nslots) {
+      for (int j = tid; j < DVS; j += NT) p.o[nh * DV + col0 + j] = 0.f;
+      return;
+    }
+    srow = (int64_t)sl * p.H + (nh - n * p.H);
+  }
+  float* S = p.S + srow * (int64_t)DK * DV + col0;
 
   // Issue the state loads first: they do not depend on the token's vectors.
   f32x4 st[RPT];

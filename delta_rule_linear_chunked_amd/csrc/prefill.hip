@@ -132,6 +132,27 @@ __global__ __launch_bounds__(256) void chunk_plan_kernel(const Params p) {
   const int total = s_carry;
   if (tid == 0) p.seq_first[p.nseq] = total;
   __syncthreads();  // seq_first complete (the workgroup-scope fence covers global memory)
+  if (p.snap) {  // first snapshot row of each sequence: exclusive scan of floor(len / stride)
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    const int stride = p.snap_chunks * CH;
+    for (int base = 0; base < p.nseq; base += 256) {
+      const int n = base + tid;
+      const int ns = n < p.nseq ? (p.cu[n + 1] - p.cu[n]) / stride : 0;
+      s_scan[tid] = ns;
+      __syncthreads();
+      for (int d = 1; d < 256; d <<= 1) {
+        const int x = tid >= d ? s_scan[tid - d] : 0;
+        __syncthreads();
+        s_scan[tid] += x;
+        __syncthreads();
+      }
+      if (n < p.nseq) p.snap_first[n] = s_carry + s_scan[tid] - ns;
+      __syncthreads();
+      if (tid == 255) s_carry += s_scan[255];
+      __syncthreads();
+    }
+  }
   for (int slot = tid; slot < p.slots; slot += 256) {
     int n = -1, c0 = 0;
     if (slot < total) {
@@ -536,6 +557,16 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     first = n * p.cps;
   }
   const int nch = (int)((len + CH - 1) / CH);
+  // state slot: row n of S0 / S_T, or state_idx[n] of a pool (outside the pool: start from
+  // zero and store no final state)
+  int64_t srow = n;
+  bool has_row = true;
+  if (p.sidx) {
+    const int32_t sl = p.sidx[n];
+    has_row = sl >= 0 && sl < p.nslots;
+    srow = sl;
+  }
+  const int64_t snap_base = !p.snap ? 0 : p.cu ? (int64_t)p.snap_first[n] : (int64_t)n * (p.T / (p.snap_chunks * CH));
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
   const int DV = p.DV;
@@ -553,7 +584,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ch = 16 * rt + 4 * g + i;
-          if (p.S0 && ch < DKR) x[i] = p.S0[(((int64_t)n * H + h) * DKR + ch) * DV + dv0 + 16 * ct + r];
+          if (p.S0 && has_row && ch < DKR) x[i] = p.S0[((srow * H + h) * DKR + ch) * DV + dv0 + 16 * ct + r];
         }
         sm.S.put4(16 * ct + r, 16 * rt + 4 * g, x);
       }
@@ -618,6 +649,25 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 #pragma unroll
     for (int m = 0; m < NRT; ++m) load_k(op, rc, m);
     load_vw(op, c);
+  };
+
+  // this workgroup's block of the fp32 state (key rows x DVB value columns) to a
+  // [d_k, d_v] state at `dst`
+  auto store_state = [&](float* dst) {
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+      const int rt = w + 4 * m;
+      if (rt < DK / 16) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int ch = 16 * rt + 4 * g + i;
+            if (ch < DKR) dst[(int64_t)ch * DV + dv0 + 16 * ct + r] = Sm[m][ct][i];
+          }
+        }
+      }
+    }
   };
 
   auto chunk = [&](int c, Ops& cur, Ops& nxt) {
@@ -746,6 +796,10 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
         }
       }
     }
+    // snapshot: the state after (c + 1) * 64 tokens, when that is a multiple of the stride
+    // and still inside the sequence
+    if (p.snap && (c + 1) % p.snap_chunks == 0 && (int64_t)(c + 1) * CH <= len)
+      store_state(p.snap + ((snap_base + (c + 1) / p.snap_chunks - 1) * H + h) * DKR * DV);
     __syncthreads();
   };
 
@@ -758,22 +812,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
   }
 
   // ---- final state out
-  if (p.S) {
-#pragma unroll
-    for (int m = 0; m < NRT; ++m) {
-      const int rt = w + 4 * m;
-      if (rt < DK / 16) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ch = 16 * rt + 4 * g + i;
-            if (ch < DKR) p.S[(((int64_t)n * H + h) * DKR + ch) * DV + dv0 + 16 * ct + r] = Sm[m][ct][i];
-          }
-        }
-      }
-    }
-  }
+  if (p.S && has_row) store_state(p.S + (srow * H + h) * DKR * DV);
 }
 
 // ============================================================================ host
@@ -804,7 +843,7 @@ PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int
   const int64_t cps = (seqlen + CH - 1) / CH;
   pl.slots = packed ? cps + num_seqs : batch * cps;
   pl.rec_size = rec_size_for(dk);
-  const int64_t tables = packed ? ((2 * pl.slots + num_seqs + 1) * 4 + 255) / 256 * 256 : 0;
+  const int64_t tables = packed ? ((2 * pl.slots + 2 * num_seqs + 1) * 4 + 255) / 256 * 256 : 0;
   pl.workspace = pl.slots * heads * pl.rec_size + tables;
   return pl;
 }
@@ -850,6 +889,7 @@ hipError_t launch_prefill(Params p, const PrefillPlan& pl, void* ws, int dk, boo
     p.chunk_seq = tables;
     p.chunk_c0 = tables + pl.slots;
     p.seq_first = tables + 2 * pl.slots;
+    p.snap_first = tables + 2 * pl.slots + p.nseq + 1;
   }
   switch (dk) {
     case 16: return launch_dvb<16>(p, pl, bf16, vec, s);

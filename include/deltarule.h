@@ -62,7 +62,7 @@ typedef enum dr_status {
   DR_ERR_SHAPE = -2,       /* negative or inconsistent sizes */
   DR_ERR_DTYPE = -3,       /* in_dtype is not DR_F32 / DR_BF16 */
   DR_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
-  DR_ERR_UNSUPPORTED = -5, /* head size outside {16, 32, 64, 128} */
+  DR_ERR_UNSUPPORTED = -5, /* head size outside {16, 32, 64, 128}, or a size beyond the limits */
   DR_ERR_VARIANT = -6,     /* unknown variant, or gate pointers that do not fit it */
   DR_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed */
 } dr_status;
@@ -130,6 +130,53 @@ int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha
 int dr_decode_step(const void* q, const void* k, const void* v, const float* alpha,
                    const float* erase, const float* write, int variant,
                    float* S, float* o, const dr_dims* dims, hipStream_t stream);
+
+/*
+ * Stored states for prefix sharing and continuous batching. Section 3 of the
+ * course page above keeps three things apart: padding, a document reset (each
+ * sequence starts from its own state) and a state snapshot kept for prefix
+ * sharing, and forbids two requests sharing a state with different content.
+ *
+ *   state_idx      [N] int32 (device) or NULL. When given, the state buffers
+ *                  (S0 and S_T of a prefill, S of a decode step) are pools of
+ *                  num_slots rows [num_slots, H, d_k, d_v] and sequence n uses
+ *                  row state_idx[n]. A slot outside [0, num_slots) means the
+ *                  sequence has no stored state: a prefill starts it from zero
+ *                  and stores no final state; a decode step writes zeros to its
+ *                  output and touches no state. Rows nobody names are left as
+ *                  they are. Two sequences naming the same slot race (undefined).
+ *   num_slots      rows of the pools (used only with state_idx).
+ *   snapshots      prefill only: float32 [num_snapshots, H, d_k, d_v] or NULL.
+ *                  Sequence n stores floor(len_n / snapshot_every) states, the
+ *                  state after (j + 1) * snapshot_every of its tokens in row
+ *                  first_n + j, where first_n = sum over m < n of
+ *                  floor(len_m / snapshot_every). Resuming a prefill from row
+ *                  first_n + j over the rest of the sequence gives the same
+ *                  outputs and final state, up to rounding.
+ *   snapshot_every a positive multiple of 64 (snapshots sit on chunk boundaries);
+ *                  otherwise DR_ERR_SHAPE.
+ * Snapshots cost one extra state write per snapshot (d_k * d_v * 4 bytes per head).
+ */
+typedef struct dr_state_opts {
+  const int32_t* state_idx;
+  int64_t num_slots;
+  float* snapshots;
+  int64_t snapshot_every;
+} dr_state_opts;
+
+/* dr_chunk_fwd with stored-state options (opts may be NULL: same as dr_chunk_fwd). */
+int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* alpha,
+                    const float* erase, const float* write, int variant,
+                    const float* S0, const int32_t* cu_seqlens,
+                    float* o, float* S_T, const dr_dims* dims, const dr_state_opts* opts,
+                    hipStream_t stream);
+
+/* dr_decode_step with a slot pool (opts may be NULL: same as dr_decode_step;
+ * snapshots must be NULL). With state_idx, S is the pool. */
+int dr_decode_step_ex(const void* q, const void* k, const void* v, const float* alpha,
+                      const float* erase, const float* write, int variant,
+                      float* S, float* o, const dr_dims* dims, const dr_state_opts* opts,
+                      hipStream_t stream);
 
 /* Static description of a status code. Never NULL. */
 const char* dr_status_string(int status);

@@ -110,3 +110,29 @@ def test_plan(lib):
     assert drl.chunk_fwd_plan(1, 32768, 16, 128, 128, num_seqs=12) == (64, 32, 768)
     # grid padded to a multiple of the 8 XCDs
     assert drl.chunk_fwd_plan(1, 64, 2, 16, 16)[2] == 8
+
+
+def _opts(state_idx=None, num_slots=0, snapshots=None, every=0):
+    return drl._StateOpts(state_idx, num_slots, snapshots, every)
+
+
+@pytest.mark.parametrize("opts,expect", [
+    (dict(snapshots=0x100000, every=100), -2),         # stride not a multiple of 64
+    (dict(snapshots=0x100000, every=0), -2),
+    (dict(snapshots=0x100004, every=64), -4),          # misaligned snapshot buffer
+    (dict(state_idx=0x100004, num_slots=4), -4),       # misaligned slot table
+    (dict(state_idx=0x100000, num_slots=-1), -2),
+])
+def test_state_options_are_checked(lib, opts, expect):
+    o = _opts(**opts)
+    st = lib.dr_chunk_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, None, FAKE, None,
+                             ctypes.byref(dims()), ctypes.byref(o), None)
+    assert st == expect, lib.dr_last_error()
+
+
+def test_decode_takes_no_snapshots(lib):
+    o = _opts(snapshots=0x100000, every=64)
+    d = dims(T=1)
+    st = lib.dr_decode_step_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, ctypes.byref(d),
+                               ctypes.byref(o), None)
+    assert st == -2, lib.dr_last_error()
