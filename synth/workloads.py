@@ -139,6 +139,32 @@ def _ckda_masks(rng, alpha, erase):
     return alpha, erase
 
 
+# Pre-activation form of each recipe, for the fused input preparation: the decay and gate
+# activations (and q/k normalisation) are then applied by the consumer, not here.
+#   alpha_act/alpha_scale: "exp_neg_softplus" with c = 1 (kda_tiny) or 0.1, or "tanh" (ckda,
+#   whose pre-activation is 1.5 z); gate_act "sigmoid" with scale 1, or 2 for ckda's beta.
+PREP = {
+    "kda_tiny": dict(l2norm_qk=True, alpha_act="exp_neg_softplus", alpha_scale=1.0, gate_act="sigmoid", gate_scale=1.0),
+    "kda": dict(l2norm_qk=True, alpha_act="exp_neg_softplus", alpha_scale=0.1, gate_act="sigmoid", gate_scale=1.0),
+    "rda": dict(l2norm_qk=True, alpha_act="exp_neg_softplus", alpha_scale=0.1, gate_act="sigmoid", gate_scale=1.0),
+    "gdn2": dict(l2norm_qk=True, alpha_act="exp_neg_softplus", alpha_scale=0.1, gate_act="sigmoid", gate_scale=1.0),
+    "ckda": dict(l2norm_qk=True, alpha_act="tanh", alpha_scale=1.0, gate_act="sigmoid", gate_scale=2.0),
+}
+
+
+def _preact_gates(rng, recipe: str, za, ze, zw):
+    """Pre-activations in the draw order of the activated recipe: Complex KDA's forced
+    decays become +-inf (tanh -> +-1) and its beta = 2 entries +inf (2 sigmoid -> 2)."""
+    if recipe == "ckda":
+        za = 1.5 * za
+        force = rng.random(za.shape) < 0.10
+        sign = np.where(rng.random(za.shape) < 0.5, -1.0, 1.0)
+        za = np.where(force, sign * np.inf, za)
+        at_two = rng.random(ze.shape) < 0.05
+        ze = np.where(at_two, np.inf, ze)
+    return za, ze, zw
+
+
 def draw_varlen_lengths(rng, n: int = 12, total: int = 32768, lo: int = 256, hi: int = 6000):
     """Draw n-1 lengths uniformly (integers in [lo, hi]) and set the last so the lengths
     sum to total; redraw until the last one also lies in [lo, hi]."""
@@ -154,9 +180,12 @@ def draw_varlen_lengths(rng, n: int = 12, total: int = 32768, lo: int = 256, hi:
 
 def make_prefill(recipe: str, B: int, T: int, H: int, dk: int, dv: int, *,
                  in_dtype: str = "bf16", seed: int = 0, random_s0: bool = True,
-                 lengths=None, chunk: int = 64, name: str = "") -> Workload:
+                 lengths=None, chunk: int = 64, name: str = "", preact: bool = False,
+                 alpha_dtype: str = "f32") -> Workload:
     """Prefill workload. With ``lengths`` the sequences are packed along T of a single
-    batch row (B must be 1) and described by cu_seqlens."""
+    batch row (B must be 1) and described by cu_seqlens. With ``preact`` q and k are not
+    normalised and alpha / erase / write hold pre-activations (``meta["prep"]`` names the
+    activations); ``alpha_dtype="bf16"`` rounds alpha to bfloat16."""
     rng = np.random.default_rng(seed)
     cu = None
     if lengths is not None:
@@ -167,52 +196,64 @@ def make_prefill(recipe: str, B: int, T: int, H: int, dk: int, dv: int, *,
         cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
     N = len(cu) - 1 if cu is not None else B
     lead = (B, T, H)
-    q = _l2_normalise(rng.standard_normal(lead + (dk,)))
-    k = _l2_normalise(rng.standard_normal(lead + (dk,)))
+    q, k = rng.standard_normal(lead + (dk,)), rng.standard_normal(lead + (dk,))
+    if not preact:
+        q, k = _l2_normalise(q), _l2_normalise(k)
     v = rng.standard_normal(lead + (dv,))
     za, ze, zw = _draw_gates(rng, recipe, lead, dk, dv)
     S0 = rng.standard_normal((N, H, dk, dv)) / np.sqrt(dk) if random_s0 else None
-    alpha, erase, write = _finish_gates(rng, recipe, za, ze, zw)
-    if recipe == "ckda":
-        alpha, erase = _ckda_masks(rng, alpha, erase)
+    if preact:
+        alpha, erase, write = _preact_gates(rng, recipe, za, ze, zw)
+    else:
+        alpha, erase, write = _finish_gates(rng, recipe, za, ze, zw)
+        if recipe == "ckda":
+            alpha, erase = _ckda_masks(rng, alpha, erase)
+    meta = {"recipe": recipe, "seed": seed, "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
+            "lengths": None if lengths is None else [int(x) for x in lengths]}
+    if preact:
+        meta["prep"] = dict(PREP[recipe], alpha_dtype=alpha_dtype)
     return Workload(
-        name=name or f"{recipe}_B{B}_T{T}_H{H}_d{dk}x{dv}",
+        name=name or f"{recipe}_B{B}_T{T}_H{H}_d{dk}x{dv}" + ("_preact" if preact else ""),
         variant=recipe_variant(recipe), in_dtype=in_dtype,
         q=_to_input(q, in_dtype), k=_to_input(k, in_dtype), v=_to_input(v, in_dtype),
-        alpha=alpha.astype(np.float32), erase=erase.astype(np.float32),
+        alpha=_to_input(alpha, alpha_dtype), erase=erase.astype(np.float32),
         write=None if write is None else write.astype(np.float32),
-        S0=None if S0 is None else S0.astype(np.float32), cu_seqlens=cu, chunk=chunk,
-        meta={"recipe": recipe, "seed": seed, "B": B, "T": T, "H": H, "dk": dk, "dv": dv,
-              "lengths": None if lengths is None else [int(x) for x in lengths]},
+        S0=None if S0 is None else S0.astype(np.float32), cu_seqlens=cu, chunk=chunk, meta=meta,
     )
 
 
 def make_decode(recipe: str, N: int, H: int, dk: int, dv: int, *, steps: int = 1,
                 in_dtype: str = "bf16", seed: int = 0, with_state: bool = True,
-                name: str = "") -> Workload:
+                name: str = "", preact: bool = False, alpha_dtype: str = "f32") -> Workload:
     """Decode workload: ``steps`` consecutive single-token inputs for N sequences x H heads.
     Token arrays have a leading step axis: q,k [steps,N,H,dk], v [steps,N,H,dv], gates
     likewise. S0 [N,H,dk,dv] is the state before the first step."""
     rng = np.random.default_rng(seed)
     lead = (steps, N, H)
-    q = _l2_normalise(rng.standard_normal(lead + (dk,)))
-    k = _l2_normalise(rng.standard_normal(lead + (dk,)))
+    q, k = rng.standard_normal(lead + (dk,)), rng.standard_normal(lead + (dk,))
+    if not preact:
+        q, k = _l2_normalise(q), _l2_normalise(k)
     v = rng.standard_normal(lead + (dv,))
     za, ze, zw = _draw_gates(rng, recipe, lead, dk, dv)
     S0 = None
     if with_state:
         S0 = (rng.standard_normal((N, H, dk, dv)) / np.sqrt(dk)).astype(np.float32)
-    alpha, erase, write = _finish_gates(rng, recipe, za, ze, zw)
-    if recipe == "ckda":
-        alpha, erase = _ckda_masks(rng, alpha, erase)
+    if preact:
+        alpha, erase, write = _preact_gates(rng, recipe, za, ze, zw)
+    else:
+        alpha, erase, write = _finish_gates(rng, recipe, za, ze, zw)
+        if recipe == "ckda":
+            alpha, erase = _ckda_masks(rng, alpha, erase)
+    meta = {"recipe": recipe, "seed": seed, "N": N, "H": H, "dk": dk, "dv": dv, "steps": steps}
+    if preact:
+        meta["prep"] = dict(PREP[recipe], alpha_dtype=alpha_dtype)
     return Workload(
-        name=name or f"decode_{recipe}_N{N}_H{H}_d{dk}x{dv}_s{steps}",
+        name=name or f"decode_{recipe}_N{N}_H{H}_d{dk}x{dv}_s{steps}" + ("_preact" if preact else ""),
         variant=recipe_variant(recipe), in_dtype=in_dtype,
         q=_to_input(q, in_dtype), k=_to_input(k, in_dtype), v=_to_input(v, in_dtype),
-        alpha=alpha.astype(np.float32), erase=erase.astype(np.float32),
+        alpha=_to_input(alpha, alpha_dtype), erase=erase.astype(np.float32),
         write=None if write is None else write.astype(np.float32),
-        S0=S0, cu_seqlens=None, chunk=1,
-        meta={"recipe": recipe, "seed": seed, "N": N, "H": H, "dk": dk, "dv": dv, "steps": steps},
+        S0=S0, cu_seqlens=None, chunk=1, meta=meta,
     )
 
 
