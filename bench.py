@@ -31,13 +31,13 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
-def prefill_work(B, T, H, dk, dv, C=64, in_bytes=2, gate_bytes=4, n_states=None):
+def prefill_work(B, T, H, dk, dv, C=64, in_bytes=2, gate_bytes=4, n_states=None, alpha_bytes=4):
     """Algorithmic bytes and useful FLOPs of one prefill call.
-    Bytes per token-head: q, k, v inputs + alpha (fp32) + gates + o (fp32); plus the
-    initial and final state of every (sequence, head). FLOPs: the chunkwise form's
-    useful (triangular) work per full chunk-head, pro rata per token."""
+    Bytes per token-head: q, k, v inputs + alpha (fp32, or bf16 pre-activations) + gates +
+    o (fp32); plus the initial and final state of every (sequence, head). FLOPs: the
+    chunkwise form's useful (triangular) work per full chunk-head, pro rata per token."""
     th = B * T * H
-    per_th = (2 * dk + dv) * in_bytes + 4 * dk + gate_bytes + 4 * dv
+    per_th = (2 * dk + dv) * in_bytes + alpha_bytes * dk + gate_bytes + 4 * dv
     n_states = B if n_states is None else n_states
     bytes_ = th * per_th + 2 * n_states * H * dk * dv * 4
     f_chunk = 2 * (C * (C - 1) // 2 * dk + C * (C + 1) // 2 * dk + C * (C - 1) * (C - 2) // 6
@@ -107,11 +107,12 @@ def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-states", action="store_true", help="skip the snapshot and slot-pool timings")
+    ap.add_argument("--no-prep", action="store_true", help="skip the fused input preparation timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the plain copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -155,17 +156,26 @@ def main():
         step(i)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # the timed steps run back to back with events only at the ends of the loop (an event
+    # between every pair of calls adds a few microseconds per call); a second loop with an
+    # event after every call gives the per-call percentiles
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     evs[0].record(stream)
     for i in range(args.steps):
         step(i)
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])  # ms per launch
-    total_ms = evs[0].elapsed_time(evs[-1])
-    ms_step = total_ms / args.steps
+    per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])  # ms per call
     tokens = B * T
     value = tokens / (ms_step * 1e-3)
     alg_bytes, flops = prefill_work(B, T, H, D, D)
@@ -198,6 +208,40 @@ def main():
                 "ms_per_step": ms, "tokens_per_s": tokens / (ms * 1e-3),
                 "snapshot_bytes": snaps.numel() * 4, "overhead_vs_plain": ms / ms_step - 1.0}
             del snaps
+
+    # fused input preparation on the same shape: raw q/k (normalised in the kernel), decay as
+    # bf16 pre-activation of exp(-0.1 softplus(z)), beta as pre-activation of sigmoid
+    fused = None
+    if not args.no_prep:
+        psets = []
+        for seed in (1002, 2002):
+            wl = synth.make_prefill("kda", B, T, H, D, D, in_dtype="bf16", seed=seed, preact=True, alpha_dtype="bf16")
+            kw = {k: v for k, v in wl.meta["prep"].items() if k != "alpha_dtype"}
+            psets.append(dict(q=t(wl.q, True), k=t(wl.k, True), v=t(wl.v, True), alpha=t(wl.alpha, True),
+                              erase=t(wl.erase), S0=t(wl.S0)))
+            del wl
+
+        def pstep(i):
+            s = psets[i % 2]
+            drl.dr_chunk_fwd_ex(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "kda", s["S0"], None,
+                                o, S_T, prep=kw)
+
+        for i in range(3):
+            pstep(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            pstep(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / args.steps
+        pbytes, _ = prefill_work(B, T, H, D, D, alpha_bytes=2)
+        fused = {"workload": "KDA prefill B=4 T=4096 H=16 d=128, raw bf16 q/k, bf16 decay pre-activations, "
+                             "beta pre-activations; normalisation and activations inside the kernels",
+                 "ms_per_step": pms, "tokens_per_s": tokens / (pms * 1e-3), "alg_bytes_per_launch": pbytes,
+                 "achieved_GBps": pbytes / (pms * 1e-3) / 1e9}
+        del psets
 
     traffic, kernel_traffic = None, None
     tfile = os.path.join(ROOT, "profiles", "chunk_fwd_kda_B4_T4096_H16_d128_traffic.json")
@@ -298,9 +342,11 @@ def main():
                  "frac_of_bf16_peak": flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                  "useful_flop_per_launch": flops},
         "latency_ms": {"p50": float(np.percentile(per, 50)), "p95": float(np.percentile(per, 95)),
-                       "p99": float(np.percentile(per, 99)), "mean": float(per.mean())},
+                       "p99": float(np.percentile(per, 99)), "mean": float(per.mean()),
+                       "from": "a second loop with an event after every call"},
         "decode": decode,
         "stored_states": states,
+        "fused_prep": fused,
         "measured_copy_GBps": copy["copy_GBps"],
         "run": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count, "torch": torch.__version__,

@@ -38,9 +38,38 @@ class _Dims(ctypes.Structure):
                 ("num_seqs", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
-class _StateOpts(ctypes.Structure):
+class _Opts(ctypes.Structure):
     _fields_ = [("state_idx", ctypes.c_void_p), ("num_slots", ctypes.c_int64),
-                ("snapshots", ctypes.c_void_p), ("snapshot_every", ctypes.c_int64)]
+                ("snapshots", ctypes.c_void_p), ("snapshot_every", ctypes.c_int64),
+                ("l2norm_qk", ctypes.c_int32), ("alpha_dtype", ctypes.c_int32), ("alpha_act", ctypes.c_int32),
+                ("alpha_scale", ctypes.c_float), ("gate_act", ctypes.c_int32), ("gate_scale", ctypes.c_float)]
+
+
+# activations of the fused input preparation (dr_act)
+ACTS = {"none": 0, "exp_neg_softplus": 1, "tanh": 2, "sigmoid": 3}
+
+
+def _opts(state_idx=None, num_slots=0, snapshots=None, snapshot_every=0, prep=None, alpha=None) -> _Opts:
+    """Options block; ``prep`` is a dict with l2norm_qk, alpha_act, alpha_scale, gate_act,
+    gate_scale (names as in ``synth``'s pre-activation workloads); alpha's element type comes
+    from the alpha tensor."""
+    o = _Opts(None if state_idx is None else state_idx.data_ptr(), num_slots,
+              None if snapshots is None else snapshots.data_ptr(), int(snapshot_every or 0))
+    if alpha is not None and alpha.dtype == torch.bfloat16:
+        o.alpha_dtype = _DT[torch.bfloat16]
+    if prep:
+        o.l2norm_qk = int(bool(prep.get("l2norm_qk", False)))
+        o.alpha_act = ACTS[prep.get("alpha_act", "none")]
+        o.alpha_scale = float(prep.get("alpha_scale", 1.0))
+        o.gate_act = ACTS[prep.get("gate_act", "none")]
+        o.gate_scale = float(prep.get("gate_scale", 1.0))
+    return o
+
+
+def _alpha_dtype(alpha, prep):
+    if alpha is not None and alpha.dtype == torch.bfloat16:
+        return torch.bfloat16
+    return torch.float32
 
 
 def library_path() -> str:
@@ -61,7 +90,7 @@ def load_library(path: Optional[str] = None):
     lib.dr_chunk_fwd.restype = ip
     lib.dr_decode_step.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, fp, ctypes.POINTER(_Dims), vp]
     lib.dr_decode_step.restype = ip
-    op = ctypes.POINTER(_StateOpts)
+    op = ctypes.POINTER(_Opts)
     lib.dr_chunk_fwd_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, vp, fp, fp, ctypes.POINTER(_Dims), op, vp]
     lib.dr_chunk_fwd_ex.restype = ip
     lib.dr_decode_step_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, fp, ctypes.POINTER(_Dims), op, vp]
@@ -141,11 +170,12 @@ def dr_chunk_fwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, o, 
 
 
 def dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, o, S_T,
-                    state_idx=None, snapshots=None, snapshot_every: int = 0) -> None:
-    """``dr_chunk_fwd`` with stored-state options. With ``state_idx`` [N] int32, S0 and S_T
-    are pools [P,H,dk,dv] whose row state_idx[n] belongs to sequence n. ``snapshots``
-    [num,H,dk,dv] fp32 receives the state after every ``snapshot_every`` tokens of each
-    sequence (rows ordered by sequence, see ``snapshot_count``)."""
+                    state_idx=None, snapshots=None, snapshot_every: int = 0, prep=None) -> None:
+    """``dr_chunk_fwd`` with options. With ``state_idx`` [N] int32, S0 and S_T are pools
+    [P,H,dk,dv] whose row state_idx[n] belongs to sequence n. ``snapshots`` [num,H,dk,dv]
+    fp32 receives the state after every ``snapshot_every`` tokens of each sequence (rows
+    ordered by sequence, see ``snapshot_count``). ``prep`` (a dict, see ``_opts``) makes the
+    kernels normalise q/k and activate alpha (fp32 or bf16) and the gates while loading."""
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -155,7 +185,7 @@ def dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, 
     _need(q, "q", (B, T, H, dk), q.dtype, dev)
     _need(k, "k", (B, T, H, dk), q.dtype, dev)
     _need(v, "v", (B, T, H, dv), q.dtype, dev)
-    _need(alpha, "alpha", (B, T, H, dk), torch.float32, dev)
+    _need(alpha, "alpha", (B, T, H, dk), _alpha_dtype(alpha, prep), dev)
     es, ws = _gate_shapes(variant, (B, T, H), dk, dv)
     _need(erase, "erase", es, torch.float32, dev)
     if ws is None:
@@ -181,8 +211,7 @@ def dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, 
         _need(snapshots, "snapshots", (snapshots.shape[0], H, dk, dv), torch.float32, dev)
     _need(o, "o", (B, T, H, dv), torch.float32, dev)
     d = _Dims(B, T, H, dk, dv, N, _DT[q.dtype], 0)
-    opts = _StateOpts(None if state_idx is None else state_idx.data_ptr(), rows,
-                      None if snapshots is None else snapshots.data_ptr(), int(snapshot_every or 0))
+    opts = _opts(state_idx, rows, snapshots, snapshot_every, prep, alpha)
     st = lib.dr_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
                              VARIANTS[variant], _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
                              ctypes.byref(d), ctypes.byref(opts), _stream(dev))
@@ -195,9 +224,10 @@ def dr_decode_step(q, k, v, alpha, erase, write, variant: str, S, o) -> None:
     dr_decode_step_ex(q, k, v, alpha, erase, write, variant, S, o)
 
 
-def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_idx=None) -> None:
-    """``dr_decode_step`` on a pool: with ``state_idx`` [N] int32, ``S`` is [P,H,dk,dv] and
-    sequence n updates row state_idx[n] in place (a slot outside the pool: o = 0, no state)."""
+def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_idx=None, prep=None) -> None:
+    """``dr_decode_step`` with options: with ``state_idx`` [N] int32, ``S`` is [P,H,dk,dv] and
+    sequence n updates row state_idx[n] in place (a slot outside the pool: o = 0, no state);
+    ``prep`` as for ``dr_chunk_fwd_ex``."""
     lib = load_library()
     N, H, dk = q.shape
     dv = v.shape[-1]
@@ -207,7 +237,7 @@ def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_id
     _need(q, "q", (N, H, dk), q.dtype, dev)
     _need(k, "k", (N, H, dk), q.dtype, dev)
     _need(v, "v", (N, H, dv), q.dtype, dev)
-    _need(alpha, "alpha", (N, H, dk), torch.float32, dev)
+    _need(alpha, "alpha", (N, H, dk), _alpha_dtype(alpha, prep), dev)
     es, ws = _gate_shapes(variant, (N, H), dk, dv)
     _need(erase, "erase", es, torch.float32, dev)
     if ws is None:
@@ -222,7 +252,7 @@ def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_id
     _need(S, "S", (rows, H, dk, dv), torch.float32, dev)
     _need(o, "o", (N, H, dv), torch.float32, dev)
     d = _Dims(N, 1, H, dk, dv, N, _DT[q.dtype], 0)
-    opts = _StateOpts(None if state_idx is None else state_idx.data_ptr(), rows, None, 0)
+    opts = _opts(state_idx, rows, None, 0, prep, alpha)
     st = lib.dr_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
                                VARIANTS[variant], _ptr(S), _ptr(o), ctypes.byref(d), ctypes.byref(opts),
                                _stream(dev))
@@ -230,7 +260,8 @@ def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_id
 
 
 def chunk_fwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, cu_seqlens=None,
-              output_final_state: bool = True, state_idx=None, snapshot_every: Optional[int] = None):
+              output_final_state: bool = True, state_idx=None, snapshot_every: Optional[int] = None,
+              prep=None):
     """Allocate o (and S_T) and run the prefill. Returns (o, S_T or None), plus the snapshot
     tensor when ``snapshot_every`` is given. With ``state_idx``, S0 is a pool of states that
     is updated in place (and returned as S_T)."""
@@ -251,13 +282,13 @@ def chunk_fwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, 
         snaps = torch.empty((snapshot_count(lens, snapshot_every), H, dk, dv), dtype=torch.float32,
                             device=q.device)
     dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T, state_idx, snaps,
-                    snapshot_every or 0)
+                    snapshot_every or 0, prep)
     return (o, S_T) if snapshot_every is None else (o, S_T, snaps)
 
 
-def decode_step(q, k, v, alpha, erase, write, variant: str, S, state_idx=None):
+def decode_step(q, k, v, alpha, erase, write, variant: str, S, state_idx=None, prep=None):
     """Allocate o and run the decode step (S, or its rows state_idx, updated in place).
     Returns o."""
     o = torch.empty((q.shape[0], q.shape[1], v.shape[-1]), dtype=torch.float32, device=q.device)
-    dr_decode_step_ex(q, k, v, alpha, erase, write, variant, S, o, state_idx)
+    dr_decode_step_ex(q, k, v, alpha, erase, write, variant, S, o, state_idx, prep)
     return o

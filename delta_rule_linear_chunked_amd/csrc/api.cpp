@@ -1,5 +1,6 @@
 // C ABI of the gated delta-rule library: argument validation and kernel dispatch.
 // Every check runs on the host before any launch; no device memory is read here.
+#include <cmath>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -171,9 +172,19 @@ int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t*
   return DR_OK;
 }
 
-// Checks of the state-pool and snapshot options shared by prefill and decode.
-static int state_opts_checks(const dr_state_opts* opts, bool prefill) {
+// Checks of the options shared by prefill and decode.
+static int opts_checks(const dr_opts* opts, bool prefill) {
   if (!opts) return DR_OK;
+  if (opts->alpha_dtype != DR_F32 && opts->alpha_dtype != DR_BF16)
+    return fail(DR_ERR_DTYPE, "alpha_dtype %d is not DR_F32 / DR_BF16", opts->alpha_dtype);
+  if (opts->alpha_act != DR_ACT_NONE && opts->alpha_act != DR_ACT_EXP_NEG_SOFTPLUS && opts->alpha_act != DR_ACT_TANH)
+    return fail(DR_ERR_UNSUPPORTED, "alpha_act %d is not a decay activation", opts->alpha_act);
+  if (opts->gate_act != DR_ACT_NONE && opts->gate_act != DR_ACT_SIGMOID)
+    return fail(DR_ERR_UNSUPPORTED, "gate_act %d is not a gate activation", opts->gate_act);
+  if (!std::isfinite(opts->alpha_scale) || !std::isfinite(opts->gate_scale))
+    return fail(DR_ERR_UNSUPPORTED, "activation scales must be finite");
+  if (opts->l2norm_qk != 0 && opts->l2norm_qk != 1)
+    return fail(DR_ERR_UNSUPPORTED, "l2norm_qk must be 0 or 1");
   if (opts->state_idx) {
     if (!aligned16(opts->state_idx)) return fail(DR_ERR_ALIGN, "state_idx must be 16-byte aligned");
     if (opts->num_slots < 0) return fail(DR_ERR_SHAPE, "num_slots (%lld) is negative", (long long)opts->num_slots);
@@ -190,6 +201,17 @@ static int state_opts_checks(const dr_state_opts* opts, bool prefill) {
   return DR_OK;
 }
 
+// Input-preparation fields of the kernel parameters.
+static void set_prep(dr::Params& p, const dr_opts* opts) {
+  if (!opts) return;
+  p.prep_l2 = opts->l2norm_qk;
+  p.a_bf16 = opts->alpha_dtype == DR_BF16;
+  p.a_act = opts->alpha_act == DR_ACT_EXP_NEG_SOFTPLUS ? 1 : opts->alpha_act == DR_ACT_TANH ? 2 : 0;
+  p.a_scale = opts->alpha_scale;
+  p.g_act = opts->gate_act == DR_ACT_SIGMOID ? 1 : 0;
+  p.g_scale = opts->gate_scale;
+}
+
 int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha,
                  const float* erase, const float* write, int variant,
                  const float* S0, const int32_t* cu_seqlens,
@@ -197,10 +219,10 @@ int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha
   return dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T, dims, nullptr, stream);
 }
 
-int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* alpha,
+int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alpha,
                     const float* erase, const float* write, int variant,
                     const float* S0, const int32_t* cu_seqlens,
-                    float* o, float* S_T, const dr_dims* dims, const dr_state_opts* opts,
+                    float* o, float* S_T, const dr_dims* dims, const dr_opts* opts,
                     hipStream_t stream) {
   g_last_error.clear();
   bool vec = false;
@@ -214,7 +236,7 @@ int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* al
   }
   st = check_ptrs({}, {{S0, "S0"}, {S_T, "S_T"}, {cu_seqlens, "cu_seqlens"}});
   if (st) return st;
-  st = state_opts_checks(opts, true);
+  st = opts_checks(opts, true);
   if (st) return st;
   if (cu_seqlens == nullptr && dims->num_seqs > 0 && dims->seqlen == 0 && S_T == nullptr)
     return DR_OK;  // nothing to compute and nothing to write (no snapshot fits in zero tokens)
@@ -241,6 +263,7 @@ int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* al
     p.snap = opts->snapshots;
     p.snap_chunks = opts->snapshots ? (int32_t)(opts->snapshot_every / 64) : 0;
   }
+  set_prep(p, opts);
   void* ws = nullptr;
   hipError_t e = hipSuccess;
   if (pl.workspace > 0) {
@@ -262,9 +285,9 @@ int dr_decode_step(const void* q, const void* k, const void* v, const float* alp
   return dr_decode_step_ex(q, k, v, alpha, erase, write, variant, S, o, dims, nullptr, stream);
 }
 
-int dr_decode_step_ex(const void* q, const void* k, const void* v, const float* alpha,
+int dr_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,
                       const float* erase, const float* write, int variant,
-                      float* S, float* o, const dr_dims* dims, const dr_state_opts* opts,
+                      float* S, float* o, const dr_dims* dims, const dr_opts* opts,
                       hipStream_t stream) {
   g_last_error.clear();
   int st = check_dims_common(dims);
@@ -280,13 +303,14 @@ int dr_decode_step_ex(const void* q, const void* k, const void* v, const float* 
   st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {alpha, "alpha"}, {erase, "erase"}, {S, "S"}, {o, "o"}},
                   {{write, "write"}});
   if (st) return st;
-  st = state_opts_checks(opts, false);
+  st = opts_checks(opts, false);
   if (st) return st;
   dr::Params p{};
   if (opts) {
     p.sidx = opts->state_idx;
     p.nslots = opts->num_slots;
   }
+  set_prep(p, opts);
   p.q = q; p.k = k; p.v = v; p.alpha = alpha;
   p.erase = erase;
   p.write = (variant == DR_KDA || variant == DR_CKDA) ? erase : write;

@@ -15,7 +15,7 @@ struct Params {
   const void* q;
   const void* k;
   const void* v;
-  const float* alpha;
+  const void* alpha;    // float32, or bfloat16 when a_bf16
   const float* erase;   // beta (KDA/CKDA), e (RDA) or b (GDN-2)
   const float* write;   // == erase for KDA/CKDA, w (RDA) or w (GDN-2)
   const float* S0;      // prefill initial states (may be null); decode: unused
@@ -43,6 +43,13 @@ struct Params {
   float* snap;          // prefill: states after every snap_chunks chunks of each sequence (may be null)
   int32_t snap_chunks;  // chunks between snapshots
   int32_t* snap_first;  // packed: first snapshot row of each sequence
+  // input preparation applied while loading (all zero: inputs are used as given)
+  int32_t prep_l2;      // q and k are divided by their L2 norm over d_k
+  int32_t a_bf16;       // alpha is stored as bfloat16
+  int32_t a_act;        // decay activation: 0 none, 1 exp(-a_scale softplus(z)), 2 tanh(z)
+  int32_t g_act;        // erase / write activation: 0 none, 1 g_scale sigmoid(z)
+  float a_scale;
+  float g_scale;
 };
 
 __device__ __forceinline__ float ld_f32(const float* p) { return *p; }
@@ -60,6 +67,29 @@ __device__ __forceinline__ void load4(const float* p, float (&x)[4]) {
   x[0] = a[0]; x[1] = a[1]; x[2] = a[2]; x[3] = a[3];
 }
 __device__ __forceinline__ void store4(float* p, const f32x4& a) { *reinterpret_cast<f32x4*>(p) = a; }
+
+// ---------------------------------------------------------------------------
+// Input preparation. The activations take pre-activations z: the decay
+// exp(-c softplus(z)) in (0, 1] or tanh(z) in [-1, 1], the gates c sigmoid(z). They are
+// built on the hardware exp2 / log2 / reciprocal (about 1 ulp each) in forms that give the
+// limits exactly: softplus(-inf) = 0 so the decay is 1, tanh(+-inf) = +-1, sigmoid(+inf) = 1,
+// sigmoid(-inf) = 0.
+constexpr float LOG2E = 1.4426950408889634f;
+// Both decay forms are evaluated and one is selected, so a call site stays one basic block.
+__device__ __forceinline__ float prep_alpha(float z, const Params& p) {
+  // exp(-c softplus(z)) = 2^(-c log2(1 + 2^(z log2 e)))
+  const float t = __builtin_amdgcn_exp2f(z * LOG2E);
+  const float dec = __builtin_amdgcn_exp2f(-p.a_scale * __builtin_amdgcn_logf(1.f + t));
+  // tanh(z) = sign(z) (1 - e) / (1 + e) with e = exp(-2 |z|); z itself near 0
+  const float az = fabsf(z);
+  const float e = __builtin_amdgcn_exp2f(-2.f * LOG2E * az);
+  const float th = az < 0x1p-12f ? z : copysignf((1.f - e) * __builtin_amdgcn_rcpf(1.f + e), z);
+  return p.a_act == 1 ? dec : p.a_act == 2 ? th : z;
+}
+__device__ __forceinline__ float prep_gate(float z, const Params& p) {
+  const float sg = p.g_scale * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * LOG2E));
+  return p.g_act == 1 ? sg : z;
+}
 
 // Eight raw input elements kept in their storage type (prefetch registers).
 template <typename InT> struct Raw8;
@@ -81,6 +111,18 @@ __device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
   const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
   for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
+}
+
+// Eight decay values starting at element `i` of alpha, in its storage type, activated.
+__device__ __forceinline__ void load_alpha8(const Params& p, int64_t i, float (&a)[8]) {
+  if (p.a_bf16) load8(static_cast<const __bf16*>(p.alpha) + i, a);
+  else load8(static_cast<const float*>(p.alpha) + i, a);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) a[j] = prep_alpha(a[j], p);
+}
+__device__ __forceinline__ float load_alpha1(const Params& p, int64_t i) {
+  const float z = p.a_bf16 ? (float)static_cast<const __bf16*>(p.alpha)[i] : static_cast<const float*>(p.alpha)[i];
+  return prep_alpha(z, p);
 }
 
 // ---------------------------------------------------------------------------

@@ -48,6 +48,7 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
   __shared__ float s_red[2][RG][DVS + 4];
   __shared__ float s_qk[RG];
   __shared__ float s_delta[DVS];
+  __shared__ float s_norm[2];
 
   const int tid = threadIdx.x;
   const int c4 = tid % COLS4;
@@ -80,10 +81,42 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
   const InT* q = static_cast<const InT*>(p.q) + nh * DK;
   const InT* k = static_cast<const InT*>(p.k) + nh * DK;
   const InT* v = static_cast<const InT*>(p.v) + nh * DV + col0;
-  const float* al = p.alpha + nh * DK;
+  // inverse L2 norms of q and k over d_k (1 when the inputs come normalised)
+  float nq = 1.f, nk = 1.f;
+  if (p.prep_l2) {
+    if (tid < 64) {
+      float sq = 0.f, sk = 0.f;
+      for (int i = tid; i < DK; i += 64) {
+        const float qi = ld_f32(q + i), ki = ld_f32(k + i);
+        sq = fmaf(qi, qi, sq);
+        sk = fmaf(ki, ki, sk);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        sq += __shfl_xor(sq, o);
+        sk += __shfl_xor(sk, o);
+      }
+      if (tid == 0) {
+        s_norm[0] = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
+        s_norm[1] = sk > 0.f ? __builtin_amdgcn_rsqf(sk) : 0.f;
+      }
+    }
+    __syncthreads();
+    nq = s_norm[0];
+    nk = s_norm[1];
+  }
+  const bool prep = p.a_act || p.g_act || p.a_bf16;  // fused activations (uniform)
   for (int i = tid; i < DK; i += NT) {
-    const float a = al[i], qi = ld_f32(q + i), ki = ld_f32(k + i);
-    const float ui = (VEC ? p.erase[nh * DK + i] : p.erase[nh]) * ki;
+    float a, ui;
+    const float qi = ld_f32(q + i) * nq, ki = ld_f32(k + i) * nk;
+    const float e = VEC ? p.erase[nh * DK + i] : p.erase[nh];
+    if (prep) {
+      a = load_alpha1(p, nh * DK + i);
+      ui = prep_gate(e, p) * ki;
+    } else {
+      a = static_cast<const float*>(p.alpha)[nh * DK + i];
+      ui = e * ki;
+    }
     s_q[i] = qi;
     s_k[i] = ki;
     s_a[i] = a;
@@ -91,8 +124,8 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
     s_aq[i] = a * qi;
   }
   for (int j = tid; j < DVS; j += NT) {
-    const float wj = VEC ? p.write[nh * DV + col0 + j] : p.write[nh];
-    s_m[j] = wj * ld_f32(v + j);
+    const float wr = VEC ? p.write[nh * DV + col0 + j] : p.write[nh];
+    s_m[j] = (prep ? prep_gate(wr, p) : wr) * ld_f32(v + j);
   }
   __syncthreads();
 

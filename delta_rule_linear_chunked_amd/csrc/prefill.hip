@@ -179,7 +179,84 @@ struct PrepSmem {
   union { float kg[CH][DK + 4]; float T[CH][LDT]; } u2;   // k . g, later T
 };
 
-template <int DKR, typename InT, bool VEC>
+// Eight decay values at element `i` of alpha for alpha mode AM: 0 float32 as given,
+// 1 float32 pre-activations, 2 bfloat16 pre-activations (activated here); 3 and 4 return
+// the bfloat16 / float32 pre-activations themselves.
+template <int AM>
+__device__ __forceinline__ void load_alpha(const Params& p, int64_t i, float (&a)[8]) {
+  if constexpr (AM == 2 || AM == 3) load8(static_cast<const __bf16*>(p.alpha) + i, a);
+  else load8(static_cast<const float*>(p.alpha) + i, a);
+  if constexpr (AM == 1 || AM == 2) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) a[j] = prep_alpha(a[j], p);
+  }
+}
+
+// A block with a gate at or extremely near zero (rare): k . g from exact suffix products and
+// the diagonal tiles of A and P from running products of the gates, exact for any gate value.
+template <int DKR, int DK, typename InT, bool VEC, int AM>
+__device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, int64_t th, bool valid, float esc,
+                                         float rq, float rk, int w, int r, int g) {
+  constexpr int KS = DK / 32;
+  const int row = 16 * w + r;
+  const InT* qp = static_cast<const InT*>(p.q);
+  const InT* kp = static_cast<const InT*>(p.k);
+  auto alpha8 = [&](int64_t i, float (&a)[8]) { load_alpha<AM>(p, i, a); };
+  auto gate = [&](float z) {
+    if constexpr (AM != 0) return prep_gate(z, p);
+    else return z;
+  };
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int ch0 = 32 * ks + 8 * g;
+    const bool live = valid && ch0 < DKR;
+    float a8[8], k8[8];
+    alpha8(th * DKR + (live ? ch0 : 0), a8);
+    load8(kp + th * DKR + (live ? ch0 : 0), k8);
+    float kgv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kgv[j] = (live ? k8[j] * rk : 0.f) * row_suffix_prod_excl(live ? a8[j] : 1.f);
+    store4(&sm.u2.kg[row][ch0], f32x4{kgv[0], kgv[1], kgv[2], kgv[3]});
+    store4(&sm.u2.kg[row][ch0 + 4], f32x4{kgv[4], kgv[5], kgv[6], kgv[7]});
+  }
+  for (int s = 0; s < 16; ++s) {
+    float ap = 0.f, pp = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * g;
+      const bool live = valid && ch0 < DKR;
+      float a2[8], k2[8], q2[8], b2[8];
+      load_alpha<AM == 0 ? 0 : AM == 2 ? 3 : 4>(p, th * DKR + (live ? ch0 : 0), a2);  // raw
+      load8(kp + th * DKR + (live ? ch0 : 0), k2);
+      load8(qp + th * DKR + (live ? ch0 : 0), q2);
+      if constexpr (VEC) load8(p.erase + th * DKR + (live ? ch0 : 0), b2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float a = 1.f;
+        if (live) {
+          if constexpr (AM != 0) a = prep_alpha(a2[j], p);  // one element at a time
+          else a = a2[j];
+        }
+        const float kk = live ? k2[j] * rk : 0.f;
+        const float qq = live ? q2[j] * rq : 0.f;
+        const float uu = (VEC ? gate(b2[j]) : esc) * kk;
+        const float rho = row_prefix_prod(r > s ? a : 1.f);
+        const float kv = __shfl(kk, 16 * g + s);
+        ap = fmaf(uu * kv, rho, ap);
+        pp = fmaf(qq * kv, rho, pp);
+      }
+    }
+    ap += __shfl_xor(ap, 16);
+    ap += __shfl_xor(ap, 32);
+    pp += __shfl_xor(pp, 16);
+    pp += __shfl_xor(pp, 32);
+    if (g == 0) {
+      sm.A[16 * w + r][16 * w + s] = (r > s) ? ap : 0.f;
+      sm.u1.P[16 * w + r][16 * w + s] = (r >= s) ? pp : 0.f;
+    }
+  }
+}
+template <int DKR, typename InT, bool VEC, int AM>
 __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
@@ -200,6 +277,12 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   const int w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
   const InT* qp = static_cast<const InT*>(p.q);
   const InT* kp = static_cast<const InT*>(p.k);
+  // decay and gate loads, with the fused activations unless AM == 0
+  auto alpha8 = [&](int64_t i, float (&a)[8]) { load_alpha<AM>(p, i, a); };
+  auto gate = [&](float z) {
+    if constexpr (AM != 0) return prep_gate(z, p);
+    else return z;
+  };
 
   // upper blocks of P are read (as zeros) by the state pass's 32-deep steps
   for (int i = tid; i < CH * LDT; i += 256) (&sm.u1.P[0][0])[i] = 0.f;
@@ -208,12 +291,54 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   const bool valid = c0 + row < len;
   const int64_t th = (bos + c0 + (valid ? row : 0)) * H + h;
 
+  // ---------------------------------------------------------------- input preparation
+  // With fused preparation the row's decay pre-activations are loaded first, so that their
+  // latency overlaps the q/k norm pass, and activated as independent chains afterwards.
+  float av[AM != 0 ? KS : 1][8];
+  if constexpr (AM != 0) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * g;
+      load_alpha<AM == 2 ? 3 : 4>(p, th * DKR + (valid && ch0 < DKR ? ch0 : 0), av[ks]);  // raw
+    }
+  }
+  // inverse L2 norms of this row's q and k over d_k (1 when the inputs come normalised): the
+  // row's channels are spread over the four lanes l, l^16, l^32, l^48
+  float rq = 1.f, rk = 1.f;
+  if (AM != 0 && p.prep_l2) {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * g;
+      if (valid && ch0 < DKR) {
+        float k8[8], q8[8];
+        load8(kp + th * DKR + ch0, k8);
+        load8(qp + th * DKR + ch0, q8);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { sq = fmaf(q8[j], q8[j], sq); sk = fmaf(k8[j], k8[j], sk); }
+      }
+    }
+    sq += __shfl_xor(sq, 16);
+    sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 16);
+    sk += __shfl_xor(sk, 32);
+    rq = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
+    rk = sk > 0.f ? __builtin_amdgcn_rsqf(sk) : 0.f;
+  }
+  if constexpr (AM != 0) {
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) av[ks][j] = prep_alpha(av[ks][j], p);
+    }
+  }
+
   // ---------------------------------------------------------------- gate preparation
   float uf[KS][8], qf[KS][8];  // u . f and q . f of this lane's row
   {
     bool ok = true;
     f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f}, pd = ad;
-    const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
+    const float esc = (!VEC && valid) ? gate(p.erase[th]) : 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch0 = 32 * ks + 8 * g;
@@ -222,8 +347,21 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       if (live) {
         load8(kp + th * DKR + ch0, k8);
         load8(qp + th * DKR + ch0, q8);
-        load8(p.alpha + th * DKR + ch0, a8);
+        if constexpr (AM != 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a8[j] = av[ks][j];
+        } else {
+          alpha8(th * DKR + ch0, a8);
+        }
         if constexpr (VEC) load8(p.erase + th * DKR + ch0, b8);
+        if constexpr (AM != 0) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            k8[j] *= rk;
+            q8[j] *= rq;
+            if constexpr (VEC) b8[j] = gate(b8[j]);
+          }
+        }
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j) { k8[j] = 0.f; q8[j] = 0.f; a8[j] = 1.f; b8[j] = 0.f; }
@@ -262,53 +400,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
         sm.u1.P[16 * w + rr][16 * w + r] = (r <= rr) ? pd[i] : 0.f;
       }
     } else {
-      // Some gate of this block is zero or nearly so: exact suffix products for k . g and
-      // the diagonal tiles from running products of the gates.
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int ch0 = 32 * ks + 8 * g;
-        const bool live = valid && ch0 < DKR;
-        float a8[8], k8[8];
-        load8(p.alpha + th * DKR + (live ? ch0 : 0), a8);
-        load8(kp + th * DKR + (live ? ch0 : 0), k8);
-        float kgv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) kgv[j] = (live ? k8[j] : 0.f) * row_suffix_prod_excl(live ? a8[j] : 1.f);
-        store4(&sm.u2.kg[row][ch0], f32x4{kgv[0], kgv[1], kgv[2], kgv[3]});
-        store4(&sm.u2.kg[row][ch0 + 4], f32x4{kgv[4], kgv[5], kgv[6], kgv[7]});
-      }
-      for (int s = 0; s < 16; ++s) {
-        float ap = 0.f, pp = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const int ch0 = 32 * ks + 8 * g;
-          const bool live = valid && ch0 < DKR;
-          float a2[8], k2[8], q2[8], b2[8];
-          load8(p.alpha + th * DKR + (live ? ch0 : 0), a2);
-          load8(kp + th * DKR + (live ? ch0 : 0), k2);
-          load8(qp + th * DKR + (live ? ch0 : 0), q2);
-          if constexpr (VEC) load8(p.erase + th * DKR + (live ? ch0 : 0), b2);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float a = live ? a2[j] : 1.f;
-            const float kk = live ? k2[j] : 0.f;
-            const float qq = live ? q2[j] : 0.f;
-            const float uu = (VEC ? b2[j] : esc) * kk;
-            const float rho = row_prefix_prod(r > s ? a : 1.f);
-            const float kv = __shfl(kk, 16 * g + s);
-            ap = fmaf(uu * kv, rho, ap);
-            pp = fmaf(qq * kv, rho, pp);
-          }
-        }
-        ap += __shfl_xor(ap, 16);
-        ap += __shfl_xor(ap, 32);
-        pp += __shfl_xor(pp, 16);
-        pp += __shfl_xor(pp, 32);
-        if (g == 0) {
-          sm.A[16 * w + r][16 * w + s] = (r > s) ? ap : 0.f;
-          sm.u1.P[16 * w + r][16 * w + s] = (r >= s) ? pp : 0.f;
-        }
-      }
+      // Some gate of this block is zero or nearly so: exact block path (out of line).
+      exact_block<DKR, DK, InT, VEC, AM>(p, sm, th, valid, esc, rq, rk, w, r, g);
     }
   }
   wave_lds_sync();
@@ -676,18 +769,22 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     // the accumulator layout
     {
       const bool vi = c0 + 16 * w + lr < len;
+      auto put_m = [&](auto gate) {
 #pragma unroll
-      for (int j4 = 0; j4 < E / 4; ++j4) {
-        f32x4 x;
+        for (int j4 = 0; j4 < E / 4; ++j4) {
+          f32x4 x;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float wg;
-          if constexpr (VEC) wg = cur.pw[4 * j4 + u];
-          else wg = cur.pw;
-          x[u] = vi ? wg * (float)cur.pv[4 * j4 + u] : 0.f;
+          for (int u = 0; u < 4; ++u) {
+            float wg;
+            if constexpr (VEC) wg = cur.pw[4 * j4 + u];
+            else wg = cur.pw;
+            x[u] = vi ? gate(wg) * (float)cur.pv[4 * j4 + u] : 0.f;
+          }
+          store4(&sm.X[w][lr][lc + 4 * j4], x);
         }
-        store4(&sm.X[w][lr][lc + 4 * j4], x);
-      }
+      };
+      if (p.g_act) put_m([&](float z) { return prep_gate(z, p); });  // fused gate activation
+      else put_m([](float z) { return z; });
     }
     wave_lds_sync();
     float mv[NCT][4];
@@ -850,13 +947,20 @@ PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int
 
 template <int DKR, int DVB, typename InT, bool VEC>
 static hipError_t launch_t(const Params& p, const PrefillPlan& pl, hipStream_t s) {
+  const bool prep = p.prep_l2 || p.a_bf16 || p.a_act || p.g_act;
   if (p.cu) {
     hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (pl.slots > 0) {
-    hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC>), dim3((unsigned)(pl.slots * p.H)), dim3(256), 0, s, p);
+    const dim3 grid((unsigned)(pl.slots * p.H));
+    if (!prep)
+      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 0>), grid, dim3(256), 0, s, p);
+    else if (!p.a_bf16)
+      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 1>), grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 2>), grid, dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -131,8 +131,19 @@ int dr_decode_step(const void* q, const void* k, const void* v, const float* alp
                    const float* erase, const float* write, int variant,
                    float* S, float* o, const dr_dims* dims, hipStream_t stream);
 
+/* Activations of the fused input preparation (dr_opts). */
+typedef enum {
+  DR_ACT_NONE = 0,              /* the input is used as given */
+  DR_ACT_EXP_NEG_SOFTPLUS = 1,  /* decay: alpha = exp(-alpha_scale * softplus(z)), in (0, 1] */
+  DR_ACT_TANH = 2,              /* decay: alpha = tanh(z), in [-1, 1] (Complex KDA) */
+  DR_ACT_SIGMOID = 3            /* erase / write: gate_scale * sigmoid(z) */
+} dr_act;
+
 /*
- * Stored states for prefix sharing and continuous batching. Section 3 of the
+ * Options of dr_chunk_fwd_ex / dr_decode_step_ex. A zero-filled block (or a NULL
+ * pointer) means the plain call.
+ *
+ * Stored states, for prefix sharing and continuous batching. Section 3 of the
  * course page above keeps three things apart: padding, a document reset (each
  * sequence starts from its own state) and a state snapshot kept for prefix
  * sharing, and forbids two requests sharing a state with different content.
@@ -156,26 +167,51 @@ int dr_decode_step(const void* q, const void* k, const void* v, const float* alp
  *   snapshot_every a positive multiple of 64 (snapshots sit on chunk boundaries);
  *                  otherwise DR_ERR_SHAPE.
  * Snapshots cost one extra state write per snapshot (d_k * d_v * 4 bytes per head).
+ *
+ * Fused input preparation: the step in front of the recurrence (the course page's
+ * section 2, "project and prepare q/k/v") done while the kernels load their
+ * inputs, so callers pass raw projections and gate pre-activations and the
+ * prepared tensors never exist in memory.
+ *   l2norm_qk      1: q and k are divided by their L2 norm over d_k (per token
+ *                  and head; a zero vector stays zero). 0: used as given.
+ *   alpha_dtype    DR_F32 or DR_BF16: element type of alpha.
+ *   alpha_act      DR_ACT_NONE, DR_ACT_EXP_NEG_SOFTPLUS or DR_ACT_TANH, applied
+ *                  to alpha with alpha_scale.
+ *   gate_act       DR_ACT_NONE or DR_ACT_SIGMOID, applied to erase and write
+ *                  (beta for KDA / CKDA) with gate_scale (2 gives Complex KDA's
+ *                  beta in [0, 2]).
+ * Pre-activations of +-inf give the limits exactly (alpha = 1 or 0, tanh = +-1,
+ * sigmoid = 1 or 0), so exact gates stay expressible. Other values, or a scale
+ * that is not finite, are DR_ERR_UNSUPPORTED / DR_ERR_DTYPE.
  */
-typedef struct dr_state_opts {
+typedef struct dr_opts {
+  /* stored states */
   const int32_t* state_idx;
   int64_t num_slots;
   float* snapshots;
   int64_t snapshot_every;
-} dr_state_opts;
+  /* input preparation */
+  int32_t l2norm_qk;
+  int32_t alpha_dtype;
+  int32_t alpha_act;
+  float alpha_scale;
+  int32_t gate_act;
+  float gate_scale;
+} dr_opts;
 
-/* dr_chunk_fwd with stored-state options (opts may be NULL: same as dr_chunk_fwd). */
-int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const float* alpha,
+/* dr_chunk_fwd with options (opts may be NULL: same as dr_chunk_fwd). alpha is
+ * float32, or bfloat16 with alpha_dtype = DR_BF16. */
+int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alpha,
                     const float* erase, const float* write, int variant,
                     const float* S0, const int32_t* cu_seqlens,
-                    float* o, float* S_T, const dr_dims* dims, const dr_state_opts* opts,
+                    float* o, float* S_T, const dr_dims* dims, const dr_opts* opts,
                     hipStream_t stream);
 
-/* dr_decode_step with a slot pool (opts may be NULL: same as dr_decode_step;
+/* dr_decode_step with options (opts may be NULL: same as dr_decode_step;
  * snapshots must be NULL). With state_idx, S is the pool. */
-int dr_decode_step_ex(const void* q, const void* k, const void* v, const float* alpha,
+int dr_decode_step_ex(const void* q, const void* k, const void* v, const void* alpha,
                       const float* erase, const float* write, int variant,
-                      float* S, float* o, const dr_dims* dims, const dr_state_opts* opts,
+                      float* S, float* o, const dr_dims* dims, const dr_opts* opts,
                       hipStream_t stream);
 
 /* Static description of a status code. Never NULL. */

@@ -112,8 +112,11 @@ def test_plan(lib):
     assert drl.chunk_fwd_plan(1, 64, 2, 16, 16)[2] == 8
 
 
-def _opts(state_idx=None, num_slots=0, snapshots=None, every=0):
-    return drl._StateOpts(state_idx, num_slots, snapshots, every)
+def _opts(state_idx=None, num_slots=0, snapshots=None, every=0, **prep):
+    o = drl._Opts(state_idx, num_slots, snapshots, every)
+    for k, v in prep.items():
+        setattr(o, k, v)
+    return o
 
 
 @pytest.mark.parametrize("opts,expect", [
@@ -122,6 +125,11 @@ def _opts(state_idx=None, num_slots=0, snapshots=None, every=0):
     (dict(snapshots=0x100004, every=64), -4),          # misaligned snapshot buffer
     (dict(state_idx=0x100004, num_slots=4), -4),       # misaligned slot table
     (dict(state_idx=0x100000, num_slots=-1), -2),
+    (dict(alpha_dtype=7), -3),                          # alpha neither fp32 nor bf16
+    (dict(alpha_act=3), -5),                           # sigmoid is not a decay activation
+    (dict(gate_act=1), -5),                            # nor softplus-decay a gate one
+    (dict(l2norm_qk=2), -5),
+    (dict(alpha_act=1, alpha_scale=float("inf")), -5),
 ])
 def test_state_options_are_checked(lib, opts, expect):
     o = _opts(**opts)
