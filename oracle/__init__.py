@@ -26,3 +26,4 @@ from .recurrence import (  # noqa: F401
 from .chunked import chunked_reference  # noqa: F401
 from . import states  # noqa: F401
 from . import prep  # noqa: F401
+from . import backward  # noqa: F401

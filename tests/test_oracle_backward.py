@@ -1,0 +1,130 @@
+"""Pins for the oracle's gradients (reverse recurrence): central finite differences of the
+forward recurrence, PyTorch float64 autograd through a literal transcription of the step
+rule, a linear-attention closed form, and packed sequences. CPU only."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import backward
+from test_oracle_pins import _rand_inputs
+
+RNG = np.random.default_rng(20261206)
+
+
+def _loss(a, variant, do, dS_T, S0, cu=None):
+    o, S_T = oracle.step_recurrence(*a, variant, S0=S0, cu_seqlens=cu)
+    return float(np.sum(o * do) + np.sum(S_T * dS_T))
+
+
+def _inputs(variant, B=1, T=6, H=1, dk=3, dv=2, signed=False, zeros=False):
+    q, k, v, alpha, erase, write, S0 = _rand_inputs(RNG, B, T, H, dk, dv, variant, signed=signed, zeros=zeros)
+    return [q, k, v, alpha, erase, write], S0
+
+
+@pytest.mark.parametrize("variant,signed,zeros", [("kda", False, False), ("rda", False, True),
+                                                  ("gdn2", False, False), ("ckda", True, True)])
+def test_gradients_match_central_differences(variant, signed, zeros):
+    a, S0 = _inputs(variant, signed=signed, zeros=zeros)
+    do = RNG.standard_normal(a[2].shape)
+    dS_T = RNG.standard_normal(S0.shape)
+    g = backward.step_recurrence_grads(*a, variant, do, dS_T=dS_T, S0=S0)
+    names = ["dq", "dk", "dv", "dalpha", "derase", "dwrite"]
+    eps = 1e-6
+    for idx, name in enumerate(names):
+        x = a[idx]
+        if x is None:
+            assert g[name] is None
+            continue
+        num = np.zeros_like(x)
+        for i in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[i] += eps
+            xm[i] -= eps
+            ap, am = list(a), list(a)
+            ap[idx], am[idx] = xp, xm
+            num[i] = (_loss(ap, variant, do, dS_T, S0) - _loss(am, variant, do, dS_T, S0)) / (2 * eps)
+        np.testing.assert_allclose(g[name], num, rtol=1e-6, atol=1e-8, err_msg=name)
+    num = np.zeros_like(S0)
+    for i in np.ndindex(S0.shape):
+        sp, sm = S0.copy(), S0.copy()
+        sp[i] += eps
+        sm[i] -= eps
+        num[i] = (_loss(a, variant, do, dS_T, sp) - _loss(a, variant, do, dS_T, sm)) / (2 * eps)
+    np.testing.assert_allclose(g["dS0"], num, rtol=1e-6, atol=1e-8, err_msg="dS0")
+
+
+def _torch_step_rule(q, k, v, alpha, erase, write, variant, S0):
+    """The step rule written out literally: S_t = (I - k u^T) Diag(alpha) S_{t-1} + k m^T."""
+    B, T, H, dk = q.shape
+    S = S0.clone()
+    outs = []
+    eye = torch.eye(dk, dtype=torch.float64)
+    for t in range(T):
+        kt, vt, qt, at = k[:, t], v[:, t], q[:, t], alpha[:, t]
+        if variant in ("kda", "ckda"):
+            u, m = erase[:, t, :, None] * kt, erase[:, t, :, None] * vt
+        elif variant == "rda":
+            u, m = erase[:, t, :, None] * kt, write[:, t, :, None] * vt
+        else:
+            u, m = erase[:, t] * kt, write[:, t] * vt
+        trans = eye - kt[..., :, None] * u[..., None, :]             # I - k u^T
+        S = trans @ (at[..., :, None] * S) + kt[..., :, None] * m[..., None, :]
+        outs.append(torch.einsum("bhij,bhi->bhj", S, qt))
+    return torch.stack(outs, 1), S
+
+
+@pytest.mark.parametrize("variant", oracle.VARIANTS)
+def test_gradients_match_torch_autograd(variant):
+    a, S0 = _inputs(variant, B=2, T=9, H=2, dk=4, dv=3, signed=(variant == "ckda"), zeros=True)
+    do = RNG.standard_normal(a[2].shape)
+    dS_T = RNG.standard_normal(S0.shape)
+    g = backward.step_recurrence_grads(*a, variant, do, dS_T=dS_T, S0=S0)
+    ts = [None if x is None else torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in a]
+    tS0 = torch.tensor(S0, dtype=torch.float64, requires_grad=True)
+    o, S_T = _torch_step_rule(*ts, variant, tS0)
+    loss = (o * torch.tensor(do)).sum() + (S_T * torch.tensor(dS_T)).sum()
+    loss.backward()
+    for name, t in zip(["dq", "dk", "dv", "dalpha", "derase", "dwrite"], ts):
+        if t is None:
+            continue
+        np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=1e-10, atol=1e-12, err_msg=name)
+    np.testing.assert_allclose(g["dS0"], tS0.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+def test_linear_attention_gradients_closed_form():
+    # alpha = 1, e = 0, w = 1 (RDA): o_t = S0^T q_t + sum_{s<=t} (q_t . k_s) v_s
+    B, T, H, dk, dv = 1, 7, 2, 4, 3
+    q = RNG.standard_normal((B, T, H, dk))
+    k = RNG.standard_normal((B, T, H, dk))
+    v = RNG.standard_normal((B, T, H, dv))
+    S0 = RNG.standard_normal((B, H, dk, dv))
+    do = RNG.standard_normal((B, T, H, dv))
+    g = backward.step_recurrence_grads(q, k, v, np.ones((B, T, H, dk)), np.zeros((B, T, H)), np.ones((B, T, H)),
+                                       "rda", do, S0=S0)
+    qk = np.einsum("bthi,bshi->bhts", q, k)                       # q_t . k_s
+    mask = np.tril(np.ones((T, T)))
+    dv_ref = np.einsum("bhts,bthj->bshj", qk * mask, do)          # sum over t >= s
+    np.testing.assert_allclose(g["dv"], dv_ref, rtol=0, atol=1e-12)
+    S = S0[:, None] + np.cumsum(np.einsum("bthi,bthj->bthij", k, v), axis=1)
+    dq_ref = np.einsum("bthij,bthj->bthi", S, do)
+    np.testing.assert_allclose(g["dq"], dq_ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(g["dS0"], np.einsum("bthi,bthj->bhij", q, do), rtol=0, atol=1e-12)
+
+
+def test_packed_sequence_gradients_are_per_sequence():
+    lens = [3, 0, 5]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    a, _ = _inputs("gdn2", T=int(cu[-1]), H=2, dk=3, dv=2)
+    S0 = RNG.standard_normal((3, 2, 3, 2))
+    do = RNG.standard_normal(a[2].shape)
+    dS_T = RNG.standard_normal(S0.shape)
+    g = backward.step_recurrence_grads(*a, "gdn2", do, dS_T=dS_T, S0=S0, cu_seqlens=cu)
+    for n in range(3):
+        t0, t1 = int(cu[n]), int(cu[n + 1])
+        sl = (slice(0, 1), slice(t0, t1))
+        gn = backward.step_recurrence_grads(*[x[sl] for x in a], "gdn2", do[sl], dS_T=dS_T[n:n + 1], S0=S0[n:n + 1])
+        for name in ("dq", "dk", "dv", "dalpha", "derase", "dwrite"):
+            np.testing.assert_array_equal(g[name][sl], gn[name])
+        np.testing.assert_array_equal(g["dS0"][n], gn["dS0"][0])
+    np.testing.assert_array_equal(g["dS0"][1], dS_T[1])            # an empty sequence passes dS_T through
