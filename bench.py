@@ -113,6 +113,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-states", action="store_true", help="skip the snapshot and slot-pool timings")
     ap.add_argument("--no-prep", action="store_true", help="skip the fused input preparation timing")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward (gradient) timing")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the plain copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -243,6 +244,36 @@ def main():
                  "achieved_GBps": pbytes / (pms * 1e-3) / 1e9}
         del psets
 
+    # backward (gradients of the same prefill, dO and dS_T random): checkpointing forward + reverse walk
+    bwd = None
+    if not args.no_backward:
+        gdO = torch.randn((B, T, H, D), device=dev)
+        gdS = torch.randn((B, H, D, D), device=dev)
+        grads = dict(dq=torch.empty((B, T, H, D), device=dev), dk=torch.empty((B, T, H, D), device=dev),
+                     dv=torch.empty((B, T, H, D), device=dev), dalpha=torch.empty((B, T, H, D), device=dev),
+                     derase=torch.empty((B, T, H), device=dev), dS0=torch.empty((B, H, D, D), device=dev))
+
+        def bstep(i):
+            s = sets[i % 2]
+            drl.dr_chunk_bwd(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "kda", s["S0"], None, gdO, gdS,
+                             grads["dq"], grads["dk"], grads["dv"], grads["dalpha"], grads["derase"], None, grads["dS0"])
+
+        bsteps = max(3, args.steps // 5)
+        for i in range(2):
+            bstep(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(bsteps):
+            bstep(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / bsteps
+        bwd = {"workload": "gradients of the KDA prefill (dq, dk, dv, dalpha, dbeta, dS0) for random dO and dS_T",
+               "ms_per_step": bms, "tokens_per_s": tokens / (bms * 1e-3), "steps": bsteps,
+               "vs_forward": bms / ms_step}
+        del gdO, gdS, grads
+
     traffic, kernel_traffic = None, None
     tfile = os.path.join(ROOT, "profiles", "chunk_fwd_kda_B4_T4096_H16_d128_traffic.json")
     if os.path.exists(tfile):
@@ -347,6 +378,7 @@ def main():
         "decode": decode,
         "stored_states": states,
         "fused_prep": fused,
+        "backward": bwd,
         "measured_copy_GBps": copy["copy_GBps"],
         "run": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count, "torch": torch.__version__,

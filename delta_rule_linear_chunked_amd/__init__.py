@@ -17,9 +17,9 @@ from typing import Optional
 
 import torch
 
-__all__ = ["dr_chunk_fwd", "dr_decode_step", "dr_chunk_fwd_ex", "dr_decode_step_ex", "chunk_fwd",
-           "decode_step", "chunk_fwd_plan", "snapshot_count", "library_path", "load_library", "VARIANTS",
-           "DeltaRuleError"]
+__all__ = ["dr_chunk_fwd", "dr_decode_step", "dr_chunk_fwd_ex", "dr_decode_step_ex", "dr_chunk_bwd",
+           "chunk_fwd", "decode_step", "chunk_bwd", "chunk_fwd_plan", "snapshot_count", "library_path",
+           "load_library", "VARIANTS", "DeltaRuleError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "lib", "libdeltarule.so")
@@ -95,6 +95,9 @@ def load_library(path: Optional[str] = None):
     lib.dr_chunk_fwd_ex.restype = ip
     lib.dr_decode_step_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, fp, ctypes.POINTER(_Dims), op, vp]
     lib.dr_decode_step_ex.restype = ip
+    lib.dr_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                                 ctypes.POINTER(_Dims), vp]
+    lib.dr_chunk_bwd.restype = ip
     lib.dr_status_string.argtypes = [ip]
     lib.dr_status_string.restype = ctypes.c_char_p
     lib.dr_last_error.argtypes = []
@@ -292,3 +295,57 @@ def decode_step(q, k, v, alpha, erase, write, variant: str, S, state_idx=None, p
     o = torch.empty((q.shape[0], q.shape[1], v.shape[-1]), dtype=torch.float32, device=q.device)
     dr_decode_step_ex(q, k, v, alpha, erase, write, variant, S, o, state_idx, prep)
     return o
+
+
+def dr_chunk_bwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, dO, dS_T,
+                 dq, dk, dv, dalpha, derase, dwrite, dS0) -> None:
+    """Gradients of ``dr_chunk_fwd`` into caller-provided fp32 tensors shaped like the inputs
+    (dwrite None for KDA / CKDA, dS_T / dS0 optional)."""
+    lib = load_library()
+    B, T, H, dk_ = q.shape
+    dv_ = v.shape[-1]
+    dev = q.device
+    if q.dtype not in _DT:
+        raise ValueError(f"q dtype {q.dtype} is not float32 or bfloat16")
+    _need(q, "q", (B, T, H, dk_), q.dtype, dev)
+    _need(k, "k", (B, T, H, dk_), q.dtype, dev)
+    _need(v, "v", (B, T, H, dv_), q.dtype, dev)
+    _need(alpha, "alpha", (B, T, H, dk_), torch.float32, dev)
+    es, ws = _gate_shapes(variant, (B, T, H), dk_, dv_)
+    _need(erase, "erase", es, torch.float32, dev)
+    if ws is None:
+        if write is not None or dwrite is not None:
+            raise ValueError(f"{variant} takes no write gate")
+    else:
+        _need(write, "write", ws, torch.float32, dev)
+        _need(dwrite, "dwrite", ws, torch.float32, dev)
+    N = B if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    if cu_seqlens is not None:
+        _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    for t, name in ((S0, "S0"), (dS_T, "dS_T"), (dS0, "dS0")):
+        if t is not None:
+            _need(t, name, (N, H, dk_, dv_), torch.float32, dev)
+    _need(dO, "dO", (B, T, H, dv_), torch.float32, dev)
+    for t, name, shape in ((dq, "dq", (B, T, H, dk_)), (dk, "dk", (B, T, H, dk_)), (dv, "dv", (B, T, H, dv_)),
+                           (dalpha, "dalpha", (B, T, H, dk_)), (derase, "derase", es)):
+        _need(t, name, shape, torch.float32, dev)
+    d = _Dims(B, T, H, dk_, dv_, N, _DT[q.dtype], 0)
+    st = lib.dr_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write), VARIANTS[variant],
+                          _ptr(S0), _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv),
+                          _ptr(dalpha), _ptr(derase), _ptr(dwrite), _ptr(dS0), ctypes.byref(d), _stream(dev))
+    _check(lib, st, "dr_chunk_bwd")
+
+
+def chunk_bwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, cu_seqlens=None, dO=None,
+              dS_T=None, need_dS0: bool = True):
+    """Allocate the gradients and run ``dr_chunk_bwd``. Returns a dict with dq, dk, dv, dalpha,
+    derase, dwrite (None for KDA / CKDA) and dS0 (None unless ``need_dS0``)."""
+    f = lambda x: torch.empty(x.shape, dtype=torch.float32, device=q.device)
+    N = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    g = dict(dq=f(q), dk=f(k), dv=f(v), dalpha=f(alpha), derase=f(erase),
+             dwrite=None if write is None else f(write),
+             dS0=torch.empty((N, q.shape[2], q.shape[3], v.shape[3]), dtype=torch.float32, device=q.device)
+             if need_dS0 else None)
+    dr_chunk_bwd(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, dO, dS_T, g["dq"], g["dk"], g["dv"],
+                 g["dalpha"], g["derase"], g["dwrite"], g["dS0"])
+    return g

@@ -20,7 +20,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdeltarule.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "backward.hip"]
 
 # Packed-fp32 instructions are disabled for every device compile; hipcc's host
 # pass does not know the feature and says so, which is harmless.

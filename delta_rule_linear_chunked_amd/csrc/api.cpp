@@ -279,6 +279,93 @@ int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alp
   return DR_OK;
 }
 
+static int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }
+
+int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                 const float* erase, const float* write, int variant,
+                 const float* S0, const int32_t* cu_seqlens,
+                 const float* dO, const float* dS_T,
+                 float* dq, float* dk, float* dv, float* dalpha, float* derase, float* dwrite,
+                 float* dS0, const dr_dims* dims, hipStream_t stream) {
+  g_last_error.clear();
+  bool vec = false;
+  int st = prefill_checks(dims, variant, erase, write, cu_seqlens, &vec);
+  if (st) return st;
+  const bool has_write = variant == DR_RDA || variant == DR_GDN2;
+  if (!has_write && dwrite != nullptr)
+    return fail(DR_ERR_VARIANT, "KDA / CKDA take no dwrite (beta's whole gradient goes to derase)");
+  const int64_t tokens = dims->batch * dims->seqlen;
+  if (tokens > 0) {
+    st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {alpha, "alpha"}, {erase, "erase"}, {dO, "dO"},
+                     {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {dalpha, "dalpha"}, {derase, "derase"}},
+                    {{write, "write"}});
+    if (st) return st;
+    if (has_write && dwrite == nullptr) return fail(DR_ERR_NULL, "dwrite is required for RDA / GDN-2");
+  }
+  st = check_ptrs({}, {{S0, "S0"}, {dS_T, "dS_T"}, {dS0, "dS0"}, {cu_seqlens, "cu_seqlens"}, {dwrite, "dwrite"}});
+  if (st) return st;
+  if (dims->num_seqs == 0) return DR_OK;
+  const int dkh = (int)dims->head_dim_k, dvh = (int)dims->head_dim_v;
+  const int64_t H = dims->num_heads, pairs = dims->num_seqs * H;
+
+  // forward pass for the checkpoints: the state after every 64 tokens, no output
+  dr::Params p{};
+  p.q = q; p.k = k; p.v = v; p.alpha = alpha;
+  p.erase = erase;
+  p.write = has_write ? write : erase;
+  p.S0 = S0; p.cu = cu_seqlens; p.o = nullptr; p.S = nullptr;
+  p.T = dims->seqlen;
+  p.H = (int32_t)H;
+  p.DV = (int32_t)dvh;
+  const dr::PrefillPlan pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen, H, dkh, dvh,
+                                              cu_seqlens != nullptr);
+  p.num_pairs = (int32_t)pairs;
+  p.ndvb = pl.ndvb;
+  p.grid_logical = (int32_t)(pairs * pl.ndvb);
+  p.nseq = (int32_t)dims->num_seqs;
+  p.snap_chunks = 1;
+  // at most floor(tokens / 64) checkpoints in all (sum of floor(len_n / 64) over the sequences)
+  const int64_t nsnap = cu_seqlens ? tokens / 64 : dims->batch * (dims->seqlen / 64);
+  const int ndvb = dvh / dr::bwd_dv_block(dvh);
+  const int64_t TH = tokens * H;
+  const int64_t off_snap = round256(pl.workspace);
+  const int64_t off_part = off_snap + round256(nsnap * H * dkh * dvh * 4);
+  const int64_t off_parts = off_part + round256((int64_t)ndvb * TH * 4 * dkh * 4);
+  const int64_t total = off_parts + round256((int64_t)ndvb * TH * 4);
+  void* ws = nullptr;
+  hipError_t e = workspace_alloc((size_t)total, stream, &ws);
+  if (e != hipSuccess)
+    return fail(DR_ERR_HIP, "backward workspace (%lld bytes) allocation failed: %s", (long long)total,
+                hipGetErrorString(e));
+  unsigned char* wsb = static_cast<unsigned char*>(ws);
+  p.snap = nsnap > 0 ? reinterpret_cast<float*>(wsb + off_snap) : nullptr;
+  if (p.snap == nullptr) p.snap_chunks = 0;
+  e = dr::launch_prefill(p, pl, ws, dkh, dims->in_dtype == DR_BF16, vec, stream);
+  if (e == hipSuccess) {
+    dr::BwdParams b{};
+    b.q = q; b.k = k; b.v = v; b.alpha = alpha;
+    b.erase = erase;
+    b.write = p.write;
+    b.S0 = S0; b.cu = cu_seqlens; b.dO = dO; b.dST = dS_T;
+    b.dq = dq; b.dk = dk; b.dv = dv; b.dalpha = dalpha; b.derase = derase; b.dwrite = dwrite; b.dS0 = dS0;
+    b.snap = p.snap;
+    b.snap_first = cu_seqlens ? dr::prefill_snap_first(ws, pl, H, dims->num_seqs) : nullptr;
+    b.part = reinterpret_cast<float*>(wsb + off_part);
+    b.parts = reinterpret_cast<float*>(wsb + off_parts);
+    b.T = dims->seqlen;
+    b.TH = TH;
+    b.H = (int32_t)H;
+    b.DV = dvh;
+    b.nseq = (int32_t)dims->num_seqs;
+    b.variant = variant;
+    e = dr::launch_backward(b, pairs, dkh, dvh, dims->in_dtype == DR_BF16, vec, stream);
+  }
+  hipError_t ef = hipFreeAsync(ws, stream);
+  if (e != hipSuccess) return fail(DR_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));
+  if (ef != hipSuccess) return fail(DR_ERR_HIP, "backward workspace release failed: %s", hipGetErrorString(ef));
+  return DR_OK;
+}
+
 int dr_decode_step(const void* q, const void* k, const void* v, const float* alpha,
                    const float* erase, const float* write, int variant,
                    float* S, float* o, const dr_dims* dims, hipStream_t stream) {

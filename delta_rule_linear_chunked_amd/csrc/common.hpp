@@ -52,6 +52,38 @@ struct Params {
   float g_scale;
 };
 
+// Parameter block of the backward pass (gradients of a prefill).
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* erase;   // beta (KDA/CKDA), e (RDA) or b (GDN-2)
+  const float* write;   // == erase for KDA/CKDA, w (RDA) or w (GDN-2)
+  const float* S0;      // initial states (may be null)
+  const int32_t* cu;    // packed sequence offsets (may be null)
+  const float* dO;      // gradient of the output
+  const float* dST;     // gradient of the final states (may be null)
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dalpha;
+  float* derase;
+  float* dwrite;        // RDA / GDN-2 only
+  float* dS0;           // may be null
+  const float* snap;    // forward states after every 64 tokens of each sequence
+  const int32_t* snap_first;  // packed: first snapshot row of each sequence
+  float* part;          // [ndvb][tokens * H][4][d_k] per-block row sums: dq, k-part of dk, du, dalpha
+  float* parts;         // [ndvb][tokens * H] per-block v . dm
+  int64_t T;
+  int64_t TH;           // tokens * H
+  int32_t H;
+  int32_t DV;
+  int32_t ndvb;
+  int32_t nseq;
+  int32_t variant;      // 0 KDA, 1 RDA, 2 GDN-2, 3 CKDA
+};
+
 __device__ __forceinline__ float ld_f32(const float* p) { return *p; }
 __device__ __forceinline__ float ld_f32(const __bf16* p) { return (float)*p; }
 

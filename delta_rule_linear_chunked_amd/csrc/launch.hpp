@@ -7,6 +7,7 @@
 namespace dr {
 
 struct Params;
+struct BwdParams;
 
 // Decode: one workgroup per (sequence, head); p.S is the state updated in place.
 hipError_t launch_decode(const Params& p, int64_t nheads, int dk, int dv, bool bf16, bool vec,
@@ -29,5 +30,15 @@ PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int
 // (sequence, head, value block). `ws` is a workspace of plan.workspace bytes.
 hipError_t launch_prefill(Params p, const PrefillPlan& plan, void* ws, int dk, bool bf16, bool vec,
                           hipStream_t s);
+
+// Packed sequences: where the prefill's workspace keeps the first snapshot row of each sequence
+// (filled by the prefill when snapshots are taken).
+int32_t* prefill_snap_first(void* ws, const PrefillPlan& plan, int64_t heads, int64_t nseq);
+
+// Backward: bwd_kernel over every (sequence, head, value block), then the reduction over the
+// blocks. p.snap must hold the forward states after every 64 tokens (the prefill's snapshots);
+// p.part / p.parts the per-block partial sums (ndvb = d_v / bwd_dv_block(d_v) blocks).
+int bwd_dv_block(int dv);
+hipError_t launch_backward(BwdParams p, int64_t pairs, int dk, int dv, bool bf16, bool vec, hipStream_t s);
 
 }  // namespace dr

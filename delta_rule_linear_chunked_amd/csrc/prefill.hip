@@ -869,7 +869,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
       wave_lds_sync();
       {
         const int64_t rw = c0 + 16 * w + lr;
-        if (rw < len) {
+        if (p.o && rw < len) {  // (no output: the states are all that is wanted)
           float* orow = p.o + ((bos + rw) * H + h) * DV + dv0 + lc;
 #pragma unroll
           for (int j4 = 0; j4 < E / 4; ++j4) store4(orow + 4 * j4, *reinterpret_cast<const f32x4*>(&sm.X[w][lr][lc + 4 * j4]));
@@ -981,6 +981,11 @@ static hipError_t launch_dvb(const Params& p, const PrefillPlan& pl, bool bf16, 
   return launch_gate<DKR, 16>(p, pl, bf16, vec, s);
 }
 
+int32_t* prefill_snap_first(void* ws, const PrefillPlan& pl, int64_t heads, int64_t nseq) {
+  return reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + pl.slots * heads * pl.rec_size) + 2 * pl.slots +
+         nseq + 1;
+}
+
 hipError_t launch_prefill(Params p, const PrefillPlan& pl, void* ws, int dk, bool bf16, bool vec,
                           hipStream_t s) {
   if (pl.workgroups == 0) return hipSuccess;
@@ -993,7 +998,7 @@ hipError_t launch_prefill(Params p, const PrefillPlan& pl, void* ws, int dk, boo
     p.chunk_seq = tables;
     p.chunk_c0 = tables + pl.slots;
     p.seq_first = tables + 2 * pl.slots;
-    p.snap_first = tables + 2 * pl.slots + p.nseq + 1;
+    p.snap_first = prefill_snap_first(ws, pl, p.H, p.nseq);
   }
   switch (dk) {
     case 16: return launch_dvb<16>(p, pl, bf16, vec, s);

@@ -214,6 +214,31 @@ int dr_decode_step_ex(const void* q, const void* k, const void* v, const void* a
                       float* S, float* o, const dr_dims* dims, const dr_opts* opts,
                       hipStream_t stream);
 
+/*
+ * Gradients of dr_chunk_fwd, for training (the course page above, section 3: training needs
+ * activations, checkpoints and the scan's intermediates). For a loss L with
+ * dO = dL/do [B, T, H, d_v] and dS_T = dL/dS_T [N, H, d_k, d_v] (NULL: zero), writes, all
+ * float32 in the shapes of the corresponding inputs:
+ *   dq, dk        [B, T, H, d_k]
+ *   dv            [B, T, H, d_v]
+ *   dalpha        [B, T, H, d_k]
+ *   derase        shape of erase: KDA / CKDA d(beta) (both of beta's uses), RDA d(e), GDN-2 d(b)
+ *   dwrite        RDA d(w) [B, T, H], GDN-2 d(w) [B, T, H, d_v]; must be NULL for KDA / CKDA
+ *   dS0           [N, H, d_k, d_v], or NULL when not wanted
+ * The inputs are those of the forward call (plain inputs: the fused preparation and the
+ * stored-state options are forward-only). The call reruns the forward to keep the state after
+ * every 64 tokens, then walks each sequence backwards, recomputing states between those
+ * checkpoints; its workspace (about 4 * d_k * 4 bytes per token-head and value block of 32
+ * columns, plus the checkpoints) comes from the library's pool like the prefill's.
+ * Deterministic: no atomics.
+ */
+int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
+                 const float* erase, const float* write, int variant,
+                 const float* S0, const int32_t* cu_seqlens,
+                 const float* dO, const float* dS_T,
+                 float* dq, float* dk, float* dv, float* dalpha, float* derase, float* dwrite,
+                 float* dS0, const dr_dims* dims, hipStream_t stream);
+
 /* Static description of a status code. Never NULL. */
 const char* dr_status_string(int status);
 
