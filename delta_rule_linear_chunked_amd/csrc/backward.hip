@@ -168,36 +168,33 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
     float k[SK], u[SK], q[SK], a[SK];
     float m[SV], dO[SV], v[SV], g[SV];
   };
+  // (branch-free: the loads are unconditional at clamped in-range indices and the result is
+  // selected, so nothing waits for them before the block is committed)
   auto load_stg = [&](Stg& r, int64_t t0) {
 #pragma unroll
     for (int x = 0; x < SK; ++x) {
-      const int e = tid + 256 * x;
+      const int e0 = tid + 256 * x;
+      const bool in = e0 < BW_SB * DK && t0 + e0 / DK < len;
+      const int e = e0 < BW_SB * DK ? e0 : 0;
       const int j = e / DK, i = e % DK;
-      const int64_t t = t0 + j;
-      float kk = 0.f, uu = 0.f, qq = 0.f, aa = 0.f;
-      if (e < BW_SB * DK && t < len) {
-        const int64_t th = (bos + t) * H + h;
-        kk = ld_f32(kp + th * DK + i);
-        qq = ld_f32(qp + th * DK + i);
-        aa = p.alpha[th * DK + i];
-        uu = (VEC ? p.erase[th * DK + i] : p.erase[th]) * kk;
-      }
-      r.k[x] = kk; r.u[x] = uu; r.q[x] = qq; r.a[x] = aa;
+      const int64_t t = t0 + j < len ? t0 + j : len - 1;
+      const int64_t th = (bos + t) * H + h;
+      const float kk = ld_f32(kp + th * DK + i), qq = ld_f32(qp + th * DK + i), aa = p.alpha[th * DK + i];
+      const float ug = VEC ? p.erase[th * DK + i] : p.erase[th];
+      r.k[x] = in ? kk : 0.f; r.u[x] = in ? ug * kk : 0.f; r.q[x] = in ? qq : 0.f; r.a[x] = in ? aa : 0.f;
     }
 #pragma unroll
     for (int x = 0; x < SV; ++x) {
-      const int e = tid + 256 * x;
+      const int e0 = tid + 256 * x;
+      const bool in = e0 < BW_SB * DVB && t0 + e0 / DVB < len;
+      const int e = e0 < BW_SB * DVB ? e0 : 0;
       const int j = e / DVB, cc = e % DVB;
-      const int64_t t = t0 + j;
-      float mm = 0.f, dd = 0.f, vv = 0.f, gg = 0.f;
-      if (e < BW_SB * DVB && t < len) {
-        const int64_t th = (bos + t) * H + h;
-        vv = ld_f32(vp + th * DV + dv0 + cc);
-        gg = VEC ? p.write[th * DV + dv0 + cc] : p.write[th];
-        mm = gg * vv;
-        dd = p.dO[th * DV + dv0 + cc];
-      }
-      r.m[x] = mm; r.dO[x] = dd; r.v[x] = vv; r.g[x] = gg;
+      const int64_t t = t0 + j < len ? t0 + j : len - 1;
+      const int64_t th = (bos + t) * H + h;
+      const float vv = ld_f32(vp + th * DV + dv0 + cc);
+      const float gg = VEC ? p.write[th * DV + dv0 + cc] : p.write[th];
+      const float dd = p.dO[th * DV + dv0 + cc];
+      r.m[x] = in ? gg * vv : 0.f; r.dO[x] = in ? dd : 0.f; r.v[x] = in ? vv : 0.f; r.g[x] = in ? gg : 0.f;
     }
   };
   auto commit_stg = [&](const Stg& r) {
