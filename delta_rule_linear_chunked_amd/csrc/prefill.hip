@@ -52,8 +52,9 @@ constexpr float FAST_LO = 0x1p-100f;
 constexpr float FAST_HI = 0x1p100f;
 
 // Operand record of one (chunk slot, head). Every fragment is 32 bytes per lane
-// (bf16 hi + lo, or eight fp32 values), stored lane-contiguously, so a wave moves a
-// fragment with two fully coalesced 16-byte accesses per lane.
+// (bf16 hi + lo, or eight fp32 values), stored as two 1 KiB halves (bytes 0-15 of
+// every lane, then bytes 16-31), so each of a wave's two 16-byte accesses per lane
+// covers one contiguous KiB.
 template <int DK>
 struct Rec {
   static constexpr int KS = DK / 32;
@@ -70,11 +71,20 @@ struct Rec {
 template <class Frag>
 __device__ __forceinline__ void st_frag(unsigned char* base, int64_t idx, int lane, const Frag& f) {
   static_assert(sizeof(Frag) == 32, "fragment size");
-  *reinterpret_cast<Frag*>(base + (idx * 64 + lane) * 32) = f;
+  const u32x4* h = reinterpret_cast<const u32x4*>(&f);
+  unsigned char* b = base + idx * 2048 + lane * 16;
+  *reinterpret_cast<u32x4*>(b) = h[0];
+  *reinterpret_cast<u32x4*>(b + 1024) = h[1];
 }
 template <class Frag>
 __device__ __forceinline__ Frag ld_frag(const unsigned char* base, int64_t idx, int lane) {
-  return *reinterpret_cast<const Frag*>(base + (idx * 64 + lane) * 32);
+  static_assert(sizeof(Frag) == 32, "fragment size");
+  Frag f;
+  u32x4* h = reinterpret_cast<u32x4*>(&f);
+  const unsigned char* b = base + idx * 2048 + lane * 16;
+  h[0] = *reinterpret_cast<const u32x4*>(b);
+  h[1] = *reinterpret_cast<const u32x4*>(b + 1024);
+  return f;
 }
 
 // Orders this wave's LDS writes before its later LDS reads by other lanes of the
@@ -734,14 +744,17 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     if constexpr (VEC) op.pw = *reinterpret_cast<const RowF*>(p.write + thv * DV + dv0 + lc);
     else op.pw = p.write[thv];
   };
+  // Same issue order as the loads spread over a chunk below (v and write gate first), so
+  // that the waits at the top of the chunk loop, which serve both the first chunk and the
+  // later ones, count the same loads in flight on both paths into the loop.
   auto load_ops = [&](Ops& op, int c) {
     const unsigned char* rc = rec_ptr(c);
+    load_vw(op, c);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) load_uq(op, rc, ks);
     load_tp(op, rc);
 #pragma unroll
     for (int m = 0; m < NRT; ++m) load_k(op, rc, m);
-    load_vw(op, c);
   };
 
   // this workgroup's block of the fp32 state (key rows x DVB value columns) to a
