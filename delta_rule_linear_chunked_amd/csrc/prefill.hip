@@ -68,22 +68,30 @@ struct Rec {
   static constexpr int64_t SIZE = (GC + DK * 4 + 255) / 256 * 256;
 };
 
+// A record is addressed through a buffer descriptor of its own (base = the record,
+// range = its size), so that fragment addresses are a per-lane 32-bit offset plus a
+// uniform byte offset: no 64-bit address arithmetic per access, and an access outside
+// the record reads zero / is dropped instead of touching other memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const unsigned char* rec, int64_t size) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(rec), 0, (int)size, 0x00020000);
+}
+// (Stores put the whole offset in the per-lane field and keep the scalar offset at zero:
+// the compiler protects the data registers of a wide buffer store from being
+// overwritten too early only in that form.)
 template <class Frag>
-__device__ __forceinline__ void st_frag(unsigned char* base, int64_t idx, int lane, const Frag& f) {
+__device__ __forceinline__ void st_frag(__amdgpu_buffer_rsrc_t rs, int off, int idx, int lane, const Frag& f) {
   static_assert(sizeof(Frag) == 32, "fragment size");
   const u32x4* h = reinterpret_cast<const u32x4*>(&f);
-  unsigned char* b = base + idx * 2048 + lane * 16;
-  *reinterpret_cast<u32x4*>(b) = h[0];
-  *reinterpret_cast<u32x4*>(b + 1024) = h[1];
+  __builtin_amdgcn_raw_buffer_store_b128(h[0], rs, lane * 16 + off + idx * 2048, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(h[1], rs, lane * 16 + 1024 + off + idx * 2048, 0, 0);
 }
 template <class Frag>
-__device__ __forceinline__ Frag ld_frag(const unsigned char* base, int64_t idx, int lane) {
+__device__ __forceinline__ Frag ld_frag(__amdgpu_buffer_rsrc_t rs, int off, int idx, int lane) {
   static_assert(sizeof(Frag) == 32, "fragment size");
   Frag f;
   u32x4* h = reinterpret_cast<u32x4*>(&f);
-  const unsigned char* b = base + idx * 2048 + lane * 16;
-  h[0] = *reinterpret_cast<const u32x4*>(b);
-  h[1] = *reinterpret_cast<const u32x4*>(b + 1024);
+  h[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, off + idx * 2048, 0);
+  h[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + 1024, off + idx * 2048, 0);
   return f;
 }
 
@@ -282,6 +290,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   int64_t bos, len, c0;
   if (!resolve_slot(p, slot, n, bos, len, c0)) return;
   unsigned char* rec = p.rec + ((int64_t)h * p.slots + slot) * p.rec_size;  // a head's chunks are adjacent
+  const __amdgpu_buffer_rsrc_t rs = rec_rsrc(rec, p.rec_size);
+  const int wu = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // the wave index, uniform
   const int H = p.H;
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
@@ -473,8 +483,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       float ut[8], qt[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) { ut[j] = uf[ks][j] * run[j]; qt[j] = qf[ks][j] * run[j]; }
-      st_frag(rec + R::UT, w * KS + ks, l, Pol::make(ut));
-      st_frag(rec + R::QT, w * KS + ks, l, Pol::make(qt));
+      st_frag(rs, R::UT, wu * KS + ks, l, Pol::make(ut));
+      st_frag(rs, R::QT, wu * KS + ks, l, Pol::make(qt));
     }
 #pragma unroll
     for (int J = 0; J < NBLK - 1; ++J) {
@@ -496,10 +506,10 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
     if (st == 0 || w >= 2) {
       float a8[8];
       load8(&sm.u1.P[16 * w + r][32 * st + 8 * g], a8);
-      st_frag(rec + R::PP, w * 2 + st, l, Pol::make(a8));
+      st_frag(rs, R::PP, wu * 2 + st, l, Pol::make(a8));
     }
   }
-  for (int rt = w; rt < DK / 16; rt += 4) {
+  for (int rt = wu; rt < DK / 16; rt += 4) {
     const int chA = 16 * rt + r;
     float tA[NBLK];
 #pragma unroll
@@ -514,7 +524,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = sm.u2.kg[k0 + j][chA] * suf;
-      st_frag(rec + R::KB, rt * 2 + st, l, Pol::make(x));
+      st_frag(rs, R::KB, rt * 2 + st, l, Pol::make(x));
     }
   }
   if (tid < DK) {
@@ -582,7 +592,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
     if (st == 0 || w >= 2) {
       float a8[8];
       load8(&sm.u2.T[16 * w + r][32 * st + 8 * g], a8);
-      st_frag(rec + R::TT, w * 2 + st, l, Pol::make(a8));
+      st_frag(rs, R::TT, wu * 2 + st, l, Pol::make(a8));
     }
   }
 }
@@ -711,28 +721,30 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     RowV pv;
     WRow pw;
   };
-  auto rec_ptr = [&](int c) -> const unsigned char* {
+  auto rec_ptr = [&](int c) -> __amdgpu_buffer_rsrc_t {
     const int cc = c < nch ? c : nch - 1;
-    return p.rec + ((int64_t)h * p.slots + first + cc) * p.rec_size;
+    return rec_rsrc(p.rec + ((int64_t)h * p.slots + first + cc) * p.rec_size, p.rec_size);
   };
-  auto load_uq = [&](Ops& op, const unsigned char* rc, int ks) {
-    op.fU[ks] = ld_frag<Frag>(rc + R::UT, w * KS + ks, l);
-    op.fQ[ks] = ld_frag<Frag>(rc + R::QT, w * KS + ks, l);
+  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, as a uniform value
+  auto load_uq = [&](Ops& op, __amdgpu_buffer_rsrc_t rc, int ks) {
+    op.fU[ks] = ld_frag<Frag>(rc, R::UT, wu * KS + ks, l);
+    op.fQ[ks] = ld_frag<Frag>(rc, R::QT, wu * KS + ks, l);
   };
   // T and P rows of block w are zero past token 16w + 15: only (w + 2) / 2 steps are loaded
-  auto load_tp = [&](Ops& op, const unsigned char* rc) {
-    op.fT[0] = ld_frag<Frag>(rc + R::TT, w * 2, l);
-    op.fP[0] = ld_frag<Frag>(rc + R::PP, w * 2, l);
+  auto load_tp = [&](Ops& op, __amdgpu_buffer_rsrc_t rc) {
+    op.fT[0] = ld_frag<Frag>(rc, R::TT, wu * 2, l);
+    op.fP[0] = ld_frag<Frag>(rc, R::PP, wu * 2, l);
     if (w >= 2) {
-      op.fT[1] = ld_frag<Frag>(rc + R::TT, w * 2 + 1, l);
-      op.fP[1] = ld_frag<Frag>(rc + R::PP, w * 2 + 1, l);
+      op.fT[1] = ld_frag<Frag>(rc, R::TT, wu * 2 + 1, l);
+      op.fP[1] = ld_frag<Frag>(rc, R::PP, wu * 2 + 1, l);
     }
   };
-  auto load_k = [&](Ops& op, const unsigned char* rc, int m) {
-    const int rt = w + 4 * m < DK / 16 ? w + 4 * m : 0;
+  auto load_k = [&](Ops& op, __amdgpu_buffer_rsrc_t rc, int m) {
+    const int rt = wu + 4 * m < DK / 16 ? wu + 4 * m : 0;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) op.fK[m][st] = ld_frag<Frag>(rc + R::KB, rt * 2 + st, l);
-    op.gC[m] = *reinterpret_cast<const f32x4*>(rc + R::GC + (16 * rt + 4 * g) * 4);
+    for (int st = 0; st < 2; ++st) op.fK[m][st] = ld_frag<Frag>(rc, R::KB, rt * 2 + st, l);
+    const u32x4 gc = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * g, R::GC + 64 * rt, 0);
+    op.gC[m] = *reinterpret_cast<const f32x4*>(&gc);
   };
   auto load_vw = [&](Ops& op, int c) {
     const int cc = c < nch ? c : nch - 1;
@@ -748,7 +760,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
   // that the waits at the top of the chunk loop, which serve both the first chunk and the
   // later ones, count the same loads in flight on both paths into the loop.
   auto load_ops = [&](Ops& op, int c) {
-    const unsigned char* rc = rec_ptr(c);
+    const __amdgpu_buffer_rsrc_t rc = rec_ptr(c);
     load_vw(op, c);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) load_uq(op, rc, ks);
@@ -808,7 +820,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     }
     // the next chunk's operands stream into `nxt` in small groups placed between the
     // MFMA groups below, so the load path and the matrix cores work at the same time
-    const unsigned char* rn = rec_ptr(c + 1);
+    const __amdgpu_buffer_rsrc_t rn = rec_ptr(c + 1);
     load_vw(nxt, c + 1);
 
     // ================= X = Utilde S0, Y = Qtilde S0, R = M - X   (block row w)
@@ -873,6 +885,10 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
           for (int ct = 0; ct < NCT; ++ct) Pol::mma(accY[ct], cur.fP[st], DF[ct][st]);
         }
       }
+      // the next chunk's Kbar and Gamma_C loads go out before the O stores below: loads
+      // issued after them could be given the stores' data registers as destinations
+#pragma unroll
+      for (int m = 0; m < NRT; ++m) load_k(nxt, rn, m);
       // O: accumulator layout -> LDS -> row segments, stored with 16-byte accesses
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -891,7 +907,6 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 #pragma unroll
       for (int m = 0; m < NRT; ++m) {
         const int rt = w + 4 * m;
-        load_k(nxt, rn, m);
         if (rt < DK / 16) {
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
