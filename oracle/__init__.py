@@ -27,3 +27,4 @@ from .chunked import chunked_reference  # noqa: F401
 from . import states  # noqa: F401
 from . import prep  # noqa: F401
 from . import backward  # noqa: F401
+from . import product  # noqa: F401
