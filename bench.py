@@ -9,7 +9,9 @@ measured HBM traffic is given per kernel beside it. Two full input sets alternat
 Cache cannot hold a step's inputs from the previous one. `value` is tokens/s
 (B*T tokens per step). The decode step (dr_decode_step) is timed in its own loop
 on 512 sequences x 32 heads with the 1 GiB fp32 state updated in place, and is
-reported as state GB/s under "decode".
+reported as state GB/s under "decode". Further legs time the snapshots, the
+fused input preparation, the backward pass and the two-transitions-per-token
+variant (prefill and decode) on the same shapes.
 
 Prints one JSON line. Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -114,6 +116,8 @@ def main():
     ap.add_argument("--no-states", action="store_true", help="skip the snapshot and slot-pool timings")
     ap.add_argument("--no-prep", action="store_true", help="skip the fused input preparation timing")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward (gradient) timing")
+    ap.add_argument("--no-product", action="store_true",
+                    help="skip the two-transitions-per-token variant's prefill and decode timings")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run the plain copy used to scale the HBM byte counters")
     args = ap.parse_args()
@@ -274,6 +278,35 @@ def main():
                "vs_forward": bms / ms_step}
         del gdO, gdS, grads
 
+    # two KDA transitions per token (PRODUCT2) on the same shape: 4 x 4096 tokens, 2 x 4096 steps
+    prod = None
+    if not args.no_product:
+        p2 = []
+        for seed in (1006, 2006):
+            wl = synth.make_product("kda", B, T, H, D, D, in_dtype="bf16", seed=seed)
+            p2.append(dict(q=t(wl.q, True), k=t(wl.k, True), v=t(wl.v, True), alpha=t(wl.alpha),
+                           erase=t(wl.erase), S0=t(wl.S0)))
+            del wl
+
+        def p2step(i):
+            s = p2[i % 2]
+            drl.dr_chunk_fwd(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "product2", s["S0"], None, o, S_T)
+
+        for i in range(3):
+            p2step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            p2step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        p2ms = e0.elapsed_time(e1) / args.steps
+        prod = {"prefill": {"workload": "two KDA transitions per token, B=4 T=4096 H=16 d=128 bf16 (8192 steps per "
+                                        "sequence)", "ms_per_step": p2ms, "tokens_per_s": tokens / (p2ms * 1e-3),
+                            "vs_kda": p2ms / ms_step}}
+        del p2
+
     traffic, kernel_traffic = None, None
     tfile = os.path.join(ROOT, "profiles", "chunk_fwd_kda_B4_T4096_H16_d128_traffic.json")
     if os.path.exists(tfile):
@@ -342,6 +375,32 @@ def main():
             pms = e0.elapsed_time(e1) / args.decode_steps
             pooled = {"us_per_step": pms * 1e3, "state_GBps": dbytes / (pms * 1e-3) / 1e9,
                       "slots": N, "order": "random permutation"}
+        if prod is not None:
+            # two transitions per token: the same state traffic, three column reductions
+            wp = synth.make_product_decode("kda", N, HD, D, D, steps=4, in_dtype="bf16", seed=1006)
+            ptoks = [dict(q=t(wp.q[i], True), k=t(wp.k[i], True), v=t(wp.v[i], True), alpha=t(wp.alpha[i]),
+                          erase=t(wp.erase[i])) for i in range(4)]
+            del wp
+
+            def p2dstep(i):
+                s = ptoks[i % 4]
+                drl.dr_decode_step(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "product2", S, od)
+
+            for i in range(10):
+                p2dstep(i)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(args.decode_steps):
+                p2dstep(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            p2d = e0.elapsed_time(e1) / args.decode_steps
+            p2bytes = dbytes + N * HD * (2 * D * 2 + 4)   # the second key, value and beta
+            prod["decode"] = {"workload": "decode, two KDA transitions per token, 512 x 32 heads, d=128, 1 GiB "
+                                          "fp32 state in place", "us_per_step": p2d * 1e3,
+                              "state_GBps": p2bytes / (p2d * 1e-3) / 1e9,
+                              "hbm_frac": p2bytes / (p2d * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            del ptoks
         decode = {
             "workload": "decode KDA, 512 sequences x 32 heads, d_k=d_v=128, fp32 state 1 GiB in place, bf16 q/k/v",
             "us_per_step": dms * 1e3,
@@ -379,6 +438,7 @@ def main():
         "stored_states": states,
         "fused_prep": fused,
         "backward": bwd,
+        "product2": prod,
         "measured_copy_GBps": copy["copy_GBps"],
         "run": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count, "torch": torch.__version__,

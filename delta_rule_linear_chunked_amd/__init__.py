@@ -23,7 +23,8 @@ __all__ = ["dr_chunk_fwd", "dr_decode_step", "dr_chunk_fwd_ex", "dr_decode_step_
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_PKG, "lib", "libdeltarule.so")
-VARIANTS = {"kda": 0, "rda": 1, "gdn2": 2, "ckda": 3}
+# "product2": two KDA transitions per token (k [.., 2, d_k], v [.., 2, d_v], beta [.., 2])
+VARIANTS = {"kda": 0, "rda": 1, "gdn2": 2, "ckda": 3, "product2": 4}
 _DT = {torch.float32: 0, torch.bfloat16: 1}
 _lib = None
 
@@ -137,6 +138,8 @@ def _need(t: Optional[torch.Tensor], name: str, shape, dtype=None, device=None):
 def _gate_shapes(variant: str, lead, dk, dv):
     if variant in ("kda", "ckda"):
         return tuple(lead), None
+    if variant == "product2":
+        return tuple(lead) + (2,), None
     if variant == "rda":
         return tuple(lead), tuple(lead)
     if variant == "gdn2":
@@ -185,9 +188,10 @@ def dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, 
     dev = q.device
     if q.dtype not in _DT:
         raise ValueError(f"q dtype {q.dtype} is not float32 or bfloat16")
+    nt = (2,) if variant == "product2" else ()  # the transition axis of k and v
     _need(q, "q", (B, T, H, dk), q.dtype, dev)
-    _need(k, "k", (B, T, H, dk), q.dtype, dev)
-    _need(v, "v", (B, T, H, dv), q.dtype, dev)
+    _need(k, "k", (B, T, H) + nt + (dk,), q.dtype, dev)
+    _need(v, "v", (B, T, H) + nt + (dv,), q.dtype, dev)
     _need(alpha, "alpha", (B, T, H, dk), _alpha_dtype(alpha, prep), dev)
     es, ws = _gate_shapes(variant, (B, T, H), dk, dv)
     _need(erase, "erase", es, torch.float32, dev)
@@ -237,9 +241,10 @@ def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_id
     dev = q.device
     if q.dtype not in _DT:
         raise ValueError(f"q dtype {q.dtype} is not float32 or bfloat16")
+    nt = (2,) if variant == "product2" else ()
     _need(q, "q", (N, H, dk), q.dtype, dev)
-    _need(k, "k", (N, H, dk), q.dtype, dev)
-    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(k, "k", (N, H) + nt + (dk,), q.dtype, dev)
+    _need(v, "v", (N, H) + nt + (dv,), q.dtype, dev)
     _need(alpha, "alpha", (N, H, dk), _alpha_dtype(alpha, prep), dev)
     es, ws = _gate_shapes(variant, (N, H), dk, dv)
     _need(erase, "erase", es, torch.float32, dev)

@@ -34,9 +34,10 @@ int check_variant(int variant, const float* erase, const float* write, bool has_
   switch (variant) {
     case DR_KDA:
     case DR_CKDA:
+    case DR_PRODUCT2:
       if (write != nullptr)
         return fail(DR_ERR_VARIANT, "variant %s takes beta as `erase` and no `write` gate",
-                    variant == DR_KDA ? "KDA" : "CKDA");
+                    variant == DR_KDA ? "KDA" : variant == DR_CKDA ? "CKDA" : "PRODUCT2");
       *vec = false;
       break;
     case DR_RDA:
@@ -162,9 +163,10 @@ int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t*
   g_last_error.clear();
   int st = check_dims_common(dims);
   if (st) return st;
-  if (variant < DR_KDA || variant > DR_CKDA) return fail(DR_ERR_VARIANT, "unknown variant %d", variant);
+  if (variant < DR_KDA || variant > DR_PRODUCT2) return fail(DR_ERR_VARIANT, "unknown variant %d", variant);
+  const int lg = variant == DR_PRODUCT2 ? 1 : 0;
   const dr::PrefillPlan pl = dr::plan_prefill(dims->num_seqs * dims->num_heads, dims->num_seqs, dims->batch,
-                                              dims->seqlen, dims->num_heads, (int)dims->head_dim_k,
+                                              dims->seqlen << lg, dims->num_heads, (int)dims->head_dim_k,
                                               (int)dims->head_dim_v, dims->batch == 1 && dims->num_seqs != 1);
   if (chunk) *chunk = pl.chunk;
   if (dv_block) *dv_block = pl.dv_block;
@@ -172,8 +174,8 @@ int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t*
   return DR_OK;
 }
 
-// Checks of the options shared by prefill and decode.
-static int opts_checks(const dr_opts* opts, bool prefill) {
+// Checks of the options shared by prefill and decode (lg: log2 of the transitions per token).
+static int opts_checks(const dr_opts* opts, bool prefill, int lg = 0) {
   if (!opts) return DR_OK;
   if (opts->alpha_dtype != DR_F32 && opts->alpha_dtype != DR_BF16)
     return fail(DR_ERR_DTYPE, "alpha_dtype %d is not DR_F32 / DR_BF16", opts->alpha_dtype);
@@ -193,9 +195,9 @@ static int opts_checks(const dr_opts* opts, bool prefill) {
   if (opts->snapshots) {
     if (!prefill) return fail(DR_ERR_SHAPE, "snapshots are a prefill option");
     if (!aligned16(opts->snapshots)) return fail(DR_ERR_ALIGN, "snapshots must be 16-byte aligned");
-    if (opts->snapshot_every <= 0 || opts->snapshot_every % 64 != 0)
-      return fail(DR_ERR_SHAPE, "snapshot_every (%lld) must be a positive multiple of 64",
-                  (long long)opts->snapshot_every);
+    if (opts->snapshot_every <= 0 || (opts->snapshot_every << lg) % 64 != 0)
+      return fail(DR_ERR_SHAPE, "snapshot_every (%lld) must be a positive multiple of %d",
+                  (long long)opts->snapshot_every, 64 >> lg);
     if (opts->snapshot_every / 64 > INT32_MAX) return fail(DR_ERR_UNSUPPORTED, "snapshot_every too large");
   }
   return DR_OK;
@@ -236,7 +238,9 @@ int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alp
   }
   st = check_ptrs({}, {{S0, "S0"}, {S_T, "S_T"}, {cu_seqlens, "cu_seqlens"}});
   if (st) return st;
-  st = opts_checks(opts, true);
+  // two transitions per token run as two steps of the prefill
+  const int lg = variant == DR_PRODUCT2 ? 1 : 0;
+  st = opts_checks(opts, true, lg);
   if (st) return st;
   if (cu_seqlens == nullptr && dims->num_seqs > 0 && dims->seqlen == 0 && S_T == nullptr)
     return DR_OK;  // nothing to compute and nothing to write (no snapshot fits in zero tokens)
@@ -245,13 +249,14 @@ int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alp
   dr::Params p{};
   p.q = q; p.k = k; p.v = v; p.alpha = alpha;
   p.erase = erase;
-  p.write = (variant == DR_KDA || variant == DR_CKDA) ? erase : write;
+  p.write = (variant == DR_RDA || variant == DR_GDN2) ? write : erase;
   p.S0 = S0; p.cu = cu_seqlens; p.o = o; p.S = S_T;
-  p.T = dims->seqlen;
+  p.lgnh = lg;
+  p.T = dims->seqlen << lg;
   p.H = (int32_t)dims->num_heads;
   p.DV = (int32_t)dims->head_dim_v;
   const int64_t pairs = dims->num_seqs * dims->num_heads;
-  const dr::PrefillPlan pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen, dims->num_heads,
+  const dr::PrefillPlan pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen << lg, dims->num_heads,
                                               (int)dims->head_dim_k, (int)dims->head_dim_v, cu_seqlens != nullptr);
   p.num_pairs = (int32_t)pairs;
   p.ndvb = pl.ndvb;
@@ -261,7 +266,7 @@ int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alp
     p.sidx = opts->state_idx;
     p.nslots = opts->num_slots;
     p.snap = opts->snapshots;
-    p.snap_chunks = opts->snapshots ? (int32_t)(opts->snapshot_every / 64) : 0;
+    p.snap_chunks = opts->snapshots ? (int32_t)((opts->snapshot_every << lg) / 64) : 0;
   }
   set_prep(p, opts);
   void* ws = nullptr;
@@ -291,6 +296,7 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
   bool vec = false;
   int st = prefill_checks(dims, variant, erase, write, cu_seqlens, &vec);
   if (st) return st;
+  if (variant == DR_PRODUCT2) return fail(DR_ERR_VARIANT, "the backward pass has no PRODUCT2 form");
   const bool has_write = variant == DR_RDA || variant == DR_GDN2;
   if (!has_write && dwrite != nullptr)
     return fail(DR_ERR_VARIANT, "KDA / CKDA take no dwrite (beta's whole gradient goes to derase)");
@@ -400,12 +406,15 @@ int dr_decode_step_ex(const void* q, const void* k, const void* v, const void* a
   set_prep(p, opts);
   p.q = q; p.k = k; p.v = v; p.alpha = alpha;
   p.erase = erase;
-  p.write = (variant == DR_KDA || variant == DR_CKDA) ? erase : write;
+  p.write = (variant == DR_RDA || variant == DR_GDN2) ? write : erase;
   p.o = o; p.S = S;
   p.H = (int32_t)dims->num_heads;
   p.DV = (int32_t)dims->head_dim_v;
-  hipError_t e = dr::launch_decode(p, nheads, (int)dims->head_dim_k, (int)dims->head_dim_v,
-                                   dims->in_dtype == DR_BF16, vec, stream);
+  hipError_t e = variant == DR_PRODUCT2
+                     ? dr::launch_decode2(p, nheads, (int)dims->head_dim_k, (int)dims->head_dim_v,
+                                          dims->in_dtype == DR_BF16, stream)
+                     : dr::launch_decode(p, nheads, (int)dims->head_dim_k, (int)dims->head_dim_v,
+                                         dims->in_dtype == DR_BF16, vec, stream);
   if (e != hipSuccess) return fail(DR_ERR_HIP, "decode launch failed: %s", hipGetErrorString(e));
   return DR_OK;
 }

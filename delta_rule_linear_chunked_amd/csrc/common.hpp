@@ -51,7 +51,23 @@ struct Params {
   int32_t g_act;        // erase / write activation: 0 none, 1 g_scale sigmoid(z)
   float a_scale;
   float g_scale;
+  // transitions per token, as a power of two (0: one, 1: two). With two, a token's two
+  // transitions are consecutive steps of the prefill: T, chunk positions and lengths
+  // count steps (cu offsets stay in tokens and are scaled on read), q and alpha rows
+  // are per token, k, v and the gates per step, and o is written after a token's last step.
+  int32_t lgnh;
 };
+
+// Row of step m (absolute step index) in the per-token arrays (q, alpha, o) and in the
+// per-step arrays (k, v, erase, write), head h; both are m * H + h with one step per token.
+__device__ __forceinline__ int64_t tok_row(const Params& p, int64_t m, int h) {
+  return (m >> p.lgnh) * p.H + h;
+}
+__device__ __forceinline__ int64_t step_row(const Params& p, int64_t m, int h) {
+  return (((m >> p.lgnh) * p.H + h) << p.lgnh) + (m & ((1 << p.lgnh) - 1));
+}
+// Offset of sequence n in steps, from the packed token offsets.
+__device__ __forceinline__ int64_t cu_steps(const Params& p, int n) { return (int64_t)p.cu[n] << p.lgnh; }
 
 // Parameter block of the backward pass (gradients of a prefill).
 struct BwdParams {

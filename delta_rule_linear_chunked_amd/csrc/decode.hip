@@ -217,4 +217,199 @@ hipError_t launch_decode(const Params& p, int64_t nheads, int dk, int dv, bool b
   return hipErrorInvalidValue;
 }
 
+// Two KDA transitions per token (PRODUCT2), in the same single pass over the state.
+// With X = Diag(alpha) S, u_j = beta_j k_j, m_j = beta_j v_j:
+//   delta_1 = m_1 - X^T u_1,            S' = X + k_1 delta_1^T
+//   delta_2 = m_2 - S'^T u_2 = m_2 - X^T u_2 - (k_1 . u_2) delta_1
+//   S_t = X + k_1 delta_1^T + k_2 delta_2^T
+//   o = S_t^T q = X^T q + (k_1 . q) delta_1 + (k_2 . q) delta_2
+// so three column reductions of S (against alpha.u_1, alpha.u_2, alpha.q) and three dot
+// products of the token's vectors give everything.
+template <int DK, int DV, typename InT>
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode2_kernel(const Params p) {
+  using Sh = DecodeShape<DK, DV>;
+  constexpr int DVS = Sh::DVS, COLS4 = Sh::COLS4, RG = Sh::RG, RPT = Sh::RPT, NT = Sh::NT;
+  __shared__ float s_q[DK], s_k1[DK], s_k2[DK], s_a[DK], s_au1[DK], s_au2[DK], s_aq[DK];
+  __shared__ float s_m1[DVS], s_m2[DVS];
+  __shared__ float s_red[3][RG][DVS + 4];
+  __shared__ float s_dot[3][RG];
+  __shared__ float s_d1[DVS], s_d2[DVS];
+  __shared__ float s_norm[3];
+
+  const int tid = threadIdx.x;
+  const int c4 = tid % COLS4;
+  const int rg = tid / COLS4;
+  const int64_t nh = blockIdx.x / Sh::NSPLIT;          // sequence * H + head
+  const int col0 = (blockIdx.x % Sh::NSPLIT) * DVS;
+  int64_t srow = nh;
+  if (p.sidx) {
+    const int64_t n = nh / p.H;
+    const int32_t sl = p.sidx[n];
+    if (sl < 0 || sl >= p.nslots) {
+      for (int j = tid; j < DVS; j += NT) p.o[nh * DV + col0 + j] = 0.f;
+      return;
+    }
+    srow = (int64_t)sl * p.H + (nh - n * p.H);
+  }
+  float* S = p.S + srow * (int64_t)DK * DV + col0;
+
+  f32x4 st[RPT];
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = rg + RG * i;
+    st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + row * DV) + c4);
+  }
+
+  const InT* q = static_cast<const InT*>(p.q) + nh * DK;
+  const InT* k1 = static_cast<const InT*>(p.k) + (2 * nh) * DK;
+  const InT* k2 = k1 + DK;
+  const InT* v1 = static_cast<const InT*>(p.v) + (2 * nh) * DV + col0;
+  const InT* v2 = v1 + DV;
+  float nq = 1.f, nk1 = 1.f, nk2 = 1.f;
+  if (p.prep_l2) {
+    if (tid < 64) {
+      float sq = 0.f, s1 = 0.f, s2 = 0.f;
+      for (int i = tid; i < DK; i += 64) {
+        const float qi = ld_f32(q + i), a = ld_f32(k1 + i), b = ld_f32(k2 + i);
+        sq = fmaf(qi, qi, sq);
+        s1 = fmaf(a, a, s1);
+        s2 = fmaf(b, b, s2);
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        sq += __shfl_xor(sq, o);
+        s1 += __shfl_xor(s1, o);
+        s2 += __shfl_xor(s2, o);
+      }
+      if (tid == 0) {
+        s_norm[0] = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
+        s_norm[1] = s1 > 0.f ? __builtin_amdgcn_rsqf(s1) : 0.f;
+        s_norm[2] = s2 > 0.f ? __builtin_amdgcn_rsqf(s2) : 0.f;
+      }
+    }
+    __syncthreads();
+    nq = s_norm[0];
+    nk1 = s_norm[1];
+    nk2 = s_norm[2];
+  }
+  const bool prep = p.a_act || p.g_act || p.a_bf16;  // fused activations (uniform)
+  float b1 = p.erase[2 * nh], b2 = p.erase[2 * nh + 1];
+  if (prep) {
+    b1 = prep_gate(b1, p);
+    b2 = prep_gate(b2, p);
+  }
+  for (int i = tid; i < DK; i += NT) {
+    const float qi = ld_f32(q + i) * nq, ai = ld_f32(k1 + i) * nk1, bi = ld_f32(k2 + i) * nk2;
+    const float a = prep ? load_alpha1(p, nh * DK + i) : static_cast<const float*>(p.alpha)[nh * DK + i];
+    s_q[i] = qi;
+    s_k1[i] = ai;
+    s_k2[i] = bi;
+    s_a[i] = a;
+    s_au1[i] = a * (b1 * ai);
+    s_au2[i] = a * (b2 * bi);
+    s_aq[i] = a * qi;
+  }
+  for (int j = tid; j < DVS; j += NT) {
+    s_m1[j] = b1 * ld_f32(v1 + j);
+    s_m2[j] = b2 * ld_f32(v2 + j);
+  }
+  __syncthreads();
+
+  float r1[4] = {0.f, 0.f, 0.f, 0.f}, r2[4] = {0.f, 0.f, 0.f, 0.f}, rq[4] = {0.f, 0.f, 0.f, 0.f};
+  float d12 = 0.f, d1q = 0.f, d2q = 0.f;
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = rg + RG * i;
+    const float au1 = s_au1[row], au2 = s_au2[row], aq = s_aq[row];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      r1[c] = fmaf(st[i][c], au1, r1[c]);
+      r2[c] = fmaf(st[i][c], au2, r2[c]);
+      rq[c] = fmaf(st[i][c], aq, rq[c]);
+    }
+    const float ka = s_k1[row], kb = s_k2[row], qr = s_q[row];
+    d12 = fmaf(ka, b2 * kb, d12);
+    d1q = fmaf(ka, qr, d1q);
+    d2q = fmaf(kb, qr, d2q);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    s_red[0][rg][4 * c4 + c] = r1[c];
+    s_red[1][rg][4 * c4 + c] = r2[c];
+    s_red[2][rg][4 * c4 + c] = rq[c];
+  }
+  if (c4 == 0) {
+    s_dot[0][rg] = d12;
+    s_dot[1][rg] = d1q;
+    s_dot[2][rg] = d2q;
+  }
+  __syncthreads();
+
+  if (tid < DVS) {
+    float u1 = 0.f, u2 = 0.f, uq = 0.f, e12 = 0.f, e1q = 0.f, e2q = 0.f;
+#pragma unroll
+    for (int g = 0; g < RG; ++g) {
+      u1 += s_red[0][g][tid];
+      u2 += s_red[1][g][tid];
+      uq += s_red[2][g][tid];
+      e12 += s_dot[0][g];
+      e1q += s_dot[1][g];
+      e2q += s_dot[2][g];
+    }
+    const float delta1 = s_m1[tid] - u1;
+    const float delta2 = s_m2[tid] - u2 - e12 * delta1;
+    s_d1[tid] = delta1;
+    s_d2[tid] = delta2;
+    p.o[nh * DV + col0 + tid] = fmaf(e2q, delta2, fmaf(e1q, delta1, uq));
+  }
+  __syncthreads();
+
+  float d1[4], d2[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    d1[c] = s_d1[4 * c4 + c];
+    d2[c] = s_d2[4 * c4 + c];
+  }
+#pragma unroll
+  for (int i = 0; i < RPT; ++i) {
+    const int row = rg + RG * i;
+    const float a = s_a[row], ka = s_k1[row], kb = s_k2[row];
+    f32x4 nv;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) nv[c] = fmaf(a, st[i][c], fmaf(ka, d1[c], kb * d2[c]));
+    __builtin_nontemporal_store(nv, reinterpret_cast<f32x4*>(S + row * DV) + c4);
+  }
+}
+
+template <int DK, int DV>
+static hipError_t launch_decode2_t(const Params& p, int64_t nheads, bool bf16, hipStream_t s) {
+  constexpr int NT = DecodeShape<DK, DV>::NT;
+  const dim3 grid((unsigned)(nheads * DecodeShape<DK, DV>::NSPLIT));
+  if (bf16) hipLaunchKernelGGL((decode2_kernel<DK, DV, __bf16>), grid, dim3(NT), 0, s, p);
+  else hipLaunchKernelGGL((decode2_kernel<DK, DV, float>), grid, dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DK>
+static hipError_t dispatch2_dv(const Params& p, int64_t nheads, int dv, bool bf16, hipStream_t s) {
+  switch (dv) {
+    case 16: return launch_decode2_t<DK, 16>(p, nheads, bf16, s);
+    case 32: return launch_decode2_t<DK, 32>(p, nheads, bf16, s);
+    case 64: return launch_decode2_t<DK, 64>(p, nheads, bf16, s);
+    case 128: return launch_decode2_t<DK, 128>(p, nheads, bf16, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode2(const Params& p, int64_t nheads, int dk, int dv, bool bf16, hipStream_t s) {
+  if (nheads == 0) return hipSuccess;
+  switch (dk) {
+    case 16: return dispatch2_dv<16>(p, nheads, dv, bf16, s);
+    case 32: return dispatch2_dv<32>(p, nheads, dv, bf16, s);
+    case 64: return dispatch2_dv<64>(p, nheads, dv, bf16, s);
+    case 128: return dispatch2_dv<128>(p, nheads, dv, bf16, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace dr

@@ -12,6 +12,8 @@ struct BwdParams;
 // Decode: one workgroup per (sequence, head); p.S is the state updated in place.
 hipError_t launch_decode(const Params& p, int64_t nheads, int dk, int dv, bool bf16, bool vec,
                          hipStream_t s);
+// Decode step with two KDA transitions per token (PRODUCT2).
+hipError_t launch_decode2(const Params& p, int64_t nheads, int dk, int dv, bool bf16, hipStream_t s);
 
 // Prefill launch shape for a problem.
 struct PrefillPlan {

@@ -110,8 +110,8 @@ __device__ __forceinline__ bool resolve_slot(const Params& p, int slot, int& n, 
   if (p.cu) {
     n = p.chunk_seq[slot];
     if (n < 0) return false;
-    bos = p.cu[n];
-    len = (int64_t)p.cu[n + 1] - bos;
+    bos = cu_steps(p, n);
+    len = cu_steps(p, n + 1) - bos;
     c0 = p.chunk_c0[slot];
   } else {
     n = slot / p.cps;
@@ -133,7 +133,7 @@ __global__ __launch_bounds__(256) void chunk_plan_kernel(const Params p) {
   __syncthreads();
   for (int base = 0; base < p.nseq; base += 256) {
     const int n = base + tid;
-    const int nc = n < p.nseq ? (p.cu[n + 1] - p.cu[n] + CH - 1) / CH : 0;
+    const int nc = n < p.nseq ? (int)((cu_steps(p, n + 1) - cu_steps(p, n) + CH - 1) / CH) : 0;
     s_scan[tid] = nc;
     __syncthreads();
     for (int d = 1; d < 256; d <<= 1) {
@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void chunk_plan_kernel(const Params p) {
     const int stride = p.snap_chunks * CH;
     for (int base = 0; base < p.nseq; base += 256) {
       const int n = base + tid;
-      const int ns = n < p.nseq ? (p.cu[n + 1] - p.cu[n]) / stride : 0;
+      const int ns = n < p.nseq ? (int)((cu_steps(p, n + 1) - cu_steps(p, n)) / stride) : 0;
       s_scan[tid] = ns;
       __syncthreads();
       for (int d = 1; d < 256; d <<= 1) {
@@ -213,7 +213,8 @@ __device__ __forceinline__ void load_alpha(const Params& p, int64_t i, float (&a
 // A block with a gate at or extremely near zero (rare): k . g from exact suffix products and
 // the diagonal tiles of A and P from running products of the gates, exact for any gate value.
 template <int DKR, int DK, typename InT, bool VEC, int AM>
-__device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, int64_t th, bool valid, float esc,
+__device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, int64_t thq, int64_t thk, bool unit_a,
+                                         bool valid, float esc,
                                          float rq, float rk, int w, int r, int g) {
   constexpr int KS = DK / 32;
   const int row = 16 * w + r;
@@ -229,11 +230,11 @@ __device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, i
     const int ch0 = 32 * ks + 8 * g;
     const bool live = valid && ch0 < DKR;
     float a8[8], k8[8];
-    alpha8(th * DKR + (live ? ch0 : 0), a8);
-    load8(kp + th * DKR + (live ? ch0 : 0), k8);
+    alpha8(thq * DKR + (live ? ch0 : 0), a8);
+    load8(kp + thk * DKR + (live ? ch0 : 0), k8);
     float kgv[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) kgv[j] = (live ? k8[j] * rk : 0.f) * row_suffix_prod_excl(live ? a8[j] : 1.f);
+    for (int j = 0; j < 8; ++j) kgv[j] = (live ? k8[j] * rk : 0.f) * row_suffix_prod_excl(live && !unit_a ? a8[j] : 1.f);
     store4(&sm.u2.kg[row][ch0], f32x4{kgv[0], kgv[1], kgv[2], kgv[3]});
     store4(&sm.u2.kg[row][ch0 + 4], f32x4{kgv[4], kgv[5], kgv[6], kgv[7]});
   }
@@ -244,14 +245,14 @@ __device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, i
       const int ch0 = 32 * ks + 8 * g;
       const bool live = valid && ch0 < DKR;
       float a2[8], k2[8], q2[8], b2[8];
-      load_alpha<AM == 0 ? 0 : AM == 2 ? 3 : 4>(p, th * DKR + (live ? ch0 : 0), a2);  // raw
-      load8(kp + th * DKR + (live ? ch0 : 0), k2);
-      load8(qp + th * DKR + (live ? ch0 : 0), q2);
-      if constexpr (VEC) load8(p.erase + th * DKR + (live ? ch0 : 0), b2);
+      load_alpha<AM == 0 ? 0 : AM == 2 ? 3 : 4>(p, thq * DKR + (live ? ch0 : 0), a2);  // raw
+      load8(kp + thk * DKR + (live ? ch0 : 0), k2);
+      load8(qp + thq * DKR + (live ? ch0 : 0), q2);
+      if constexpr (VEC) load8(p.erase + thk * DKR + (live ? ch0 : 0), b2);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float a = 1.f;
-        if (live) {
+        if (live && !unit_a) {
           if constexpr (AM != 0) a = prep_alpha(a2[j], p);  // one element at a time
           else a = a2[j];
         }
@@ -309,7 +310,11 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
 
   const int row = 16 * w + r;
   const bool valid = c0 + row < len;
-  const int64_t th = (bos + c0 + (valid ? row : 0)) * H + h;
+  // rows of this lane's step in the per-token (q, alpha) and per-step (k, gates) arrays; the
+  // decay acts on the first step of a token only
+  const int64_t mstep = bos + c0 + (valid ? row : 0);
+  const int64_t thq = tok_row(p, mstep, h), thk = step_row(p, mstep, h);
+  const bool unit_a = (mstep & ((1 << p.lgnh) - 1)) != 0;
 
   // ---------------------------------------------------------------- input preparation
   // With fused preparation the row's decay pre-activations are loaded first, so that their
@@ -319,7 +324,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch0 = 32 * ks + 8 * g;
-      load_alpha<AM == 2 ? 3 : 4>(p, th * DKR + (valid && ch0 < DKR ? ch0 : 0), av[ks]);  // raw
+      load_alpha<AM == 2 ? 3 : 4>(p, thq * DKR + (valid && ch0 < DKR ? ch0 : 0), av[ks]);  // raw
     }
   }
   // inverse L2 norms of this row's q and k over d_k (1 when the inputs come normalised): the
@@ -332,8 +337,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       const int ch0 = 32 * ks + 8 * g;
       if (valid && ch0 < DKR) {
         float k8[8], q8[8];
-        load8(kp + th * DKR + ch0, k8);
-        load8(qp + th * DKR + ch0, q8);
+        load8(kp + thk * DKR + ch0, k8);
+        load8(qp + thq * DKR + ch0, q8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) { sq = fmaf(q8[j], q8[j], sq); sk = fmaf(k8[j], k8[j], sk); }
       }
@@ -349,7 +354,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) av[ks][j] = prep_alpha(av[ks][j], p);
+      for (int j = 0; j < 8; ++j) av[ks][j] = unit_a ? 1.f : prep_alpha(av[ks][j], p);
     }
   }
 
@@ -358,22 +363,24 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   {
     bool ok = true;
     f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f}, pd = ad;
-    const float esc = (!VEC && valid) ? gate(p.erase[th]) : 0.f;
+    const float esc = (!VEC && valid) ? gate(p.erase[thk]) : 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch0 = 32 * ks + 8 * g;
       const bool live = valid && ch0 < DKR;
       float a8[8], k8[8], q8[8], b8[8];
       if (live) {
-        load8(kp + th * DKR + ch0, k8);
-        load8(qp + th * DKR + ch0, q8);
+        load8(kp + thk * DKR + ch0, k8);
+        load8(qp + thq * DKR + ch0, q8);
         if constexpr (AM != 0) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) a8[j] = av[ks][j];
         } else {
-          alpha8(th * DKR + ch0, a8);
+          alpha8(thq * DKR + ch0, a8);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) a8[j] = unit_a ? 1.f : a8[j];
         }
-        if constexpr (VEC) load8(p.erase + th * DKR + ch0, b8);
+        if constexpr (VEC) load8(p.erase + thk * DKR + ch0, b8);
         if constexpr (AM != 0) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       }
     } else {
       // Some gate of this block is zero or nearly so: exact block path (out of line).
-      exact_block<DKR, DK, InT, VEC, AM>(p, sm, th, valid, esc, rq, rk, w, r, g);
+      exact_block<DKR, DK, InT, VEC, AM>(p, sm, thq, thk, unit_a, valid, esc, rq, rk, w, r, g);
     }
   }
   wave_lds_sync();
@@ -661,8 +668,8 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
   int64_t bos, len;
   int first;
   if (p.cu) {
-    bos = p.cu[n];
-    len = (int64_t)p.cu[n + 1] - bos;
+    bos = cu_steps(p, n);
+    len = cu_steps(p, n + 1) - bos;
     first = p.seq_first[n];
   } else {
     bos = (int64_t)n * p.T;
@@ -751,7 +758,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     const int64_t last = bos + len - 1;
     int64_t tv = bos + (int64_t)cc * CH + 16 * w + lr;
     tv = tv > last ? last : tv;
-    const int64_t thv = tv * H + h;
+    const int64_t thv = step_row(p, tv, h);
     op.pv = *reinterpret_cast<const RowV*>(vp + thv * DV + dv0 + lc);
     if constexpr (VEC) op.pw = *reinterpret_cast<const RowF*>(p.write + thv * DV + dv0 + lc);
     else op.pw = p.write[thv];
@@ -885,8 +892,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
           for (int ct = 0; ct < NCT; ++ct) Pol::mma(accY[ct], cur.fP[st], DF[ct][st]);
         }
       }
-      // the next chunk's Kbar and Gamma_C loads go out before the O stores below: loads
-      // issued after them could be given the stores' data registers as destinations
+      // the next chunk's Kbar and Gamma_C loads, issued ahead of the O stores
 #pragma unroll
       for (int m = 0; m < NRT; ++m) load_k(nxt, rn, m);
       // O: accumulator layout -> LDS -> row segments, stored with 16-byte accesses
@@ -898,8 +904,11 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
       wave_lds_sync();
       {
         const int64_t rw = c0 + 16 * w + lr;
-        if (p.o && rw < len) {  // (no output: the states are all that is wanted)
-          float* orow = p.o + ((bos + rw) * H + h) * DV + dv0 + lc;
+        // (no output: the states are all that is wanted; with two steps per token the
+        // output row follows the token's second step)
+        const int lastm = (1 << p.lgnh) - 1;
+        if (p.o && rw < len && ((bos + rw) & lastm) == lastm) {
+          float* orow = p.o + tok_row(p, bos + rw, h) * DV + dv0 + lc;
 #pragma unroll
           for (int j4 = 0; j4 < E / 4; ++j4) store4(orow + 4 * j4, *reinterpret_cast<const f32x4*>(&sm.X[w][lr][lc + 4 * j4]));
         }

@@ -17,6 +17,19 @@
  *     DR_RDA       e_t     [.., H]   u = e k      w_t [.., H],    m = w v
  *     DR_GDN2      b_t     [.., H, d_k] u = b.k   w_t [.., H, d_v], m = w.v
  *
+ * DR_PRODUCT2 applies two such transitions per token, each with KDA's rule and
+ * its own key, value and beta, the decay acting once before the first and the
+ * readout after the second:
+ *
+ *     S' = (I - b_1 k_1 k_1^T) Diag(alpha_t) S_{t-1} + b_1 k_1 v_1^T
+ *     S_t = (I - b_2 k_2 k_2^T) S'                    + b_2 k_2 v_2^T,   o_t = S_t^T q_t
+ *
+ * (the composition of two delta-rule transitions per update that the Complex KDA
+ * abstract cites as prior work, DeltaProduct with two factors). Its k is
+ * [.., H, 2, d_k], v [.., H, 2, d_v] and beta (erase) [.., H, 2]; q and alpha keep
+ * one row per token and write is NULL. It has a prefill and a decode step but no
+ * backward pass (DR_ERR_VARIANT), and its snapshot_every must be a multiple of 32.
+ *
  * The state S has d_k rows (key channels) and d_v columns; Diag(alpha_t) scales
  * its rows. The readout uses the updated state and no 1/sqrt(d_k) factor.
  * Gate values are not range-checked: CKDA differs from KDA only in the values
@@ -51,7 +64,7 @@
 extern "C" {
 #endif
 
-typedef enum dr_variant { DR_KDA = 0, DR_RDA = 1, DR_GDN2 = 2, DR_CKDA = 3 } dr_variant;
+typedef enum dr_variant { DR_KDA = 0, DR_RDA = 1, DR_GDN2 = 2, DR_CKDA = 3, DR_PRODUCT2 = 4 } dr_variant;
 
 /* Element type of q, k and v. Gates, states and outputs are always float32. */
 typedef enum dr_dtype { DR_F32 = 0, DR_BF16 = 1 } dr_dtype;

@@ -10,6 +10,8 @@ from .workloads import (  # noqa: F401
     draw_varlen_lengths,
     make_prefill,
     make_decode,
+    make_product,
+    make_product_decode,
     preset,
     PRESETS,
 )

@@ -257,6 +257,77 @@ def make_decode(recipe: str, N: int, H: int, dk: int, dv: int, *, steps: int = 1
     )
 
 
+def _product_draw(rng, recipe: str, lead: tuple, dk: int, dv: int, preact: bool):
+    """q, k (two keys per token), v (two values), alpha, beta (two) in that draw order."""
+    if recipe not in ("kda", "ckda"):
+        raise ValueError("two-transition workloads use the kda or ckda gate recipe")
+    q = rng.standard_normal(lead + (dk,))
+    k = rng.standard_normal(lead + (2, dk))
+    if not preact:
+        q, k = _l2_normalise(q), _l2_normalise(k)
+    v = rng.standard_normal(lead + (2, dv))
+    za = rng.standard_normal(lead + (dk,))
+    zb = rng.standard_normal(lead + (2,))
+    if preact:
+        alpha, beta, _ = _preact_gates(rng, recipe, za, zb, None)
+    else:
+        alpha, beta, _ = _finish_gates(rng, recipe, za, zb, None)
+        if recipe == "ckda":
+            alpha, beta = _ckda_masks(rng, alpha, beta)
+    return q, k, v, alpha, beta
+
+
+def make_product(recipe: str, B: int, T: int, H: int, dk: int, dv: int, *, in_dtype: str = "bf16",
+                 seed: int = 0, random_s0: bool = True, lengths=None, name: str = "", preact: bool = False,
+                 alpha_dtype: str = "f32") -> Workload:
+    """Prefill workload of the two-transitions-per-token variant: q, alpha [B,T,H,dk];
+    k [B,T,H,2,dk] (each key L2-normalised); v [B,T,H,2,dv]; erase = beta [B,T,H,2] with the
+    gate recipe's distribution for each transition; write None. ``lengths`` packs as in
+    ``make_prefill``."""
+    rng = np.random.default_rng(seed)
+    cu = None
+    if lengths is not None:
+        if B != 1:
+            raise ValueError("packed sequences need B == 1")
+        lengths = np.asarray(lengths, dtype=np.int64)
+        T = int(lengths.sum())
+        cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    N = len(cu) - 1 if cu is not None else B
+    q, k, v, alpha, beta = _product_draw(rng, recipe, (B, T, H), dk, dv, preact)
+    S0 = rng.standard_normal((N, H, dk, dv)) / np.sqrt(dk) if random_s0 else None
+    meta = {"recipe": recipe, "seed": seed, "B": B, "T": T, "H": H, "dk": dk, "dv": dv, "transitions": 2,
+            "lengths": None if lengths is None else [int(x) for x in lengths]}
+    if preact:
+        meta["prep"] = dict(PREP[recipe], alpha_dtype=alpha_dtype)
+    return Workload(
+        name=name or f"product2_{recipe}_B{B}_T{T}_H{H}_d{dk}x{dv}" + ("_preact" if preact else ""),
+        variant="product2", in_dtype=in_dtype,
+        q=_to_input(q, in_dtype), k=_to_input(k, in_dtype), v=_to_input(v, in_dtype),
+        alpha=_to_input(alpha, alpha_dtype), erase=beta.astype(np.float32), write=None,
+        S0=None if S0 is None else S0.astype(np.float32), cu_seqlens=cu, chunk=64, meta=meta,
+    )
+
+
+def make_product_decode(recipe: str, N: int, H: int, dk: int, dv: int, *, steps: int = 1,
+                        in_dtype: str = "bf16", seed: int = 0, name: str = "", preact: bool = False,
+                        alpha_dtype: str = "f32") -> Workload:
+    """Decode workload of the two-transitions-per-token variant: q, alpha [steps,N,H,dk];
+    k [steps,N,H,2,dk]; v [steps,N,H,2,dv]; beta [steps,N,H,2]; S0 [N,H,dk,dv]."""
+    rng = np.random.default_rng(seed)
+    q, k, v, alpha, beta = _product_draw(rng, recipe, (steps, N, H), dk, dv, preact)
+    S0 = (rng.standard_normal((N, H, dk, dv)) / np.sqrt(dk)).astype(np.float32)
+    meta = {"recipe": recipe, "seed": seed, "N": N, "H": H, "dk": dk, "dv": dv, "steps": steps, "transitions": 2}
+    if preact:
+        meta["prep"] = dict(PREP[recipe], alpha_dtype=alpha_dtype)
+    return Workload(
+        name=name or f"decode_product2_{recipe}_N{N}_H{H}_d{dk}x{dv}_s{steps}",
+        variant="product2", in_dtype=in_dtype,
+        q=_to_input(q, in_dtype), k=_to_input(k, in_dtype), v=_to_input(v, in_dtype),
+        alpha=_to_input(alpha, alpha_dtype), erase=beta.astype(np.float32), write=None,
+        S0=S0, cu_seqlens=None, chunk=1, meta=meta,
+    )
+
+
 # The five workloads the path is measured and checked on.  Seeds are 1000 + the
 # workload number (1-based).
 PRESETS = {
@@ -283,6 +354,11 @@ PRESETS = {
                         in_dtype="bf16", seed=1005),
     "decode_ckda": dict(kind="decode", recipe="ckda", N=512, H=32, dk=128, dv=128,
                         in_dtype="bf16", seed=1005),
+    # the two-transitions-per-token variant at the KDA prefill and decode shapes
+    "product2_prefill": dict(kind="product", recipe="kda", B=4, T=4096, H=16, dk=128, dv=128,
+                             in_dtype="bf16", seed=1006, random_s0=True),
+    "decode_product2": dict(kind="product_decode", recipe="kda", N=512, H=32, dk=128, dv=128,
+                            in_dtype="bf16", seed=1006),
 }
 
 
@@ -303,4 +379,10 @@ def preset(name: str, **override) -> Workload:
     if kind == "decode":
         return make_decode(p.pop("recipe"), p.pop("N"), p.pop("H"), p.pop("dk"), p.pop("dv"),
                            name=name, **p)
+    if kind == "product":
+        return make_product(p.pop("recipe"), p.pop("B"), p.pop("T"), p.pop("H"), p.pop("dk"),
+                            p.pop("dv"), name=name, **p)
+    if kind == "product_decode":
+        return make_product_decode(p.pop("recipe"), p.pop("N"), p.pop("H"), p.pop("dk"), p.pop("dv"),
+                                   name=name, **p)
     raise ValueError(kind)

@@ -67,6 +67,7 @@ def chunk(lib, d, variant=0, write=None, S0=None, cu=None, q=FAKE, o=FAKE):
     (dict(d=dims(), variant=9), -6),
     (dict(d=dims(), variant=0, write=FAKE), -6),     # KDA takes no write gate
     (dict(d=dims(), variant=3, write=FAKE), -6),     # CKDA neither
+    (dict(d=dims(), variant=4, write=FAKE), -6),     # nor the two-transition variant
     (dict(d=dims(), variant=1, write=None), -6),     # RDA needs one
     (dict(d=dims(), variant=2, write=None), -6),     # GDN-2 needs one
     (dict(d=dims(B=2, N=3)), -2),                    # N must equal B without cu_seqlens
@@ -136,6 +137,19 @@ def test_state_options_are_checked(lib, opts, expect):
     st = lib.dr_chunk_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, None, FAKE, None,
                              ctypes.byref(dims()), ctypes.byref(o), None)
     assert st == expect, lib.dr_last_error()
+
+
+def test_two_transition_variant_options(lib):
+    # snapshots count tokens: a multiple of 32 tokens is a multiple of 64 steps
+    o = _opts(snapshots=0x100000, every=48)
+    st = lib.dr_chunk_fwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, None, None, FAKE, None,
+                             ctypes.byref(dims()), ctypes.byref(o), None)
+    assert st == -2, lib.dr_last_error()
+    assert "multiple of 32" in lib.dr_last_error().decode()
+    # no backward pass for it
+    st = lib.dr_chunk_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, None, None, FAKE, None,
+                          FAKE, FAKE, FAKE, FAKE, FAKE, None, None, ctypes.byref(dims()), None)
+    assert st == -6, lib.dr_last_error()
 
 
 def test_decode_takes_no_snapshots(lib):
