@@ -892,10 +892,25 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
           for (int ct = 0; ct < NCT; ++ct) Pol::mma(accY[ct], cur.fP[st], DF[ct][st]);
         }
       }
-      // the next chunk's Kbar and Gamma_C loads, issued ahead of the O stores
+      // the next chunk's Kbar and Gamma_C loads
 #pragma unroll
       for (int m = 0; m < NRT; ++m) load_k(nxt, rn, m);
-      // O: accumulator layout -> LDS -> row segments, stored with 16-byte accesses
+      // S <- Diag(Gamma_C) S0 + Kbar^T delta (the sequential chain) issued first ...
+      f32x4 accS[NRT][NCT];
+#pragma unroll
+      for (int m = 0; m < NRT; ++m) {
+        const int rt = w + 4 * m;
+        if (rt < DK / 16) {
+#pragma unroll
+          for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) accS[m][ct][i] = cur.gC[m][i] * Sm[m][ct][i];
+#pragma unroll
+            for (int st = 0; st < 2; ++st) Pol::mma(accS[m][ct], cur.fK[m][st], DF[ct][st]);
+          }
+        }
+      }
+      // ... and O written while those MFMAs run: accumulator layout -> LDS -> row segments
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
@@ -904,13 +919,15 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
       wave_lds_sync();
       {
         const int64_t rw = c0 + 16 * w + lr;
-        // (no output: the states are all that is wanted; with two steps per token the
-        // output row follows the token's second step)
         const int lastm = (1 << p.lgnh) - 1;
         if (p.o && rw < len && ((bos + rw) & lastm) == lastm) {
-          float* orow = p.o + tok_row(p, bos + rw, h) * DV + dv0 + lc;
+          // lane (row, q) stores columns 16 j + 4 q .. + 3: each store of the wave covers 64
+          // contiguous bytes of every row it touches
+          float* orow = p.o + tok_row(p, bos + rw, h) * DV + dv0 + 4 * (l & 3);
 #pragma unroll
-          for (int j4 = 0; j4 < E / 4; ++j4) store4(orow + 4 * j4, *reinterpret_cast<const f32x4*>(&sm.X[w][lr][lc + 4 * j4]));
+          for (int j4 = 0; j4 < E / 4; ++j4)
+            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sm.X[w][lr][16 * j4 + 4 * (l & 3)]),
+                                        reinterpret_cast<f32x4*>(orow + 16 * j4));
         }
       }
 #pragma unroll
@@ -919,13 +936,8 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
         if (rt < DK / 16) {
 #pragma unroll
           for (int ct = 0; ct < NCT; ++ct) {
-            f32x4 acc;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = cur.gC[m][i] * Sm[m][ct][i];
-#pragma unroll
-            for (int st = 0; st < 2; ++st) Pol::mma(acc, cur.fK[m][st], DF[ct][st]);
-            Sm[m][ct] = acc;
-            sm.S.put4(16 * ct + r, 16 * rt + 4 * g, acc);
+            Sm[m][ct] = accS[m][ct];
+            sm.S.put4(16 * ct + r, 16 * rt + 4 * g, accS[m][ct]);
           }
         }
       }
