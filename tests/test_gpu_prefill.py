@@ -41,6 +41,18 @@ def test_small_all_variants(variant, dk, dv, in_dtype):
     check(wl)
 
 
+@pytest.mark.parametrize("block", ["16", "32", "64"])
+@pytest.mark.parametrize("variant", ["kda", "gdn2"])
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_value_block_widths(block, variant, in_dtype, monkeypatch):
+    # every value-column block width of the state pass (the planner picks 16 or 32; the
+    # DR_DV_BLOCK override reaches 64 too), on a packed ragged problem with d_v = 128
+    monkeypatch.setenv("DR_DV_BLOCK", block)
+    wl = synth.make_prefill(RECIPE[variant], 1, 0, 2, 128, 128, in_dtype=in_dtype,
+                            seed=seed_of("dvb", block, variant, in_dtype), lengths=[150, 64, 1, 77])
+    check(wl, f"dv_block={block}")
+
+
 @pytest.mark.parametrize("T", [1, 15, 16, 17, 63, 64, 65, 128, 200])
 def test_ragged_lengths(T):
     wl = synth.make_prefill("ckda", 2, T, 3, 64, 64, in_dtype="bf16", seed=T)
