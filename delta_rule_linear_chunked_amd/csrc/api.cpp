@@ -139,7 +139,7 @@ const char* dr_status_string(int status) {
 
 const char* dr_last_error(void) { return g_last_error.c_str(); }
 
-int dr_version(void) { return 100; }
+int dr_version(void) { return 200; }
 
 static int prefill_checks(const dr_dims* dims, int variant, const float* erase, const float* write,
                           const int32_t* cu_seqlens, bool* vec) {

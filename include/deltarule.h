@@ -40,7 +40,8 @@
  * aligned. The caller owns every argument buffer; the library keeps no pointer
  * to them after a call returns. dr_decode_step uses no other device memory.
  * dr_chunk_fwd needs a workspace between its two kernels (about 128.5 KiB per
- * 64-token chunk and head at d_k = 128); it takes it stream-ordered on `stream`
+ * 64-step chunk and head at d_k = 128; a step is a token, or half a token for
+ * DR_PRODUCT2); it takes it stream-ordered on `stream`
  * from a per-device memory pool owned by the library, which keeps what it has
  * reserved for later calls (a larger problem grows it once). Apart from that
  * pool the library holds only a thread-local error message. Work is enqueued
@@ -109,6 +110,8 @@ typedef struct dr_dims {
  *   alpha      [B, T, H, d_k]  float32, channel-wise decay
  *   erase      [B, T, H] float32 (KDA/CKDA beta, RDA e) or [B, T, H, d_k] (GDN-2 b)
  *   write      NULL (KDA/CKDA), [B, T, H] (RDA w) or [B, T, H, d_v] (GDN-2 w)
+ *              (DR_PRODUCT2: k [B, T, H, 2, d_k], v [B, T, H, 2, d_v], erase [B, T, H, 2],
+ *              write NULL)
  *   S0         [N, H, d_k, d_v] float32 initial states, or NULL for zero states
  *   cu_seqlens [N + 1] int32 or NULL. When given, B must be 1 and sequence n is
  *              tokens cu_seqlens[n] .. cu_seqlens[n+1]-1 of the packed row; each
@@ -134,6 +137,7 @@ int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha
  * with T at decode).
  *
  *   q, k       [N, H, d_k]  in_dtype;   v [N, H, d_v] in_dtype
+ *              (DR_PRODUCT2: k [N, H, 2, d_k], v [N, H, 2, d_v], erase [N, H, 2])
  *   alpha      [N, H, d_k]  float32
  *   erase      [N, H] or [N, H, d_k] (GDN-2);  write NULL, [N, H] or [N, H, d_v]
  *   S          [N, H, d_k, d_v] float32, read and overwritten with S_t
@@ -177,8 +181,8 @@ typedef enum {
  *                  floor(len_m / snapshot_every). Resuming a prefill from row
  *                  first_n + j over the rest of the sequence gives the same
  *                  outputs and final state, up to rounding.
- *   snapshot_every a positive multiple of 64 (snapshots sit on chunk boundaries);
- *                  otherwise DR_ERR_SHAPE.
+ *   snapshot_every a positive multiple of 64, or of 32 for DR_PRODUCT2 (snapshots
+ *                  sit on boundaries of 64-step chunks); otherwise DR_ERR_SHAPE.
  * Snapshots cost one extra state write per snapshot (d_k * d_v * 4 bytes per head).
  *
  * Fused input preparation: the step in front of the recurrence (the course page's
