@@ -24,6 +24,7 @@ from __future__ import annotations
 import numpy as np
 
 from .recurrence import _f64, step
+from .backward import step_recurrence_grads
 
 
 def product_step(S, q, k, v, alpha, beta):
@@ -79,3 +80,39 @@ def product_recurrence(q, k, v, alpha, beta, S0=None, cu_seqlens=None):
             S, o[0, t] = product_step(S, q[0, t], k[0, t], v[0, t], alpha[0, t], beta[0, t])
         S_T[n] = S
     return o, S_T
+
+
+def product_grads(q, k, v, alpha, beta, do, dS_T=None, S0=None, cu_seqlens=None):
+    """Gradients of L = sum(o * do) + sum(S_T * dS_T) with respect to every input of
+    ``product_recurrence``: a dict with dq, dalpha [B,T,H,d_k], dk [B,T,H,2,d_k],
+    dv [B,T,H,2,d_v], dbeta [B,T,H,2] and dS0 [N,H,d_k,d_v], in float64.
+
+    The two transitions of a token are two steps of KDA's rule, the decay alpha_t on the
+    first and 1 on the second, and the output is read after the second; so this runs the
+    reverse recurrence of ``backward.step_recurrence_grads`` on that sequence of 2T steps
+    (zero output gradient after first steps) and maps the result back: k, v and beta
+    per step, q and alpha from the step where they act.
+
+    Pinned by central finite differences of ``product_recurrence`` on small inputs
+    (signed gates, beta in [0, 2], packed sequences)."""
+    q, k, v, alpha, beta, do = _f64(q), _f64(k), _f64(v), _f64(alpha), _f64(beta), _f64(do)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    q2 = np.repeat(q, 2, axis=1)
+    k2 = k.transpose(0, 1, 3, 2, 4).reshape(B, 2 * T, H, dk)
+    v2 = v.transpose(0, 1, 3, 2, 4).reshape(B, 2 * T, H, dv)
+    b2 = beta.transpose(0, 1, 3, 2).reshape(B, 2 * T, H)
+    a2 = np.ones((B, 2 * T, H, dk))
+    a2[:, 0::2] = alpha
+    do2 = np.zeros((B, 2 * T, H, dv))
+    do2[:, 1::2] = do
+    cu2 = None if cu_seqlens is None else 2 * np.asarray(cu_seqlens, dtype=np.int64)
+    g = step_recurrence_grads(q2, k2, v2, a2, b2, None, "kda", do2, dS_T=dS_T, S0=S0, cu_seqlens=cu2)
+    return {
+        "dq": g["dq"][:, 0::2] + g["dq"][:, 1::2],
+        "dalpha": g["dalpha"][:, 0::2],
+        "dk": g["dk"].reshape(B, T, 2, H, dk).transpose(0, 1, 3, 2, 4),
+        "dv": g["dv"].reshape(B, T, 2, H, dv).transpose(0, 1, 3, 2, 4),
+        "dbeta": g["derase"].reshape(B, T, 2, H).transpose(0, 1, 3, 2),
+        "dS0": g["dS0"],
+    }

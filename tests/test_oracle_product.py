@@ -1,6 +1,7 @@
 """Pins for the two-transitions-per-token oracle (oracle.product): explicit transition
 matrices, the rotation closed form, orthogonality, reduction to KDA, the interleaved
-single-transition sequence, packing and decode. CPU only."""
+single-transition sequence, packing, decode, and the gradients against central finite
+differences. CPU only."""
 import numpy as np
 import pytest
 
@@ -122,3 +123,37 @@ def test_decode_steps_equal_the_recurrence():
         S, o_t = product.product_decode_step(S, q[:, t], k[:, t], v[:, t], alpha[:, t], beta[:, t])
         np.testing.assert_array_equal(o_t, o[:, t])
     np.testing.assert_array_equal(S, S_T)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_gradients_match_finite_differences(packed):
+    rng = np.random.default_rng(11 + packed)
+    if packed:
+        cu = np.array([0, 3, 3, 7])
+        B, T, N = 1, 7, 3
+    else:
+        cu, B, T, N = None, 2, 4, 2
+    H, dk, dv = 2, 3, 2
+    q, k, v, alpha, beta = _inputs(rng, B, T, H, dk, dv)
+    S0 = rng.standard_normal((N, H, dk, dv))
+    do = rng.standard_normal((B, T, H, dv))
+    dS = rng.standard_normal((N, H, dk, dv))
+    g = product.product_grads(q, k, v, alpha, beta, do, dS_T=dS, S0=S0, cu_seqlens=cu)
+
+    def loss(q_, k_, v_, a_, b_, s_):
+        o, S_T = product.product_recurrence(q_, k_, v_, a_, b_, S0=s_, cu_seqlens=cu)
+        return float(np.sum(o * do) + np.sum(S_T * dS))
+
+    args = [q, k, v, alpha, beta, S0]
+    names = ["dq", "dk", "dv", "dalpha", "dbeta", "dS0"]
+    eps = 1e-6
+    for ai, name in enumerate(names):
+        x = args[ai]
+        fd = np.zeros_like(x)
+        for idx in np.ndindex(x.shape):
+            xp = [a.copy() for a in args]
+            xm = [a.copy() for a in args]
+            xp[ai][idx] += eps
+            xm[ai][idx] -= eps
+            fd[idx] = (loss(*xp) - loss(*xm)) / (2 * eps)
+        np.testing.assert_allclose(g[name], fd, rtol=1e-6, atol=1e-7, err_msg=name)
