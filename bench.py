@@ -305,6 +305,27 @@ def main():
         prod = {"prefill": {"workload": "two KDA transitions per token, B=4 T=4096 H=16 d=128 bf16 (8192 steps per "
                                         "sequence)", "ms_per_step": p2ms, "tokens_per_s": tokens / (p2ms * 1e-3),
                             "vs_kda": p2ms / ms_step}}
+        if not args.no_backward:
+            s = p2[0]
+            gdO = torch.randn((B, T, H, D), device=dev)
+            g2 = dict(dq=torch.empty((B, T, H, D), device=dev), dk=torch.empty((B, T, H, 2, D), device=dev),
+                      dv=torch.empty((B, T, H, 2, D), device=dev), dalpha=torch.empty((B, T, H, D), device=dev),
+                      derase=torch.empty((B, T, H, 2), device=dev), dS0=torch.empty((B, H, D, D), device=dev))
+
+            def p2b():
+                drl.dr_chunk_bwd(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "product2", s["S0"], None,
+                                 gdO, None, g2["dq"], g2["dk"], g2["dv"], g2["dalpha"], g2["derase"], None, g2["dS0"])
+
+            p2b()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(3):
+                p2b()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            p2bms = e0.elapsed_time(e1) / 3
+            prod["backward"] = {"ms_per_step": p2bms, "tokens_per_s": tokens / (p2bms * 1e-3), "steps": 3}
+            del gdO, g2
         del p2
 
     traffic, kernel_traffic = None, None

@@ -312,9 +312,10 @@ def dr_chunk_bwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, dO,
     dev = q.device
     if q.dtype not in _DT:
         raise ValueError(f"q dtype {q.dtype} is not float32 or bfloat16")
+    nt = (2,) if variant == "product2" else ()  # the transition axis of k and v
     _need(q, "q", (B, T, H, dk_), q.dtype, dev)
-    _need(k, "k", (B, T, H, dk_), q.dtype, dev)
-    _need(v, "v", (B, T, H, dv_), q.dtype, dev)
+    _need(k, "k", (B, T, H) + nt + (dk_,), q.dtype, dev)
+    _need(v, "v", (B, T, H) + nt + (dv_,), q.dtype, dev)
     _need(alpha, "alpha", (B, T, H, dk_), torch.float32, dev)
     es, ws = _gate_shapes(variant, (B, T, H), dk_, dv_)
     _need(erase, "erase", es, torch.float32, dev)
@@ -331,8 +332,9 @@ def dr_chunk_bwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, dO,
         if t is not None:
             _need(t, name, (N, H, dk_, dv_), torch.float32, dev)
     _need(dO, "dO", (B, T, H, dv_), torch.float32, dev)
-    for t, name, shape in ((dq, "dq", (B, T, H, dk_)), (dk, "dk", (B, T, H, dk_)), (dv, "dv", (B, T, H, dv_)),
-                           (dalpha, "dalpha", (B, T, H, dk_)), (derase, "derase", es)):
+    for t, name, shape in ((dq, "dq", (B, T, H, dk_)), (dk, "dk", (B, T, H) + nt + (dk_,)),
+                           (dv, "dv", (B, T, H) + nt + (dv_,)), (dalpha, "dalpha", (B, T, H, dk_)),
+                           (derase, "derase", es)):
         _need(t, name, shape, torch.float32, dev)
     d = _Dims(B, T, H, dk_, dv_, N, _DT[q.dtype], 0)
     st = lib.dr_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write), VARIANTS[variant],
@@ -349,7 +351,7 @@ def chunk_bwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, 
     N = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
     g = dict(dq=f(q), dk=f(k), dv=f(v), dalpha=f(alpha), derase=f(erase),
              dwrite=None if write is None else f(write),
-             dS0=torch.empty((N, q.shape[2], q.shape[3], v.shape[3]), dtype=torch.float32, device=q.device)
+             dS0=torch.empty((N, q.shape[2], q.shape[3], v.shape[-1]), dtype=torch.float32, device=q.device)
              if need_dS0 else None)
     dr_chunk_bwd(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, dO, dS_T, g["dq"], g["dk"], g["dv"],
                  g["dalpha"], g["derase"], g["dwrite"], g["dS0"])

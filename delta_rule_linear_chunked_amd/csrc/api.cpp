@@ -296,8 +296,8 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
   bool vec = false;
   int st = prefill_checks(dims, variant, erase, write, cu_seqlens, &vec);
   if (st) return st;
-  if (variant == DR_PRODUCT2) return fail(DR_ERR_VARIANT, "the backward pass has no PRODUCT2 form");
   const bool has_write = variant == DR_RDA || variant == DR_GDN2;
+  const int lg = variant == DR_PRODUCT2 ? 1 : 0;  // two transitions per token: 2T steps
   if (!has_write && dwrite != nullptr)
     return fail(DR_ERR_VARIANT, "KDA / CKDA take no dwrite (beta's whole gradient goes to derase)");
   const int64_t tokens = dims->batch * dims->seqlen;
@@ -314,26 +314,28 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
   const int dkh = (int)dims->head_dim_k, dvh = (int)dims->head_dim_v;
   const int64_t H = dims->num_heads, pairs = dims->num_seqs * H;
 
-  // forward pass for the checkpoints: the state after every 64 tokens, no output
+  // forward pass for the checkpoints: the state after every 64 steps, no output
   dr::Params p{};
   p.q = q; p.k = k; p.v = v; p.alpha = alpha;
   p.erase = erase;
   p.write = has_write ? write : erase;
   p.S0 = S0; p.cu = cu_seqlens; p.o = nullptr; p.S = nullptr;
-  p.T = dims->seqlen;
+  p.lgnh = lg;
+  p.T = dims->seqlen << lg;
   p.H = (int32_t)H;
   p.DV = (int32_t)dvh;
-  const dr::PrefillPlan pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen, H, dkh, dvh,
+  const dr::PrefillPlan pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen << lg, H, dkh, dvh,
                                               cu_seqlens != nullptr);
   p.num_pairs = (int32_t)pairs;
   p.ndvb = pl.ndvb;
   p.grid_logical = (int32_t)(pairs * pl.ndvb);
   p.nseq = (int32_t)dims->num_seqs;
   p.snap_chunks = 1;
-  // at most floor(tokens / 64) checkpoints in all (sum of floor(len_n / 64) over the sequences)
-  const int64_t nsnap = cu_seqlens ? tokens / 64 : dims->batch * (dims->seqlen / 64);
+  // at most floor(steps / 64) checkpoints in all (sum of floor(len_n / 64) over the sequences)
+  const int64_t steps = tokens << lg;
+  const int64_t nsnap = cu_seqlens ? steps / 64 : dims->batch * ((dims->seqlen << lg) / 64);
   const int ndvb = dvh / dr::bwd_dv_block(dvh);
-  const int64_t TH = tokens * H;
+  const int64_t TH = steps * H;
   const int64_t off_snap = round256(pl.workspace);
   const int64_t off_part = off_snap + round256(nsnap * H * dkh * dvh * 4);
   const int64_t off_parts = off_part + round256((int64_t)ndvb * TH * 4 * dkh * 4);
@@ -358,8 +360,9 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
     b.snap_first = cu_seqlens ? dr::prefill_snap_first(ws, pl, H, dims->num_seqs) : nullptr;
     b.part = reinterpret_cast<float*>(wsb + off_part);
     b.parts = reinterpret_cast<float*>(wsb + off_parts);
-    b.T = dims->seqlen;
+    b.T = dims->seqlen << lg;
     b.TH = TH;
+    b.lgnh = lg;
     b.H = (int32_t)H;
     b.DV = dvh;
     b.nseq = (int32_t)dims->num_seqs;

@@ -133,9 +133,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
   const int H = p.H, DV = p.DV;
   const int n = pair / H, h = pair % H;
   int64_t bos, len, snap_base;
-  if (p.cu) {
-    bos = p.cu[n];
-    len = (int64_t)p.cu[n + 1] - bos;
+  if (p.cu) {  // (offsets in steps)
+    bos = (int64_t)p.cu[n] << p.lgnh;
+    len = ((int64_t)p.cu[n + 1] << p.lgnh) - bos;
     snap_base = p.snap_first[n];
   } else {
     bos = (int64_t)n * p.T;
@@ -161,8 +161,15 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
     for (int i = 0; i < RPL; ++i) dS[cc][i] = p.dST ? p.dST[state_off + (int64_t)(row0 + i) * DV + cc] : 0.f;
   }
 
-  // inputs of tokens t0 .. t0+7 of the sequence (past the end: zeros), as the rules use them;
-  // loaded into registers one staged block ahead of use, then committed to LDS
+  // inputs of steps t0 .. t0+7 of the sequence (past the end: zeros), as the rules use them;
+  // loaded into registers one staged block ahead of use, then committed to LDS. With two
+  // steps per token, q, alpha and dO come from the token's row: the decay only on its first
+  // step (1 on the second), the output gradient only after its last.
+  const int lastm = (1 << p.lgnh) - 1;
+  auto rows = [&](int64_t m, int64_t& tq, int64_t& tk) {  // absolute step -> token / step rows
+    tq = (m >> p.lgnh) * H + h;
+    tk = (tq << p.lgnh) + (m & lastm);
+  };
   constexpr int SK = (BW_SB * DK + 255) / 256, SV = (BW_SB * DVB + 255) / 256;
   struct Stg {
     float k[SK], u[SK], q[SK], a[SK];
@@ -178,10 +185,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
       const int e = e0 < BW_SB * DK ? e0 : 0;
       const int j = e / DK, i = e % DK;
       const int64_t t = t0 + j < len ? t0 + j : len - 1;
-      const int64_t th = (bos + t) * H + h;
-      const float kk = ld_f32(kp + th * DK + i), qq = ld_f32(qp + th * DK + i), aa = p.alpha[th * DK + i];
-      const float ug = VEC ? p.erase[th * DK + i] : p.erase[th];
-      r.k[x] = in ? kk : 0.f; r.u[x] = in ? ug * kk : 0.f; r.q[x] = in ? qq : 0.f; r.a[x] = in ? aa : 0.f;
+      int64_t tq, tk;
+      rows(bos + t, tq, tk);
+      const float kk = ld_f32(kp + tk * DK + i), qq = ld_f32(qp + tq * DK + i), aa = p.alpha[tq * DK + i];
+      const float ug = VEC ? p.erase[tk * DK + i] : p.erase[tk];
+      const bool first = ((bos + t) & lastm) == 0;
+      r.k[x] = in ? kk : 0.f; r.u[x] = in ? ug * kk : 0.f; r.q[x] = in ? qq : 0.f;
+      r.a[x] = in ? (first ? aa : 1.f) : 0.f;
     }
 #pragma unroll
     for (int x = 0; x < SV; ++x) {
@@ -190,11 +200,13 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
       const int e = e0 < BW_SB * DVB ? e0 : 0;
       const int j = e / DVB, cc = e % DVB;
       const int64_t t = t0 + j < len ? t0 + j : len - 1;
-      const int64_t th = (bos + t) * H + h;
-      const float vv = ld_f32(vp + th * DV + dv0 + cc);
-      const float gg = VEC ? p.write[th * DV + dv0 + cc] : p.write[th];
-      const float dd = p.dO[th * DV + dv0 + cc];
-      r.m[x] = in ? gg * vv : 0.f; r.dO[x] = in ? dd : 0.f; r.v[x] = in ? vv : 0.f; r.g[x] = in ? gg : 0.f;
+      int64_t tq, tk;
+      rows(bos + t, tq, tk);
+      const float vv = ld_f32(vp + tk * DV + dv0 + cc);
+      const float gg = VEC ? p.write[tk * DV + dv0 + cc] : p.write[tk];
+      const float dd = p.dO[tq * DV + dv0 + cc];
+      const bool last = ((bos + t) & lastm) == lastm;
+      r.m[x] = in ? gg * vv : 0.f; r.dO[x] = in && last ? dd : 0.f; r.v[x] = in ? vv : 0.f; r.g[x] = in ? gg : 0.f;
     }
   };
   auto commit_stg = [&](const Stg& r) {
@@ -363,12 +375,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
             }
             vdm = fmaf(vv[cc], ddelta[cc], vdm);
           }
-          const int64_t th = (bos + c0 + BW_SB * sb + j) * H + h;
+          const int64_t th = (bos + c0 + BW_SB * sb + j) * H + h;  // step-major row of the partial sums
           if (rg == 0) {
+            int64_t tq, tk;
+            rows(bos + c0 + BW_SB * sb + j, tq, tk);
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
-              p.dv[th * DV + dv0 + col0 + cc] = gg[cc] * ddelta[cc];  // m = g . v
-              if constexpr (VEC) p.dwrite[th * DV + dv0 + col0 + cc] = vv[cc] * ddelta[cc];
+              p.dv[tk * DV + dv0 + col0 + cc] = gg[cc] * ddelta[cc];  // m = g . v
+              if constexpr (VEC) p.dwrite[tk * DV + dv0 + col0 + cc] = vv[cc] * ddelta[cc];
             }
           }
           // sums over the wave's column groups (lane bit 32, and 16 when a group is 16 lanes)
@@ -417,11 +431,17 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
 // Adds the column blocks' row sums and applies the erase / write chain rule:
 // u = beta k (KDA, CKDA) or e k (RDA): dk += u-gate * du, d(gate) = k . du (+ v . dm for beta);
 // u = b . k (GDN-2): dk += b . du, db = k . du. One wave per token-head.
+// With two steps per token (the partial sums are per step), dq comes from a token's last step
+// and dalpha from its first.
 template <int DK, typename InT, bool VEC>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdParams p) {
-  const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // step-major row
   const int lw = threadIdx.x & 63;
   if (th >= p.TH) return;
+  const int lastm = (1 << p.lgnh) - 1;
+  const int64_t m = th / p.H, hh = th - m * p.H;
+  const int64_t tq = (m >> p.lgnh) * p.H + hh, tk = (tq << p.lgnh) + (m & lastm);
+  const bool first = (m & lastm) == 0, last = (m & lastm) == lastm;
   const InT* kp = static_cast<const InT*>(p.k);
   float kdu = 0.f;
   for (int i = lw; i < DK; i += 64) {
@@ -430,12 +450,12 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdParams p) {
 #pragma unroll
       for (int qn = 0; qn < 4; ++qn) s[qn] += p.part[(((int64_t)b * p.TH + th) * 4 + qn) * DK + i];
     }
-    const float kk = ld_f32(kp + th * DK + i);
-    const float ug = VEC ? p.erase[th * DK + i] : p.erase[th];
-    p.dq[th * DK + i] = s[0];
-    p.dk[th * DK + i] = fmaf(ug, s[2], s[1]);
-    p.dalpha[th * DK + i] = s[3];
-    if constexpr (VEC) p.derase[th * DK + i] = kk * s[2];
+    const float kk = ld_f32(kp + tk * DK + i);
+    const float ug = VEC ? p.erase[tk * DK + i] : p.erase[tk];
+    if (last) p.dq[tq * DK + i] = s[0];
+    p.dk[tk * DK + i] = fmaf(ug, s[2], s[1]);
+    if (first) p.dalpha[tq * DK + i] = s[3];
+    if constexpr (VEC) p.derase[tk * DK + i] = kk * s[2];
     kdu = fmaf(kk, s[2], kdu);
   }
   if constexpr (!VEC) {
@@ -445,10 +465,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdParams p) {
       float vdm = 0.f;
       for (int b = 0; b < p.ndvb; ++b) vdm += p.parts[(int64_t)b * p.TH + th];
       if (p.variant == 1) {  // RDA: e k and w v are separate gates
-        p.derase[th] = kdu;
-        p.dwrite[th] = vdm;
-      } else {               // KDA / CKDA: beta is both
-        p.derase[th] = kdu + vdm;
+        p.derase[tk] = kdu;
+        p.dwrite[tk] = vdm;
+      } else {               // KDA / CKDA / two transitions: beta is both
+        p.derase[tk] = kdu + vdm;
       }
     }
   }

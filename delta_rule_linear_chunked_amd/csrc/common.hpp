@@ -98,7 +98,9 @@ struct BwdParams {
   int32_t DV;
   int32_t ndvb;
   int32_t nseq;
-  int32_t variant;      // 0 KDA, 1 RDA, 2 GDN-2, 3 CKDA
+  int32_t variant;      // 0 KDA, 1 RDA, 2 GDN-2, 3 CKDA, 4 two KDA transitions per token
+  int32_t lgnh;         // transitions per token, as a power of two (see Params); T, TH and the
+                        // partial sums count steps
 };
 
 __device__ __forceinline__ float ld_f32(const float* p) { return *p; }

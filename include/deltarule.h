@@ -27,8 +27,8 @@
  * (the composition of two delta-rule transitions per update that the Complex KDA
  * abstract cites as prior work, DeltaProduct with two factors). Its k is
  * [.., H, 2, d_k], v [.., H, 2, d_v] and beta (erase) [.., H, 2]; q and alpha keep
- * one row per token and write is NULL. It has a prefill and a decode step but no
- * backward pass (DR_ERR_VARIANT), and its snapshot_every must be a multiple of 32.
+ * one row per token and write is NULL; its gradients (dr_chunk_bwd) take the same
+ * layouts, and its snapshot_every must be a multiple of 32.
  *
  * The state S has d_k rows (key channels) and d_v columns; Diag(alpha_t) scales
  * its rows. The readout uses the updated state and no 1/sqrt(d_k) factor.
@@ -240,6 +240,7 @@ int dr_decode_step_ex(const void* q, const void* k, const void* v, const void* a
  *   dv            [B, T, H, d_v]
  *   dalpha        [B, T, H, d_k]
  *   derase        shape of erase: KDA / CKDA d(beta) (both of beta's uses), RDA d(e), GDN-2 d(b)
+ *                 (DR_PRODUCT2: dk [B, T, H, 2, d_k], dv [B, T, H, 2, d_v], derase [B, T, H, 2])
  *   dwrite        RDA d(w) [B, T, H], GDN-2 d(w) [B, T, H, d_v]; must be NULL for KDA / CKDA
  *   dS0           [N, H, d_k, d_v], or NULL when not wanted
  * The inputs are those of the forward call (plain inputs: the fused preparation and the

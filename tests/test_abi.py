@@ -146,9 +146,9 @@ def test_two_transition_variant_options(lib):
                              ctypes.byref(dims()), ctypes.byref(o), None)
     assert st == -2, lib.dr_last_error()
     assert "multiple of 32" in lib.dr_last_error().decode()
-    # no backward pass for it
+    # its beta is one gate for both uses: no separate write gradient
     st = lib.dr_chunk_bwd(FAKE, FAKE, FAKE, FAKE, FAKE, None, 4, None, None, FAKE, None,
-                          FAKE, FAKE, FAKE, FAKE, FAKE, None, None, ctypes.byref(dims()), None)
+                          FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, ctypes.byref(dims()), None)
     assert st == -6, lib.dr_last_error()
 
 

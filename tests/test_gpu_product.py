@@ -1,7 +1,8 @@
 """GPU parity of the two-transitions-per-token variant ("product2": KDA's rule twice per
 token, the decay once) against the fp64 oracle ``oracle.product``: prefill (fixed length,
 ragged, packed, snapshots, state pools, fused input preparation, the full KDA prefill
-shape on sampled pairs) and decode (every head size, pools, fused preparation).
+shape on sampled pairs), decode (every head size, pools, fused preparation) and the
+gradients (dr_chunk_bwd) against ``oracle.product.product_grads``.
 Tolerance max |err| / RMS(ref): 1e-4 for fp32 inputs, 1e-2 for bf16 inputs."""
 import numpy as np
 import pytest
@@ -159,3 +160,51 @@ def test_decode_state_pool_and_preparation():
         o_np = _np(o)
         _check(f"decode pool step {t}", [(o_np[live], o_ref), (_np(S), ref)], 1e-4)
         assert np.all(o_np[~live] == 0.0)
+
+
+def _grads(wl, rng):
+    a = _dev(wl)
+    dO = rng.standard_normal(wl.q.shape[:3] + (wl.v.shape[-1],)).astype(np.float32)
+    N = wl.num_seqs
+    dS = rng.standard_normal((N,) + wl.S0.shape[1:]).astype(np.float32)
+    g = drl.chunk_bwd(a["q"], a["k"], a["v"], a["alpha"], a["erase"], None, "product2", a["S0"], a["cu_seqlens"],
+                      dO=to_dev(dO), dS_T=to_dev(dS))
+    torch.cuda.synchronize()
+    g = {k: (None if v is None else _np(v)) for k, v in g.items()}
+    return g, dO, dS
+
+
+NAMES = (("dq", "dq"), ("dk", "dk"), ("dv", "dv"), ("dalpha", "dalpha"), ("derase", "dbeta"), ("dS0", "dS0"))
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("recipe", ["kda", "ckda"])
+@pytest.mark.parametrize("dk,dv", [(16, 16), (64, 32), (128, 128)])
+def test_backward(recipe, dk, dv, in_dtype):
+    wl = synth.make_product(recipe, 2, 75, 2, dk, dv, in_dtype=in_dtype, seed=seed_of("p2 bwd", recipe, dk, dv, in_dtype))
+    g, dO, dS = _grads(wl, np.random.default_rng(seed_of("p2 bwd do", dk, dv)))
+    ref = product.product_grads(wl.q, wl.k, wl.v, wl.alpha, wl.erase, dO, dS_T=dS, S0=wl.S0)
+    assert g["dwrite"] is None
+    _check(f"backward {recipe} d{dk}x{dv} {in_dtype}", [(g[a], ref[b]) for a, b in NAMES], TOL[in_dtype])
+
+
+def test_backward_packed():
+    lens = [40, 0, 1, 33, 70]
+    wl = synth.make_product("ckda", 1, 0, 2, 64, 64, in_dtype="f32", seed=seed_of("p2 bwd packed"), lengths=lens)
+    g, dO, dS = _grads(wl, np.random.default_rng(4))
+    ref = product.product_grads(wl.q, wl.k, wl.v, wl.alpha, wl.erase, dO, dS_T=dS, S0=wl.S0,
+                                cu_seqlens=wl.cu_seqlens)
+    _check("backward packed", [(g[a], ref[b]) for a, b in NAMES], TOL["f32"])
+    np.testing.assert_array_equal(g["dS0"][1], dS[1].astype(np.float64))  # empty sequence
+
+
+def test_backward_full_size_sampled_pair():
+    # the KDA prefill shape with two transitions per token; the oracle runs one (sequence, head)
+    wl = synth.preset("product2_prefill")
+    g, dO, dS = _grads(wl, np.random.default_rng(1006))
+    n, h = 2, 7
+    sl = (slice(n, n + 1), slice(None), slice(h, h + 1))
+    ref = product.product_grads(wl.q[sl], wl.k[sl], wl.v[sl], wl.alpha[sl], wl.erase[sl], dO[sl],
+                                dS_T=dS[n:n + 1, h:h + 1], S0=wl.S0[n:n + 1, h:h + 1])
+    pairs = [(g[a][sl], ref[b]) for a, b in NAMES if a != "dS0"] + [(g["dS0"][n, h], ref["dS0"][0, 0])]
+    _check("backward full size", pairs, TOL["bf16"])
