@@ -116,6 +116,8 @@ def main():
     ap.add_argument("--no-states", action="store_true", help="skip the snapshot and slot-pool timings")
     ap.add_argument("--no-prep", action="store_true", help="skip the fused input preparation timing")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward (gradient) timing")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the timings of the varlen (RDA, GDN-2) and long-context (CKDA) prefill workloads")
     ap.add_argument("--no-product", action="store_true",
                     help="skip the two-transitions-per-token variant's prefill and decode timings")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -328,6 +330,42 @@ def main():
             del gdO, g2
         del p2
 
+    # the other prefill workloads (checked for parity elsewhere), timed for context
+    others = None
+    if not args.no_configs:
+        others = {}
+        for name, gate_bytes in (("rda_varlen", 8), ("gdn2_varlen", 4 * (D + D)), ("ckda_long", 4)):
+            wl = synth.preset(name)
+            a = dict(q=t(wl.q, True), k=t(wl.k, True), v=t(wl.v, True), alpha=t(wl.alpha), erase=t(wl.erase),
+                     write=t(wl.write), S0=t(wl.S0), cu=None if wl.cu_seqlens is None else t(wl.cu_seqlens))
+            Bw, Tw = wl.q.shape[0], wl.q.shape[1]
+            N = wl.num_seqs
+            ow = torch.empty((Bw, Tw, H, D), dtype=torch.float32, device=dev)
+            Sw = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+            variant = wl.variant
+            del wl
+
+            def ostep():
+                drl.dr_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["erase"], a["write"], variant, a["S0"], a["cu"],
+                                 ow, Sw)
+
+            for i in range(3):
+                ostep()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(10):
+                ostep()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            oms = e0.elapsed_time(e1) / 10
+            ob, _ = prefill_work(Bw, Tw, H, D, D, gate_bytes=gate_bytes, n_states=N)
+            others[name] = {"ms_per_step": oms, "tokens_per_s": Bw * Tw / (oms * 1e-3), "sequences": N,
+                            "tokens": Bw * Tw, "alg_bytes_per_launch": ob,
+                            "achieved_GBps": ob / (oms * 1e-3) / 1e9,
+                            "hbm_frac": ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            del a, ow, Sw
+
     traffic, kernel_traffic = None, None
     tfile = os.path.join(ROOT, "profiles", "chunk_fwd_kda_B4_T4096_H16_d128_traffic.json")
     if os.path.exists(tfile):
@@ -354,7 +392,9 @@ def main():
             s = toks[i % pool]
             drl.dr_decode_step(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "kda", S, od)
 
-        for i in range(10):
+        # warm-up: about 40 ms of decode steps (the first steps after the prefill legs run slower
+        # while the clocks settle)
+        for i in range(100):
             dstep(i)
         torch.cuda.synchronize()
         # mean over back-to-back steps with events only at the ends of the loop (an event between
@@ -396,6 +436,33 @@ def main():
             pms = e0.elapsed_time(e1) / args.decode_steps
             pooled = {"us_per_step": pms * 1e3, "state_GBps": dbytes / (pms * 1e-3) / 1e9,
                       "slots": N, "order": "random permutation"}
+        dvariants = None
+        if not args.no_configs:
+            # the other variants' decode steps on the same shape and state
+            dvariants = {}
+            for vname in ("rda", "gdn2", "ckda"):
+                wv = synth.preset(f"decode_{vname}", steps=4)
+                vt = [dict(q=t(wv.q[i], True), k=t(wv.k[i], True), v=t(wv.v[i], True), alpha=t(wv.alpha[i]),
+                           erase=t(wv.erase[i]), write=None if wv.write is None else t(wv.write[i])) for i in range(4)]
+                del wv
+
+                def vstep(i):
+                    s_ = vt[i % 4]
+                    drl.dr_decode_step(s_["q"], s_["k"], s_["v"], s_["alpha"], s_["erase"], s_["write"], vname, S, od)
+
+                for i in range(10):
+                    vstep(i)
+                torch.cuda.synchronize()
+                e0.record(stream)
+                for i in range(args.decode_steps):
+                    vstep(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                vus = e0.elapsed_time(e1) / args.decode_steps * 1e3
+                vbytes = decode_bytes(N, HD, D, D, gate_bytes=(8 if vname == "rda" else 4 * (D + D) if vname == "gdn2" else 4))
+                dvariants[vname] = {"us_per_step": vus, "state_GBps": vbytes / (vus * 1e-6) / 1e9,
+                                    "hbm_frac": vbytes / (vus * 1e-6) / 1e9 / HBM_PEAK_GBS}
+                del vt
         if prod is not None:
             # two transitions per token: the same state traffic, three column reductions
             wp = synth.make_product_decode("kda", N, HD, D, D, steps=4, in_dtype="bf16", seed=1006)
@@ -432,6 +499,7 @@ def main():
             "hbm_frac": dbytes / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "bytes_per_step": dbytes, "steps": args.decode_steps,
             "slot_pool": pooled,
+            "other_variants": dvariants,
         }
 
     copy = copy_calibration(dev, mib=256, reps=3)
@@ -460,6 +528,7 @@ def main():
         "fused_prep": fused,
         "backward": bwd,
         "product2": prod,
+        "other_workloads": others,
         "measured_copy_GBps": copy["copy_GBps"],
         "run": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count, "torch": torch.__version__,
