@@ -145,6 +145,8 @@ static int prefill_checks(const dr_dims* dims, int variant, const float* erase, 
                           const int32_t* cu_seqlens, bool* vec) {
   int st = check_dims_common(dims);
   if (st) return st;
+  if (variant == DR_PRODUCT2 && dims->batch * dims->seqlen >= ((int64_t)1 << 30))
+    return fail(DR_ERR_SHAPE, "problem too large: two transitions per token need 2 * tokens < 2^31 steps");
   st = check_variant(variant, erase, write, dims->batch * dims->seqlen > 0, vec);
   if (st) return st;
   if (cu_seqlens != nullptr) {
