@@ -69,7 +69,26 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
   }
   float* S = p.S + srow * (int64_t)DK * DV + col0;
 
-  // Issue the state loads first: they do not depend on the token's vectors.
+  // The token's vectors first (one element per thread; they are small and the staging below
+  // needs them), then the state: memory returns in issue order, so the staging does not wait
+  // for the state to arrive.
+  const InT* q = static_cast<const InT*>(p.q) + nh * DK;
+  const InT* k = static_cast<const InT*>(p.k) + nh * DK;
+  const InT* v = static_cast<const InT*>(p.v) + nh * DV + col0;
+  static_assert(DK <= NT && DVS <= NT, "one token element per thread");
+  const bool prep = p.a_act || p.g_act || p.a_bf16;  // fused activations (uniform)
+  float qi = 0.f, ki = 0.f, az = 0.f, e = 0.f, vj = 0.f, wr = 0.f;
+  if (tid < DK) {
+    qi = ld_f32(q + tid);
+    ki = ld_f32(k + tid);
+    az = p.a_bf16 ? (float)static_cast<const __bf16*>(p.alpha)[nh * DK + tid]
+                  : static_cast<const float*>(p.alpha)[nh * DK + tid];
+    e = VEC ? p.erase[nh * DK + tid] : p.erase[nh];
+  }
+  if (tid < DVS) {
+    vj = ld_f32(v + tid);
+    wr = VEC ? p.write[nh * DV + col0 + tid] : p.write[nh];
+  }
   f32x4 st[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -77,56 +96,45 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
     st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + row * DV) + c4);
   }
 
-  // Stage the token's vectors.
-  const InT* q = static_cast<const InT*>(p.q) + nh * DK;
-  const InT* k = static_cast<const InT*>(p.k) + nh * DK;
-  const InT* v = static_cast<const InT*>(p.v) + nh * DV + col0;
   // inverse L2 norms of q and k over d_k (1 when the inputs come normalised)
   float nq = 1.f, nk = 1.f;
   if (p.prep_l2) {
-    if (tid < 64) {
-      float sq = 0.f, sk = 0.f;
-      for (int i = tid; i < DK; i += 64) {
-        const float qi = ld_f32(q + i), ki = ld_f32(k + i);
-        sq = fmaf(qi, qi, sq);
-        sk = fmaf(ki, ki, sk);
-      }
+    float sq = qi * qi, sk = ki * ki;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        sq += __shfl_xor(sq, o);
-        sk += __shfl_xor(sk, o);
+    for (int o = 32; o > 0; o >>= 1) {
+      sq += __shfl_xor(sq, o);
+      sk += __shfl_xor(sk, o);
+    }
+    if ((tid & 63) == 0 && tid < DK) {
+      s_red[0][0][tid >> 6] = sq;
+      s_red[1][0][tid >> 6] = sk;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float tq = 0.f, tk = 0.f;
+      for (int wv = 0; wv < (DK + 63) / 64; ++wv) {
+        tq += s_red[0][0][wv];
+        tk += s_red[1][0][wv];
       }
-      if (tid == 0) {
-        s_norm[0] = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
-        s_norm[1] = sk > 0.f ? __builtin_amdgcn_rsqf(sk) : 0.f;
-      }
+      s_norm[0] = tq > 0.f ? __builtin_amdgcn_rsqf(tq) : 0.f;
+      s_norm[1] = tk > 0.f ? __builtin_amdgcn_rsqf(tk) : 0.f;
     }
     __syncthreads();
     nq = s_norm[0];
     nk = s_norm[1];
   }
-  const bool prep = p.a_act || p.g_act || p.a_bf16;  // fused activations (uniform)
-  for (int i = tid; i < DK; i += NT) {
-    float a, ui;
-    const float qi = ld_f32(q + i) * nq, ki = ld_f32(k + i) * nk;
-    const float e = VEC ? p.erase[nh * DK + i] : p.erase[nh];
-    if (prep) {
-      a = load_alpha1(p, nh * DK + i);
-      ui = prep_gate(e, p) * ki;
-    } else {
-      a = static_cast<const float*>(p.alpha)[nh * DK + i];
-      ui = e * ki;
-    }
-    s_q[i] = qi;
-    s_k[i] = ki;
-    s_a[i] = a;
-    s_au[i] = a * ui;
-    s_aq[i] = a * qi;
+  if (tid < DK) {
+    const float a = prep ? prep_alpha(az, p) : az;
+    const float ug = prep ? prep_gate(e, p) : e;
+    qi *= nq;
+    ki *= nk;
+    s_q[tid] = qi;
+    s_k[tid] = ki;
+    s_a[tid] = a;
+    s_au[tid] = a * (ug * ki);
+    s_aq[tid] = a * qi;
   }
-  for (int j = tid; j < DVS; j += NT) {
-    const float wr = VEC ? p.write[nh * DV + col0 + j] : p.write[nh];
-    s_m[j] = (prep ? prep_gate(wr, p) : wr) * ld_f32(v + j);
-  }
+  if (tid < DVS) s_m[tid] = (prep ? prep_gate(wr, p) : wr) * vj;
   __syncthreads();
 
   // Partial reductions over this thread's rows.
@@ -253,6 +261,27 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode2_kernel(cons
   }
   float* S = p.S + srow * (int64_t)DK * DV + col0;
 
+  // token vectors first, then the state (see decode_kernel)
+  const InT* q = static_cast<const InT*>(p.q) + nh * DK;
+  const InT* k1 = static_cast<const InT*>(p.k) + (2 * nh) * DK;
+  const InT* k2 = k1 + DK;
+  const InT* v1 = static_cast<const InT*>(p.v) + (2 * nh) * DV + col0;
+  const InT* v2 = v1 + DV;
+  static_assert(DK <= NT && DVS <= NT, "one token element per thread");
+  const bool prep = p.a_act || p.g_act || p.a_bf16;  // fused activations (uniform)
+  float qi = 0.f, ai = 0.f, bi = 0.f, az = 0.f, w1 = 0.f, w2 = 0.f;
+  float b1 = p.erase[2 * nh], b2 = p.erase[2 * nh + 1];
+  if (tid < DK) {
+    qi = ld_f32(q + tid);
+    ai = ld_f32(k1 + tid);
+    bi = ld_f32(k2 + tid);
+    az = p.a_bf16 ? (float)static_cast<const __bf16*>(p.alpha)[nh * DK + tid]
+                  : static_cast<const float*>(p.alpha)[nh * DK + tid];
+  }
+  if (tid < DVS) {
+    w1 = ld_f32(v1 + tid);
+    w2 = ld_f32(v2 + tid);
+  }
   f32x4 st[RPT];
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
@@ -260,58 +289,57 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode2_kernel(cons
     st[i] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(S + row * DV) + c4);
   }
 
-  const InT* q = static_cast<const InT*>(p.q) + nh * DK;
-  const InT* k1 = static_cast<const InT*>(p.k) + (2 * nh) * DK;
-  const InT* k2 = k1 + DK;
-  const InT* v1 = static_cast<const InT*>(p.v) + (2 * nh) * DV + col0;
-  const InT* v2 = v1 + DV;
   float nq = 1.f, nk1 = 1.f, nk2 = 1.f;
   if (p.prep_l2) {
-    if (tid < 64) {
-      float sq = 0.f, s1 = 0.f, s2 = 0.f;
-      for (int i = tid; i < DK; i += 64) {
-        const float qi = ld_f32(q + i), a = ld_f32(k1 + i), b = ld_f32(k2 + i);
-        sq = fmaf(qi, qi, sq);
-        s1 = fmaf(a, a, s1);
-        s2 = fmaf(b, b, s2);
-      }
+    float sq = qi * qi, s1 = ai * ai, s2 = bi * bi;
 #pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        sq += __shfl_xor(sq, o);
-        s1 += __shfl_xor(s1, o);
-        s2 += __shfl_xor(s2, o);
+    for (int o = 32; o > 0; o >>= 1) {
+      sq += __shfl_xor(sq, o);
+      s1 += __shfl_xor(s1, o);
+      s2 += __shfl_xor(s2, o);
+    }
+    if ((tid & 63) == 0 && tid < DK) {
+      s_red[0][0][tid >> 6] = sq;
+      s_red[1][0][tid >> 6] = s1;
+      s_red[2][0][tid >> 6] = s2;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      float tq = 0.f, t1 = 0.f, t2 = 0.f;
+      for (int wv = 0; wv < (DK + 63) / 64; ++wv) {
+        tq += s_red[0][0][wv];
+        t1 += s_red[1][0][wv];
+        t2 += s_red[2][0][wv];
       }
-      if (tid == 0) {
-        s_norm[0] = sq > 0.f ? __builtin_amdgcn_rsqf(sq) : 0.f;
-        s_norm[1] = s1 > 0.f ? __builtin_amdgcn_rsqf(s1) : 0.f;
-        s_norm[2] = s2 > 0.f ? __builtin_amdgcn_rsqf(s2) : 0.f;
-      }
+      s_norm[0] = tq > 0.f ? __builtin_amdgcn_rsqf(tq) : 0.f;
+      s_norm[1] = t1 > 0.f ? __builtin_amdgcn_rsqf(t1) : 0.f;
+      s_norm[2] = t2 > 0.f ? __builtin_amdgcn_rsqf(t2) : 0.f;
     }
     __syncthreads();
     nq = s_norm[0];
     nk1 = s_norm[1];
     nk2 = s_norm[2];
   }
-  const bool prep = p.a_act || p.g_act || p.a_bf16;  // fused activations (uniform)
-  float b1 = p.erase[2 * nh], b2 = p.erase[2 * nh + 1];
   if (prep) {
     b1 = prep_gate(b1, p);
     b2 = prep_gate(b2, p);
   }
-  for (int i = tid; i < DK; i += NT) {
-    const float qi = ld_f32(q + i) * nq, ai = ld_f32(k1 + i) * nk1, bi = ld_f32(k2 + i) * nk2;
-    const float a = prep ? load_alpha1(p, nh * DK + i) : static_cast<const float*>(p.alpha)[nh * DK + i];
-    s_q[i] = qi;
-    s_k1[i] = ai;
-    s_k2[i] = bi;
-    s_a[i] = a;
-    s_au1[i] = a * (b1 * ai);
-    s_au2[i] = a * (b2 * bi);
-    s_aq[i] = a * qi;
+  if (tid < DK) {
+    const float a = prep ? prep_alpha(az, p) : az;
+    qi *= nq;
+    ai *= nk1;
+    bi *= nk2;
+    s_q[tid] = qi;
+    s_k1[tid] = ai;
+    s_k2[tid] = bi;
+    s_a[tid] = a;
+    s_au1[tid] = a * (b1 * ai);
+    s_au2[tid] = a * (b2 * bi);
+    s_aq[tid] = a * qi;
   }
-  for (int j = tid; j < DVS; j += NT) {
-    s_m1[j] = b1 * ld_f32(v1 + j);
-    s_m2[j] = b2 * ld_f32(v2 + j);
+  if (tid < DVS) {
+    s_m1[tid] = b1 * w1;
+    s_m2[tid] = b2 * w2;
   }
   __syncthreads();
 
