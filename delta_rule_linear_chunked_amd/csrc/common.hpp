@@ -142,22 +142,6 @@ __device__ __forceinline__ float prep_gate(float z, const Params& p) {
   return p.g_act == 1 ? sg : z;
 }
 
-// Eight raw input elements kept in their storage type (prefetch registers).
-template <typename InT> struct Raw8;
-template <> struct Raw8<__bf16> {
-  bf16x8 v;
-  __device__ __forceinline__ void load(const __bf16* p) { v = *reinterpret_cast<const bf16x8*>(p); }
-  __device__ __forceinline__ float get(int j) const { return (float)v[j]; }
-};
-template <> struct Raw8<float> {
-  f32x4 a, b;
-  __device__ __forceinline__ void load(const float* p) {
-    a = *reinterpret_cast<const f32x4*>(p);
-    b = *reinterpret_cast<const f32x4*>(p + 4);
-  }
-  __device__ __forceinline__ float get(int j) const { return j < 4 ? a[j] : b[j - 4]; }
-};
-
 __device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
   const bf16x8 a = *reinterpret_cast<const bf16x8*>(p);
 #pragma unroll
