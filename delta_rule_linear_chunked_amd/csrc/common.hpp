@@ -148,18 +148,6 @@ __device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
   for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
 }
 
-// Eight decay values starting at element `i` of alpha, in its storage type, activated.
-__device__ __forceinline__ void load_alpha8(const Params& p, int64_t i, float (&a)[8]) {
-  if (p.a_bf16) load8(static_cast<const __bf16*>(p.alpha) + i, a);
-  else load8(static_cast<const float*>(p.alpha) + i, a);
-#pragma unroll
-  for (int j = 0; j < 8; ++j) a[j] = prep_alpha(a[j], p);
-}
-__device__ __forceinline__ float load_alpha1(const Params& p, int64_t i) {
-  const float z = p.a_bf16 ? (float)static_cast<const __bf16*>(p.alpha)[i] : static_cast<const float*>(p.alpha)[i];
-  return prep_alpha(z, p);
-}
-
 // ---------------------------------------------------------------------------
 // MFMA 16x16 tiles with a 32-deep reduction per call.
 //
@@ -170,40 +158,19 @@ __device__ __forceinline__ float load_alpha1(const Params& p, int64_t i) {
 // the sum over all four lane groups and eight items covers the slice exactly
 // once.
 //
-// A 16-deep variant (mma16) takes four items per lane, reduction indices
-// 4*(l/16) + j: the same assignment as the accumulator's rows, so an
-// accumulator can be fed back as the B operand of the next product unchanged.
-//
 // PolF32: eight v_mfma_f32_16x16x4_f32, instruction j taking item j of every
-//         lane group (exact fp32 products); four for mma16.
+//         lane group (exact fp32 products).
 // PolBF3: operands split x = hi + lo (hi = bf16(x), lo = bf16(x - hi)) and
 //         hi*hi + hi*lo + lo*hi accumulated with v_mfma_f32_16x16x32_bf16;
 //         the dropped lo*lo term and the rounding of lo leave a relative error
-//         of about 2^-16 per product. mma16 uses v_mfma_f32_16x16x16_bf16.
+//         of about 2^-16 per product.
 // ---------------------------------------------------------------------------
 struct PolF32 {
   struct Frag { float v[8]; };
-  struct Frag4 { float v[4]; };
-  static __device__ __forceinline__ Frag4 make4(const float (&x)[4]) {
-    Frag4 f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f.v[j] = x[j];
-    return f;
-  }
-  static __device__ __forceinline__ void mma16(f32x4& acc, const Frag4& a, const Frag4& b) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
-  }
   static __device__ __forceinline__ Frag make(const float (&x)[8]) {
     Frag f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) f.v[j] = x[j];
-    return f;
-  }
-  static __device__ __forceinline__ Frag zero() {
-    Frag f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) f.v[j] = 0.f;
     return f;
   }
   static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
@@ -214,22 +181,6 @@ struct PolF32 {
 
 struct PolBF3 {
   struct Frag { bf16x8 hi, lo; };
-  struct Frag4 { bf16x4 hi, lo; };
-  static __device__ __forceinline__ Frag4 make4(const float (&x)[4]) {
-    Frag4 f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const __bf16 h = (__bf16)x[j];
-      f.hi[j] = h;
-      f.lo[j] = (__bf16)(x[j] - (float)h);
-    }
-    return f;
-  }
-  static __device__ __forceinline__ void mma16(f32x4& acc, const Frag4& a, const Frag4& b) {
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.lo, b.hi, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.lo, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a.hi, b.hi, acc, 0, 0, 0);
-  }
   static __device__ __forceinline__ Frag make(const float (&x)[8]) {
     Frag f;
 #pragma unroll
@@ -238,12 +189,6 @@ struct PolBF3 {
       f.hi[j] = h;
       f.lo[j] = (__bf16)(x[j] - (float)h);
     }
-    return f;
-  }
-  static __device__ __forceinline__ Frag zero() {
-    Frag f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) { f.hi[j] = (__bf16)0.f; f.lo[j] = (__bf16)0.f; }
     return f;
   }
   static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {
