@@ -192,3 +192,11 @@ def test_full_size_sampled_pairs(name):
     if wl.cu_seqlens is not None:   # always include the longest sequence
         pairs[0] = (int(np.argmax(np.diff(wl.cu_seqlens))), pairs[0][1])
     check(wl, "full-sampled", pairs=pairs)
+
+
+# ----------------------------------------------------------------- a very long single sequence
+def test_long_single_sequence():
+    # 131072 tokens in one sequence (2048 chunks on one serial chain, a 263 MB workspace per
+    # head) with Complex KDA gates, against the step recurrence
+    wl = synth.make_prefill("ckda", 1, 131072, 2, 64, 64, in_dtype="bf16", seed=seed_of("long"))
+    check(wl, "T=131072", pairs=[(0, 1)])
