@@ -137,6 +137,21 @@ __device__ __forceinline__ float prep_alpha(float z, const Params& p) {
   const float th = az < 0x1p-12f ? z : copysignf((1.f - e) * __builtin_amdgcn_rcpf(1.f + e), z);
   return p.a_act == 1 ? dec : p.a_act == 2 ? th : z;
 }
+// One decay activation fixed at compile time (ACT 1: exp(-c softplus(z)), 2: tanh(z), 0: z),
+// for kernels instantiated per activation.
+template <int ACT>
+__device__ __forceinline__ float prep_alpha_as(float z, float c) {
+  if constexpr (ACT == 1) {
+    const float t = __builtin_amdgcn_exp2f(z * LOG2E);
+    return __builtin_amdgcn_exp2f(-c * __builtin_amdgcn_logf(1.f + t));
+  } else if constexpr (ACT == 2) {
+    const float az = fabsf(z);
+    const float e = __builtin_amdgcn_exp2f(-2.f * LOG2E * az);
+    return az < 0x1p-12f ? z : copysignf((1.f - e) * __builtin_amdgcn_rcpf(1.f + e), z);
+  } else {
+    return z;
+  }
+}
 __device__ __forceinline__ float prep_gate(float z, const Params& p) {
   const float sg = p.g_scale * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z * LOG2E));
   return p.g_act == 1 ? sg : z;

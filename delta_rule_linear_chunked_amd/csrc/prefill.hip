@@ -200,19 +200,19 @@ struct PrepSmem {
 // Eight decay values at element `i` of alpha for alpha mode AM: 0 float32 as given,
 // 1 float32 pre-activations, 2 bfloat16 pre-activations (activated here); 3 and 4 return
 // the bfloat16 / float32 pre-activations themselves.
-template <int AM>
+template <int AM, int ACT = 0>
 __device__ __forceinline__ void load_alpha(const Params& p, int64_t i, float (&a)[8]) {
   if constexpr (AM == 2 || AM == 3) load8(static_cast<const __bf16*>(p.alpha) + i, a);
   else load8(static_cast<const float*>(p.alpha) + i, a);
   if constexpr (AM == 1 || AM == 2) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) a[j] = prep_alpha(a[j], p);
+    for (int j = 0; j < 8; ++j) a[j] = prep_alpha_as<ACT>(a[j], p.a_scale);
   }
 }
 
 // A block with a gate at or extremely near zero (rare): k . g from exact suffix products and
 // the diagonal tiles of A and P from running products of the gates, exact for any gate value.
-template <int DKR, int DK, typename InT, bool VEC, int AM>
+template <int DKR, int DK, typename InT, bool VEC, int AM, int ACT>
 __device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, int64_t thq, int64_t thk, bool unit_a,
                                          bool valid, float esc,
                                          float rq, float rk, int w, int r, int g) {
@@ -220,7 +220,7 @@ __device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, i
   const int row = 16 * w + r;
   const InT* qp = static_cast<const InT*>(p.q);
   const InT* kp = static_cast<const InT*>(p.k);
-  auto alpha8 = [&](int64_t i, float (&a)[8]) { load_alpha<AM>(p, i, a); };
+  auto alpha8 = [&](int64_t i, float (&a)[8]) { load_alpha<AM, ACT>(p, i, a); };
   auto gate = [&](float z) {
     if constexpr (AM != 0) return prep_gate(z, p);
     else return z;
@@ -253,7 +253,7 @@ __device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, i
       for (int j = 0; j < 8; ++j) {
         float a = 1.f;
         if (live && !unit_a) {
-          if constexpr (AM != 0) a = prep_alpha(a2[j], p);  // one element at a time
+          if constexpr (AM != 0) a = prep_alpha_as<ACT>(a2[j], p.a_scale);  // one element at a time
           else a = a2[j];
         }
         const float kk = live ? k2[j] * rk : 0.f;
@@ -275,7 +275,7 @@ __device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, i
     }
   }
 }
-template <int DKR, typename InT, bool VEC, int AM>
+template <int DKR, typename InT, bool VEC, int AM, int ACT>
 __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   const InT* qp = static_cast<const InT*>(p.q);
   const InT* kp = static_cast<const InT*>(p.k);
   // decay and gate loads, with the fused activations unless AM == 0
-  auto alpha8 = [&](int64_t i, float (&a)[8]) { load_alpha<AM>(p, i, a); };
+  auto alpha8 = [&](int64_t i, float (&a)[8]) { load_alpha<AM, ACT>(p, i, a); };
   auto gate = [&](float z) {
     if constexpr (AM != 0) return prep_gate(z, p);
     else return z;
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) av[ks][j] = unit_a ? 1.f : prep_alpha(av[ks][j], p);
+      for (int j = 0; j < 8; ++j) av[ks][j] = unit_a ? 1.f : prep_alpha_as<ACT>(av[ks][j], p.a_scale);
     }
   }
 
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       }
     } else {
       // Some gate of this block is zero or nearly so: exact block path (out of line).
-      exact_block<DKR, DK, InT, VEC, AM>(p, sm, thq, thk, unit_a, valid, esc, rq, rk, w, r, g);
+      exact_block<DKR, DK, InT, VEC, AM, ACT>(p, sm, thq, thk, unit_a, valid, esc, rq, rk, w, r, g);
     }
   }
   wave_lds_sync();
@@ -1004,12 +1004,22 @@ static hipError_t launch_t(const Params& p, const PrefillPlan& pl, hipStream_t s
   }
   if (pl.slots > 0) {
     const dim3 grid((unsigned)(pl.slots * p.H));
+    // the decay's storage type and activation are template arguments: each instance evaluates
+    // only its own activation
     if (!prep)
-      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 0>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 0, 0>), grid, dim3(256), 0, s, p);
+    else if (!p.a_bf16 && p.a_act == 1)
+      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 1, 1>), grid, dim3(256), 0, s, p);
+    else if (!p.a_bf16 && p.a_act == 2)
+      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 1, 2>), grid, dim3(256), 0, s, p);
     else if (!p.a_bf16)
-      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 1>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 1, 0>), grid, dim3(256), 0, s, p);
+    else if (p.a_act == 1)
+      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 2, 1>), grid, dim3(256), 0, s, p);
+    else if (p.a_act == 2)
+      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 2, 2>), grid, dim3(256), 0, s, p);
     else
-      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 2>), grid, dim3(256), 0, s, p);
+      hipLaunchKernelGGL((chunk_prep_kernel<DKR, InT, VEC, 2, 0>), grid, dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
