@@ -171,13 +171,19 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
     tk = (tq << p.lgnh) + (m & lastm);
   };
   constexpr int SK = (BW_SB * DK + 255) / 256, SV = (BW_SB * DVB + 255) / 256;
+  static_assert(SK <= 16 && SV <= 16, "flag bits");
+  // Raw values as loaded, and per element bit flags (bit x: element x is inside the sequence;
+  // bit 16 + x: alpha applies / the output gradient applies). Nothing reads the loaded values
+  // before the block is committed, so the loads stay in flight across the steps in between.
   struct Stg {
-    float k[SK], u[SK], q[SK], a[SK];
-    float m[SV], dO[SV], v[SV], g[SV];
+    InT k[SK], q[SK], v[SV];
+    float a[SK], ug[SK], g[SV], dO[SV];
+    unsigned fk, fv;
   };
-  // (branch-free: the loads are unconditional at clamped in-range indices and the result is
-  // selected, so nothing waits for them before the block is committed)
+  // (the loads are unconditional, at clamped in-range indices; the flags select at commit)
   auto load_stg = [&](Stg& r, int64_t t0) {
+    r.fk = 0u;
+    r.fv = 0u;
 #pragma unroll
     for (int x = 0; x < SK; ++x) {
       const int e0 = tid + 256 * x;
@@ -187,11 +193,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
       const int64_t t = t0 + j < len ? t0 + j : len - 1;
       int64_t tq, tk;
       rows(bos + t, tq, tk);
-      const float kk = ld_f32(kp + tk * DK + i), qq = ld_f32(qp + tq * DK + i), aa = p.alpha[tq * DK + i];
-      const float ug = VEC ? p.erase[tk * DK + i] : p.erase[tk];
+      r.k[x] = kp[tk * DK + i];
+      r.q[x] = qp[tq * DK + i];
+      r.a[x] = p.alpha[tq * DK + i];
+      r.ug[x] = VEC ? p.erase[tk * DK + i] : p.erase[tk];
       const bool first = ((bos + t) & lastm) == 0;
-      r.k[x] = in ? kk : 0.f; r.u[x] = in ? ug * kk : 0.f; r.q[x] = in ? qq : 0.f;
-      r.a[x] = in ? (first ? aa : 1.f) : 0.f;
+      r.fk |= (in ? 1u << x : 0u) | (first ? 1u << (16 + x) : 0u);
     }
 #pragma unroll
     for (int x = 0; x < SV; ++x) {
@@ -202,11 +209,11 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
       const int64_t t = t0 + j < len ? t0 + j : len - 1;
       int64_t tq, tk;
       rows(bos + t, tq, tk);
-      const float vv = ld_f32(vp + tk * DV + dv0 + cc);
-      const float gg = VEC ? p.write[tk * DV + dv0 + cc] : p.write[tk];
-      const float dd = p.dO[tq * DV + dv0 + cc];
+      r.v[x] = vp[tk * DV + dv0 + cc];
+      r.g[x] = VEC ? p.write[tk * DV + dv0 + cc] : p.write[tk];
+      r.dO[x] = p.dO[tq * DV + dv0 + cc];
       const bool last = ((bos + t) & lastm) == lastm;
-      r.m[x] = in ? gg * vv : 0.f; r.dO[x] = in && last ? dd : 0.f; r.v[x] = in ? vv : 0.f; r.g[x] = in ? gg : 0.f;
+      r.fv |= (in ? 1u << x : 0u) | (last ? 1u << (16 + x) : 0u);
     }
   };
   auto commit_stg = [&](const Stg& r) {
@@ -215,7 +222,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
       const int e = tid + 256 * x;
       if (e < BW_SB * DK) {
         const int j = e / DK, i = e % DK;
-        sm.k[j][i] = r.k[x]; sm.u[j][i] = r.u[x]; sm.q[j][i] = r.q[x]; sm.a[j][i] = r.a[x];
+        const bool in = (r.fk >> x) & 1u, first = (r.fk >> (16 + x)) & 1u;
+        const float kk = (float)r.k[x];
+        sm.k[j][i] = in ? kk : 0.f;
+        sm.u[j][i] = in ? r.ug[x] * kk : 0.f;
+        sm.q[j][i] = in ? (float)r.q[x] : 0.f;
+        sm.a[j][i] = in ? (first ? r.a[x] : 1.f) : 0.f;
       }
     }
 #pragma unroll
@@ -223,7 +235,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
       const int e = tid + 256 * x;
       if (e < BW_SB * DVB) {
         const int j = e / DVB, cc = e % DVB;
-        sm.m[j][cc] = r.m[x]; sm.dO[j][cc] = r.dO[x]; sm.v[j][cc] = r.v[x]; sm.g[j][cc] = r.g[x];
+        const bool in = (r.fv >> x) & 1u, last = (r.fv >> (16 + x)) & 1u;
+        const float vv = (float)r.v[x];
+        sm.m[j][cc] = in ? r.g[x] * vv : 0.f;
+        sm.dO[j][cc] = in && last ? r.dO[x] : 0.f;
+        sm.v[j][cc] = in ? vv : 0.f;
+        sm.g[j][cc] = in ? r.g[x] : 0.f;
       }
     }
   };
@@ -249,7 +266,8 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
       --pch;
       pi = 0;
     }
-    if (pch >= 0) load_stg(pre, block_t0(pch, pi));
+    // (past the last block: a harmless reload of the first, never committed)
+    load_stg(pre, block_t0(pch >= 0 ? pch : 0, pch >= 0 ? pi : 0));
   };
 
   // one forward step of token j of the staged block: S <- X + k delta^T; delta of the lane's columns
@@ -406,7 +424,10 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
           if (lw == 0) sm.reds[buf][w] = vdm;
           __syncthreads();
           // across the four waves
-          for (int o = tid; o < RG * NV; o += 256) {
+#pragma unroll
+          for (int x = 0; x < (RG * NV + 255) / 256; ++x) {
+            const int o = tid + 256 * x;
+            if (o >= RG * NV) break;
             const int org = o / NV, idx = o % NV;
             const float sum = sm.red[buf][0][org][idx] + sm.red[buf][1][org][idx] + sm.red[buf][2][org][idx] +
                               sm.red[buf][3][org][idx];
