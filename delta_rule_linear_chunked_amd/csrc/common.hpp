@@ -44,6 +44,7 @@ struct Params {
   float* snap;          // prefill: states after every snap_chunks chunks of each sequence (may be null)
   int32_t snap_chunks;  // chunks between snapshots
   int32_t* snap_first;  // packed: first snapshot row of each sequence
+  int32_t* seq_order;   // packed: sequences by decreasing chunk count (the state pass's order)
   // input preparation applied while loading (all zero: inputs are used as given)
   int32_t prep_l2;      // q and k are divided by their L2 norm over d_k
   int32_t a_bf16;       // alpha is stored as bfloat16

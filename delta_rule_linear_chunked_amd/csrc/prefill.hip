@@ -171,6 +171,26 @@ __global__ __launch_bounds__(256) void chunk_plan_kernel(const Params p) {
       __syncthreads();
     }
   }
+  // sequences by decreasing chunk count (ties by index): the state pass starts the longest
+  // chains first. Ranked by comparison for up to 1024 sequences, else kept in index order.
+  {
+    __shared__ int s_nc[1024];
+    if (p.nseq <= 1024) {
+      for (int n = tid; n < p.nseq; n += 256) s_nc[n] = (int)((cu_steps(p, n + 1) - cu_steps(p, n) + CH - 1) / CH);
+      __syncthreads();
+      for (int n = tid; n < p.nseq; n += 256) {
+        const int c = s_nc[n];
+        int r = 0;
+        for (int m = 0; m < p.nseq; ++m) {
+          const int cm = s_nc[m];
+          r += (cm > c || (cm == c && m < n)) ? 1 : 0;
+        }
+        p.seq_order[r] = n;
+      }
+    } else {
+      for (int n = tid; n < p.nseq; n += 256) p.seq_order[n] = n;
+    }
+  }
   for (int slot = tid; slot < p.slots; slot += 256) {
     int n = -1, c0 = 0;
     if (slot < total) {
@@ -659,11 +679,25 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 
   __shared__ __align__(16) StateSmem<Pol, DK, DVB> sm;
 
-  const int lid = xcd_remap(blockIdx.x, gridDim.x);
-  if (lid >= p.grid_logical) return;
-  const int pair = lid / p.ndvb;
-  const int dv0 = (lid % p.ndvb) * DVB;
   const int H = p.H;
+  int pair, dv0;
+  if (p.cu) {
+    // packed sequences: the (sequence, head) pairs in order of decreasing length, dealt
+    // round-robin over the XCDs (workgroup b runs on XCD b % 8), each XCD taking its pairs
+    // longest first; the value-column blocks of a pair stay on one XCD and share its L2.
+    // (In sequence order each XCD took a contiguous range of pairs, and with uneven lengths
+    // one XCD held the longest chains back to back.)
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int k = (j / p.ndvb) * 8 + x;
+    if (k >= p.num_pairs) return;
+    pair = p.seq_order[k / H] * H + k % H;
+    dv0 = (j % p.ndvb) * DVB;
+  } else {
+    const int lid = xcd_remap(blockIdx.x, gridDim.x);
+    if (lid >= p.grid_logical) return;
+    pair = lid / p.ndvb;
+    dv0 = (lid % p.ndvb) * DVB;
+  }
   const int n = pair / H, h = pair % H;
   int64_t bos, len;
   int first;
@@ -985,11 +1019,13 @@ PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int
   }
   pl.ndvb = dv / pl.dv_block;
   const int64_t logical = num_pairs * pl.ndvb;
-  pl.workgroups = (logical + 7) / 8 * 8;
+  // (packed: whole rows of 8 pairs, one pair per XCD, times the column blocks)
+  pl.workgroups = packed ? (num_pairs + 7) / 8 * 8 * pl.ndvb : (logical + 7) / 8 * 8;
   const int64_t cps = (seqlen + CH - 1) / CH;
   pl.slots = packed ? cps + num_seqs : batch * cps;
   pl.rec_size = rec_size_for(dk);
-  const int64_t tables = packed ? ((2 * pl.slots + 2 * num_seqs + 1) * 4 + 255) / 256 * 256 : 0;
+  // chunk_seq, chunk_c0 [slots]; seq_first [nseq + 1]; snap_first, seq_order [nseq]
+  const int64_t tables = packed ? ((2 * pl.slots + 3 * num_seqs + 1) * 4 + 255) / 256 * 256 : 0;
   pl.workspace = pl.slots * heads * pl.rec_size + tables;
   return pl;
 }
@@ -1058,6 +1094,7 @@ hipError_t launch_prefill(Params p, const PrefillPlan& pl, void* ws, int dk, boo
     p.chunk_c0 = tables + pl.slots;
     p.seq_first = tables + 2 * pl.slots;
     p.snap_first = prefill_snap_first(ws, pl, p.H, p.nseq);
+    p.seq_order = p.snap_first + p.nseq;
   }
   switch (dk) {
     case 16: return launch_dvb<16>(p, pl, bf16, vec, s);
