@@ -73,6 +73,19 @@ def test_packed_varlen_with_empty_and_short_sequences():
         assert np.array_equal(S_T[1], wl.S0[1].astype(np.float64))
 
 
+@pytest.mark.parametrize("nseq", [300, 1500])
+def test_many_packed_sequences(nseq):
+    # uneven lengths with many ties, empty sequences included: the state pass takes the
+    # sequences longest first (ranked up to 1024 sequences, in index order beyond that), and
+    # every (sequence, head) pair must be computed exactly once
+    rng = np.random.default_rng(nseq)
+    lens = rng.integers(0, 90, size=nseq)
+    lens[::7] = 64
+    lens[3::11] = 0
+    wl = synth.make_prefill("rda", 1, 0, 2, 16, 32, in_dtype="f32", seed=seed_of("many", nseq), lengths=lens)
+    check(wl, f"nseq={nseq}")
+
+
 def test_exact_zero_and_unit_gates():
     """alpha = 0 exactly, alpha = +-1 and beta = 2 (Complex KDA ranges); zeros force the
     exact running-product path for the block's diagonal tile."""
