@@ -260,6 +260,8 @@ int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alp
   const int64_t pairs = dims->num_seqs * dims->num_heads;
   const dr::PrefillPlan pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen << lg, dims->num_heads,
                                               (int)dims->head_dim_k, (int)dims->head_dim_v, cu_seqlens != nullptr);
+  if (pl.workgroups > INT32_MAX || pl.slots * dims->num_heads > INT32_MAX)
+    return fail(DR_ERR_UNSUPPORTED, "problem too large: more than 2^31 - 1 workgroups per kernel");
   p.num_pairs = (int32_t)pairs;
   p.ndvb = pl.ndvb;
   p.grid_logical = (int32_t)(pairs * pl.ndvb);
@@ -328,6 +330,8 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
   p.DV = (int32_t)dvh;
   const dr::PrefillPlan pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen << lg, H, dkh, dvh,
                                               cu_seqlens != nullptr);
+  if (pl.workgroups > INT32_MAX || pl.slots * H > INT32_MAX || pairs * (dvh / dr::bwd_dv_block(dvh)) > INT32_MAX)
+    return fail(DR_ERR_UNSUPPORTED, "problem too large: more than 2^31 - 1 workgroups per kernel");
   p.num_pairs = (int32_t)pairs;
   p.ndvb = pl.ndvb;
   p.grid_logical = (int32_t)(pairs * pl.ndvb);

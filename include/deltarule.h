@@ -270,7 +270,8 @@ int dr_version(void);
 /*
  * Launch shape the prefill would use for `dims` (for tests and profiling):
  * chunk length, value columns per workgroup of the sequential state pass, and
- * that pass's number of workgroups.
+ * that pass's number of workgroups (taking the sequences as packed when batch
+ * is 1 and num_seqs is not).
  * Returns DR_OK or an argument error.
  */
 int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t* dv_block,

@@ -76,6 +76,9 @@ def chunk(lib, d, variant=0, write=None, S0=None, cu=None, q=FAKE, o=FAKE):
     (dict(d=dims(), o=None), -1),
     (dict(d=dims(), q=MISALIGNED), -4),
     (dict(d=dims(), S0=MISALIGNED), -4),
+    # 2^27 sequences x 15 heads pass the 32-bit count checks, but the state pass would need
+    # more than 2^31 - 1 workgroups
+    (dict(d=dims(B=1, T=1 << 28, H=15, dk=128, dv=128, N=1 << 27), cu=FAKE), -5),
 ])
 def test_chunk_fwd_rejects_bad_arguments(lib, case, expect):
     st = chunk(lib, **case)
