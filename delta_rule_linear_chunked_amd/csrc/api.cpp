@@ -364,6 +364,7 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
     b.dq = dq; b.dk = dk; b.dv = dv; b.dalpha = dalpha; b.derase = derase; b.dwrite = dwrite; b.dS0 = dS0;
     b.snap = p.snap;
     b.snap_first = cu_seqlens ? dr::prefill_snap_first(ws, pl, H, dims->num_seqs) : nullptr;
+    b.seq_order = cu_seqlens ? b.snap_first + dims->num_seqs : nullptr;  // written by the prefill's plan pass
     b.part = reinterpret_cast<float*>(wsb + off_part);
     b.parts = reinterpret_cast<float*>(wsb + off_parts);
     b.T = dims->seqlen << lg;

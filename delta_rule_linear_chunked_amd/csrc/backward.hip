@@ -127,7 +127,9 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
   constexpr int RG = Sh::RG, CPL = Sh::CPL, RPL = Sh::RPL, NV = Sh::NV, NVR = Sh::NVR;
   __shared__ __align__(16) BwdSmem<DK, DVB> sm;
 
-  const int pair = blockIdx.x / p.ndvb;
+  // packed sequences: the longest first, so that the last workgroups to start are short ones
+  const int pair = p.seq_order ? p.seq_order[blockIdx.x / p.ndvb / p.H] * p.H + (int)(blockIdx.x / p.ndvb % p.H)
+                               : (int)(blockIdx.x / p.ndvb);
   const int blk = blockIdx.x % p.ndvb;
   const int dv0 = blk * DVB;
   const int H = p.H, DV = p.DV;

@@ -91,6 +91,7 @@ struct BwdParams {
   float* dS0;           // may be null
   const float* snap;    // forward states after every 64 tokens of each sequence
   const int32_t* snap_first;  // packed: first snapshot row of each sequence
+  const int32_t* seq_order;   // packed: sequences by decreasing length (walked longest first)
   float* part;          // [ndvb][tokens * H][4][d_k] per-block row sums: dq, k-part of dk, du, dalpha
   float* parts;         // [ndvb][tokens * H] per-block v . dm
   int64_t T;
