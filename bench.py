@@ -98,11 +98,23 @@ def cpu_baseline():
     t0 = time.perf_counter()
     oracle.step_recurrence(wl.q, wl.k, wl.v, wl.alpha, wl.erase, None, "kda", S0=wl.S0)
     dt = time.perf_counter() - t0
+    del wl
+    # decode: one step of 32 of the 512 sequences (x 32 heads), the fp64 state of the subset
+    # (128 MiB) updated once
+    wd = synth.make_decode("kda", 32, 32, 128, 128, steps=1, in_dtype="bf16", seed=1005)
+    S = wd.S0.astype(np.float64)
+    t1 = time.perf_counter()
+    oracle.decode_step(S, wd.q[0], wd.k[0], wd.v[0], wd.alpha[0], wd.erase[0], None, "kda")
+    dd = time.perf_counter() - t1
     if ctx is not None:
         ctx.__exit__(None, None, None)
+    cpu = platform.processor() or platform.machine()
     return {"value": 4 * 4096 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"the whole KDA prefill workload (4 x 4096 tokens x 16 heads, fp64 step "
-                      f"recurrence) in {dt:.1f} s on one core of {platform.processor() or platform.machine()}"}
+                      f"recurrence) in {dt:.1f} s on one core of {cpu}",
+            "decode": {"value": 32 * 32 / dd, "unit": "head-steps/s", "cores": 1,
+                       "sample": f"one KDA decode step of 32 sequences x 32 heads (1/16 of the decode "
+                                 f"workload, fp64 state) in {dd:.2f} s on one core of {cpu}"}}
 
 
 def main():
