@@ -124,7 +124,9 @@ __device__ __forceinline__ bool resolve_slot(const Params& p, int slot, int& n, 
 
 // ============================================================================ pass 0
 // Packed sequences: first chunk slot of each sequence (exclusive scan of the chunk
-// counts) and, for every slot, its sequence and first token. One workgroup.
+// counts), first snapshot row of each sequence, the sequences in order of decreasing
+// chunk count (the state pass's order), and, for every slot, its sequence and first
+// token. One workgroup.
 __global__ __launch_bounds__(256) void chunk_plan_kernel(const Params p) {
   __shared__ int s_scan[256];
   __shared__ int s_carry;
