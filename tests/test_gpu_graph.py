@@ -1,7 +1,8 @@
-"""The decode step captured in a HIP graph (torch.cuda.CUDAGraph on ROCm): the step allocates
-nothing and never synchronises, so a serving loop can replay it. Each replay is checked
-against the same step run eagerly (same kernel, same inputs: bit-identical), with eager work
-and synchronisations between the replays."""
+"""The decode step and the prefill captured in HIP graphs (torch.cuda.CUDAGraph on ROCm). The
+decode step allocates nothing and never synchronises; the prefill takes its workspace
+stream-ordered, which the capture records as memory nodes. Each replay is checked against the
+same call run eagerly (same kernels, same inputs: bit-identical), with eager work and
+synchronisations between the replays."""
 import numpy as np
 import pytest
 import torch
@@ -57,3 +58,45 @@ def test_decode_step_replays_from_a_graph(variant):
         assert torch.equal(o_g, o_e), f"replay {s}: output differs from the eager step"
         assert torch.equal(S_g, S_e), f"replay {s}: state differs from the eager step"
     print(f"[graph decode {variant}] {steps} replays bit-identical to eager steps", flush=True)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_prefill_replays_from_a_graph(packed):
+    # the prefill's workspace is taken and released stream-ordered, which a capture records
+    # as graph memory nodes; the packed call's plan pass is captured with it
+    from gpu_util import prefill_inputs
+    if packed:
+        wl = synth.make_prefill("rda", 1, 0, 2, 128, 128, in_dtype="bf16", seed=seed_of("graph pf", 1),
+                                lengths=[70, 0, 130, 64])
+    else:
+        wl = synth.make_prefill("kda", 2, 150, 2, 128, 128, in_dtype="bf16", seed=seed_of("graph pf", 0))
+    a = prefill_inputs(wl)
+    B, T, H, _ = wl.q.shape
+    dev = torch.device("cuda:0")
+    o_g = torch.empty((B, T, H, 128), device=dev)
+    S_g = torch.empty((wl.S0.shape[0], H, 128, 128), device=dev)
+
+    def call(o, S):
+        drl.dr_chunk_fwd(a["q"], a["k"], a["v"], a["alpha"], a["erase"], a["write"], a["variant"], a["S0"],
+                         a["cu_seqlens"], o, S)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(torch.empty_like(o_g), torch.empty_like(S_g))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(o_g, S_g)
+    torch.cuda.synchronize()
+    for r in range(4):
+        o_g.zero_()
+        S_g.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_e, S_e = torch.empty_like(o_g), torch.empty_like(S_g)
+        call(o_e, S_e)  # eager, between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_e) and torch.equal(S_g, S_e), f"replay {r} differs from the eager call"
+    print(f"[graph prefill packed={packed}] 4 replays bit-identical to eager calls", flush=True)
