@@ -54,13 +54,18 @@ def decode_bytes(N, H, dk, dv, in_bytes=2, gate_bytes=4):
 
 
 def kernel_source_digest():
-    """sha256 of the prefill kernel's sources: a stored traffic measurement is used only while
-    it matches the code that is being timed."""
+    """sha256 of the prefill kernel's sources with comments and whitespace removed: a stored
+    traffic measurement is used only while it matches the code that is being timed (an edit
+    of a comment leaves it valid, any change of code does not)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("prefill.hip", "common.hpp"):
-        with open(os.path.join(ROOT, "delta_rule_linear_chunked_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "delta_rule_linear_chunked_amd", "csrc", f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)  # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                # line comments
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 
