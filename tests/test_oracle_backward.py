@@ -128,3 +128,39 @@ def test_packed_sequence_gradients_are_per_sequence():
             np.testing.assert_array_equal(g[name][sl], gn[name])
         np.testing.assert_array_equal(g["dS0"][n], gn["dS0"][0])
     np.testing.assert_array_equal(g["dS0"][1], dS_T[1])            # an empty sequence passes dS_T through
+
+
+@pytest.mark.parametrize("signed", [False, True])
+def test_reverse_chain_is_a_time_reversed_forward_run(signed):
+    # With a symmetric erase factor (I - e_t k_t k_t^T) (KDA, RDA, Complex KDA) the gradient
+    # chain E_{t-1} = Diag(alpha_t) (I - e_t k_t k_t^T) E_t + q_{t-1} do_{t-1}^T is the forward
+    # recurrence itself, in RDA form, on reversed and interleaved steps: an erase-only step
+    # (key k_t, erase e_t) and a write-only step (decay alpha_t, key q_{t-1}, value do_{t-1}).
+    # Its readout with query k_t after the write-only step that forms E_t is d(delta)_t, and its
+    # final state is dS0: the reverse recurrence is pinned against the forward one.
+    rng = np.random.default_rng(31 + signed)
+    T, H, dk, dv = 9, 2, 5, 4
+    q, k = rng.standard_normal((1, T, H, dk)), rng.standard_normal((1, T, H, dk))
+    v = rng.standard_normal((1, T, H, dv))
+    alpha = rng.uniform(-1.0, 1.0, (1, T, H, dk)) if signed else rng.uniform(0.3, 1.0, (1, T, H, dk))
+    e, w = rng.uniform(0.0, 2.0, (1, T, H)), rng.uniform(0.1, 1.0, (1, T, H))
+    S0, dS_T = rng.standard_normal((1, H, dk, dv)), rng.standard_normal((1, H, dk, dv))
+    dO = rng.standard_normal((1, T, H, dv))
+    g = backward.step_recurrence_grads(q, k, v, alpha, e, w, "rda", dO, dS_T=dS_T, S0=S0)
+
+    n = 2 * T + 1
+    Q, K = np.zeros((1, n, H, dk)), np.zeros((1, n, H, dk))
+    V, A = np.zeros((1, n, H, dv)), np.ones((1, n, H, dk))
+    E, W = np.zeros((1, n, H)), np.zeros((1, n, H))
+    K[0, 0], V[0, 0], W[0, 0], Q[0, 0] = q[0, T - 1], dO[0, T - 1], 1.0, k[0, T - 1]  # forms E_{T-1}
+    for i, t in enumerate(range(T - 1, -1, -1)):
+        a, b = 1 + 2 * i, 2 + 2 * i
+        K[0, a], E[0, a] = k[0, t], e[0, t]                  # (I - e_t k_t k_t^T)
+        A[0, b] = alpha[0, t]                                # Diag(alpha_t)
+        if t >= 1:                                           # + q_{t-1} do_{t-1}^T, read with k_{t-1}
+            K[0, b], V[0, b], W[0, b], Q[0, b] = q[0, t - 1], dO[0, t - 1], 1.0, k[0, t - 1]
+    o_r, S_r = oracle.step_recurrence(Q, K, V, A, E, W, "rda", S0=dS_T)
+    np.testing.assert_allclose(S_r, g["dS0"], rtol=1e-10, atol=1e-10)
+    for t in range(T):
+        dR = o_r[0, 2 * (T - 1 - t)]                         # d(delta)_t = dL/dm_t
+        np.testing.assert_allclose(w[0, t][:, None] * dR, g["dv"][0, t], rtol=1e-10, atol=1e-10)
