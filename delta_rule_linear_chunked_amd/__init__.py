@@ -219,9 +219,10 @@ def dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, 
     _need(o, "o", (B, T, H, dv), torch.float32, dev)
     d = _Dims(B, T, H, dk, dv, N, _DT[q.dtype], 0)
     opts = _opts(state_idx, rows, snapshots, snapshot_every, prep, alpha)
-    st = lib.dr_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
-                             VARIANTS[variant], _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
-                             ctypes.byref(d), ctypes.byref(opts), _stream(dev))
+    with torch.cuda.device(dev):  # the library launches on the current device
+        st = lib.dr_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
+                                 VARIANTS[variant], _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
+                                 ctypes.byref(d), ctypes.byref(opts), _stream(dev))
     _check(lib, st, "dr_chunk_fwd")
 
 
@@ -261,9 +262,10 @@ def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_id
     _need(o, "o", (N, H, dv), torch.float32, dev)
     d = _Dims(N, 1, H, dk, dv, N, _DT[q.dtype], 0)
     opts = _opts(state_idx, rows, None, 0, prep, alpha)
-    st = lib.dr_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
-                               VARIANTS[variant], _ptr(S), _ptr(o), ctypes.byref(d), ctypes.byref(opts),
-                               _stream(dev))
+    with torch.cuda.device(dev):
+        st = lib.dr_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
+                                   VARIANTS[variant], _ptr(S), _ptr(o), ctypes.byref(d), ctypes.byref(opts),
+                                   _stream(dev))
     _check(lib, st, "dr_decode_step")
 
 
@@ -337,9 +339,10 @@ def dr_chunk_bwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, dO,
                            (derase, "derase", es)):
         _need(t, name, shape, torch.float32, dev)
     d = _Dims(B, T, H, dk_, dv_, N, _DT[q.dtype], 0)
-    st = lib.dr_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write), VARIANTS[variant],
-                          _ptr(S0), _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv),
-                          _ptr(dalpha), _ptr(derase), _ptr(dwrite), _ptr(dS0), ctypes.byref(d), _stream(dev))
+    with torch.cuda.device(dev):
+        st = lib.dr_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write), VARIANTS[variant],
+                              _ptr(S0), _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv),
+                              _ptr(dalpha), _ptr(derase), _ptr(dwrite), _ptr(dS0), ctypes.byref(d), _stream(dev))
     _check(lib, st, "dr_chunk_bwd")
 
 
