@@ -143,6 +143,29 @@ def test_deterministic():
     assert torch.equal(o1, o2) and torch.equal(s1, s2)
 
 
+@pytest.mark.parametrize("variant", ["kda", "gdn2", "ckda"])
+def test_linear_in_initial_state_and_values(variant):
+    # with q, k and the gates fixed, o and S_T are linear in (S0, v) jointly: the GPU result for
+    # a S0_1 + b S0_2, a v_1 + b v_2 is a times the first plus b times the second (fp32 inputs,
+    # so the combined values are exact inputs too)
+    wl = synth.make_prefill(variant, 1, 0, 2, 64, 64, in_dtype="f32", seed=seed_of("linear", variant),
+                            lengths=[150, 0, 77])
+    rng = np.random.default_rng(seed_of("linear 2", variant))
+    a = prefill_inputs(wl)
+    v2 = torch.from_numpy(rng.standard_normal(wl.v.shape).astype(np.float32)).to(a["v"].device)
+    S2 = torch.from_numpy(rng.standard_normal(wl.S0.shape).astype(np.float32)).to(a["v"].device)
+    ca, cb = 0.75, -1.25
+    o1, s1 = drl.chunk_fwd(**a)
+    o2, s2 = drl.chunk_fwd(**dict(a, v=v2, S0=S2))
+    o3, s3 = drl.chunk_fwd(**dict(a, v=ca * a["v"] + cb * v2, S0=ca * a["S0"] + cb * S2))
+    torch.cuda.synchronize()
+    f = lambda x: x.cpu().numpy().astype(np.float64)
+    eo = oracle.rel_err(f(o3), ca * f(o1) + cb * f(o2))
+    es = oracle.rel_err(f(s3), ca * f(s1) + cb * f(s2))
+    print(f"[prefill linearity {variant}] err o={eo:.3e} S_T={es:.3e}", flush=True)
+    assert eo <= TOL["f32"] and es <= TOL["f32"], (eo, es)
+
+
 def test_state_in_place_and_optional_states():
     wl = synth.make_prefill("rda", 2, 100, 2, 64, 64, in_dtype="bf16", seed=83)
     a = prefill_inputs(wl)
