@@ -51,3 +51,11 @@ def test_decode_roofline_arithmetic():
     per_head = 8 * 128 * 128 + (2 * 128 + 128) * 2 + 4 * 128 + 4 + 4 * 128
     assert per_head == 132_868
     assert bench.decode_bytes(512, 32, 128, 128) == 512 * 32 * per_head == 2_176_909_312
+
+
+def test_more_than_one_gpu_is_refused():
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=60)
+    assert r.returncode == 2 and "one GPU" in r.stderr, (r.returncode, r.stderr)
+    assert r.stdout == ""  # no JSON line
