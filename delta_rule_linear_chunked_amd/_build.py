@@ -38,10 +38,16 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
+# The backward walk is bound by the issue and latency of its per-token VALU work; the
+# backend's ILP-first machine scheduler runs it about 1% faster with identical results (the
+# prefill and decode kernels measured slower or equal with it).
+FILE_FLAGS = {"backward.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(OBJDIR, os.path.basename(src) + ".o")
     lang = ["-x", "hip"] if src.endswith((".hip", ".cpp")) else []
-    cmd = [_hipcc(), *HIPFLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *HIPFLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
