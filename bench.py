@@ -53,6 +53,10 @@ def decode_bytes(N, H, dk, dv, in_bytes=2, gate_bytes=4):
     return N * H * (8 * dk * dv + (2 * dk + dv) * in_bytes + 4 * dk + gate_bytes + 4 * dv)
 
 
+# the prefill kernels' sources (both passes and what they include)
+PREFILL_SOURCES = ("prefill.hip", "prefill_state.hip", "prefill.hpp", "common.hpp")
+
+
 def kernel_source_digest():
     """sha256 of the prefill kernel's sources with comments and whitespace removed: a stored
     traffic measurement is used only while it matches the code that is being timed (an edit
@@ -60,7 +64,7 @@ def kernel_source_digest():
     import hashlib
     import re
     h = hashlib.sha256()
-    for f in ("prefill.hip", "common.hpp"):
+    for f in PREFILL_SOURCES:
         with open(os.path.join(ROOT, "delta_rule_linear_chunked_amd", "csrc", f), encoding="utf-8") as fh:
             src = fh.read()
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)  # block comments

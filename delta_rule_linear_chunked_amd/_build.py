@@ -20,7 +20,7 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdeltarule.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "backward.hip"]
+SOURCES = ["api.cpp", "decode.hip", "prefill.hip", "prefill_state.hip", "backward.hip"]
 
 # Packed-fp32 instructions are disabled for every device compile; hipcc's host
 # pass does not know the feature and says so, which is harmless.
@@ -38,10 +38,11 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-# The backward walk is bound by the issue and latency of its per-token VALU work; the
-# backend's ILP-first machine scheduler runs it about 1% faster with identical results (the
-# prefill and decode kernels measured slower or equal with it).
-FILE_FLAGS = {"backward.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+# The prefill's state pass and the backward walk are bound by latency and issue; the backend's
+# ILP-first machine scheduler runs them a few percent faster with identical results (the
+# preparation and decode kernels measured slower or equal with it, so they keep the default).
+_ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
+FILE_FLAGS = {"prefill_state.hip": _ILP, "backward.hip": _ILP}
 
 
 def _compile(src: str) -> str:

@@ -20,7 +20,7 @@
 // Two passes. chunk_prep_kernel (one workgroup per chunk and head, all chunks in
 // parallel) computes everything that does not depend on the state — gate
 // products, A, P, T, Utilde, Qtilde, Kbar, Gamma_C — and writes it to a
-// workspace record as MFMA operand fragments. chunk_state_kernel (one workgroup
+// workspace record as MFMA operand fragments. chunk_state_kernel (prefill_state.hip; one workgroup
 // per sequence, head and block of value columns) then walks the chunks in order
 // with the state held in registers, doing only the state-dependent products.
 //
@@ -40,69 +40,13 @@
 #include <cstdlib>
 #include <type_traits>
 
-#include "common.hpp"
-#include "launch.hpp"
+#include "prefill.hpp"
 
 namespace dr {
 
-constexpr int CH = 64;    // chunk length
-constexpr int NBLK = 4;   // 16-token blocks per chunk
 constexpr int LDT = 68;   // padded row stride of 64-wide fp32 tiles
 constexpr float FAST_LO = 0x1p-100f;
 constexpr float FAST_HI = 0x1p100f;
-
-// Operand record of one (chunk slot, head). Every fragment is 32 bytes per lane
-// (bf16 hi + lo, or eight fp32 values), stored as two 1 KiB halves (bytes 0-15 of
-// every lane, then bytes 16-31), so each of a wave's two 16-byte accesses per lane
-// covers one contiguous KiB.
-template <int DK>
-struct Rec {
-  static constexpr int KS = DK / 32;
-  static constexpr int64_t FR = 64 * 32;                        // bytes of one fragment
-  static constexpr int64_t UT = 0;                              // Utilde  [block][ks]
-  static constexpr int64_t QT = UT + NBLK * KS * FR;            // Qtilde  [block][ks]
-  static constexpr int64_t KB = QT + NBLK * KS * FR;            // Kbar^T  [key tile][token step]
-  static constexpr int64_t TT = KB + (DK / 16) * 2 * FR;        // T       [block][token step]
-  static constexpr int64_t PP = TT + NBLK * 2 * FR;             // P       [block][token step]
-  static constexpr int64_t GC = PP + NBLK * 2 * FR;             // Gamma_C [DK] fp32
-  static constexpr int64_t SIZE = (GC + DK * 4 + 255) / 256 * 256;
-};
-
-// A record is addressed through a buffer descriptor of its own (base = the record,
-// range = its size), so that fragment addresses are a per-lane 32-bit offset plus a
-// uniform byte offset: no 64-bit address arithmetic per access, and an access outside
-// the record reads zero / is dropped instead of touching other memory.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const unsigned char* rec, int64_t size) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<unsigned char*>(rec), 0, (int)size, 0x00020000);
-}
-// (Stores put the whole offset in the per-lane field and keep the scalar offset at zero:
-// the compiler protects the data registers of a wide buffer store from being
-// overwritten too early only in that form.)
-template <class Frag>
-__device__ __forceinline__ void st_frag(__amdgpu_buffer_rsrc_t rs, int off, int idx, int lane, const Frag& f) {
-  static_assert(sizeof(Frag) == 32, "fragment size");
-  const u32x4* h = reinterpret_cast<const u32x4*>(&f);
-  __builtin_amdgcn_raw_buffer_store_b128(h[0], rs, lane * 16 + off + idx * 2048, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b128(h[1], rs, lane * 16 + 1024 + off + idx * 2048, 0, 0);
-}
-template <class Frag>
-__device__ __forceinline__ Frag ld_frag(__amdgpu_buffer_rsrc_t rs, int off, int idx, int lane) {
-  static_assert(sizeof(Frag) == 32, "fragment size");
-  Frag f;
-  u32x4* h = reinterpret_cast<u32x4*>(&f);
-  h[0] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16, off + idx * 2048, 0);
-  h[1] = __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + 1024, off + idx * 2048, 0);
-  return f;
-}
-
-// Orders this wave's LDS writes before its later LDS reads by other lanes of the
-// same wave (LDS executes a wave's instructions in order; this stops the compiler
-// from reordering across the point).
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 // Sequence, first token and length of a chunk slot. Returns false for an unused slot.
 __device__ __forceinline__ bool resolve_slot(const Params& p, int slot, int& n, int64_t& bos, int64_t& len,
@@ -626,377 +570,6 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   }
 }
 
-// ============================================================================ pass 2
-// Split-operand tile in LDS: a row-major matrix whose fragments are 8 consecutive
-// columns of a row (the reduction index), written 4 columns at a time from an
-// accumulator.
-template <class Pol, int ROWS, int COLS> struct OpTile;
-template <int ROWS, int COLS> struct OpTile<PolBF3, ROWS, COLS> {
-  __bf16 hi[ROWS][COLS + 8], lo[ROWS][COLS + 8];
-  __device__ __forceinline__ void put4(int row, int col, const f32x4& x) {
-    bf16x4 h, o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = (__bf16)x[i];
-      o[i] = (__bf16)(x[i] - (float)h[i]);
-    }
-    *reinterpret_cast<bf16x4*>(&hi[row][col]) = h;
-    *reinterpret_cast<bf16x4*>(&lo[row][col]) = o;
-  }
-  __device__ __forceinline__ PolBF3::Frag get8(int row, int col) const {
-    PolBF3::Frag f;
-    f.hi = *reinterpret_cast<const bf16x8*>(&hi[row][col]);
-    f.lo = *reinterpret_cast<const bf16x8*>(&lo[row][col]);
-    return f;
-  }
-};
-template <int ROWS, int COLS> struct OpTile<PolF32, ROWS, COLS> {
-  float v[ROWS][COLS + 4];
-  __device__ __forceinline__ void put4(int row, int col, const f32x4& x) { store4(&v[row][col], x); }
-  __device__ __forceinline__ PolF32::Frag get8(int row, int col) const {
-    PolF32::Frag f;
-    load8(&v[row][col], f.v);
-    return f;
-  }
-};
-
-template <class Pol, int DK, int DVB>
-struct StateSmem {
-  OpTile<Pol, DVB, DK> S;   // state, transposed: [value column][key channel]
-  OpTile<Pol, DVB, CH> R;   // (M - Utilde S0)^T: [value column][token]
-  OpTile<Pol, DVB, CH> D;   // delta^T
-  float X[NBLK][16][DVB + 4];  // per wave: m = w . v in, then O out, between row and accumulator layouts
-};
-
-template <int DKR, int DVB, typename InT, bool VEC>
-__global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
-  using Pol = typename PolicyFor<InT>::type;
-  using Frag = typename Pol::Frag;
-  constexpr int DK = DKR < 32 ? 32 : DKR;
-  constexpr int KS = DK / 32;
-  constexpr int NCT = DVB / 16;
-  constexpr int NRT = (DK / 16 + 3) / 4;  // key-channel tiles per wave (rounded up)
-  using R = Rec<DK>;
-  static_assert(DVB % 16 == 0 && DVB <= 64, "value block");
-
-  __shared__ __align__(16) StateSmem<Pol, DK, DVB> sm;
-
-  const int H = p.H;
-  int pair, dv0;
-  if (p.cu) {
-    // packed sequences: the (sequence, head) pairs in order of decreasing length, dealt
-    // round-robin over the XCDs (workgroup b runs on XCD b % 8), each XCD taking its pairs
-    // longest first; the value-column blocks of a pair stay on one XCD and share its L2.
-    // (In sequence order each XCD took a contiguous range of pairs, and with uneven lengths
-    // one XCD held the longest chains back to back.)
-    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
-    const int k = (j / p.ndvb) * 8 + x;
-    if (k >= p.num_pairs) return;
-    pair = p.seq_order[k / H] * H + k % H;
-    dv0 = (j % p.ndvb) * DVB;
-  } else {
-    const int lid = xcd_remap(blockIdx.x, gridDim.x);
-    if (lid >= p.grid_logical) return;
-    pair = lid / p.ndvb;
-    dv0 = (lid % p.ndvb) * DVB;
-  }
-  const int n = pair / H, h = pair % H;
-  int64_t bos, len;
-  int first;
-  if (p.cu) {
-    bos = cu_steps(p, n);
-    len = cu_steps(p, n + 1) - bos;
-    first = p.seq_first[n];
-  } else {
-    bos = (int64_t)n * p.T;
-    len = p.T;
-    first = n * p.cps;
-  }
-  const int nch = (int)((len + CH - 1) / CH);
-  // state slot: row n of S0 / S_T, or state_idx[n] of a pool (outside the pool: start from
-  // zero and store no final state)
-  int64_t srow = n;
-  bool has_row = true;
-  if (p.sidx) {
-    const int32_t sl = p.sidx[n];
-    has_row = sl >= 0 && sl < p.nslots;
-    srow = sl;
-  }
-  const int64_t snap_base = !p.snap ? 0 : p.cu ? (int64_t)p.snap_first[n] : (int64_t)n * (p.T / (p.snap_chunks * CH));
-  const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
-  const int DV = p.DV;
-  const InT* vp = static_cast<const InT*>(p.v);
-
-  // ---- state: fp32 master in registers (this wave's key-channel tiles), split copy in LDS
-  f32x4 Sm[NRT][NCT];
-#pragma unroll
-  for (int m = 0; m < NRT; ++m) {
-    const int rt = w + 4 * m;
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (rt < DK / 16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ch = 16 * rt + 4 * g + i;
-          if (p.S0 && has_row && ch < DKR) x[i] = p.S0[((srow * H + h) * DKR + ch) * DV + dv0 + 16 * ct + r];
-        }
-        sm.S.put4(16 * ct + r, 16 * rt + 4 * g, x);
-      }
-      Sm[m][ct] = x;
-    }
-  }
-
-  // ---- operands of a chunk, in registers. Two sets alternate: while chunk c is computed
-  // from one, the loads of chunk c + 1 stream into the other, so the load path works in
-  // parallel with the MFMAs (past the last chunk the last record is reloaded and unused).
-  // v and the write gate move as row segments: lane l holds token 16w + l/4 of the wave's
-  // block, value columns (l % 4) * E .. + E - 1 of the block, with 16-byte accesses.
-  constexpr int E = DVB / 4;
-  typedef InT RowV __attribute__((ext_vector_type(E)));
-  typedef float RowF __attribute__((ext_vector_type(E)));
-  using WRow = typename std::conditional<VEC, RowF, float>::type;
-  const int lr = l >> 2, lc = (l & 3) * E;
-  struct Ops {
-    Frag fU[KS], fQ[KS], fT[2], fP[2], fK[NRT][2];
-    f32x4 gC[NRT];
-    RowV pv;
-    WRow pw;
-  };
-  auto rec_ptr = [&](int c) -> __amdgpu_buffer_rsrc_t {
-    const int cc = c < nch ? c : nch - 1;
-    return rec_rsrc(p.rec + ((int64_t)h * p.slots + first + cc) * p.rec_size, p.rec_size);
-  };
-  const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, as a uniform value
-  auto load_uq = [&](Ops& op, __amdgpu_buffer_rsrc_t rc, int ks) {
-    op.fU[ks] = ld_frag<Frag>(rc, R::UT, wu * KS + ks, l);
-    op.fQ[ks] = ld_frag<Frag>(rc, R::QT, wu * KS + ks, l);
-  };
-  // T and P rows of block w are zero past token 16w + 15: only (w + 2) / 2 steps are loaded
-  auto load_tp = [&](Ops& op, __amdgpu_buffer_rsrc_t rc) {
-    op.fT[0] = ld_frag<Frag>(rc, R::TT, wu * 2, l);
-    op.fP[0] = ld_frag<Frag>(rc, R::PP, wu * 2, l);
-    if (w >= 2) {
-      op.fT[1] = ld_frag<Frag>(rc, R::TT, wu * 2 + 1, l);
-      op.fP[1] = ld_frag<Frag>(rc, R::PP, wu * 2 + 1, l);
-    }
-  };
-  auto load_k = [&](Ops& op, __amdgpu_buffer_rsrc_t rc, int m) {
-    const int rt = wu + 4 * m < DK / 16 ? wu + 4 * m : 0;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) op.fK[m][st] = ld_frag<Frag>(rc, R::KB, rt * 2 + st, l);
-    const u32x4 gc = __builtin_amdgcn_raw_buffer_load_b128(rc, 16 * g, R::GC + 64 * rt, 0);
-    op.gC[m] = *reinterpret_cast<const f32x4*>(&gc);
-  };
-  auto load_vw = [&](Ops& op, int c) {
-    const int cc = c < nch ? c : nch - 1;
-    const int64_t last = bos + len - 1;
-    int64_t tv = bos + (int64_t)cc * CH + 16 * w + lr;
-    tv = tv > last ? last : tv;
-    const int64_t thv = step_row(p, tv, h);
-    op.pv = *reinterpret_cast<const RowV*>(vp + thv * DV + dv0 + lc);
-    if constexpr (VEC) op.pw = *reinterpret_cast<const RowF*>(p.write + thv * DV + dv0 + lc);
-    else op.pw = p.write[thv];
-  };
-  // Same issue order as the loads spread over a chunk below (v and write gate first), so
-  // that the waits at the top of the chunk loop, which serve both the first chunk and the
-  // later ones, count the same loads in flight on both paths into the loop.
-  auto load_ops = [&](Ops& op, int c) {
-    const __amdgpu_buffer_rsrc_t rc = rec_ptr(c);
-    load_vw(op, c);
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) load_uq(op, rc, ks);
-    load_tp(op, rc);
-#pragma unroll
-    for (int m = 0; m < NRT; ++m) load_k(op, rc, m);
-  };
-
-  // this workgroup's block of the fp32 state (key rows x DVB value columns) to a
-  // [d_k, d_v] state at `dst`
-  auto store_state = [&](float* dst) {
-#pragma unroll
-    for (int m = 0; m < NRT; ++m) {
-      const int rt = w + 4 * m;
-      if (rt < DK / 16) {
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ch = 16 * rt + 4 * g + i;
-            if (ch < DKR) dst[(int64_t)ch * DV + dv0 + 16 * ct + r] = Sm[m][ct][i];
-          }
-        }
-      }
-    }
-  };
-
-  auto chunk = [&](int c, Ops& cur, Ops& nxt) {
-    const int64_t c0 = (int64_t)c * CH;
-    // write values m = w . v (zero past the sequence end), row layout -> LDS -> rows 4g+i of
-    // the accumulator layout
-    {
-      const bool vi = c0 + 16 * w + lr < len;
-      auto put_m = [&](auto gate) {
-#pragma unroll
-        for (int j4 = 0; j4 < E / 4; ++j4) {
-          f32x4 x;
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            float wg;
-            if constexpr (VEC) wg = cur.pw[4 * j4 + u];
-            else wg = cur.pw;
-            x[u] = vi ? gate(wg) * (float)cur.pv[4 * j4 + u] : 0.f;
-          }
-          store4(&sm.X[w][lr][lc + 4 * j4], x);
-        }
-      };
-      if (p.g_act) put_m([&](float z) { return prep_gate(z, p); });  // fused gate activation
-      else put_m([](float z) { return z; });
-    }
-    wave_lds_sync();
-    float mv[NCT][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) mv[ct][i] = sm.X[w][4 * g + i][16 * ct + r];
-    }
-    // the next chunk's operands stream into `nxt` in small groups placed between the
-    // MFMA groups below, so the load path and the matrix cores work at the same time
-    const __amdgpu_buffer_rsrc_t rn = rec_ptr(c + 1);
-    load_vw(nxt, c + 1);
-
-    // ================= X = Utilde S0, Y = Qtilde S0, R = M - X   (block row w)
-    f32x4 accY[NCT];
-    {
-      f32x4 accX[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) { accX[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; accY[ct] = accX[ct]; }
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        load_uq(nxt, rn, ks);
-#pragma unroll
-        for (int ct = 0; ct < NCT; ++ct) {
-          const Frag B = sm.S.get8(16 * ct + r, 32 * ks + 8 * g);
-          Pol::mma(accX[ct], cur.fU[ks], B);
-          Pol::mma(accY[ct], cur.fQ[ks], B);
-        }
-        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);        // 4 global loads
-        __builtin_amdgcn_sched_group_barrier(0x008, 6 * NCT, 0);  // then this slice's MFMAs
-      }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        f32x4 rv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) rv[i] = mv[ct][i] - accX[ct][i];
-        sm.R.put4(16 * ct + r, 16 * w + 4 * g, rv);
-      }
-    }
-    __syncthreads();
-
-    // ================= delta = T R   (block row w)
-    const int nst = (w + 2) / 2;
-    load_tp(nxt, rn);
-    {
-      f32x4 accD[NCT];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) accD[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (st < nst) {
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Pol::mma(accD[ct], cur.fT[st], sm.R.get8(16 * ct + r, 32 * st + 8 * g));
-        }
-      }
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) sm.D.put4(16 * ct + r, 16 * w + 4 * g, accD[ct]);
-    }
-    __syncthreads();
-
-    // ================= O = Y + P delta, and S <- Diag(Gamma_C) S0 + Kbar^T delta
-    {
-      Frag DF[NCT][2];
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int st = 0; st < 2; ++st) DF[ct][st] = sm.D.get8(16 * ct + r, 32 * st + 8 * g);
-      }
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (st < nst) {
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Pol::mma(accY[ct], cur.fP[st], DF[ct][st]);
-        }
-      }
-      // the next chunk's Kbar and Gamma_C loads
-#pragma unroll
-      for (int m = 0; m < NRT; ++m) load_k(nxt, rn, m);
-      // S <- Diag(Gamma_C) S0 + Kbar^T delta (the sequential chain) issued first ...
-      f32x4 accS[NRT][NCT];
-#pragma unroll
-      for (int m = 0; m < NRT; ++m) {
-        const int rt = w + 4 * m;
-        if (rt < DK / 16) {
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) accS[m][ct][i] = cur.gC[m][i] * Sm[m][ct][i];
-#pragma unroll
-            for (int st = 0; st < 2; ++st) Pol::mma(accS[m][ct], cur.fK[m][st], DF[ct][st]);
-          }
-        }
-      }
-      // ... and O written while those MFMAs run: accumulator layout -> LDS -> row segments
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sm.X[w][4 * g + i][16 * ct + r] = accY[ct][i];
-      }
-      wave_lds_sync();
-      {
-        const int64_t rw = c0 + 16 * w + lr;
-        const int lastm = (1 << p.lgnh) - 1;
-        if (p.o && rw < len && ((bos + rw) & lastm) == lastm) {
-          // lane (row, q) stores columns 16 j + 4 q .. + 3: each store of the wave covers 64
-          // contiguous bytes of every row it touches
-          float* orow = p.o + tok_row(p, bos + rw, h) * DV + dv0 + 4 * (l & 3);
-#pragma unroll
-          for (int j4 = 0; j4 < E / 4; ++j4)
-            __builtin_nontemporal_store(*reinterpret_cast<const f32x4*>(&sm.X[w][lr][16 * j4 + 4 * (l & 3)]),
-                                        reinterpret_cast<f32x4*>(orow + 16 * j4));
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < NRT; ++m) {
-        const int rt = w + 4 * m;
-        if (rt < DK / 16) {
-#pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) {
-            Sm[m][ct] = accS[m][ct];
-            sm.S.put4(16 * ct + r, 16 * rt + 4 * g, accS[m][ct]);
-          }
-        }
-      }
-    }
-    // snapshot: the state after (c + 1) * 64 tokens, when that is a multiple of the stride
-    // and still inside the sequence
-    if (p.snap && (c + 1) % p.snap_chunks == 0 && (int64_t)(c + 1) * CH <= len)
-      store_state(p.snap + ((snap_base + (c + 1) / p.snap_chunks - 1) * H + h) * DKR * DV);
-    __syncthreads();
-  };
-
-  Ops opA, opB;
-  if (nch > 0) load_ops(opA, 0);
-  __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
-    chunk(c, opA, opB);
-    if (c + 1 < nch) chunk(c + 1, opB, opA);
-  }
-
-  // ---- final state out
-  if (p.S && has_row) store_state(p.S + (srow * H + h) * DKR * DV);
-}
-
 // ============================================================================ host
 static int64_t rec_size_for(int dk) {
   switch (dk) {
@@ -1032,7 +605,7 @@ PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int
   return pl;
 }
 
-template <int DKR, int DVB, typename InT, bool VEC>
+template <int DKR, typename InT, bool VEC>
 static hipError_t launch_t(const Params& p, const PrefillPlan& pl, hipStream_t s) {
   const bool prep = p.prep_l2 || p.a_bf16 || p.a_act || p.g_act;
   if (p.cu) {
@@ -1061,21 +634,13 @@ static hipError_t launch_t(const Params& p, const PrefillPlan& pl, hipStream_t s
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((chunk_state_kernel<DKR, DVB, InT, VEC>), dim3((unsigned)pl.workgroups), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
-template <int DKR, int DVB>
-static hipError_t launch_gate(const Params& p, const PrefillPlan& pl, bool bf16, bool vec, hipStream_t s) {
-  if (bf16) return vec ? launch_t<DKR, DVB, __bf16, true>(p, pl, s) : launch_t<DKR, DVB, __bf16, false>(p, pl, s);
-  return vec ? launch_t<DKR, DVB, float, true>(p, pl, s) : launch_t<DKR, DVB, float, false>(p, pl, s);
+  return launch_state_pass(p, pl.workgroups, DKR, pl.dv_block, std::is_same<InT, __bf16>::value, VEC, s);
 }
 
 template <int DKR>
-static hipError_t launch_dvb(const Params& p, const PrefillPlan& pl, bool bf16, bool vec, hipStream_t s) {
-  if (pl.dv_block == 64) return launch_gate<DKR, 64>(p, pl, bf16, vec, s);
-  if (pl.dv_block == 32) return launch_gate<DKR, 32>(p, pl, bf16, vec, s);
-  return launch_gate<DKR, 16>(p, pl, bf16, vec, s);
+static hipError_t launch_dk(const Params& p, const PrefillPlan& pl, bool bf16, bool vec, hipStream_t s) {
+  if (bf16) return vec ? launch_t<DKR, __bf16, true>(p, pl, s) : launch_t<DKR, __bf16, false>(p, pl, s);
+  return vec ? launch_t<DKR, float, true>(p, pl, s) : launch_t<DKR, float, false>(p, pl, s);
 }
 
 int32_t* prefill_snap_first(void* ws, const PrefillPlan& pl, int64_t heads, int64_t nseq) {
@@ -1099,10 +664,10 @@ hipError_t launch_prefill(Params p, const PrefillPlan& pl, void* ws, int dk, boo
     p.seq_order = p.snap_first + p.nseq;
   }
   switch (dk) {
-    case 16: return launch_dvb<16>(p, pl, bf16, vec, s);
-    case 32: return launch_dvb<32>(p, pl, bf16, vec, s);
-    case 64: return launch_dvb<64>(p, pl, bf16, vec, s);
-    case 128: return launch_dvb<128>(p, pl, bf16, vec, s);
+    case 16: return launch_dk<16>(p, pl, bf16, vec, s);
+    case 32: return launch_dk<32>(p, pl, bf16, vec, s);
+    case 64: return launch_dk<64>(p, pl, bf16, vec, s);
+    case 128: return launch_dk<128>(p, pl, bf16, vec, s);
   }
   return hipErrorInvalidValue;
 }

@@ -15,7 +15,7 @@ import bench  # noqa: E402
 def _tree(tmp_path):
     d = tmp_path / "delta_rule_linear_chunked_amd" / "csrc"
     d.mkdir(parents=True)
-    for f in ("prefill.hip", "common.hpp"):
+    for f in bench.PREFILL_SOURCES:
         shutil.copy(os.path.join(ROOT, "delta_rule_linear_chunked_amd", "csrc", f), d / f)
     return d
 
@@ -25,9 +25,10 @@ def test_digest_ignores_comments_and_sees_code(tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
     base = bench.kernel_source_digest()
     src = (d / "prefill.hip").read_text()
+    assert "constexpr int LDT = 68;" in src
     (d / "prefill.hip").write_text("// a new comment line\n" + src.replace("\n", "\n   ", 3) + "\n/* trailing\n block */\n")
     assert bench.kernel_source_digest() == base
-    (d / "prefill.hip").write_text(src.replace("constexpr int CH = 64;", "constexpr int CH = 32;"))
+    (d / "prefill.hip").write_text(src.replace("constexpr int LDT = 68;", "constexpr int LDT = 72;"))
     assert bench.kernel_source_digest() != base
 
 
