@@ -58,9 +58,10 @@ PREFILL_SOURCES = ("prefill.hip", "prefill_state.hip", "prefill.hpp", "common.hp
 
 
 def kernel_source_digest():
-    """sha256 of the prefill kernel's sources with comments and whitespace removed: a stored
-    traffic measurement is used only while it matches the code that is being timed (an edit
-    of a comment leaves it valid, any change of code does not)."""
+    """sha256 of the prefill kernel's sources with comments and whitespace removed, and of their
+    per-file compiler options: a stored traffic measurement is used only while it matches the
+    code that is being timed (an edit of a comment leaves it valid, any change of code or of
+    its build options does not)."""
     import hashlib
     import re
     h = hashlib.sha256()
@@ -70,6 +71,13 @@ def kernel_source_digest():
         src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)  # block comments
         src = re.sub(r"//[^\n]*", " ", src)                # line comments
         h.update(" ".join(src.split()).encode())
+    # the per-file compiler options change the kernels as much as their sources do
+    import importlib.util
+    spec = importlib.util.spec_from_file_location(
+        "_dr_build", os.path.join(os.path.dirname(os.path.abspath(__file__)), "delta_rule_linear_chunked_amd", "_build.py"))
+    build = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(build)
+    h.update(repr(sorted((f, build.FILE_FLAGS.get(f, [])) for f in PREFILL_SOURCES)).encode())
     return h.hexdigest()
 
 

@@ -38,11 +38,13 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-# The prefill's state pass and the backward walk are bound by latency and issue; the backend's
-# ILP-first machine scheduler runs them a few percent faster with identical results (the
-# preparation and decode kernels measured slower or equal with it, so they keep the default).
+# Backend options per compilation unit, each measured on its kernels (results identical bit for
+# bit): the ILP-first machine scheduler speeds up the latency-bound prefill state pass and
+# backward walk but slows the preparation and decode kernels; MFMA accumulators in
+# architectural VGPRs (rather than AGPRs) speed up both prefill passes.
 _ILP = ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]
-FILE_FLAGS = {"prefill_state.hip": _ILP, "backward.hip": _ILP}
+_MFMA_VGPR = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+FILE_FLAGS = {"prefill.hip": _MFMA_VGPR, "prefill_state.hip": _ILP + _MFMA_VGPR, "backward.hip": _ILP}
 
 
 def _compile(src: str) -> str:
