@@ -304,10 +304,33 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         bms = e0.elapsed_time(e1) / bsteps
+        # the same gradients given the forward's checkpoints (a training step's forward taken with
+        # snapshot_every = 64): the call then skips its own forward pass
+        ckpts = [torch.empty((B * (T // 64), H, D, D), dtype=torch.float32, device=dev) for _ in sets]
+        for s, c in zip(sets, ckpts):
+            drl.dr_chunk_fwd_ex(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "kda", s["S0"], None, o, S_T,
+                                snapshots=c, snapshot_every=64)
+
+        def cstep(i):
+            s = sets[i % 2]
+            drl.dr_chunk_bwd(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "kda", s["S0"], None, gdO, gdS,
+                             grads["dq"], grads["dk"], grads["dv"], grads["dalpha"], grads["derase"], None, grads["dS0"],
+                             checkpoints=ckpts[i % 2])
+
+        for i in range(2):
+            cstep(i)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(bsteps):
+            cstep(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / bsteps
         bwd = {"workload": "gradients of the KDA prefill (dq, dk, dv, dalpha, dbeta, dS0) for random dO and dS_T",
                "ms_per_step": bms, "tokens_per_s": tokens / (bms * 1e-3), "steps": bsteps,
-               "vs_forward": bms / ms_step}
-        del gdO, gdS, grads
+               "vs_forward": bms / ms_step,
+               "ms_per_step_given_checkpoints": cms}
+        del gdO, gdS, grads, ckpts
 
     # two KDA transitions per token (PRODUCT2) on the same shape: 4 x 4096 tokens, 2 x 4096 steps
     prod = None

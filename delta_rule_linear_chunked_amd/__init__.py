@@ -99,6 +99,9 @@ def load_library(path: Optional[str] = None):
     lib.dr_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                                  ctypes.POINTER(_Dims), vp]
     lib.dr_chunk_bwd.restype = ip
+    lib.dr_chunk_bwd_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
+                                    ctypes.POINTER(_Dims), vp]
+    lib.dr_chunk_bwd_ex.restype = ip
     lib.dr_status_string.argtypes = [ip]
     lib.dr_status_string.restype = ctypes.c_char_p
     lib.dr_last_error.argtypes = []
@@ -305,9 +308,11 @@ def decode_step(q, k, v, alpha, erase, write, variant: str, S, state_idx=None, p
 
 
 def dr_chunk_bwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, dO, dS_T,
-                 dq, dk, dv, dalpha, derase, dwrite, dS0) -> None:
+                 dq, dk, dv, dalpha, derase, dwrite, dS0, checkpoints=None) -> None:
     """Gradients of ``dr_chunk_fwd`` into caller-provided fp32 tensors shaped like the inputs
-    (dwrite None for KDA / CKDA, dS_T / dS0 optional)."""
+    (dwrite None for KDA / CKDA, dS_T / dS0 optional). ``checkpoints``: the snapshots of a
+    ``chunk_fwd`` on the same inputs with ``snapshot_every`` 64 (32 for product2); with them the
+    call skips its own forward pass (``dr_chunk_bwd_ex``)."""
     lib = load_library()
     B, T, H, dk_ = q.shape
     dv_ = v.shape[-1]
@@ -338,18 +343,26 @@ def dr_chunk_bwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, dO,
                            (dv, "dv", (B, T, H) + nt + (dv_,)), (dalpha, "dalpha", (B, T, H, dk_)),
                            (derase, "derase", es)):
         _need(t, name, shape, torch.float32, dev)
+    if checkpoints is not None:
+        # rows: sum over the sequences of floor(len / 64) (32 for product2); for packed sequences
+        # that needs the lengths on the host, so only the row shape is checked there
+        every = 32 if variant == "product2" else 64
+        rows = B * (T // every) if cu_seqlens is None else checkpoints.shape[0]
+        _need(checkpoints, "checkpoints", (rows, H, dk_, dv_), torch.float32, dev)
     d = _Dims(B, T, H, dk_, dv_, N, _DT[q.dtype], 0)
     with torch.cuda.device(dev):
-        st = lib.dr_chunk_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write), VARIANTS[variant],
-                              _ptr(S0), _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv),
-                              _ptr(dalpha), _ptr(derase), _ptr(dwrite), _ptr(dS0), ctypes.byref(d), _stream(dev))
+        st = lib.dr_chunk_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write), VARIANTS[variant],
+                                 _ptr(S0), _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(dalpha), _ptr(derase), _ptr(dwrite), _ptr(dS0), _ptr(checkpoints),
+                                 ctypes.byref(d), _stream(dev))
     _check(lib, st, "dr_chunk_bwd")
 
 
 def chunk_bwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, cu_seqlens=None, dO=None,
-              dS_T=None, need_dS0: bool = True):
+              dS_T=None, need_dS0: bool = True, checkpoints=None):
     """Allocate the gradients and run ``dr_chunk_bwd``. Returns a dict with dq, dk, dv, dalpha,
-    derase, dwrite (None for KDA / CKDA) and dS0 (None unless ``need_dS0``)."""
+    derase, dwrite (None for KDA / CKDA) and dS0 (None unless ``need_dS0``). ``checkpoints`` as
+    for ``dr_chunk_bwd``."""
     f = lambda x: torch.empty(x.shape, dtype=torch.float32, device=q.device)
     N = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
     g = dict(dq=f(q), dk=f(k), dv=f(v), dalpha=f(alpha), derase=f(erase),
@@ -357,5 +370,5 @@ def chunk_bwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, 
              dS0=torch.empty((N, q.shape[2], q.shape[3], v.shape[-1]), dtype=torch.float32, device=q.device)
              if need_dS0 else None)
     dr_chunk_bwd(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, dO, dS_T, g["dq"], g["dk"], g["dv"],
-                 g["dalpha"], g["derase"], g["dwrite"], g["dS0"])
+                 g["dalpha"], g["derase"], g["dwrite"], g["dS0"], checkpoints)
     return g

@@ -296,6 +296,16 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
                  const float* dO, const float* dS_T,
                  float* dq, float* dk, float* dv, float* dalpha, float* derase, float* dwrite,
                  float* dS0, const dr_dims* dims, hipStream_t stream) {
+  return dr_chunk_bwd_ex(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, dO, dS_T, dq, dk, dv, dalpha,
+                         derase, dwrite, dS0, nullptr, dims, stream);
+}
+
+int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* alpha,
+                    const float* erase, const float* write, int variant,
+                    const float* S0, const int32_t* cu_seqlens,
+                    const float* dO, const float* dS_T,
+                    float* dq, float* dk, float* dv, float* dalpha, float* derase, float* dwrite,
+                    float* dS0, const float* checkpoints, const dr_dims* dims, hipStream_t stream) {
   g_last_error.clear();
   bool vec = false;
   int st = prefill_checks(dims, variant, erase, write, cu_seqlens, &vec);
@@ -312,13 +322,15 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
     if (st) return st;
     if (has_write && dwrite == nullptr) return fail(DR_ERR_NULL, "dwrite is required for RDA / GDN-2");
   }
-  st = check_ptrs({}, {{S0, "S0"}, {dS_T, "dS_T"}, {dS0, "dS0"}, {cu_seqlens, "cu_seqlens"}, {dwrite, "dwrite"}});
+  st = check_ptrs({}, {{S0, "S0"}, {dS_T, "dS_T"}, {dS0, "dS0"}, {cu_seqlens, "cu_seqlens"}, {dwrite, "dwrite"},
+                       {checkpoints, "checkpoints"}});
   if (st) return st;
   if (dims->num_seqs == 0) return DR_OK;
   const int dkh = (int)dims->head_dim_k, dvh = (int)dims->head_dim_v;
   const int64_t H = dims->num_heads, pairs = dims->num_seqs * H;
 
-  // forward pass for the checkpoints: the state after every 64 steps, no output
+  // the states after every 64 steps: the caller's (a prefill's snapshots), or a forward pass
+  // with no output
   dr::Params p{};
   p.q = q; p.k = k; p.v = v; p.alpha = alpha;
   p.erase = erase;
@@ -342,8 +354,14 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
   const int64_t nsnap = cu_seqlens ? steps / 64 : dims->batch * ((dims->seqlen << lg) / 64);
   const int ndvb = dvh / dr::bwd_dv_block(dvh);
   const int64_t TH = steps * H;
-  const int64_t off_snap = round256(pl.workspace);
-  const int64_t off_part = off_snap + round256(nsnap * H * dkh * dvh * 4);
+  // with the caller's checkpoints only the packed plan's tables are needed, not the records
+  dr::PrefillPlan plw = pl;
+  if (checkpoints) {
+    plw.workspace -= pl.slots * H * pl.rec_size;
+    plw.rec_size = 0;
+  }
+  const int64_t off_snap = round256(plw.workspace);
+  const int64_t off_part = off_snap + (checkpoints ? 0 : round256(nsnap * H * dkh * dvh * 4));
   const int64_t off_parts = off_part + round256((int64_t)ndvb * TH * 4 * dkh * 4);
   const int64_t total = off_parts + round256((int64_t)ndvb * TH * 4);
   void* ws = nullptr;
@@ -352,9 +370,16 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
     return fail(DR_ERR_HIP, "backward workspace (%lld bytes) allocation failed: %s", (long long)total,
                 hipGetErrorString(e));
   unsigned char* wsb = static_cast<unsigned char*>(ws);
-  p.snap = nsnap > 0 ? reinterpret_cast<float*>(wsb + off_snap) : nullptr;
-  if (p.snap == nullptr) p.snap_chunks = 0;
-  e = dr::launch_prefill(p, pl, ws, dkh, dims->in_dtype == DR_BF16, vec, stream);
+  if (checkpoints) {
+    // read only here: the plan pass uses the pointer's presence to lay out the rows
+    p.snap = nsnap > 0 ? const_cast<float*>(checkpoints) : nullptr;
+    if (p.snap == nullptr) p.snap_chunks = 0;
+    e = dr::launch_plan_only(p, plw, ws, stream);
+  } else {
+    p.snap = nsnap > 0 ? reinterpret_cast<float*>(wsb + off_snap) : nullptr;
+    if (p.snap == nullptr) p.snap_chunks = 0;
+    e = dr::launch_prefill(p, pl, ws, dkh, dims->in_dtype == DR_BF16, vec, stream);
+  }
   if (e == hipSuccess) {
     dr::BwdParams b{};
     b.q = q; b.k = k; b.v = v; b.alpha = alpha;
@@ -363,7 +388,7 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
     b.S0 = S0; b.cu = cu_seqlens; b.dO = dO; b.dST = dS_T;
     b.dq = dq; b.dk = dk; b.dv = dv; b.dalpha = dalpha; b.derase = derase; b.dwrite = dwrite; b.dS0 = dS0;
     b.snap = p.snap;
-    b.snap_first = cu_seqlens ? dr::prefill_snap_first(ws, pl, H, dims->num_seqs) : nullptr;
+    b.snap_first = cu_seqlens ? dr::prefill_snap_first(ws, plw, H, dims->num_seqs) : nullptr;
     b.seq_order = cu_seqlens ? b.snap_first + dims->num_seqs : nullptr;  // written by the prefill's plan pass
     b.part = reinterpret_cast<float*>(wsb + off_part);
     b.parts = reinterpret_cast<float*>(wsb + off_parts);

@@ -34,8 +34,12 @@ hipError_t launch_prefill(Params p, const PrefillPlan& plan, void* ws, int dk, b
                           hipStream_t s);
 
 // Packed sequences: where the prefill's workspace keeps the first snapshot row of each sequence
-// (filled by the prefill when snapshots are taken).
+// (filled by the prefill when snapshots are taken), followed by the sequences' longest-first order.
 int32_t* prefill_snap_first(void* ws, const PrefillPlan& plan, int64_t heads, int64_t nseq);
+
+// Only the packed-sequence plan pass of a prefill (chunk slots, first snapshot rows, sequence
+// order) into `ws`; nothing for fixed-length sequences.
+hipError_t launch_plan_only(Params p, const PrefillPlan& plan, void* ws, hipStream_t s);
 
 // Backward: bwd_kernel over every (sequence, head, value block), then the reduction over the
 // blocks. p.snap must hold the forward states after every 64 tokens (the prefill's snapshots);

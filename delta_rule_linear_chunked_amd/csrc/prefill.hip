@@ -648,9 +648,8 @@ int32_t* prefill_snap_first(void* ws, const PrefillPlan& pl, int64_t heads, int6
          nseq + 1;
 }
 
-hipError_t launch_prefill(Params p, const PrefillPlan& pl, void* ws, int dk, bool bf16, bool vec,
-                          hipStream_t s) {
-  if (pl.workgroups == 0) return hipSuccess;
+// Workspace pointers of a call: the records, then (packed sequences) the plan's tables.
+static void set_workspace(Params& p, const PrefillPlan& pl, void* ws) {
   p.rec = static_cast<unsigned char*>(ws);
   p.rec_size = pl.rec_size;
   p.slots = (int32_t)pl.slots;
@@ -663,6 +662,19 @@ hipError_t launch_prefill(Params p, const PrefillPlan& pl, void* ws, int dk, boo
     p.snap_first = prefill_snap_first(ws, pl, p.H, p.nseq);
     p.seq_order = p.snap_first + p.nseq;
   }
+}
+
+hipError_t launch_plan_only(Params p, const PrefillPlan& pl, void* ws, hipStream_t s) {
+  if (!p.cu || pl.workgroups == 0) return hipSuccess;
+  set_workspace(p, pl, ws);
+  hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill(Params p, const PrefillPlan& pl, void* ws, int dk, bool bf16, bool vec,
+                          hipStream_t s) {
+  if (pl.workgroups == 0) return hipSuccess;
+  set_workspace(p, pl, ws);
   switch (dk) {
     case 16: return launch_dk<16>(p, pl, bf16, vec, s);
     case 32: return launch_dk<32>(p, pl, bf16, vec, s);

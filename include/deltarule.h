@@ -257,6 +257,22 @@ int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha
                  float* dq, float* dk, float* dv, float* dalpha, float* derase, float* dwrite,
                  float* dS0, const dr_dims* dims, hipStream_t stream);
 
+/*
+ * dr_chunk_bwd with the forward's checkpoints supplied by the caller, for training steps that
+ * ran the forward anyway (the course page's section 3: training keeps checkpoints of the
+ * forward). `checkpoints` is the `snapshots` buffer of a dr_chunk_fwd_ex call on the same
+ * inputs (same S0 and cu_seqlens, no fused preparation) with snapshot_every = 64, or 32 for
+ * DR_PRODUCT2: float32 [sum_n floor(len_n / snapshot_every), H, d_k, d_v]. With it the call
+ * skips its own forward pass and only reads the checkpoints; NULL is dr_chunk_bwd. A buffer that
+ * does not hold those states gives undefined gradients (the library cannot check its contents).
+ */
+int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* alpha,
+                    const float* erase, const float* write, int variant,
+                    const float* S0, const int32_t* cu_seqlens,
+                    const float* dO, const float* dS_T,
+                    float* dq, float* dk, float* dv, float* dalpha, float* derase, float* dwrite,
+                    float* dS0, const float* checkpoints, const dr_dims* dims, hipStream_t stream);
+
 /* Static description of a status code. Never NULL. */
 const char* dr_status_string(int status);
 

@@ -161,3 +161,11 @@ def test_decode_takes_no_snapshots(lib):
     st = lib.dr_decode_step_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, FAKE, FAKE, ctypes.byref(d),
                                ctypes.byref(o), None)
     assert st == -2, lib.dr_last_error()
+
+
+def test_backward_checkpoints_are_checked(lib):
+    # a misaligned checkpoint buffer is rejected before anything runs
+    st = lib.dr_chunk_bwd_ex(FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None, None, FAKE, None,
+                             FAKE, FAKE, FAKE, FAKE, FAKE, None, None, MISALIGNED, ctypes.byref(dims()), None)
+    assert st == -4, lib.dr_last_error()
+    assert "checkpoints" in lib.dr_last_error().decode()

@@ -208,3 +208,17 @@ def test_backward_full_size_sampled_pair():
                                 dS_T=dS[n:n + 1, h:h + 1], S0=wl.S0[n:n + 1, h:h + 1])
     pairs = [(g[a][sl], ref[b]) for a, b in NAMES if a != "dS0"] + [(g["dS0"][n, h], ref["dS0"][0, 0])]
     _check("backward full size", pairs, TOL["bf16"])
+
+
+def test_backward_given_checkpoints():
+    # the two-transition variant's checkpoints are the forward's snapshots every 32 tokens
+    wl = synth.make_product("ckda", 2, 100, 2, 64, 64, in_dtype="bf16", seed=seed_of("p2 ckpt"))
+    a = _dev(wl)
+    _, _, snaps = drl.chunk_fwd(**a, snapshot_every=32)
+    rng = np.random.default_rng(3)
+    dO = to_dev(rng.standard_normal(wl.q.shape[:3] + (wl.v.shape[-1],)).astype(np.float32))
+    g0 = drl.chunk_bwd(**a, dO=dO)
+    g1 = drl.chunk_bwd(**a, dO=dO, checkpoints=snaps)
+    torch.cuda.synchronize()
+    for name, t in g0.items():
+        assert (t is None and g1[name] is None) or torch.equal(t, g1[name]), name
