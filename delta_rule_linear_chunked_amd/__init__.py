@@ -219,7 +219,8 @@ def dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, 
         _need(S_T, "S_T", (rows, H, dk, dv), torch.float32, dev)
     if snapshots is not None:
         _need(snapshots, "snapshots", (snapshots.shape[0], H, dk, dv), torch.float32, dev)
-    _need(o, "o", (B, T, H, dv), torch.float32, dev)
+    if o is not None:  # None: final states / snapshots only
+        _need(o, "o", (B, T, H, dv), torch.float32, dev)
     d = _Dims(B, T, H, dk, dv, N, _DT[q.dtype], 0)
     opts = _opts(state_idx, rows, snapshots, snapshot_every, prep, alpha)
     with torch.cuda.device(dev):  # the library launches on the current device
@@ -274,14 +275,14 @@ def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_id
 
 def chunk_fwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, cu_seqlens=None,
               output_final_state: bool = True, state_idx=None, snapshot_every: Optional[int] = None,
-              prep=None):
+              prep=None, output: bool = True):
     """Allocate o (and S_T) and run the prefill. Returns (o, S_T or None), plus the snapshot
     tensor when ``snapshot_every`` is given. With ``state_idx``, S0 is a pool of states that
-    is updated in place (and returned as S_T)."""
+    is updated in place (and returned as S_T). ``output=False``: no o (None), states only."""
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     N = B if cu_seqlens is None else cu_seqlens.shape[0] - 1
-    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device)
+    o = torch.empty((B, T, H, dv), dtype=torch.float32, device=q.device) if output else None
     if state_idx is not None:
         if S0 is None:
             raise ValueError("state_idx needs the pool of states as S0")

@@ -234,8 +234,8 @@ int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alp
   if (st) return st;
   const int64_t tokens = dims->batch * dims->seqlen;
   if (tokens > 0) {
-    st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {alpha, "alpha"}, {erase, "erase"}, {o, "o"}},
-                    {{write, "write"}});
+    st = check_ptrs({{q, "q"}, {k, "k"}, {v, "v"}, {alpha, "alpha"}, {erase, "erase"}},
+                    {{write, "write"}, {o, "o"}});
     if (st) return st;
   }
   st = check_ptrs({}, {{S0, "S0"}, {S_T, "S_T"}, {cu_seqlens, "cu_seqlens"}});

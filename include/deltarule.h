@@ -118,7 +118,8 @@ typedef struct dr_dims {
  *              sequence starts from its own S0[n] and no state crosses a boundary
  *              (the same course page, section 3: document reset). Without it,
  *              sequence n is batch row n.
- *   o          [B, T, H, d_v] float32 output (written)
+ *   o          [B, T, H, d_v] float32 output (written), or NULL when only the final states
+ *              (or snapshots) are wanted
  *   S_T        [N, H, d_k, d_v] float32 final states, or NULL to skip; may alias S0
  *              for an in-place update.
  * o must not alias any input. Results do not depend on how the library chunks

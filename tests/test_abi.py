@@ -73,7 +73,7 @@ def chunk(lib, d, variant=0, write=None, S0=None, cu=None, q=FAKE, o=FAKE):
     (dict(d=dims(B=2, N=3)), -2),                    # N must equal B without cu_seqlens
     (dict(d=dims(B=2, N=3), cu=FAKE), -2),           # packed needs B == 1
     (dict(d=dims(), q=None), -1),
-    (dict(d=dims(), o=None), -1),
+    (dict(d=dims(), o=MISALIGNED), -4),             # o is optional (states only), but aligned
     (dict(d=dims(), q=MISALIGNED), -4),
     (dict(d=dims(), S0=MISALIGNED), -4),
     # 2^27 sequences x 15 heads pass the 32-bit count checks, but the state pass would need

@@ -153,3 +153,19 @@ def test_bad_state_options_are_rejected():
     wl = synth.make_prefill("kda", 1, 200, 1, 16, 16, in_dtype="f32", seed=1)
     with pytest.raises(drl.DeltaRuleError):
         drl.chunk_fwd(**prefill_inputs(wl), snapshot_every=100)  # not a multiple of 64
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_states_only_prefill(packed):
+    # o = NULL: the final states and snapshots are those of the full call, nothing else is written
+    if packed:
+        wl = synth.make_prefill("gdn2", 1, 0, 2, 64, 64, in_dtype="bf16", seed=seed_of("states only", 1),
+                                lengths=[130, 0, 64, 7])
+    else:
+        wl = synth.make_prefill("kda", 2, 200, 2, 128, 128, in_dtype="bf16", seed=seed_of("states only", 0))
+    a = prefill_inputs(wl)
+    o, S_T, snaps = drl.chunk_fwd(**a, snapshot_every=64)
+    o2, S2, snaps2 = drl.chunk_fwd(**a, snapshot_every=64, output=False)
+    torch.cuda.synchronize()
+    assert o2 is None
+    assert torch.equal(S_T, S2) and torch.equal(snaps, snaps2)
