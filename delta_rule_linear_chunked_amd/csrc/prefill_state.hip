@@ -52,7 +52,9 @@ struct StateSmem {
   float X[NBLK][16][DVB + 4];  // per wave: m = w . v in, then O out, between row and accumulator layouts
 };
 
-template <int DKR, int DVB, typename InT, bool VEC>
+// OUT = false (no output requested): the Qtilde S0 and P delta products and the Qtilde / P loads
+// are left out, and only the states are produced.
+template <int DKR, int DVB, typename InT, bool VEC, bool OUT>
 __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
@@ -155,15 +157,15 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
   const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, as a uniform value
   auto load_uq = [&](Ops& op, __amdgpu_buffer_rsrc_t rc, int ks) {
     op.fU[ks] = ld_frag<Frag>(rc, R::UT, wu * KS + ks, l);
-    op.fQ[ks] = ld_frag<Frag>(rc, R::QT, wu * KS + ks, l);
+    if constexpr (OUT) op.fQ[ks] = ld_frag<Frag>(rc, R::QT, wu * KS + ks, l);
   };
   // T and P rows of block w are zero past token 16w + 15: only (w + 2) / 2 steps are loaded
   auto load_tp = [&](Ops& op, __amdgpu_buffer_rsrc_t rc) {
     op.fT[0] = ld_frag<Frag>(rc, R::TT, wu * 2, l);
-    op.fP[0] = ld_frag<Frag>(rc, R::PP, wu * 2, l);
+    if constexpr (OUT) op.fP[0] = ld_frag<Frag>(rc, R::PP, wu * 2, l);
     if (w >= 2) {
       op.fT[1] = ld_frag<Frag>(rc, R::TT, wu * 2 + 1, l);
-      op.fP[1] = ld_frag<Frag>(rc, R::PP, wu * 2 + 1, l);
+      if constexpr (OUT) op.fP[1] = ld_frag<Frag>(rc, R::PP, wu * 2 + 1, l);
     }
   };
   auto load_k = [&](Ops& op, __amdgpu_buffer_rsrc_t rc, int m) {
@@ -263,10 +265,10 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
         for (int ct = 0; ct < NCT; ++ct) {
           const Frag B = sm.S.get8(16 * ct + r, 32 * ks + 8 * g);
           Pol::mma(accX[ct], cur.fU[ks], B);
-          Pol::mma(accY[ct], cur.fQ[ks], B);
+          if constexpr (OUT) Pol::mma(accY[ct], cur.fQ[ks], B);
         }
-        __builtin_amdgcn_sched_group_barrier(0x020, 4, 0);        // 4 global loads
-        __builtin_amdgcn_sched_group_barrier(0x008, 6 * NCT, 0);  // then this slice's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x020, OUT ? 4 : 2, 0);          // the slice's global loads
+        __builtin_amdgcn_sched_group_barrier(0x008, (OUT ? 6 : 3) * NCT, 0);  // then its MFMAs
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -305,11 +307,13 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) DF[ct][st] = sm.D.get8(16 * ct + r, 32 * st + 8 * g);
       }
+      if constexpr (OUT) {
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        if (st < nst) {
+        for (int st = 0; st < 2; ++st) {
+          if (st < nst) {
 #pragma unroll
-          for (int ct = 0; ct < NCT; ++ct) Pol::mma(accY[ct], cur.fP[st], DF[ct][st]);
+            for (int ct = 0; ct < NCT; ++ct) Pol::mma(accY[ct], cur.fP[st], DF[ct][st]);
+          }
         }
       }
       // the next chunk's Kbar and Gamma_C loads
@@ -331,13 +335,13 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
         }
       }
       // ... and O written while those MFMAs run: accumulator layout -> LDS -> row segments
+      if constexpr (OUT) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
+        for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sm.X[w][4 * g + i][16 * ct + r] = accY[ct][i];
-      }
-      wave_lds_sync();
-      {
+          for (int i = 0; i < 4; ++i) sm.X[w][4 * g + i][16 * ct + r] = accY[ct][i];
+        }
+        wave_lds_sync();
         const int64_t rw = c0 + 16 * w + lr;
         const int lastm = (1 << p.lgnh) - 1;
         if (p.o && rw < len && ((bos + rw) & lastm) == lastm) {
@@ -384,7 +388,10 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 // ============================================================================ host
 template <int DKR, int DVB, typename InT, bool VEC>
 static hipError_t launch_state_t(const Params& p, int64_t workgroups, hipStream_t s) {
-  hipLaunchKernelGGL((chunk_state_kernel<DKR, DVB, InT, VEC>), dim3((unsigned)workgroups), dim3(256), 0, s, p);
+  if (p.o)
+    hipLaunchKernelGGL((chunk_state_kernel<DKR, DVB, InT, VEC, true>), dim3((unsigned)workgroups), dim3(256), 0, s, p);
+  else  // states (and snapshots) only
+    hipLaunchKernelGGL((chunk_state_kernel<DKR, DVB, InT, VEC, false>), dim3((unsigned)workgroups), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
