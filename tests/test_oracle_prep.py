@@ -55,6 +55,28 @@ def test_tanh_decay_limits_and_oddness():
     np.testing.assert_allclose(prep.alpha_from(-z, "tanh"), -prep.alpha_from(z, "tanh"), rtol=0, atol=0)
 
 
+@pytest.mark.parametrize("x,exact", [(2.0, 3 / 5), (3.0, 4 / 5), (5.0, 12 / 13), (9.0, 40 / 41),
+                                     (1.5, 5 / 13)])
+def test_tanh_decay_hand_values(x, exact):
+    # tanh z = (e^{2z} - 1) / (e^{2z} + 1); at z = ln x that is (x^2 - 1) / (x^2 + 1):
+    # tanh(ln 2) = 3/5, tanh(ln 3) = 4/5, tanh(ln 5) = 12/13, tanh(ln 9) = 40/41, tanh(ln 1.5) = 5/13
+    assert exact == pytest.approx((x * x - 1) / (x * x + 1), abs=1e-15)
+    assert prep.alpha_from(np.log(x), "tanh") == pytest.approx(exact, abs=2e-16)
+    assert prep.alpha_from(-np.log(x), "tanh") == pytest.approx(-exact, abs=2e-16)
+
+
+def test_tanh_decay_small_and_moderate_arguments():
+    # tanh z = z - z^3/3 + 2 z^5/15 - 17 z^7/315 + ... near zero, and 1 - tanh z =
+    # 2 e^{-2z} / (1 + e^{-2z}) exactly; a slightly rescaled argument (tanh(1.0001 z)) or a
+    # softsign fails both
+    z = np.array([1e-3, 1e-2, 3e-2])
+    series = z - z ** 3 / 3 + 2 * z ** 5 / 15 - 17 * z ** 7 / 315
+    np.testing.assert_allclose(prep.alpha_from(z, "tanh"), series, rtol=1e-13, atol=0)
+    z = np.array([0.5, 1.0, 2.0, 3.0])
+    e = np.exp(-2 * z)
+    np.testing.assert_allclose(1.0 - prep.alpha_from(z, "tanh"), 2 * e / (1 + e), rtol=1e-12, atol=0)
+
+
 def test_gate_scale_two_spans_zero_to_two():
     z = np.array([-np.inf, 0.0, np.inf])
     np.testing.assert_array_equal(prep.gate_from(z, "sigmoid", 2.0), [0.0, 1.0, 2.0])
