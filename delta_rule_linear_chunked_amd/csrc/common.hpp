@@ -20,7 +20,7 @@ struct Params {
   const float* erase;   // beta (KDA/CKDA), e (RDA) or b (GDN-2)
   const float* write;   // == erase for KDA/CKDA, w (RDA) or w (GDN-2)
   const float* S0;      // prefill initial states (may be null); decode: unused
-  const int32_t* cu;    // packed sequence offsets (may be null)
+  const int32_t* cu;    // packed sequence offsets (may be null); past the plan pass, its clamped copy
   float* o;
   float* S;             // prefill: final states (may be null); decode: state in/out
   int64_t T;            // tokens per batch row (prefill)
@@ -45,6 +45,8 @@ struct Params {
   int32_t snap_chunks;  // chunks between snapshots
   int32_t* snap_first;  // packed: first snapshot row of each sequence
   int32_t* seq_order;   // packed: sequences by decreasing chunk count (the state pass's order)
+  int32_t* cu_ok;       // packed: the plan pass's copy of the offsets, clamped to [0, tokens] and
+                        // non-decreasing (the later passes read their spans from it)
   // input preparation applied while loading (all zero: inputs are used as given)
   int32_t prep_l2;      // q and k are divided by their L2 norm over d_k
   int32_t a_bf16;       // alpha is stored as bfloat16
@@ -128,15 +130,34 @@ __device__ __forceinline__ void store4(float* p, const f32x4& a) { *reinterpret_
 // limits exactly: softplus(-inf) = 0 so the decay is 1, tanh(+-inf) = +-1, sigmoid(+inf) = 1,
 // sigmoid(-inf) = 0.
 constexpr float LOG2E = 1.4426950408889634f;
+// exp(-c softplus(z)) = 2^(-c sp), sp = softplus(z) log2(e) = max(z log2 e, 0) + log2(1 + 2^(-|z| log2 e)):
+// the exponent never overflows (the form 2^(-c log2(1 + 2^(z log2 e))) gave 0 for z above about 88
+// whatever c was, and NaN for c = 0), and z = -inf gives exactly 1.
+__device__ __forceinline__ float act_decay_softplus(float z, float c) {
+  const float zl = z * LOG2E;
+  const float sp = fmaxf(zl, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(zl)));
+  return __builtin_amdgcn_exp2f(-c * sp);
+}
+// tanh(z): the odd Taylor polynomial through z^11 for |z| < 1/4 (truncation below 3e-10 relative),
+// else sign(z) (1 - e) / (1 + e) with e = exp(-2 |z|) <= 0.61, where 1 - e has no cancellation;
+// +-inf give +-1. Both forms are evaluated and one selected, so a call stays one basic block.
+__device__ __forceinline__ float act_tanh(float z) {
+  const float az = fabsf(z);
+  const float z2 = z * z;
+  float s = -1382.f / 155925.f;
+  s = fmaf(s, z2, 62.f / 2835.f);
+  s = fmaf(s, z2, -17.f / 315.f);
+  s = fmaf(s, z2, 2.f / 15.f);
+  s = fmaf(s, z2, -1.f / 3.f);
+  const float poly = fmaf(s * z2, z, z);
+  const float e = __builtin_amdgcn_exp2f(-2.f * LOG2E * az);
+  const float big = copysignf((1.f - e) * __builtin_amdgcn_rcpf(1.f + e), z);
+  return az < 0.25f ? poly : big;
+}
 // Both decay forms are evaluated and one is selected, so a call site stays one basic block.
 __device__ __forceinline__ float prep_alpha(float z, const Params& p) {
-  // exp(-c softplus(z)) = 2^(-c log2(1 + 2^(z log2 e)))
-  const float t = __builtin_amdgcn_exp2f(z * LOG2E);
-  const float dec = __builtin_amdgcn_exp2f(-p.a_scale * __builtin_amdgcn_logf(1.f + t));
-  // tanh(z) = sign(z) (1 - e) / (1 + e) with e = exp(-2 |z|); z itself near 0
-  const float az = fabsf(z);
-  const float e = __builtin_amdgcn_exp2f(-2.f * LOG2E * az);
-  const float th = az < 0x1p-12f ? z : copysignf((1.f - e) * __builtin_amdgcn_rcpf(1.f + e), z);
+  const float dec = act_decay_softplus(z, p.a_scale);
+  const float th = act_tanh(z);
   return p.a_act == 1 ? dec : p.a_act == 2 ? th : z;
 }
 // One decay activation fixed at compile time (ACT 1: exp(-c softplus(z)), 2: tanh(z), 0: z),
@@ -144,12 +165,9 @@ __device__ __forceinline__ float prep_alpha(float z, const Params& p) {
 template <int ACT>
 __device__ __forceinline__ float prep_alpha_as(float z, float c) {
   if constexpr (ACT == 1) {
-    const float t = __builtin_amdgcn_exp2f(z * LOG2E);
-    return __builtin_amdgcn_exp2f(-c * __builtin_amdgcn_logf(1.f + t));
+    return act_decay_softplus(z, c);
   } else if constexpr (ACT == 2) {
-    const float az = fabsf(z);
-    const float e = __builtin_amdgcn_exp2f(-2.f * LOG2E * az);
-    return az < 0x1p-12f ? z : copysignf((1.f - e) * __builtin_amdgcn_rcpf(1.f + e), z);
+    return act_tanh(z);
   } else {
     return z;
   }

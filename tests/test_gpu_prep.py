@@ -126,3 +126,47 @@ def test_prepared_decode(variant):
         eo, es = oracle.rel_err(_np(o), o_ref), oracle.rel_err(_np(S), S_ref)
         print(f"[prep decode {variant} step {t}] err o={eo:.3e} S={es:.3e}", flush=True)
         assert eo <= 1e-4 and es <= 1e-4
+
+
+@pytest.mark.parametrize("act,scale", [("exp_neg_softplus", 0.01), ("exp_neg_softplus", 0.1),
+                                       ("exp_neg_softplus", 0.0), ("tanh", 1.0)])
+def test_extreme_and_small_preactivations(act, scale):
+    """Decay pre-activations spread from -1e3 to 1e3 (exp(-c softplus(z)) must follow exp(-c z) for
+    large z instead of collapsing to 0, and give exactly 1 for c = 0) and crowded near 0 (tanh's
+    small-argument range), in the prefill (fp32 and bf16 alpha) and the decode step."""
+    B, T, H, d = 1, 150, 2, 64
+    rng = np.random.default_rng(seed_of("extreme", act, scale))
+    q = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    k = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    v = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    mag = np.where(rng.random((B, T, H, d)) < 0.5, 10.0 ** rng.uniform(-4, 0, (B, T, H, d)),
+                   10.0 ** rng.uniform(0, 3, (B, T, H, d)))
+    za = (np.sign(rng.standard_normal((B, T, H, d))) * mag).astype(np.float32)
+    zb = rng.standard_normal((B, T, H)).astype(np.float32)
+    S0 = (rng.standard_normal((B, H, d, d)) / np.sqrt(d)).astype(np.float32)
+    kw = dict(l2norm_qk=True, alpha_act=act, alpha_scale=scale, gate_act="sigmoid", gate_scale=1.0)
+    variant = "ckda" if act == "tanh" else "kda"
+    for adt in ("f32", "bf16"):
+        za_d = to_dev(za, adt)
+        z_used = za_d.float().cpu().numpy()   # the values the kernel sees (bf16-rounded for bf16 alpha)
+        o, S_T = drl.chunk_fwd(to_dev(q), to_dev(k), to_dev(v), za_d, to_dev(zb), None, variant, to_dev(S0), prep=kw)
+        torch.cuda.synchronize()
+        qp, kp, ap, bp, _ = prep.prepare(q, k, z_used, zb, None, **kw)
+        assert np.all(np.isfinite(ap))
+        o_ref, S_ref = oracle.step_recurrence(qp, kp, v, ap, bp, None, variant, S0=S0)
+        eo, es = oracle.rel_err(_np(o), o_ref), oracle.rel_err(_np(S_T), S_ref)
+        print(f"[prep extreme {act} c={scale} alpha {adt}] err o={eo:.3e} S_T={es:.3e}", flush=True)
+        assert eo <= TOL["f32"] and es <= TOL["f32"], (eo, es)
+    # decode: one step per token of the first four
+    S = to_dev(S0[0])[None].contiguous()
+    S_ref = S0[0][None].astype(np.float64)
+    for t in range(4):
+        sl = lambda x: np.ascontiguousarray(x[:, t])  # noqa: E731
+        od = drl.decode_step(to_dev(sl(q)), to_dev(sl(k)), to_dev(sl(v)), to_dev(sl(za)), to_dev(sl(zb)), None,
+                             variant, S, prep=kw)
+        qp, kp, ap, bp, _ = prep.prepare(sl(q), sl(k), sl(za), sl(zb), None, **kw)
+        S_ref, od_ref = oracle.decode_step(S_ref, qp, kp, sl(v), ap, bp, None, variant)
+    torch.cuda.synchronize()
+    eo, es = oracle.rel_err(_np(od), od_ref), oracle.rel_err(_np(S), S_ref)
+    print(f"[prep extreme decode {act} c={scale}] err o={eo:.3e} S={es:.3e}", flush=True)
+    assert eo <= TOL["f32"] and es <= TOL["f32"], (eo, es)
