@@ -18,7 +18,8 @@ from typing import Optional
 import torch
 
 __all__ = ["dr_chunk_fwd", "dr_decode_step", "dr_chunk_fwd_ex", "dr_decode_step_ex", "dr_chunk_bwd",
-           "chunk_fwd", "decode_step", "chunk_bwd", "chunk_fwd_plan", "snapshot_count", "library_path",
+           "chunk_fwd", "decode_step", "chunk_bwd", "chunk_fwd_plan", "snapshot_count", "check_offsets",
+           "library_path",
            "load_library", "VARIANTS", "DeltaRuleError"]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -78,11 +79,12 @@ def library_path() -> str:
 
 
 def load_library(path: Optional[str] = None):
-    """Load libdeltarule.so once and declare its signatures."""
+    """Load libdeltarule.so once and declare its signatures. DELTARULE_LIBRARY in the environment
+    names another build of the same library (a sanitizer build of the host code, say)."""
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or _LIB_PATH
+    p = path or os.environ.get("DELTARULE_LIBRARY") or _LIB_PATH
     if not os.path.exists(p):
         raise DeltaRuleError(f"{p} is missing: build it with `python -m delta_rule_linear_chunked_amd._build`")
     lib = ctypes.CDLL(p)
@@ -170,6 +172,25 @@ def snapshot_count(lengths, every: int) -> int:
     return int(sum(int(n) // int(every) for n in lengths))
 
 
+def check_offsets(cu_seqlens, T: int):
+    """Copy ``cu_seqlens`` to the host (a synchronisation) and check that it starts at 0, never
+    decreases and ends at most at ``T``; returns the sequence lengths. Raises ValueError."""
+    cu = [int(x) for x in cu_seqlens.tolist()]
+    if not cu or cu[0] != 0:
+        raise ValueError(f"cu_seqlens must start at 0, got {cu[:1]}")
+    lens = [b - a for a, b in zip(cu[:-1], cu[1:])]
+    bad = [n for n, x in enumerate(lens) if x < 0]
+    if bad:
+        raise ValueError(f"cu_seqlens decreases at index {bad[0] + 1}")
+    if cu[-1] > T:
+        raise ValueError(f"cu_seqlens ends at {cu[-1]}, past the {T} tokens of the row")
+    return lens
+
+
+def _capturing() -> bool:
+    return torch.cuda.is_available() and torch.cuda.is_current_stream_capturing()
+
+
 def dr_chunk_fwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, o, S_T) -> None:
     """Chunkwise prefill into caller-provided ``o`` (and ``S_T``). Shapes as in
     include/deltarule.h: q,k [B,T,H,dk]; v [B,T,H,dv]; alpha [B,T,H,dk] fp32; gates per
@@ -218,7 +239,17 @@ def dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, 
     if S_T is not None:
         _need(S_T, "S_T", (rows, H, dk, dv), torch.float32, dev)
     if snapshots is not None:
-        _need(snapshots, "snapshots", (snapshots.shape[0], H, dk, dv), torch.float32, dev)
+        # rows: floor(len / every) per sequence; packed lengths need cu_seqlens on the host
+        # (checked there too), which a graph capture cannot read: the row count is then the caller's
+        if not snapshot_every or snapshot_every <= 0:
+            raise ValueError("snapshots need a positive snapshot_every")
+        if cu_seqlens is None:
+            rows_s = B * (T // int(snapshot_every))
+        elif not _capturing():
+            rows_s = snapshot_count(check_offsets(cu_seqlens, T), snapshot_every)
+        else:
+            rows_s = snapshots.shape[0]
+        _need(snapshots, "snapshots", (rows_s, H, dk, dv), torch.float32, dev)
     if o is not None:  # None: final states / snapshots only
         _need(o, "o", (B, T, H, dv), torch.float32, dev)
     d = _Dims(B, T, H, dk, dv, N, _DT[q.dtype], 0)
@@ -291,8 +322,13 @@ def chunk_fwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, 
         S_T = (torch.empty((N, H, dk, dv), dtype=torch.float32, device=q.device)
                if output_final_state else None)
     snaps = None
+    if cu_seqlens is not None and not _capturing():
+        lens = check_offsets(cu_seqlens, T)
     if snapshot_every is not None:
-        lens = [T] * B if cu_seqlens is None else (cu_seqlens[1:] - cu_seqlens[:-1]).tolist()
+        if cu_seqlens is None:
+            lens = [T] * B
+        elif _capturing():
+            raise ValueError("snapshots of packed sequences need cu_seqlens on the host: not inside a graph capture")
         snaps = torch.empty((snapshot_count(lens, snapshot_every), H, dk, dv), dtype=torch.float32,
                             device=q.device)
     dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T, state_idx, snaps,
@@ -346,9 +382,14 @@ def dr_chunk_bwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, dO,
         _need(t, name, shape, torch.float32, dev)
     if checkpoints is not None:
         # rows: sum over the sequences of floor(len / 64) (32 for product2); for packed sequences
-        # that needs the lengths on the host, so only the row shape is checked there
+        # that needs the lengths on the host, which a graph capture cannot read
         every = 32 if variant == "product2" else 64
-        rows = B * (T // every) if cu_seqlens is None else checkpoints.shape[0]
+        if cu_seqlens is None:
+            rows = B * (T // every)
+        elif not _capturing():
+            rows = snapshot_count(check_offsets(cu_seqlens, T), every)
+        else:
+            rows = checkpoints.shape[0]
         _need(checkpoints, "checkpoints", (rows, H, dk_, dv_), torch.float32, dev)
     d = _Dims(B, T, H, dk_, dv_, N, _DT[q.dtype], 0)
     with torch.cuda.device(dev):
@@ -366,6 +407,8 @@ def chunk_bwd(q, k, v, alpha, erase, write=None, variant: str = "kda", S0=None, 
     for ``dr_chunk_bwd``."""
     f = lambda x: torch.empty(x.shape, dtype=torch.float32, device=q.device)
     N = q.shape[0] if cu_seqlens is None else cu_seqlens.shape[0] - 1
+    if cu_seqlens is not None and not _capturing():
+        check_offsets(cu_seqlens, q.shape[1])
     g = dict(dq=f(q), dk=f(k), dv=f(v), dalpha=f(alpha), derase=f(erase),
              dwrite=None if write is None else f(write),
              dS0=torch.empty((N, q.shape[2], q.shape[3], v.shape[-1]), dtype=torch.float32, device=q.device)

@@ -4,8 +4,10 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/deltarule.h"
 #include "common.hpp"
@@ -117,6 +119,29 @@ hipError_t workspace_alloc(size_t bytes, hipStream_t stream, void** ptr) {
     pool = pools[dev];
   }
   return hipMallocFromPoolAsync(ptr, bytes, pool, stream);
+}
+
+// DR_DEBUG_VALIDATE set (and not "0") in the environment: the prefill and backward entry points
+// also copy cu_seqlens to the host and check it.
+bool debug_validate() {
+  const char* e = getenv("DR_DEBUG_VALIDATE");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+}
+
+// cu_seqlens [nseq + 1] (device) must start at 0, never decrease and end at most at `tokens`.
+// A synchronising copy on `stream`.
+int check_offsets(const int32_t* cu, int64_t nseq, int64_t tokens, hipStream_t stream) {
+  std::vector<int32_t> h((size_t)nseq + 1);
+  hipError_t e = hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return fail(DR_ERR_HIP, "DR_DEBUG_VALIDATE: reading cu_seqlens failed: %s", hipGetErrorString(e));
+  if (h[0] != 0) return fail(DR_ERR_SHAPE, "cu_seqlens[0] is %d, not 0", h[0]);
+  for (int64_t n = 0; n < nseq; ++n)
+    if (h[n + 1] < h[n])
+      return fail(DR_ERR_SHAPE, "cu_seqlens decreases at %lld (%d after %d)", (long long)(n + 1), h[n + 1], h[n]);
+  if (h[nseq] > tokens)
+    return fail(DR_ERR_SHAPE, "cu_seqlens ends at %d, past the %lld tokens of the row", h[nseq], (long long)tokens);
+  return DR_OK;
 }
 
 }  // namespace
@@ -244,6 +269,10 @@ int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alp
   const int lg = variant == DR_PRODUCT2 ? 1 : 0;
   st = opts_checks(opts, true, lg);
   if (st) return st;
+  if (cu_seqlens != nullptr && debug_validate()) {
+    st = check_offsets(cu_seqlens, dims->num_seqs, dims->seqlen, stream);
+    if (st) return st;
+  }
   if (cu_seqlens == nullptr && dims->num_seqs > 0 && dims->seqlen == 0 && S_T == nullptr)
     return DR_OK;  // nothing to compute and nothing to write (no snapshot fits in zero tokens)
   if (dims->num_seqs == 0) return DR_OK;
@@ -325,6 +354,10 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
   st = check_ptrs({}, {{S0, "S0"}, {dS_T, "dS_T"}, {dS0, "dS0"}, {cu_seqlens, "cu_seqlens"}, {dwrite, "dwrite"},
                        {checkpoints, "checkpoints"}});
   if (st) return st;
+  if (cu_seqlens != nullptr && debug_validate()) {
+    st = check_offsets(cu_seqlens, dims->num_seqs, dims->seqlen, stream);
+    if (st) return st;
+  }
   if (dims->num_seqs == 0) return DR_OK;
   const int dkh = (int)dims->head_dim_k, dvh = (int)dims->head_dim_v;
   const int64_t H = dims->num_heads, pairs = dims->num_seqs * H;
@@ -385,7 +418,8 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
     b.q = q; b.k = k; b.v = v; b.alpha = alpha;
     b.erase = erase;
     b.write = p.write;
-    b.S0 = S0; b.cu = cu_seqlens; b.dO = dO; b.dST = dS_T;
+    b.S0 = S0; b.dO = dO; b.dST = dS_T;
+    b.cu = cu_seqlens ? dr::prefill_cu_table(ws, plw, H, dims->num_seqs) : nullptr;  // the plan pass's clamped copy
     b.dq = dq; b.dk = dk; b.dv = dv; b.dalpha = dalpha; b.derase = derase; b.dwrite = dwrite; b.dS0 = dS0;
     b.snap = p.snap;
     b.snap_first = cu_seqlens ? dr::prefill_snap_first(ws, plw, H, dims->num_seqs) : nullptr;

@@ -520,8 +520,6 @@ static hipError_t launch_bwd_dk(const BwdParams& p, int64_t pairs, int dvb, bool
   return dvb == 32 ? launch_bwd_g<DK, 32>(p, pairs, bf16, vec, s) : launch_bwd_g<DK, 16>(p, pairs, bf16, vec, s);
 }
 
-int bwd_dv_block(int dv) { return dv >= 32 ? 32 : 16; }
-
 hipError_t launch_backward(BwdParams p, int64_t pairs, int dk, int dv, bool bf16, bool vec, hipStream_t s) {
   const int dvb = bwd_dv_block(dv);
   p.ndvb = dv / dvb;

@@ -36,6 +36,9 @@ hipError_t launch_prefill(Params p, const PrefillPlan& plan, void* ws, int dk, b
 // Packed sequences: where the prefill's workspace keeps the first snapshot row of each sequence
 // (filled by the prefill when snapshots are taken), followed by the sequences' longest-first order.
 int32_t* prefill_snap_first(void* ws, const PrefillPlan& plan, int64_t heads, int64_t nseq);
+// Packed sequences: the plan pass's clamped, non-decreasing copy of the offsets [nseq + 1], from which
+// every later pass (the backward's included) takes its sequence spans.
+int32_t* prefill_cu_table(void* ws, const PrefillPlan& plan, int64_t heads, int64_t nseq);
 
 // Only the packed-sequence plan pass of a prefill (chunk slots, first snapshot rows, sequence
 // order) into `ws`; nothing for fixed-length sequences.

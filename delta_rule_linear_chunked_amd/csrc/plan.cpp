@@ -1,0 +1,56 @@
+// Host-side planning of the prefill and backward launches: launch shapes, workspace sizes and the
+// offsets of the workspace tables. No device code runs here; the kernels that fill the tables
+// live in prefill.hip.
+#include <cstdlib>
+
+#include "prefill.hpp"
+
+namespace dr {
+
+static int64_t rec_size_for(int dk) {
+  switch (dk) {
+    case 16: case 32: return Rec<32>::SIZE;
+    case 64: return Rec<64>::SIZE;
+    default: return Rec<128>::SIZE;
+  }
+}
+
+PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int64_t seqlen,
+                         int64_t heads, int dk, int dv, bool packed) {
+  PrefillPlan pl;
+  pl.chunk = CH;
+  // Value columns per state workgroup: every workgroup of a head reads the head's whole
+  // operand record each chunk, so wider blocks cut the load traffic per CU; narrower
+  // blocks are used only when wide ones would leave CUs idle. DR_DV_BLOCK overrides
+  // (16, 32 or 64) for tuning.
+  pl.dv_block = (dv >= 32 && num_pairs * (dv / 32) >= 256) ? 32 : 16;
+  if (const char* e = getenv("DR_DV_BLOCK")) {
+    const int b = atoi(e);
+    if ((b == 16 || b == 32 || b == 64) && b <= dv) pl.dv_block = b;
+  }
+  pl.ndvb = dv / pl.dv_block;
+  const int64_t logical = num_pairs * pl.ndvb;
+  // (packed: whole rows of 8 pairs, one pair per XCD, times the column blocks)
+  pl.workgroups = packed ? (num_pairs + 7) / 8 * 8 * pl.ndvb : (logical + 7) / 8 * 8;
+  const int64_t cps = (seqlen + CH - 1) / CH;
+  pl.slots = packed ? cps + num_seqs : batch * cps;
+  pl.rec_size = rec_size_for(dk);
+  // chunk_seq, chunk_c0 [slots]; seq_first [nseq + 1]; snap_first, seq_order [nseq]; cu_ok [nseq + 1]
+  const int64_t tables = packed ? ((2 * pl.slots + 4 * num_seqs + 2) * 4 + 255) / 256 * 256 : 0;
+  pl.workspace = pl.slots * heads * pl.rec_size + tables;
+  return pl;
+}
+
+
+int32_t* prefill_snap_first(void* ws, const PrefillPlan& pl, int64_t heads, int64_t nseq) {
+  return reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + pl.slots * heads * pl.rec_size) + 2 * pl.slots +
+         nseq + 1;
+}
+
+int32_t* prefill_cu_table(void* ws, const PrefillPlan& pl, int64_t heads, int64_t nseq) {
+  return prefill_snap_first(ws, pl, heads, nseq) + 2 * nseq;
+}
+
+int bwd_dv_block(int dv) { return dv >= 32 ? 32 : 16; }
+
+}  // namespace dr

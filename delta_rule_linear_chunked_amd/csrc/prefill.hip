@@ -37,7 +37,6 @@
 // factorisation is used only while every |f| of the block lies in [2^-100, 2^100];
 // otherwise (gates at or extremely close to zero) the block's diagonal tiles and
 // g come from running products, which are exact for any gate value.
-#include <cstdlib>
 #include <type_traits>
 
 #include "prefill.hpp"
@@ -71,10 +70,36 @@ __device__ __forceinline__ bool resolve_slot(const Params& p, int slot, int& n, 
 // counts), first snapshot row of each sequence, the sequences in order of decreasing
 // chunk count (the state pass's order), and, for every slot, its sequence and first
 // token. One workgroup.
-__global__ __launch_bounds__(256) void chunk_plan_kernel(const Params p) {
+__global__ __launch_bounds__(256) void chunk_plan_kernel(Params p) {
   __shared__ int s_scan[256];
   __shared__ int s_carry;
   const int tid = threadIdx.x;
+  // The offsets, clamped to [0, tokens] and made non-decreasing by a running maximum, into
+  // cu_ok; this pass and the later ones take every span from that copy, so a malformed
+  // cu_seqlens gives wrong spans but no access outside the token rows, the chunk slots or the
+  // snapshot rows those spans imply.
+  {
+    const int32_t ntok = (int32_t)(p.T >> p.lgnh);
+    if (tid == 0) s_carry = 0;
+    __syncthreads();
+    for (int base = 0; base <= p.nseq; base += 256) {
+      const int n = base + tid;
+      int x = n <= p.nseq ? min(max(p.cu[n], 0), ntok) : 0;
+      s_scan[tid] = x;
+      __syncthreads();
+      for (int d = 1; d < 256; d <<= 1) {
+        const int y = tid >= d ? s_scan[tid - d] : 0;
+        __syncthreads();
+        s_scan[tid] = max(s_scan[tid], y);
+        __syncthreads();
+      }
+      if (n <= p.nseq) p.cu_ok[n] = max(s_scan[tid], s_carry);
+      __syncthreads();
+      if (tid == 255) s_carry = max(s_carry, s_scan[255]);
+      __syncthreads();
+    }
+    p.cu = p.cu_ok;  // (the workgroup-scope fence of the barriers above covers global memory)
+  }
   if (tid == 0) s_carry = 0;
   __syncthreads();
   for (int base = 0; base < p.nseq; base += 256) {
@@ -571,48 +596,16 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
 }
 
 // ============================================================================ host
-static int64_t rec_size_for(int dk) {
-  switch (dk) {
-    case 16: case 32: return Rec<32>::SIZE;
-    case 64: return Rec<64>::SIZE;
-    default: return Rec<128>::SIZE;
-  }
-}
-
-PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int64_t seqlen,
-                         int64_t heads, int dk, int dv, bool packed) {
-  PrefillPlan pl;
-  pl.chunk = CH;
-  // Value columns per state workgroup: every workgroup of a head reads the head's whole
-  // operand record each chunk, so wider blocks cut the load traffic per CU; narrower
-  // blocks are used only when wide ones would leave CUs idle. DR_DV_BLOCK overrides
-  // (16, 32 or 64) for tuning.
-  pl.dv_block = (dv >= 32 && num_pairs * (dv / 32) >= 256) ? 32 : 16;
-  if (const char* e = getenv("DR_DV_BLOCK")) {
-    const int b = atoi(e);
-    if ((b == 16 || b == 32 || b == 64) && b <= dv) pl.dv_block = b;
-  }
-  pl.ndvb = dv / pl.dv_block;
-  const int64_t logical = num_pairs * pl.ndvb;
-  // (packed: whole rows of 8 pairs, one pair per XCD, times the column blocks)
-  pl.workgroups = packed ? (num_pairs + 7) / 8 * 8 * pl.ndvb : (logical + 7) / 8 * 8;
-  const int64_t cps = (seqlen + CH - 1) / CH;
-  pl.slots = packed ? cps + num_seqs : batch * cps;
-  pl.rec_size = rec_size_for(dk);
-  // chunk_seq, chunk_c0 [slots]; seq_first [nseq + 1]; snap_first, seq_order [nseq]
-  const int64_t tables = packed ? ((2 * pl.slots + 3 * num_seqs + 1) * 4 + 255) / 256 * 256 : 0;
-  pl.workspace = pl.slots * heads * pl.rec_size + tables;
-  return pl;
-}
-
 template <int DKR, typename InT, bool VEC>
-static hipError_t launch_t(const Params& p, const PrefillPlan& pl, hipStream_t s) {
-  const bool prep = p.prep_l2 || p.a_bf16 || p.a_act || p.g_act;
-  if (p.cu) {
-    hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, s, p);
+static hipError_t launch_t(const Params& p0, const PrefillPlan& pl, hipStream_t s) {
+  const bool prep = p0.prep_l2 || p0.a_bf16 || p0.a_act || p0.g_act;
+  if (p0.cu) {
+    hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, s, p0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  Params p = p0;
+  if (p.cu) p.cu = p.cu_ok;  // every later pass reads the plan's clamped offsets
   if (pl.slots > 0) {
     const dim3 grid((unsigned)(pl.slots * p.H));
     // the decay's storage type and activation are template arguments: each instance evaluates
@@ -643,11 +636,6 @@ static hipError_t launch_dk(const Params& p, const PrefillPlan& pl, bool bf16, b
   return vec ? launch_t<DKR, float, true>(p, pl, s) : launch_t<DKR, float, false>(p, pl, s);
 }
 
-int32_t* prefill_snap_first(void* ws, const PrefillPlan& pl, int64_t heads, int64_t nseq) {
-  return reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + pl.slots * heads * pl.rec_size) + 2 * pl.slots +
-         nseq + 1;
-}
-
 // Workspace pointers of a call: the records, then (packed sequences) the plan's tables.
 static void set_workspace(Params& p, const PrefillPlan& pl, void* ws) {
   p.rec = static_cast<unsigned char*>(ws);
@@ -661,6 +649,7 @@ static void set_workspace(Params& p, const PrefillPlan& pl, void* ws) {
     p.seq_first = tables + 2 * pl.slots;
     p.snap_first = prefill_snap_first(ws, pl, p.H, p.nseq);
     p.seq_order = p.snap_first + p.nseq;
+    p.cu_ok = prefill_cu_table(ws, pl, p.H, p.nseq);
   }
 }
 

@@ -51,9 +51,19 @@
  * Errors. Argument errors are detected on the host before anything is launched
  * and return a negative status (nothing is written). A failed kernel launch
  * returns DR_ERR_HIP. dr_last_error() describes the most recent failure on the
- * calling thread. The contents of cu_seqlens (device memory) are not read on
- * the host: a cu_seqlens that is not non-decreasing from 0 to T is undefined
- * behaviour.
+ * calling thread.
+ *
+ * cu_seqlens. A valid cu_seqlens starts at 0, never decreases and ends at most
+ * at T (rows past cu_seqlens[N] are neither read nor written). Its contents
+ * live in device memory and are not read on the host by default: the kernels
+ * take every sequence span from a copy clamped to [0, T] and made
+ * non-decreasing, so an invalid cu_seqlens gives unspecified results (and, with
+ * snapshots, snapshot rows for the clamped lengths) but no access outside the
+ * token rows, the states or the workspace. With DR_DEBUG_VALIDATE set in the
+ * environment (to anything but "0"), dr_chunk_fwd(_ex) and dr_chunk_bwd(_ex)
+ * also copy cu_seqlens to the host (synchronising `stream`, so not inside a
+ * graph capture) and return DR_ERR_SHAPE for an invalid one, with nothing
+ * launched.
  */
 #ifndef DELTARULE_H
 #define DELTARULE_H

@@ -169,3 +169,52 @@ def test_backward_checkpoints_are_checked(lib):
                              FAKE, FAKE, FAKE, FAKE, FAKE, None, None, MISALIGNED, ctypes.byref(dims()), None)
     assert st == -4, lib.dr_last_error()
     assert "checkpoints" in lib.dr_last_error().decode()
+
+
+# ----------------------------------------------------------------- the binding's host checks
+# (CPU tensors: every case below raises in the binding before the library is called)
+def _cpu_prefill(B=1, T=130, H=2, d=64):
+    import torch
+    z = lambda *s: torch.zeros(s, dtype=torch.float32)  # noqa: E731
+    return dict(q=z(B, T, H, d), k=z(B, T, H, d), v=z(B, T, H, d), alpha=z(B, T, H, d), erase=z(B, T, H),
+                write=None, variant="kda", S0=None)
+
+
+def test_binding_checks_offsets():
+    import torch
+    T = 130
+    assert drl.check_offsets(torch.tensor([0, 50, 50, 130], dtype=torch.int32), T) == [50, 0, 80]
+    assert drl.check_offsets(torch.tensor([0, 64], dtype=torch.int32), T) == [64]   # rows past the end
+    for bad, msg in (([1, 50, 130], "start at 0"), ([0, 80, 50, 130], "decreases"), ([0, 70, 131], "past")):
+        with pytest.raises(ValueError, match=msg):
+            drl.check_offsets(torch.tensor(bad, dtype=torch.int32), T)
+    a = _cpu_prefill(T=T)
+    with pytest.raises(ValueError, match="decreases"):
+        drl.chunk_fwd(**a, cu_seqlens=torch.tensor([0, 80, 50, 130], dtype=torch.int32))
+
+
+def test_binding_checks_snapshot_rows():
+    import torch
+    a = _cpu_prefill(B=2, T=130)
+    o = torch.empty(2, 130, 2, 64)
+    # fixed length: floor(130 / 64) = 2 rows per sequence, 4 in all
+    for rows in (3, 5):
+        snaps = torch.empty(rows, 2, 64, 64)
+        with pytest.raises(ValueError, match="snapshots has shape"):
+            drl.dr_chunk_fwd_ex(a["q"], a["k"], a["v"], a["alpha"], a["erase"], None, "kda", None, None, o, None,
+                                snapshots=snaps, snapshot_every=64)
+    # packed: rows from the host copy of the offsets (64 + 66 -> 1 + 1)
+    p = _cpu_prefill(B=1, T=130)
+    cu = torch.tensor([0, 64, 130], dtype=torch.int32)
+    with pytest.raises(ValueError, match="snapshots has shape"):
+        drl.dr_chunk_fwd_ex(p["q"], p["k"], p["v"], p["alpha"], p["erase"], None, "kda", None, cu,
+                            torch.empty(1, 130, 2, 64), None, snapshots=torch.empty(1, 2, 64, 64),
+                            snapshot_every=64)
+    with pytest.raises(ValueError, match="decreases"):
+        drl.dr_chunk_fwd_ex(p["q"], p["k"], p["v"], p["alpha"], p["erase"], None, "kda", None,
+                            torch.tensor([0, 90, 40, 130], dtype=torch.int32), torch.empty(1, 130, 2, 64), None,
+                            snapshots=torch.empty(1, 2, 64, 64), snapshot_every=64)
+    # the backward's checkpoints: floor(len / 64) rows per sequence as well
+    with pytest.raises(ValueError, match="checkpoints has shape"):
+        drl.chunk_bwd(**{k: v for k, v in a.items() if k != "variant"}, variant="kda",
+                      dO=torch.zeros(2, 130, 2, 64), checkpoints=torch.empty(3, 2, 64, 64))
