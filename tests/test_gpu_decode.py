@@ -67,8 +67,8 @@ def test_kda_is_rda_with_equal_gates_bitwise():
 @pytest.mark.parametrize("variant", ["kda", "rda", "gdn2", "ckda"])
 def test_full_size_decode(variant):
     """512 sequences x 32 heads x 128 x 128 fp32 state (1 GiB) updated in place. Step 1 is
-    checked on every head; after 10 and 100 steps (inputs cycled from a pool of 16
-    distinct token sets) 64 seeded heads are checked."""
+    checked on every head; after 10, 100 and 1000 consecutive steps (inputs cycled from a pool
+    of 16 distinct token sets) 64 seeded heads are checked."""
     pool = 16
     wl = synth.preset(f"decode_{variant}", steps=pool)
     N, H = wl.S0.shape[:2]
@@ -97,15 +97,36 @@ def test_full_size_decode(variant):
     S_ref, _ = oracle.decode_step(S_ref, wl.q[0][ns, hs], wl.k[0][ns, hs], wl.v[0][ns, hs],
                                   wl.alpha[0][ns, hs], wl.erase[0][ns, hs],
                                   None if wl.write is None else wl.write[0][ns, hs], variant)
-    for step in range(1, 100):
+    for step in range(1, 1000):
         t = step % pool
         o = drl.decode_step(S=S, **toks[t])
         S_ref, o_ref = oracle.decode_step(S_ref, wl.q[t][ns, hs], wl.k[t][ns, hs], wl.v[t][ns, hs],
                                           wl.alpha[t][ns, hs], wl.erase[t][ns, hs],
                                           None if wl.write is None else wl.write[t][ns, hs], variant)
-        if step + 1 in (10, 100):
+        if step + 1 in (10, 100, 1000):
             torch.cuda.synchronize()
             eo = oracle.rel_err(o.cpu().numpy()[ns, hs], o_ref)
             es = oracle.rel_err(S.cpu().numpy()[ns, hs], S_ref)
             print(f"[decode full {variant}] step {step + 1}, 64 heads: err o={eo:.3e} S={es:.3e}", flush=True)
             assert eo <= tol and es <= tol
+
+
+def test_nan_stays_in_its_head():
+    """NaN / Inf in one head's token leave every other head's output and state bit for bit as in
+    a clean step (no two requests share a state: the course page "GDN, KDA và Mamba-2", section 3)."""
+    for variant in ("kda", "gdn2"):
+        wl = synth.make_decode(variant, 6, 4, 128, 128, steps=1, seed=seed_of("nan decode", variant))
+        a = decode_inputs(wl, 0)
+        S1 = to_dev(wl.S0).clone()
+        S2 = S1.clone()
+        o1 = drl.decode_step(S=S1, **a)
+        b = {key: (x.clone() if torch.is_tensor(x) else x) for key, x in a.items()}
+        b["q"][2, 1, 5] = float("nan")
+        b["v"][2, 1, 0] = float("inf")
+        b["alpha"][2, 1, 9] = float("nan")
+        o2 = drl.decode_step(S=S2, **b)
+        torch.cuda.synchronize()
+        keep = torch.ones(o1.shape[:2], dtype=torch.bool, device=o1.device)
+        keep[2, 1] = False
+        assert not torch.isfinite(o2[2, 1]).all()
+        assert torch.equal(o1[keep], o2[keep]) and torch.equal(S1[keep], S2[keep])
