@@ -17,7 +17,8 @@ from typing import Optional
 
 import torch
 
-__all__ = ["dr_chunk_fwd", "dr_decode_step", "dr_chunk_fwd_ex", "dr_decode_step_ex", "dr_chunk_bwd",
+__all__ = ["dr_chunk_fwd", "dr_decode_step", "dr_chunk_fwd_ex", "dr_chunk_fwd_noalloc", "dr_decode_step_ex",
+           "dr_chunk_bwd",
            "chunk_fwd", "decode_step", "chunk_bwd", "chunk_fwd_plan", "snapshot_count", "check_offsets",
            "library_path",
            "load_library", "VARIANTS", "DeltaRuleError"]
@@ -28,6 +29,8 @@ _LIB_PATH = os.path.join(_PKG, "lib", "libdeltarule.so")
 VARIANTS = {"kda": 0, "rda": 1, "gdn2": 2, "ckda": 3, "product2": 4}
 _DT = {torch.float32: 0, torch.bfloat16: 1}
 _lib = None
+# bytes of the static device scratch behind dr_chunk_fwd_noalloc (DR_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 
 class DeltaRuleError(RuntimeError):
@@ -96,6 +99,8 @@ def load_library(path: Optional[str] = None):
     op = ctypes.POINTER(_Opts)
     lib.dr_chunk_fwd_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, vp, fp, fp, ctypes.POINTER(_Dims), op, vp]
     lib.dr_chunk_fwd_ex.restype = ip
+    lib.dr_chunk_fwd_noalloc.argtypes = lib.dr_chunk_fwd_ex.argtypes
+    lib.dr_chunk_fwd_noalloc.restype = ip
     lib.dr_decode_step_ex.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, fp, ctypes.POINTER(_Dims), op, vp]
     lib.dr_decode_step_ex.restype = ip
     lib.dr_chunk_bwd.argtypes = [vp, vp, vp, fp, fp, fp, ip, fp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
@@ -206,6 +211,21 @@ def dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, 
     fp32 receives the state after every ``snapshot_every`` tokens of each sequence (rows
     ordered by sequence, see ``snapshot_count``). ``prep`` (a dict, see ``_opts``) makes the
     kernels normalise q/k and activate alpha (fp32 or bf16) and the gates while loading."""
+    _chunk_fwd_call("dr_chunk_fwd_ex", q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T,
+                    state_idx, snapshots, snapshot_every, prep)
+
+
+def dr_chunk_fwd_noalloc(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, o, S_T,
+                         state_idx=None, snapshots=None, snapshot_every: int = 0, prep=None) -> None:
+    """``dr_chunk_fwd_ex`` with its workspace in the library's static device scratch instead of an
+    allocation (for callers that cannot allocate; problems whose workspace exceeds
+    ``NOALLOC_SCRATCH_BYTES`` raise). Calls that overlap on one GPU race."""
+    _chunk_fwd_call("dr_chunk_fwd_noalloc", q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T,
+                    state_idx, snapshots, snapshot_every, prep)
+
+
+def _chunk_fwd_call(entry, q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T, state_idx, snapshots,
+                    snapshot_every, prep) -> None:
     lib = load_library()
     B, T, H, dk = q.shape
     dv = v.shape[-1]
@@ -255,10 +275,10 @@ def dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, 
     d = _Dims(B, T, H, dk, dv, N, _DT[q.dtype], 0)
     opts = _opts(state_idx, rows, snapshots, snapshot_every, prep, alpha)
     with torch.cuda.device(dev):  # the library launches on the current device
-        st = lib.dr_chunk_fwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
+        st = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
                                  VARIANTS[variant], _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
                                  ctypes.byref(d), ctypes.byref(opts), _stream(dev))
-    _check(lib, st, "dr_chunk_fwd")
+    _check(lib, st, entry)
 
 
 def dr_decode_step(q, k, v, alpha, erase, write, variant: str, S, o) -> None:

@@ -248,11 +248,13 @@ int dr_chunk_fwd(const void* q, const void* k, const void* v, const float* alpha
   return dr_chunk_fwd_ex(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T, dims, nullptr, stream);
 }
 
-int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alpha,
-                    const float* erase, const float* write, int variant,
-                    const float* S0, const int32_t* cu_seqlens,
-                    float* o, float* S_T, const dr_dims* dims, const dr_opts* opts,
-                    hipStream_t stream) {
+// The prefill behind dr_chunk_fwd_ex (workspace from the pool) and dr_chunk_fwd_noalloc (workspace
+// in the static scratch array).
+static int chunk_fwd_impl(const void* q, const void* k, const void* v, const void* alpha,
+                          const float* erase, const float* write, int variant,
+                          const float* S0, const int32_t* cu_seqlens,
+                          float* o, float* S_T, const dr_dims* dims, const dr_opts* opts,
+                          hipStream_t stream, bool noalloc) {
   g_last_error.clear();
   bool vec = false;
   int st = prefill_checks(dims, variant, erase, write, cu_seqlens, &vec);
@@ -304,17 +306,42 @@ int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alp
   set_prep(p, opts);
   void* ws = nullptr;
   hipError_t e = hipSuccess;
-  if (pl.workspace > 0) {
+  if (noalloc) {
+    if ((uint64_t)pl.workspace > DR_NOALLOC_SCRATCH_BYTES)
+      return fail(DR_ERR_UNSUPPORTED, "dr_chunk_fwd_noalloc: this problem needs %lld bytes of workspace, above the "
+                  "%llu-byte static scratch (split the call, or use dr_chunk_fwd_ex)", (long long)pl.workspace,
+                  (unsigned long long)DR_NOALLOC_SCRATCH_BYTES);
+    if (pl.workspace > 0) {
+      e = dr::scratch_buffer(&ws);
+      if (e != hipSuccess) return fail(DR_ERR_HIP, "static scratch lookup failed: %s", hipGetErrorString(e));
+    }
+  } else if (pl.workspace > 0) {
     e = workspace_alloc((size_t)pl.workspace, stream, &ws);
     if (e != hipSuccess)
       return fail(DR_ERR_HIP, "prefill workspace (%lld bytes) allocation failed: %s", (long long)pl.workspace,
                   hipGetErrorString(e));
   }
   e = dr::launch_prefill(p, pl, ws, (int)dims->head_dim_k, dims->in_dtype == DR_BF16, vec, stream);
-  hipError_t ef = ws ? hipFreeAsync(ws, stream) : hipSuccess;
+  hipError_t ef = (ws && !noalloc) ? hipFreeAsync(ws, stream) : hipSuccess;
   if (e != hipSuccess) return fail(DR_ERR_HIP, "prefill launch failed: %s", hipGetErrorString(e));
   if (ef != hipSuccess) return fail(DR_ERR_HIP, "prefill workspace release failed: %s", hipGetErrorString(ef));
   return DR_OK;
+}
+
+int dr_chunk_fwd_ex(const void* q, const void* k, const void* v, const void* alpha,
+                    const float* erase, const float* write, int variant,
+                    const float* S0, const int32_t* cu_seqlens,
+                    float* o, float* S_T, const dr_dims* dims, const dr_opts* opts,
+                    hipStream_t stream) {
+  return chunk_fwd_impl(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T, dims, opts, stream, false);
+}
+
+int dr_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* alpha,
+                         const float* erase, const float* write, int variant,
+                         const float* S0, const int32_t* cu_seqlens,
+                         float* o, float* S_T, const dr_dims* dims, const dr_opts* opts,
+                         hipStream_t stream) {
+  return chunk_fwd_impl(q, k, v, alpha, erase, write, variant, S0, cu_seqlens, o, S_T, dims, opts, stream, true);
 }
 
 static int64_t round256(int64_t b) { return (b + 255) / 256 * 256; }

@@ -44,6 +44,10 @@ int32_t* prefill_cu_table(void* ws, const PrefillPlan& plan, int64_t heads, int6
 // order) into `ws`; nothing for fixed-length sequences.
 hipError_t launch_plan_only(Params p, const PrefillPlan& plan, void* ws, hipStream_t s);
 
+// Device address of this device's static scratch array (DR_NOALLOC_SCRATCH_BYTES bytes), looked up
+// once per device.
+hipError_t scratch_buffer(void** ptr);
+
 // Backward: bwd_kernel over every (sequence, head, value block), then the reduction over the
 // blocks. p.snap must hold the forward states after every 64 tokens (the prefill's snapshots);
 // p.part / p.parts the per-block partial sums (ndvb = d_v / bwd_dv_block(d_v) blocks).

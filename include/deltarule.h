@@ -243,6 +243,24 @@ int dr_decode_step_ex(const void* q, const void* k, const void* v, const void* a
                       hipStream_t stream);
 
 /*
+ * dr_chunk_fwd_ex for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). Same arguments, semantics and results
+ * (the same kernels run); the prefill's workspace is instead a static device array of
+ * DR_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it runs on until the process
+ * ends. The call allocates nothing: no hipMalloc, hipFree or pool allocation. A problem whose
+ * workspace does not fit (at d_k = 128 about 128.5 KiB per 64-step chunk and head, so about 2000
+ * chunk-heads, e.g. 8192 tokens x 16 heads) returns DR_ERR_UNSUPPORTED with nothing launched.
+ * Every call on one GPU uses that GPU's one array, so calls that overlap on a GPU (on different
+ * streams, or from different threads) race and give undefined results: serialise them.
+ */
+#define DR_NOALLOC_SCRATCH_BYTES (256ull << 20)
+int dr_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void* alpha,
+                         const float* erase, const float* write, int variant,
+                         const float* S0, const int32_t* cu_seqlens,
+                         float* o, float* S_T, const dr_dims* dims, const dr_opts* opts,
+                         hipStream_t stream);
+
+/*
  * Gradients of dr_chunk_fwd, for training (the course page above, section 3: training needs
  * activations, checkpoints and the scan's intermediates). For a loss L with
  * dO = dL/do [B, T, H, d_v] and dS_T = dL/dS_T [N, H, d_k, d_v] (NULL: zero), writes, all

@@ -12,5 +12,6 @@ hipError_t launch_decode2(const Params&, int64_t, int, int, bool, hipStream_t) {
 hipError_t launch_prefill(Params, const PrefillPlan&, void*, int, bool, bool, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_plan_only(Params, const PrefillPlan&, void*, hipStream_t) { return hipErrorNoDevice; }
 hipError_t launch_backward(BwdParams, int64_t, int, int, bool, bool, hipStream_t) { return hipErrorNoDevice; }
+hipError_t scratch_buffer(void**) { return hipErrorNoDevice; }
 
 }  // namespace dr
