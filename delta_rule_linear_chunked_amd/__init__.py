@@ -19,7 +19,8 @@ import torch
 
 __all__ = ["dr_chunk_fwd", "dr_decode_step", "dr_chunk_fwd_ex", "dr_chunk_fwd_noalloc", "dr_decode_step_ex",
            "dr_chunk_bwd",
-           "chunk_fwd", "decode_step", "chunk_bwd", "chunk_fwd_plan", "snapshot_count", "check_offsets",
+           "chunk_fwd", "decode_step", "chunk_bwd", "chunk_fwd_plan", "chunk_fwd_plan_ex", "snapshot_count",
+           "check_offsets",
            "library_path",
            "load_library", "VARIANTS", "DeltaRuleError"]
 
@@ -48,6 +49,11 @@ class _Opts(ctypes.Structure):
                 ("snapshots", ctypes.c_void_p), ("snapshot_every", ctypes.c_int64),
                 ("l2norm_qk", ctypes.c_int32), ("alpha_dtype", ctypes.c_int32), ("alpha_act", ctypes.c_int32),
                 ("alpha_scale", ctypes.c_float), ("gate_act", ctypes.c_int32), ("gate_scale", ctypes.c_float)]
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("chunk", ctypes.c_int32), ("dv_block", ctypes.c_int32), ("workgroups", ctypes.c_int64),
+                ("window_chunks", ctypes.c_int64), ("windows", ctypes.c_int64), ("workspace", ctypes.c_int64)]
 
 
 # activations of the fused input preparation (dr_act)
@@ -117,6 +123,8 @@ def load_library(path: Optional[str] = None):
     lib.dr_chunk_fwd_plan.argtypes = [ctypes.POINTER(_Dims), ip, ctypes.POINTER(ctypes.c_int32),
                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int64)]
     lib.dr_chunk_fwd_plan.restype = ip
+    lib.dr_chunk_fwd_plan_ex.argtypes = [ctypes.POINTER(_Dims), ip, ip, ctypes.POINTER(_Plan)]
+    lib.dr_chunk_fwd_plan_ex.restype = ip
     if path is None:
         _lib = lib
     return lib
@@ -170,6 +178,18 @@ def chunk_fwd_plan(B: int, T: int, H: int, dk: int, dv: int, num_seqs: Optional[
     _check(lib, lib.dr_chunk_fwd_plan(ctypes.byref(d), VARIANTS[variant], ctypes.byref(c),
                                       ctypes.byref(b), ctypes.byref(w)), "dr_chunk_fwd_plan")
     return c.value, b.value, w.value
+
+
+def chunk_fwd_plan_ex(B: int, T: int, H: int, dk: int, dv: int, num_seqs: Optional[int] = None,
+                      variant: str = "kda", in_dtype: torch.dtype = torch.bfloat16, noalloc: bool = False) -> dict:
+    """The prefill's full launch plan (dr_chunk_fwd_plan_ex) as a dict: chunk, dv_block, workgroups,
+    window_chunks, windows, workspace (bytes)."""
+    lib = load_library()
+    d = _Dims(B, T, H, dk, dv, B if num_seqs is None else num_seqs, _DT[in_dtype], 0)
+    pl = _Plan()
+    _check(lib, lib.dr_chunk_fwd_plan_ex(ctypes.byref(d), VARIANTS[variant], int(noalloc), ctypes.byref(pl)),
+           "dr_chunk_fwd_plan_ex")
+    return {name: getattr(pl, name) for name, _ in _Plan._fields_}
 
 
 def snapshot_count(lengths, every: int) -> int:

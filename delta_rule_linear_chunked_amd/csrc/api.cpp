@@ -201,6 +201,40 @@ int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t*
   return DR_OK;
 }
 
+// The prefill's plan; with noalloc, windows small enough that the workspace fits the static scratch
+// (when that is possible: packed sequences run as one window).
+static dr::PrefillPlan make_plan(const dr_dims* dims, int lg, bool packed, bool noalloc) {
+  const int64_t pairs = dims->num_seqs * dims->num_heads;
+  dr::PrefillPlan pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen << lg, dims->num_heads,
+                                        (int)dims->head_dim_k, (int)dims->head_dim_v, packed);
+  if (noalloc && !packed && (uint64_t)pl.workspace > DR_NOALLOC_SCRATCH_BYTES) {
+    // smaller windows: the records of one window and the carried state must fit the scratch
+    const int64_t carry = pairs * dims->head_dim_k * dims->head_dim_v * 4;
+    const int64_t room = (int64_t)DR_NOALLOC_SCRATCH_BYTES - carry;
+    if (room > 0)
+      pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen << lg, dims->num_heads,
+                            (int)dims->head_dim_k, (int)dims->head_dim_v, packed, room);
+  }
+  return pl;
+}
+
+int dr_chunk_fwd_plan_ex(const dr_dims* dims, int variant, int noalloc, dr_plan* plan) {
+  g_last_error.clear();
+  int st = check_dims_common(dims);
+  if (st) return st;
+  if (variant < DR_KDA || variant > DR_PRODUCT2) return fail(DR_ERR_VARIANT, "unknown variant %d", variant);
+  if (plan == nullptr) return fail(DR_ERR_NULL, "plan is NULL");
+  const int lg = variant == DR_PRODUCT2 ? 1 : 0;
+  const dr::PrefillPlan pl = make_plan(dims, lg, dims->batch == 1 && dims->num_seqs != 1, noalloc != 0);
+  plan->chunk = pl.chunk;
+  plan->dv_block = pl.dv_block;
+  plan->workgroups = pl.workgroups;
+  plan->window_chunks = pl.win_k;
+  plan->windows = pl.windows;
+  plan->workspace = pl.workspace;
+  return DR_OK;
+}
+
 // Checks of the options shared by prefill and decode (lg: log2 of the transitions per token).
 static int opts_checks(const dr_opts* opts, bool prefill, int lg = 0) {
   if (!opts) return DR_OK;
@@ -289,8 +323,7 @@ static int chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
   p.H = (int32_t)dims->num_heads;
   p.DV = (int32_t)dims->head_dim_v;
   const int64_t pairs = dims->num_seqs * dims->num_heads;
-  const dr::PrefillPlan pl = dr::plan_prefill(pairs, dims->num_seqs, dims->batch, dims->seqlen << lg, dims->num_heads,
-                                              (int)dims->head_dim_k, (int)dims->head_dim_v, cu_seqlens != nullptr);
+  const dr::PrefillPlan pl = make_plan(dims, lg, cu_seqlens != nullptr, noalloc);
   if (pl.workgroups > INT32_MAX || pl.slots * dims->num_heads > INT32_MAX)
     return fail(DR_ERR_UNSUPPORTED, "problem too large: more than 2^31 - 1 workgroups per kernel");
   p.num_pairs = (int32_t)pairs;

@@ -37,6 +37,16 @@ struct Params {
   int32_t* seq_first;   // packed: first chunk slot of each sequence
   int32_t slots;        // chunk slots
   int32_t cps;          // fixed length: chunks per sequence
+  // fixed length: one launch of the two passes covers chunks win_c0 .. win_c0 + win_nc - 1 of every
+  // sequence (a window), whose records sit at slot n * win_k + (c - win_c0); the state passes from
+  // one window to the next through `carry` [N, H, d_k, d_v] (read when carry_in, written instead of
+  // the final state when carry_out). Packed sequences run as one window of all their chunks.
+  int32_t win_c0;
+  int32_t win_nc;
+  int32_t win_k;
+  float* carry;
+  int32_t carry_in;
+  int32_t carry_out;
   int32_t nseq;         // sequences
   // state pools and snapshots
   const int32_t* sidx;  // slot of each sequence in the state buffers (null: slot n)

@@ -21,12 +21,23 @@ struct PrefillPlan {
   int dv_block;
   int ndvb;
   int64_t workgroups;  // state pass: padded to a multiple of 8 (XCD count)
-  int64_t slots;       // chunk slots (an upper bound for packed sequences)
+  int64_t slots;       // chunk slots of one window (an upper bound for packed sequences)
   int64_t rec_size;    // bytes of one (chunk slot, head) operand record
-  int64_t workspace;   // bytes of workspace (records + packed-sequence tables)
+  int64_t win_k;       // fixed length: chunks of every sequence per window (packed: 0, one window)
+  int64_t windows;     // launches of the two passes
+  int64_t carry;       // bytes of the state carried between windows (0 for one window)
+  int64_t workspace;   // bytes of workspace (records of one window + packed-sequence tables + carry)
 };
+// Operand records of one window are kept to about this many bytes, which bounds the workspace of
+// any fixed-length prefill. Measured on the KDA prefill (4 x 4096 tokens, 16 heads, d = 128),
+// windows small enough for the 256 MB Infinity Cache (four of 16 chunks) halve the time the state
+// pass needs to read its records, but the pass is then bound by its per-chunk chain and the two
+// passes take 2-4 % longer in all (more, shorter launches), so the default budget is set high
+// enough that such problems run as one window.
+constexpr int64_t PREFILL_WINDOW_BYTES = (int64_t)1 << 30;
 PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int64_t seqlen,
-                         int64_t heads, int dk, int dv, bool packed);
+                         int64_t heads, int dk, int dv, bool packed,
+                         int64_t window_bytes = PREFILL_WINDOW_BYTES);
 
 // Prefill: chunk preparation over every (chunk, head), then the state pass over every
 // (sequence, head, value block). `ws` is a workspace of plan.workspace bytes.
@@ -39,6 +50,8 @@ int32_t* prefill_snap_first(void* ws, const PrefillPlan& plan, int64_t heads, in
 // Packed sequences: the plan pass's clamped, non-decreasing copy of the offsets [nseq + 1], from which
 // every later pass (the backward's included) takes its sequence spans.
 int32_t* prefill_cu_table(void* ws, const PrefillPlan& plan, int64_t heads, int64_t nseq);
+// Fixed length over several windows: the state carried from one window to the next (NULL otherwise).
+float* prefill_carry(void* ws, const PrefillPlan& plan, int64_t heads);
 
 // Only the packed-sequence plan pass of a prefill (chunk slots, first snapshot rows, sequence
 // order) into `ws`; nothing for fixed-length sequences.

@@ -16,7 +16,7 @@ static int64_t rec_size_for(int dk) {
 }
 
 PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int64_t seqlen,
-                         int64_t heads, int dk, int dv, bool packed) {
+                         int64_t heads, int dk, int dv, bool packed, int64_t window_bytes) {
   PrefillPlan pl;
   pl.chunk = CH;
   // Value columns per state workgroup: every workgroup of a head reads the head's whole
@@ -33,11 +33,30 @@ PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int
   // (packed: whole rows of 8 pairs, one pair per XCD, times the column blocks)
   pl.workgroups = packed ? (num_pairs + 7) / 8 * 8 * pl.ndvb : (logical + 7) / 8 * 8;
   const int64_t cps = (seqlen + CH - 1) / CH;
-  pl.slots = packed ? cps + num_seqs : batch * cps;
   pl.rec_size = rec_size_for(dk);
+  pl.win_k = 0;
+  pl.windows = 1;
+  pl.carry = 0;
+  if (packed) {
+    pl.slots = cps + num_seqs;
+  } else {
+    // windows of equal numbers of chunks, as few as keep one window's records within the budget
+    // (DR_WINDOW_BYTES overrides the budget, for tests)
+    if (const char* e = getenv("DR_WINDOW_BYTES")) {
+      const long long b = atoll(e);
+      if (b > 0) window_bytes = b;
+    }
+    const int64_t per_chunk = batch * heads * pl.rec_size;  // records of one chunk of every sequence
+    int64_t kmax = per_chunk > 0 ? window_bytes / per_chunk : cps;
+    if (kmax < 1) kmax = 1;
+    pl.windows = cps > 0 ? (cps + kmax - 1) / kmax : 1;
+    pl.win_k = cps > 0 ? (cps + pl.windows - 1) / pl.windows : 0;
+    pl.slots = batch * pl.win_k;
+    if (pl.windows > 1) pl.carry = num_seqs * heads * (int64_t)dk * dv * 4;
+  }
   // chunk_seq, chunk_c0 [slots]; seq_first [nseq + 1]; snap_first, seq_order [nseq]; cu_ok [nseq + 1]
   const int64_t tables = packed ? ((2 * pl.slots + 4 * num_seqs + 2) * 4 + 255) / 256 * 256 : 0;
-  pl.workspace = pl.slots * heads * pl.rec_size + tables;
+  pl.workspace = pl.slots * heads * pl.rec_size + tables + pl.carry;
   return pl;
 }
 
@@ -49,6 +68,12 @@ int32_t* prefill_snap_first(void* ws, const PrefillPlan& pl, int64_t heads, int6
 
 int32_t* prefill_cu_table(void* ws, const PrefillPlan& pl, int64_t heads, int64_t nseq) {
   return prefill_snap_first(ws, pl, heads, nseq) + 2 * nseq;
+}
+
+float* prefill_carry(void* ws, const PrefillPlan& pl, int64_t heads) {
+  // after the records (fixed length has no tables)
+  return pl.carry > 0 ? reinterpret_cast<float*>(static_cast<unsigned char*>(ws) + pl.slots * heads * pl.rec_size)
+                      : nullptr;
 }
 
 int bwd_dv_block(int dv) { return dv >= 32 ? 32 : 16; }

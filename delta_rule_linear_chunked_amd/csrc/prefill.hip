@@ -47,20 +47,24 @@ constexpr int LDT = 68;   // padded row stride of 64-wide fp32 tiles
 constexpr float FAST_LO = 0x1p-100f;
 constexpr float FAST_HI = 0x1p100f;
 
-// Sequence, first token and length of a chunk slot. Returns false for an unused slot.
+// Sequence, first token, length and record slot of the chunk that workgroup slot `slot` prepares.
+// Returns false for an unused slot.
 __device__ __forceinline__ bool resolve_slot(const Params& p, int slot, int& n, int64_t& bos, int64_t& len,
-                                             int64_t& c0) {
+                                             int64_t& c0, int& rslot) {
   if (p.cu) {
     n = p.chunk_seq[slot];
     if (n < 0) return false;
     bos = cu_steps(p, n);
     len = cu_steps(p, n + 1) - bos;
     c0 = p.chunk_c0[slot];
-  } else {
-    n = slot / p.cps;
+    rslot = slot;
+  } else {  // chunk win_c0 + slot % win_nc of sequence slot / win_nc
+    n = slot / p.win_nc;
+    const int cw = slot % p.win_nc;
     bos = (int64_t)n * p.T;
     len = p.T;
-    c0 = (int64_t)(slot % p.cps) * CH;
+    c0 = (int64_t)(p.win_c0 + cw) * CH;
+    rslot = n * p.win_k + cw;
   }
   return true;
 }
@@ -278,10 +282,10 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
 
   const int slot = blockIdx.x / p.H;
   const int h = blockIdx.x % p.H;
-  int n;
+  int n, rslot;
   int64_t bos, len, c0;
-  if (!resolve_slot(p, slot, n, bos, len, c0)) return;
-  unsigned char* rec = p.rec + ((int64_t)h * p.slots + slot) * p.rec_size;  // a head's chunks are adjacent
+  if (!resolve_slot(p, slot, n, bos, len, c0, rslot)) return;
+  unsigned char* rec = p.rec + ((int64_t)h * p.slots + rslot) * p.rec_size;  // a head's chunks are adjacent
   const __amdgpu_buffer_rsrc_t rs = rec_rsrc(rec, p.rec_size);
   const int wu = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // the wave index, uniform
   const int H = p.H;
@@ -597,8 +601,10 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
 
 // ============================================================================ host
 template <int DKR, typename InT, bool VEC>
+static hipError_t launch_window_t(Params p, const PrefillPlan& pl, int64_t wi, hipStream_t s);
+
+template <int DKR, typename InT, bool VEC>
 static hipError_t launch_t(const Params& p0, const PrefillPlan& pl, hipStream_t s) {
-  const bool prep = p0.prep_l2 || p0.a_bf16 || p0.a_act || p0.g_act;
   if (p0.cu) {
     hipLaunchKernelGGL(chunk_plan_kernel, dim3(1), dim3(256), 0, s, p0);
     hipError_t e = hipGetLastError();
@@ -606,8 +612,29 @@ static hipError_t launch_t(const Params& p0, const PrefillPlan& pl, hipStream_t 
   }
   Params p = p0;
   if (p.cu) p.cu = p.cu_ok;  // every later pass reads the plan's clamped offsets
-  if (pl.slots > 0) {
-    const dim3 grid((unsigned)(pl.slots * p.H));
+  for (int64_t wi = 0; wi < pl.windows; ++wi) {
+    const hipError_t e = launch_window_t<DKR, InT, VEC>(p, pl, wi, s);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// One window: the chunk preparation of its chunks, then the state pass over them.
+template <int DKR, typename InT, bool VEC>
+static hipError_t launch_window_t(Params p, const PrefillPlan& pl, int64_t wi, hipStream_t s) {
+  const bool prep = p.prep_l2 || p.a_bf16 || p.a_act || p.g_act;
+  int64_t prep_slots = pl.slots;
+  if (!p.cu) {
+    const int64_t cps = p.cps;
+    p.win_c0 = (int32_t)(wi * pl.win_k);
+    p.win_nc = (int32_t)(cps - p.win_c0 < pl.win_k ? cps - p.win_c0 : pl.win_k);
+    p.win_k = (int32_t)pl.win_k;
+    p.carry_in = wi > 0;
+    p.carry_out = wi + 1 < pl.windows;
+    prep_slots = pl.win_k > 0 ? (pl.slots / pl.win_k) * p.win_nc : 0;  // batch rows x this window's chunks
+  }
+  if (prep_slots > 0) {
+    const dim3 grid((unsigned)(prep_slots * p.H));
     // the decay's storage type and activation are template arguments: each instance evaluates
     // only its own activation
     if (!prep)
@@ -642,6 +669,11 @@ static void set_workspace(Params& p, const PrefillPlan& pl, void* ws) {
   p.rec_size = pl.rec_size;
   p.slots = (int32_t)pl.slots;
   p.cps = (int32_t)((p.T + CH - 1) / CH);
+  p.win_c0 = 0;
+  p.win_nc = p.cps;
+  p.win_k = (int32_t)pl.win_k;
+  p.carry = prefill_carry(ws, pl, p.H);
+  p.carry_in = p.carry_out = 0;
   if (p.cu) {
     int32_t* tables = reinterpret_cast<int32_t*>(p.rec + pl.slots * p.H * pl.rec_size);
     p.chunk_seq = tables;

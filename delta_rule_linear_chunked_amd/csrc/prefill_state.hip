@@ -93,12 +93,15 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     bos = cu_steps(p, n);
     len = cu_steps(p, n + 1) - bos;
     first = p.seq_first[n];
-  } else {
+  } else {  // this window's chunks win_c0 .. sit at record slots n * win_k + (c - win_c0)
     bos = (int64_t)n * p.T;
     len = p.T;
-    first = n * p.cps;
+    first = n * p.win_k - p.win_c0;
   }
   const int nch = (int)((len + CH - 1) / CH);
+  // the chunks this launch covers: all of them (packed sequences), or the window's
+  const int cbeg = p.cu ? 0 : p.win_c0;
+  const int cend = p.cu ? nch : (p.win_c0 + p.win_nc < nch ? p.win_c0 + p.win_nc : nch);
   // state slot: row n of S0 / S_T, or state_idx[n] of a pool (outside the pool: start from
   // zero and store no final state)
   int64_t srow = n;
@@ -126,7 +129,10 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int ch = 16 * rt + 4 * g + i;
-          if (p.S0 && has_row && ch < DKR) x[i] = p.S0[((srow * H + h) * DKR + ch) * DV + dv0 + 16 * ct + r];
+          if (ch < DKR) {
+            if (p.carry_in) x[i] = p.carry[(((int64_t)n * H + h) * DKR + ch) * DV + dv0 + 16 * ct + r];
+            else if (p.S0 && has_row) x[i] = p.S0[((srow * H + h) * DKR + ch) * DV + dv0 + 16 * ct + r];
+          }
         }
         sm.S.put4(16 * ct + r, 16 * rt + 4 * g, x);
       }
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     WRow pw;
   };
   auto rec_ptr = [&](int c) -> __amdgpu_buffer_rsrc_t {
-    const int cc = c < nch ? c : nch - 1;
+    const int cc = c < cend ? c : cend - 1;
     return rec_rsrc(p.rec + ((int64_t)h * p.slots + first + cc) * p.rec_size, p.rec_size);
   };
   const int wu = __builtin_amdgcn_readfirstlane(w);  // the wave index, as a uniform value
@@ -176,7 +182,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     op.gC[m] = *reinterpret_cast<const f32x4*>(&gc);
   };
   auto load_vw = [&](Ops& op, int c) {
-    const int cc = c < nch ? c : nch - 1;
+    const int cc = c < cend ? c : cend - 1;
     const int64_t last = bos + len - 1;
     int64_t tv = bos + (int64_t)cc * CH + 16 * w + lr;
     tv = tv > last ? last : tv;
@@ -374,15 +380,16 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
   };
 
   Ops opA, opB;
-  if (nch > 0) load_ops(opA, 0);
+  if (cend > cbeg) load_ops(opA, cbeg);
   __syncthreads();
-  for (int c = 0; c < nch; c += 2) {
+  for (int c = cbeg; c < cend; c += 2) {
     chunk(c, opA, opB);
-    if (c + 1 < nch) chunk(c + 1, opB, opA);
+    if (c + 1 < cend) chunk(c + 1, opB, opA);
   }
 
-  // ---- final state out
-  if (p.S && has_row) store_state(p.S + (srow * H + h) * DKR * DV);
+  // ---- the state for the next window, or the final state
+  if (p.carry_out) store_state(p.carry + ((int64_t)n * H + h) * DKR * DV);
+  else if (p.S && has_row) store_state(p.S + (srow * H + h) * DKR * DV);
 }
 
 // ============================================================================ host

@@ -40,8 +40,9 @@
  * aligned. The caller owns every argument buffer; the library keeps no pointer
  * to them after a call returns. dr_decode_step uses no other device memory.
  * dr_chunk_fwd needs a workspace between its two kernels (about 128.5 KiB per
- * 64-step chunk and head at d_k = 128; a step is a token, or half a token for
- * DR_PRODUCT2); it takes it stream-ordered on `stream`
+ * 64-step chunk and head at d_k = 128 for the chunks of one window, see
+ * dr_chunk_fwd_plan_ex; a step is a token, or half a token for DR_PRODUCT2); it
+ * takes it stream-ordered on `stream`
  * from a per-device memory pool owned by the library, which keeps what it has
  * reserved for later calls (a larger problem grows it once). Apart from that
  * pool the library holds only a thread-local error message. Work is enqueued
@@ -248,8 +249,11 @@ int dr_decode_step_ex(const void* q, const void* k, const void* v, const void* a
  * (the same kernels run); the prefill's workspace is instead a static device array of
  * DR_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it runs on until the process
  * ends. The call allocates nothing: no hipMalloc, hipFree or pool allocation. A problem whose
- * workspace does not fit (at d_k = 128 about 128.5 KiB per 64-step chunk and head, so about 2000
- * chunk-heads, e.g. 8192 tokens x 16 heads) returns DR_ERR_UNSUPPORTED with nothing launched.
+ * workspace does not fit returns DR_ERR_UNSUPPORTED with nothing launched: fixed-length problems
+ * run in windows small enough for the array (one chunk of every sequence at the least, so up to
+ * about 2000 sequence-heads at d_k = 128), while packed sequences run as one window (about
+ * 128.5 KiB per 64-step chunk and head at d_k = 128, so about 2000 chunk-heads, e.g. 8192 tokens
+ * x 16 heads).
  * Every call on one GPU uses that GPU's one array, so calls that overlap on a GPU (on different
  * streams, or from different threads) race and give undefined results: serialise them.
  */
@@ -321,6 +325,27 @@ int dr_version(void);
  */
 int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t* dv_block,
                       int64_t* workgroups);
+
+/*
+ * The prefill's launch plan for `dims` in full (for tests, profiling and callers that size their
+ * memory): the fixed-length prefill runs its two passes over windows of chunk positions (a few
+ * chunks of every sequence at a time, the state carried between windows), so that one window's
+ * operand records (about 128.5 KiB per chunk and head at d_k = 128) stay within 1 GiB: the
+ * workspace of a fixed-length prefill is at most about 1 GiB plus the carried state (num_seqs *
+ * heads * d_k * d_v * 4 bytes) whatever its length. Packed sequences run as one window.
+ * DR_WINDOW_BYTES in the environment sets another budget (in bytes). With noalloc != 0 the plan is the one dr_chunk_fwd_noalloc
+ * uses (windows small enough for its static scratch). Sequences are taken as packed when batch is 1
+ * and num_seqs is not.
+ */
+typedef struct dr_plan {
+  int32_t chunk;          /* steps per chunk */
+  int32_t dv_block;       /* value columns per workgroup of the state pass */
+  int64_t workgroups;     /* workgroups of the state pass */
+  int64_t window_chunks;  /* chunks of every sequence per window (0 for packed sequences) */
+  int64_t windows;        /* launches of the two passes */
+  int64_t workspace;      /* bytes of workspace of the call */
+} dr_plan;
+int dr_chunk_fwd_plan_ex(const dr_dims* dims, int variant, int noalloc, dr_plan* plan);
 
 #ifdef __cplusplus
 }

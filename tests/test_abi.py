@@ -218,3 +218,25 @@ def test_binding_checks_snapshot_rows():
     with pytest.raises(ValueError, match="checkpoints has shape"):
         drl.chunk_bwd(**{k: v for k, v in a.items() if k != "variant"}, variant="kda",
                       dO=torch.zeros(2, 130, 2, 64), checkpoints=torch.empty(3, 2, 64, 64))
+
+
+def test_window_plans_bound_the_workspace(monkeypatch):
+    monkeypatch.delenv("DR_WINDOW_BYTES", raising=False)
+    # the KDA prefill workload (B=4, T=4096, H=16, d=128) needs 526 MB of records in all and runs
+    # as one window under the 1 GiB default budget
+    pl = drl.chunk_fwd_plan_ex(4, 4096, 16, 128, 128)
+    assert pl["windows"] == 1 and pl["window_chunks"] == 64 and pl["workspace"] < 2 ** 30, pl
+    # a 1M-token, 32-head sequence (69 GB of records as one window) runs in windows within 1 GiB
+    # plus the carried state (32 x 128 x 128 x 4 bytes)
+    pl = drl.chunk_fwd_plan_ex(1, 2 ** 20, 32, 128, 128)
+    assert pl["windows"] > 1 and pl["workspace"] <= 2 ** 30 + 32 * 128 * 128 * 4, pl
+    # the allocation-free plan of that sequence fits its static scratch
+    pl = drl.chunk_fwd_plan_ex(1, 2 ** 20, 32, 128, 128, noalloc=True)
+    assert pl["workspace"] <= drl.NOALLOC_SCRATCH_BYTES, pl
+    # packed sequences run as one window
+    pl = drl.chunk_fwd_plan_ex(1, 32768, 16, 128, 128, num_seqs=12)
+    assert pl["windows"] == 1 and pl["window_chunks"] == 0, pl
+    # under a smaller budget the KDA workload takes four windows of 16 chunks
+    monkeypatch.setenv("DR_WINDOW_BYTES", str(144 * 2 ** 20))
+    pl = drl.chunk_fwd_plan_ex(4, 4096, 16, 128, 128)
+    assert pl["windows"] == 4 and pl["window_chunks"] == 16, pl

@@ -3,8 +3,10 @@ entry point it mirrors (dr_chunk_fwd_ex, whose workspace comes from the library'
 
 Two calls in a row, the second on a smaller problem, so the second runs on what the first left in
 the static scratch; both must equal the pooled call bit for bit (the same kernels run on the same
-inputs) and match the fp64 oracle within the parity bar. A problem whose workspace exceeds the
-scratch is rejected before anything is launched."""
+inputs) and match the fp64 oracle within the parity bar. Fixed-length problems whose records would
+not fit run in more, shorter windows of chunk positions and still equal the pooled call bit for bit;
+packed sequences (one window) whose workspace exceeds the scratch are rejected before anything is
+launched."""
 import numpy as np
 import pytest
 import torch
@@ -48,15 +50,29 @@ def test_noalloc_matches_the_pooled_entry_point_on_two_calls():
         assert eo <= TOL["bf16"] and es <= TOL["bf16"], (eo, es)
 
 
+def test_noalloc_runs_a_long_fixed_length_problem_in_windows():
+    # 16384 tokens x 16 heads at d = 128: about 526 MB of records as one window; in windows of
+    # chunk positions the workspace fits the scratch
+    wl = synth.make_prefill("kda", 1, 16384, 16, 128, 128, in_dtype="bf16", seed=seed_of("noalloc", 3))
+    plan = drl.chunk_fwd_plan_ex(1, 16384, 16, 128, 128, variant="kda", noalloc=True)
+    assert plan["windows"] > 1 and plan["workspace"] <= drl.NOALLOC_SCRATCH_BYTES, plan
+    (o_ref, S_ref), (o, S) = _both(wl)
+    assert torch.equal(o, o_ref) and torch.equal(S, S_ref)
+
+
 def test_noalloc_rejects_a_workspace_beyond_the_scratch():
-    # 16384 tokens x 16 heads at d = 128: 4096 chunk-heads of records, about 526 MB of workspace
+    # two packed sequences of 8192 tokens x 16 heads at d = 128: packed sequences run as one
+    # window, about 526 MB of workspace
     B, T, H, d = 1, 16384, 16, 128
     dev = torch.device("cuda:0")
     q = torch.zeros((B, T, H, d), dtype=torch.bfloat16, device=dev)
     alpha = torch.ones((B, T, H, d), dtype=torch.float32, device=dev)
     beta = torch.zeros((B, T, H), dtype=torch.float32, device=dev)
+    cu = torch.tensor([0, 8192, 16384], dtype=torch.int32, device=dev)
     o = torch.full((B, T, H, d), 7.0, dtype=torch.float32, device=dev)
+    plan = drl.chunk_fwd_plan_ex(1, 16384, 16, 128, 128, num_seqs=2, variant="kda", noalloc=True)
+    assert plan["workspace"] > drl.NOALLOC_SCRATCH_BYTES, plan
     with pytest.raises(drl.DeltaRuleError, match="DR_ERR_UNSUPPORTED"):
-        drl.dr_chunk_fwd_noalloc(q, q, q, alpha, beta, None, "kda", None, None, o, None)
+        drl.dr_chunk_fwd_noalloc(q, q, q, alpha, beta, None, "kda", None, cu, o, None)
     torch.cuda.synchronize()
     assert bool((o == 7.0).all())
