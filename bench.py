@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+SETTLE_CALLS = 100           # untimed prefill calls before the warm-up steps (see main)
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 
 
@@ -101,21 +102,113 @@ def copy_calibration(dev, mib=512, reps=5):
             "ms_per_copy": ms, "copy_GBps": 2 * n * 4 / (ms * 1e-3) / 1e9}
 
 
-def cpu_baseline():
-    """The fp64 oracle, as it is, on the whole prefill workload (4 sequences x 16 heads x
-    4096 tokens, a few seconds of host time) on one host core."""
+def gpu_clocks():
+    """The GPU's shader and memory clock levels as the kernel driver lists them in sysfs (the
+    current level is marked with '*'); read from files, so no other program is started."""
+    import glob
+    out = {}
+    for card in sorted(glob.glob("/sys/class/drm/card*/device")):
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                with open(os.path.join(card, name)) as fh:
+                    levels = [ln.strip() for ln in fh if ln.strip()]
+            except OSError:
+                continue
+            out.setdefault(os.path.basename(os.path.dirname(card)), {})[name] = levels
+    return out or None
+
+
+def run_conditions():
+    """Host CPU model, the CPUs this process may use and the date."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        ncpu = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        ncpu = os.cpu_count()
+    return {"host_cpu_model": model or platform.processor() or platform.machine(), "host_cpus_usable": ncpu,
+            "date_utc": time.strftime("%Y-%m-%dT%H:%M:%SZ", time.gmtime())}
+
+
+_CPU_WL = {}   # the workload the forked oracle workers read (set before the pool is made)
+_PRESETS = {}  # workloads the CPU baseline generated, kept for the GPU legs of the same run
+
+
+def _pin_worker(counter, cpus):
+    """Pool initializer: pin this worker process to a core of its own (the i-th worker started takes
+    the i-th usable core)."""
+    with counter.get_lock():
+        i = counter.value
+        counter.value += 1
+    try:
+        os.sched_setaffinity(0, {cpus[i % len(cpus)]})
+    except (AttributeError, OSError):  # pragma: no cover
+        pass
+
+
+def _pinned_worker(heads):
+    """Run the oracle's step recurrence over the given heads of the current workload in this (pinned)
+    worker; returns (seconds, token-heads)."""
+    import oracle
+    wl = _CPU_WL["wl"]
+    h = list(heads)
+    g = lambda x: None if x is None else np.ascontiguousarray(x[:, :, h])  # noqa: E731
+    args_ = (g(wl.q), g(wl.k), g(wl.v), g(wl.alpha), g(wl.erase), g(wl.write))
+    S0 = None if wl.S0 is None else np.ascontiguousarray(wl.S0[:, h])
+    t0 = time.perf_counter()
+    oracle.step_recurrence(*args_, wl.variant, S0=S0, cu_seqlens=wl.cu_seqlens)
+    return time.perf_counter() - t0, wl.q.shape[0] * wl.q.shape[1] * len(h)
+
+
+def cpu_baseline(full=False):
+    """The fp64 oracle as it is (never tuned), on the host cores, in two modes: one process pinned to
+    one core (numpy limited to one thread), and the heads split over as many pinned processes as
+    there are usable cores. Every workload runs whole in the multi-process mode; on one core the
+    KDA prefill runs on 4 of its 16 heads and the varlen and long-context workloads on 1 (all of
+    them with ``full``). Rates are tokens/s of the whole workload (token-heads/s divided by its 16
+    heads). Decode: one oracle step of 1/16 of the decode workload on one core."""
+    import multiprocessing as mp
     try:
         from threadpoolctl import threadpool_limits
     except ImportError:  # pragma: no cover
         threadpool_limits = None
     import oracle
     import synth
-    wl = synth.make_prefill("kda", 4, 4096, 16, 128, 128, in_dtype="bf16", seed=1002)
     ctx = threadpool_limits(1) if threadpool_limits else None
-    t0 = time.perf_counter()
-    oracle.step_recurrence(wl.q, wl.k, wl.v, wl.alpha, wl.erase, None, "kda", S0=wl.S0)
-    dt = time.perf_counter() - t0
-    del wl
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    cpus = sorted(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else list(range(os.cpu_count() or 1))
+    H = 16
+    out = {}
+    for name, sample_heads in (("kda_prefill", 4), ("rda_varlen", 1), ("gdn2_varlen", 1), ("ckda_long", 1)):
+        _CPU_WL["wl"] = _PRESETS[name] = synth.preset(name)
+        ctx_fork = mp.get_context("fork")
+        workers = min(len(cpus), H)
+        pool = ctx_fork.Pool(workers, initializer=_pin_worker, initargs=(ctx_fork.Value("i", 0), cpus))
+        try:
+            nh = H if full else sample_heads
+            dt, th = pool.apply(_pinned_worker, (range(nh),))
+            one = {"tokens_per_s": th / dt / H, "seconds": dt, "cores": 1,
+                   "sample": "whole workload" if nh == H else f"{nh} of {H} heads, every sequence"}
+            # one head per task, the pool's processes pinned to distinct cores: the rate is all
+            # token-heads over the wall time of the whole map (rounds of tasks where there are more
+            # heads than cores)
+            tw = time.perf_counter()
+            res = pool.map(_pinned_worker, [range(i, i + 1) for i in range(H)], chunksize=1)
+            span = time.perf_counter() - tw
+            many = {"tokens_per_s": sum(r[1] for r in res) / span / H, "seconds": span,
+                    "cores": workers, "sample": "whole workload, one head per task"}
+            out[name] = {"one_core": one, "all_cores": many}
+        finally:
+            pool.close()
+            pool.join()
+            _CPU_WL.clear()
     # decode: one step of 32 of the 512 sequences (x 32 heads), the fp64 state of the subset
     # (128 MiB) updated once
     wd = synth.make_decode("kda", 32, 32, 128, 128, steps=1, in_dtype="bf16", seed=1005)
@@ -125,13 +218,19 @@ def cpu_baseline():
     dd = time.perf_counter() - t1
     if ctx is not None:
         ctx.__exit__(None, None, None)
-    cpu = platform.processor() or platform.machine()
-    return {"value": 4 * 4096 / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"the whole KDA prefill workload (4 x 4096 tokens x 16 heads, fp64 step "
-                      f"recurrence) in {dt:.1f} s on one core of {cpu}",
+    cond = run_conditions()
+    _PRESETS.pop("kda_prefill", None)  # the GPU legs draw their own KDA inputs
+    k2 = out["kda_prefill"]["one_core"]
+    nh = H if full else 4
+    return {"value": k2["tokens_per_s"], "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nh} of the 16 heads of the KDA prefill workload (4 x 4096 tokens, fp64 step recurrence) "
+                      f"in {k2['seconds']:.1f} s in one process pinned to one core of {cond['host_cpu_model']}; "
+                      f"rate scaled to the whole workload's tokens",
+            "modes": out,
             "decode": {"value": 32 * 32 / dd, "unit": "head-steps/s", "cores": 1,
                        "sample": f"one KDA decode step of 32 sequences x 32 heads (1/16 of the decode "
-                                 f"workload, fp64 state) in {dd:.2f} s on one core of {cpu}"}}
+                                 f"workload, fp64 state) in {dd:.2f} s on one core"},
+            "conditions": cond}
 
 
 def main():
@@ -141,6 +240,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--decode-steps", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-full", action="store_true",
+                    help="run the oracle on every head of every workload on one core too (minutes)")
+    ap.add_argument("--no-recurrence", action="store_true",
+                    help="skip the GPU step recurrence (the decode kernel token by token) beside the prefill")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-states", action="store_true", help="skip the snapshot and slot-pool timings")
     ap.add_argument("--no-prep", action="store_true", help="skip the fused input preparation timing")
@@ -156,6 +259,11 @@ def main():
         print("bench.py measures one GPU only; --gpus must be 1 (the path runs per GPU with no "
               "communication, see the sharding notes)", file=sys.stderr)
         sys.exit(2)
+
+    # run conditions first, then the oracle's CPU baseline in processes forked before anything
+    # touches the GPU
+    conditions = run_conditions()
+    cpu = None if (args.no_cpu_baseline or args.calibrate_copy) else cpu_baseline(full=args.cpu_full)
 
     import torch
     import delta_rule_linear_chunked_amd as drl
@@ -188,6 +296,14 @@ def main():
         s = sets[i % 2]
         drl.dr_chunk_fwd(s["q"], s["k"], s["v"], s["alpha"], s["erase"], None, "kda", s["S0"], None, o, S_T)
 
+    # The GPU idled while the CPU baseline and the inputs were made. Per-call times measured from
+    # idle: the first few calls are fast, calls 5-25 run about 10% slower while the GPU's power
+    # management reacts to the load, and from about call 30 on the time holds steady (plain copies
+    # do not bring this about). So SETTLE_CALLS untimed calls run first, then the W warm-up steps,
+    # then the K timed steps; the line reports SETTLE_CALLS.
+    for i in range(SETTLE_CALLS):
+        step(i)
+    torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -212,11 +328,79 @@ def main():
         evs[i + 1].record(stream)
     torch.cuda.synchronize()
     per = np.array([evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)])  # ms per call
+    clocks_after_timing = gpu_clocks()
     tokens = B * T
     value = tokens / (ms_step * 1e-3)
     alg_bytes, flops = prefill_work(B, T, H, D, D)
     achieved_gbs = alg_bytes / (ms_step * 1e-3) / 1e9
     plan = drl.chunk_fwd_plan(B, T, H, D, D)
+
+    # the same tokens through the step recurrence on the GPU: the decode kernel applied once per
+    # token (4096 launches over the 64 (sequence, head) states, bf16 inputs, fp32 state), timed as
+    # an eager loop and as one replayed HIP graph, with its error against the chunked call
+    recurrence = None
+    if not args.no_recurrence:
+        s = sets[0]
+        per_tok = {name: s[name].transpose(0, 1).contiguous() for name in ("q", "k", "v", "alpha", "erase")}
+        S_rec = torch.empty_like(S_T)
+        o_rec = torch.empty((T, B, H, D), dtype=torch.float32, device=dev)
+
+        def recur():
+            S_rec.copy_(s["S0"])
+            for t_ in range(T):
+                drl.dr_decode_step(per_tok["q"][t_], per_tok["k"][t_], per_tok["v"][t_], per_tok["alpha"][t_],
+                                   per_tok["erase"][t_], None, "kda", S_rec, o_rec[t_])
+
+        recur()
+        step(0)  # the chunked call on the same inputs (sets[0])
+        torch.cuda.synchronize()
+        o_r = o_rec.transpose(0, 1)
+        rms_o = o.pow(2).mean().sqrt().item()
+        rms_s = S_T.pow(2).mean().sqrt().item()
+        err_o = (o_r - o).abs().max().item() / rms_o
+        err_s = (S_rec - S_T).abs().max().item() / rms_s
+        reps = 3
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            recur()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = e0.elapsed_time(e1) / reps
+        graph_ms = None
+        try:
+            g = torch.cuda.CUDAGraph()
+            cap = torch.cuda.Stream(dev)
+            cap.wait_stream(stream)
+            with torch.cuda.stream(cap):
+                recur()  # one eager pass on the capture stream first
+            stream.wait_stream(cap)
+            torch.cuda.synchronize()
+            with torch.cuda.graph(g):
+                recur()
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(o_rec.transpose(0, 1), o_r):
+                raise RuntimeError("graph replay differs from the eager recurrence")
+            e0.record(stream)
+            for _ in range(reps):
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            graph_ms = e0.elapsed_time(e1) / reps
+            del g
+        except Exception as exc:  # noqa: BLE001 - the graph timing is optional; say why it is missing
+            graph_ms = f"not timed: {exc}"
+        best = min(eager_ms, graph_ms) if isinstance(graph_ms, float) else eager_ms
+        recurrence = {
+            "workload": "the KDA prefill's tokens (4 x 4096, 16 heads, d=128, bf16 inputs, fp32 state) through "
+                        "dr_decode_step once per token",
+            "ms_eager_loop": eager_ms, "ms_graph_replay": graph_ms, "tokens_per_s": tokens / (best * 1e-3),
+            "chunked_speedup": best / ms_step,
+            "err_o_vs_chunked": err_o, "err_S_T_vs_chunked": err_s,
+            "err_metric": "max |recurrence - chunked| / RMS(chunked), on o and on S_T"}
+        del per_tok, S_rec, o_rec, o_r
 
     # stored-state options on the same workload: snapshots every 64 and every 1024 tokens
     states = None
@@ -387,7 +571,7 @@ def main():
     if not args.no_configs:
         others = {}
         for name, gate_bytes in (("rda_varlen", 8), ("gdn2_varlen", 4 * (D + D)), ("ckda_long", 4)):
-            wl = synth.preset(name)
+            wl = _PRESETS.pop(name, None) or synth.preset(name)
             a = dict(q=t(wl.q, True), k=t(wl.k, True), v=t(wl.v, True), alpha=t(wl.alpha), erase=t(wl.erase),
                      write=t(wl.write), S0=t(wl.S0), cu=None if wl.cu_seqlens is None else t(wl.cu_seqlens))
             Bw, Tw = wl.q.shape[0], wl.q.shape[1]
@@ -425,6 +609,15 @@ def main():
         if tj.get("kernel_source_sha256") == kernel_source_digest():
             traffic = tj.get("bytes_per_launch")
             kernel_traffic = {k: v["bytes"] for k, v in tj.get("kernels", {}).items()}
+
+    # matrix-core busy fraction of each prefill kernel, from rocprofv3 counters taken on this
+    # workload and these kernel sources: SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x CUs x 4 SIMDs)
+    mfma_busy = None
+    mfile = os.path.join(ROOT, "profiles", "chunk_fwd_kda_B4_T4096_H16_d128_mfma.json")
+    if os.path.exists(mfile):
+        mj = json.load(open(mfile))
+        if mj.get("kernel_source_sha256") == kernel_source_digest():
+            mfma_busy = {k: v["mfma_busy_frac"] for k, v in mj.get("kernels", {}).items()}
 
     # ------------------------------------------------------------------ decode
     decode = None
@@ -571,11 +764,12 @@ def main():
                      "alg_bytes_per_launch": alg_bytes, "traffic_per_kernel": kernel_traffic},
         "mfma": {"useful_tflops": flops / (ms_step * 1e-3) / 1e12,
                  "frac_of_bf16_peak": flops / (ms_step * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
-                 "useful_flop_per_launch": flops},
+                 "useful_flop_per_launch": flops, "busy_frac_per_kernel": mfma_busy},
         "latency_ms": {"p50": float(np.percentile(per, 50)), "p95": float(np.percentile(per, 95)),
                        "p99": float(np.percentile(per, 99)), "mean": float(per.mean()),
                        "from": "a second loop with an event after every call"},
         "decode": decode,
+        "step_recurrence": recurrence,
         "stored_states": states,
         "fused_prep": fused,
         "backward": bwd,
@@ -584,11 +778,11 @@ def main():
         "measured_copy_GBps": copy["copy_GBps"],
         "run": {"gpu": props.name, "arch": getattr(props, "gcnArchName", ""),
                 "cus": props.multi_processor_count, "torch": torch.__version__,
-                "hip": getattr(torch.version, "hip", None), "host_cpu": platform.processor(),
-                "wall_s_timed": wall},
+                "hip": getattr(torch.version, "hip", None), "wall_s_timed": wall, "settle_calls_before_warmup": SETTLE_CALLS, **conditions,
+                "gpu_clocks_after_timing": clocks_after_timing},
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
+    if cpu is not None:
+        line["cpu_baseline"] = cpu
     print(json.dumps(line))
 
 
