@@ -224,16 +224,28 @@ struct PolF32 {
   }
 };
 
+// Split of two fp32 values into bf16 hi (round to nearest even) and the bf16 of the remainder
+// x - hi, as two packed pairs: one packed conversion for the two hi halves, their fp32 values by a
+// shift and a mask, two subtractions and one packed conversion for lo (converting value by value
+// leads the compiler to convert each hi twice).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void split2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+  const float ha = __builtin_bit_cast(float, hi << 16);
+  const float hb = __builtin_bit_cast(float, hi & 0xffff0000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a - ha, b - hb}, bf16x2));
+}
+
 struct PolBF3 {
   struct Frag { bf16x8 hi, lo; };
   static __device__ __forceinline__ Frag make(const float (&x)[8]) {
-    Frag f;
+    uint32_t h[4], o[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const __bf16 h = (__bf16)x[j];
-      f.hi[j] = h;
-      f.lo[j] = (__bf16)(x[j] - (float)h);
-    }
+    for (int j = 0; j < 4; ++j) split2(x[2 * j], x[2 * j + 1], h[j], o[j]);
+    Frag f;
+    f.hi = __builtin_bit_cast(bf16x8, h);
+    f.lo = __builtin_bit_cast(bf16x8, o);
     return f;
   }
   static __device__ __forceinline__ void mma(f32x4& acc, const Frag& a, const Frag& b) {

@@ -18,14 +18,11 @@ template <class Pol, int ROWS, int COLS> struct OpTile;
 template <int ROWS, int COLS> struct OpTile<PolBF3, ROWS, COLS> {
   __bf16 hi[ROWS][COLS + 8], lo[ROWS][COLS + 8];
   __device__ __forceinline__ void put4(int row, int col, const f32x4& x) {
-    bf16x4 h, o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      h[i] = (__bf16)x[i];
-      o[i] = (__bf16)(x[i] - (float)h[i]);
-    }
-    *reinterpret_cast<bf16x4*>(&hi[row][col]) = h;
-    *reinterpret_cast<bf16x4*>(&lo[row][col]) = o;
+    uint32_t h[2], o[2];
+    split2(x[0], x[1], h[0], o[0]);
+    split2(x[2], x[3], h[1], o[1]);
+    *reinterpret_cast<bf16x4*>(&hi[row][col]) = __builtin_bit_cast(bf16x4, h);
+    *reinterpret_cast<bf16x4*>(&lo[row][col]) = __builtin_bit_cast(bf16x4, o);
   }
   __device__ __forceinline__ PolBF3::Frag get8(int row, int col) const {
     PolBF3::Frag f;
