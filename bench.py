@@ -242,6 +242,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-full", action="store_true",
                     help="run the oracle on every head of every workload on one core too (minutes)")
+    ap.add_argument("--no-strided", action="store_true",
+                    help="skip the prefill on q, k, v given as views of one fused projection")
     ap.add_argument("--no-recurrence", action="store_true",
                     help="skip the GPU step recurrence (the decode kernel token by token) beside the prefill")
     ap.add_argument("--no-decode", action="store_true")
@@ -401,6 +403,39 @@ def main():
             "err_o_vs_chunked": err_o, "err_S_T_vs_chunked": err_s,
             "err_metric": "max |recurrence - chunked| / RMS(chunked), on o and on S_T"}
         del per_tok, S_rec, o_rec, o_r
+
+    # q, k, v as views of one fused [B, T, 3, H, d] projection (read through their strides, no copy)
+    strided = None
+    if not args.no_strided:
+        fused_sets = [torch.stack([s_["q"], s_["k"], s_["v"]], dim=2).contiguous() for s_ in sets]
+
+        def fstep(i):
+            s_, f_ = sets[i % 2], fused_sets[i % 2]
+            drl.dr_chunk_fwd(f_[:, :, 0], f_[:, :, 1], f_[:, :, 2], s_["alpha"], s_["erase"], None, "kda", s_["S0"],
+                             None, o, S_T)
+
+        for i in range(10):
+            fstep(i)
+        torch.cuda.synchronize()
+        # blocks of dense and strided calls in alternation (medians of the block means), so that
+        # a drift of the clocks between two loops does not pass for a cost of the strides
+        blocks = {"dense": [], "strided": []}
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for rnd in range(8):
+            order = (("dense", step), ("strided", fstep)) if rnd % 2 == 0 else (("strided", fstep), ("dense", step))
+            for name, fn in order:
+                e0.record(stream)
+                for i in range(10):
+                    fn(i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                blocks[name].append(e0.elapsed_time(e1) / 10)
+        fms, dms_ = float(np.median(blocks["strided"])), float(np.median(blocks["dense"]))
+        strided = {"workload": "the KDA prefill with q, k, v as views of one [4, 4096, 3, 16, 128] bf16 tensor "
+                               "(token stride 3 H d)", "ms_per_step": fms, "tokens_per_s": tokens / (fms * 1e-3),
+                   "dense_ms_same_blocks": dms_, "vs_dense": fms / dms_,
+                   "timing": "medians of 8 blocks of 10 calls each, dense and strided blocks alternating"}
+        del fused_sets
 
     # stored-state options on the same workload: snapshots every 64 and every 1024 tokens
     states = None
@@ -770,6 +805,7 @@ def main():
                        "from": "a second loop with an event after every call"},
         "decode": decode,
         "step_recurrence": recurrence,
+        "strided_inputs": strided,
         "stored_states": states,
         "fused_prep": fused,
         "backward": bwd,

@@ -41,7 +41,17 @@ class DeltaRuleError(RuntimeError):
 class _Dims(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("num_heads", ctypes.c_int64),
                 ("head_dim_k", ctypes.c_int64), ("head_dim_v", ctypes.c_int64),
-                ("num_seqs", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("num_seqs", ctypes.c_int64), ("in_dtype", ctypes.c_int32), ("version", ctypes.c_int32)]
+
+
+DIMS_V2 = 2  # dr_dims.version of a dr_dims_v2 (strided q, k, v)
+
+
+class _DimsV2(ctypes.Structure):
+    _fields_ = [("base", _Dims),
+                ("q_token_stride", ctypes.c_int64), ("q_batch_stride", ctypes.c_int64),
+                ("k_token_stride", ctypes.c_int64), ("k_batch_stride", ctypes.c_int64),
+                ("v_token_stride", ctypes.c_int64), ("v_batch_stride", ctypes.c_int64)]
 
 
 class _Opts(ctypes.Structure):
@@ -153,6 +163,46 @@ def _need(t: Optional[torch.Tensor], name: str, shape, dtype=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _need_rows(t: Optional[torch.Tensor], name: str, shape, nlead: int, dtype, device):
+    """Check q, k or v: shape, dtype and device as ``_need``, and a layout the kernels can read
+    through strides: the dimensions after the ``nlead`` leading ones (batch and token, or the
+    sequence for decode) dense. Returns the element strides of the leading dimensions (0 for a
+    dimension of size 1, which is never stepped over)."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.numel() == 0:  # nothing is read
+        return (0,) * nlead
+    inner = 1
+    for dim in range(t.dim() - 1, nlead - 1, -1):
+        if t.shape[dim] != 1 and t.stride(dim) != inner:
+            raise ValueError(f"{name}: the dimensions after its first {nlead} must be dense (strides "
+                             f"{tuple(t.stride())}); only its batch and token strides may be free")
+        inner *= t.shape[dim]
+    return tuple(0 if t.shape[dim] == 1 else t.stride(dim) for dim in range(nlead))
+
+
+def _dims_for(B, T, H, dk, dv, N, dtype, strides):
+    """dr_dims for dense q, k, v, else a dr_dims_v2 with their strides ((token, batch) x 3)."""
+    d = _Dims(B, T, H, dk, dv, N, _DT[dtype], 0)
+    if strides is None:
+        return d
+    d.version = DIMS_V2
+    return _DimsV2(d, *strides)
+
+
+def _dims_arg(d):
+    """The pointer to pass where the C ABI takes a const dr_dims* (a dr_dims_v2 starts with one)."""
+    if isinstance(d, _DimsV2):
+        return ctypes.cast(ctypes.pointer(d), ctypes.POINTER(_Dims))
+    return ctypes.byref(d)
+
+
 def _gate_shapes(variant: str, lead, dk, dv):
     if variant in ("kda", "ckda"):
         return tuple(lead), None
@@ -253,9 +303,11 @@ def _chunk_fwd_call(entry, q, k, v, alpha, erase, write, variant, S0, cu_seqlens
     if q.dtype not in _DT:
         raise ValueError(f"q dtype {q.dtype} is not float32 or bfloat16")
     nt = (2,) if variant == "product2" else ()  # the transition axis of k and v
-    _need(q, "q", (B, T, H, dk), q.dtype, dev)
-    _need(k, "k", (B, T, H) + nt + (dk,), q.dtype, dev)
-    _need(v, "v", (B, T, H) + nt + (dv,), q.dtype, dev)
+    # q, k, v may be views (e.g. of one fused projection): batch and token strides are free
+    sq = _need_rows(q, "q", (B, T, H, dk), 2, q.dtype, dev)
+    sk = _need_rows(k, "k", (B, T, H) + nt + (dk,), 2, q.dtype, dev)
+    sv = _need_rows(v, "v", (B, T, H) + nt + (dv,), 2, q.dtype, dev)
+    strides = None if all(x.is_contiguous() for x in (q, k, v)) else (sq[1], sq[0], sk[1], sk[0], sv[1], sv[0])
     _need(alpha, "alpha", (B, T, H, dk), _alpha_dtype(alpha, prep), dev)
     es, ws = _gate_shapes(variant, (B, T, H), dk, dv)
     _need(erase, "erase", es, torch.float32, dev)
@@ -292,12 +344,12 @@ def _chunk_fwd_call(entry, q, k, v, alpha, erase, write, variant, S0, cu_seqlens
         _need(snapshots, "snapshots", (rows_s, H, dk, dv), torch.float32, dev)
     if o is not None:  # None: final states / snapshots only
         _need(o, "o", (B, T, H, dv), torch.float32, dev)
-    d = _Dims(B, T, H, dk, dv, N, _DT[q.dtype], 0)
+    d = _dims_for(B, T, H, dk, dv, N, q.dtype, strides)
     opts = _opts(state_idx, rows, snapshots, snapshot_every, prep, alpha)
     with torch.cuda.device(dev):  # the library launches on the current device
         st = getattr(lib, entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
                                  VARIANTS[variant], _ptr(S0), _ptr(cu_seqlens), _ptr(o), _ptr(S_T),
-                                 ctypes.byref(d), ctypes.byref(opts), _stream(dev))
+                                 _dims_arg(d), ctypes.byref(opts), _stream(dev))
     _check(lib, st, entry)
 
 
@@ -318,9 +370,11 @@ def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_id
     if q.dtype not in _DT:
         raise ValueError(f"q dtype {q.dtype} is not float32 or bfloat16")
     nt = (2,) if variant == "product2" else ()
-    _need(q, "q", (N, H, dk), q.dtype, dev)
-    _need(k, "k", (N, H) + nt + (dk,), q.dtype, dev)
-    _need(v, "v", (N, H) + nt + (dv,), q.dtype, dev)
+    # q, k, v may be views with a free stride between sequences
+    sq = _need_rows(q, "q", (N, H, dk), 1, q.dtype, dev)[0]
+    sk = _need_rows(k, "k", (N, H) + nt + (dk,), 1, q.dtype, dev)[0]
+    sv = _need_rows(v, "v", (N, H) + nt + (dv,), 1, q.dtype, dev)[0]
+    strides = None if all(x.is_contiguous() for x in (q, k, v)) else (0, sq, 0, sk, 0, sv)
     _need(alpha, "alpha", (N, H, dk), _alpha_dtype(alpha, prep), dev)
     es, ws = _gate_shapes(variant, (N, H), dk, dv)
     _need(erase, "erase", es, torch.float32, dev)
@@ -335,11 +389,11 @@ def dr_decode_step_ex(q, k, v, alpha, erase, write, variant: str, S, o, state_id
         rows = S.shape[0]
     _need(S, "S", (rows, H, dk, dv), torch.float32, dev)
     _need(o, "o", (N, H, dv), torch.float32, dev)
-    d = _Dims(N, 1, H, dk, dv, N, _DT[q.dtype], 0)
+    d = _dims_for(N, 1, H, dk, dv, N, q.dtype, strides)
     opts = _opts(state_idx, rows, None, 0, prep, alpha)
     with torch.cuda.device(dev):
         st = lib.dr_decode_step_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write),
-                                   VARIANTS[variant], _ptr(S), _ptr(o), ctypes.byref(d), ctypes.byref(opts),
+                                   VARIANTS[variant], _ptr(S), _ptr(o), _dims_arg(d), ctypes.byref(opts),
                                    _stream(dev))
     _check(lib, st, "dr_decode_step")
 

@@ -59,11 +59,48 @@ int check_variant(int variant, const float* erase, const float* write, bool has_
   return DR_OK;
 }
 
+// Element strides of q, k, v: {q token, q batch, k token, k batch, v token, v batch}, the
+// caller's (dr_dims_v2) or those of dense inputs with `rows` tokens per batch row (lg: log2 of
+// the steps per token).
+static void input_strides(const dr_dims* d, int lg, int64_t rows, int64_t st[6]) {
+  if (d->version == DR_DIMS_V2) {
+    const dr_dims_v2* v = reinterpret_cast<const dr_dims_v2*>(d);
+    st[0] = v->q_token_stride; st[1] = v->q_batch_stride;
+    st[2] = v->k_token_stride; st[3] = v->k_batch_stride;
+    st[4] = v->v_token_stride; st[5] = v->v_batch_stride;
+    return;
+  }
+  st[0] = d->num_heads * d->head_dim_k;
+  st[2] = (d->num_heads * d->head_dim_k) << lg;
+  st[4] = (d->num_heads * d->head_dim_v) << lg;
+  st[1] = rows * st[0]; st[3] = rows * st[2]; st[5] = rows * st[4];
+}
+
+// (rows: tokens per batch row; the decode step has one)
+static void set_strides(dr::Params& p, const dr_dims* d, int lg, int64_t rows) {
+  int64_t st[6];
+  input_strides(d, lg, rows, st);
+  p.q_ts = st[0]; p.q_bs = st[1]; p.k_ts = st[2]; p.k_bs = st[3]; p.v_ts = st[4]; p.v_bs = st[5];
+}
+
 int check_dims_common(const dr_dims* d) {
   if (d == nullptr) return fail(DR_ERR_NULL, "dims is NULL");
-  if (d->reserved != 0) return fail(DR_ERR_SHAPE, "dims.reserved must be 0");
   if (d->in_dtype != DR_F32 && d->in_dtype != DR_BF16)
     return fail(DR_ERR_DTYPE, "in_dtype %d is neither DR_F32 nor DR_BF16", d->in_dtype);
+  if (d->version != 0 && d->version != DR_DIMS_V2)
+    return fail(DR_ERR_SHAPE, "dims.version %d is neither 0 nor DR_DIMS_V2", d->version);
+  if (d->version == DR_DIMS_V2) {
+    int64_t st[6];
+    input_strides(d, 0, d->seqlen, st);
+    static const char* names[6] = {"q token", "q batch", "k token", "k batch", "v token", "v batch"};
+    const int64_t esz = d->in_dtype == DR_BF16 ? 2 : 4;
+    for (int i = 0; i < 6; ++i) {
+      if (st[i] < 0) return fail(DR_ERR_SHAPE, "%s stride %lld is negative", names[i], (long long)st[i]);
+      if (st[i] > ((int64_t)1 << 40) || (st[i] * esz) % 16 != 0)
+        return fail(DR_ERR_ALIGN, "%s stride %lld is not a multiple of 16 bytes (or is beyond 2^40)", names[i],
+                    (long long)st[i]);
+    }
+  }
   if (d->batch < 0 || d->seqlen < 0 || d->num_heads < 1 || d->num_seqs < 0)
     return fail(DR_ERR_SHAPE, "bad sizes: batch=%lld seqlen=%lld heads=%lld seqs=%lld",
                 (long long)d->batch, (long long)d->seqlen, (long long)d->num_heads,
@@ -319,6 +356,7 @@ static int chunk_fwd_impl(const void* q, const void* k, const void* v, const voi
   p.write = (variant == DR_RDA || variant == DR_GDN2) ? write : erase;
   p.S0 = S0; p.cu = cu_seqlens; p.o = o; p.S = S_T;
   p.lgnh = lg;
+  set_strides(p, dims, lg, dims->seqlen);
   p.T = dims->seqlen << lg;
   p.H = (int32_t)dims->num_heads;
   p.DV = (int32_t)dims->head_dim_v;
@@ -422,6 +460,16 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
   const int dkh = (int)dims->head_dim_k, dvh = (int)dims->head_dim_v;
   const int64_t H = dims->num_heads, pairs = dims->num_seqs * H;
 
+  if (dims->version == DR_DIMS_V2) {
+    dr_dims dense = *dims;
+    dense.version = 0;
+    int64_t a[6], b[6];
+    input_strides(dims, lg, dims->seqlen, a);
+    input_strides(&dense, lg, dims->seqlen, b);
+    for (int j = 0; j < 6; ++j)
+      if (a[j] != b[j] && !(j % 2 == 1 && dims->batch <= 1))
+        return fail(DR_ERR_UNSUPPORTED, "the backward pass takes dense q, k, v (strides other than the dense ones)");
+  }
   // the states after every 64 steps: the caller's (a prefill's snapshots), or a forward pass
   // with no output
   dr::Params p{};
@@ -430,6 +478,7 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
   p.write = has_write ? write : erase;
   p.S0 = S0; p.cu = cu_seqlens; p.o = nullptr; p.S = nullptr;
   p.lgnh = lg;
+  set_strides(p, dims, lg, dims->seqlen);  // dense (checked above)
   p.T = dims->seqlen << lg;
   p.H = (int32_t)H;
   p.DV = (int32_t)dvh;
@@ -539,6 +588,7 @@ int dr_decode_step_ex(const void* q, const void* k, const void* v, const void* a
   p.o = o; p.S = S;
   p.H = (int32_t)dims->num_heads;
   p.DV = (int32_t)dims->head_dim_v;
+  set_strides(p, dims, variant == DR_PRODUCT2 ? 1 : 0, 1);
   hipError_t e = variant == DR_PRODUCT2
                      ? dr::launch_decode2(p, nheads, (int)dims->head_dim_k, (int)dims->head_dim_v,
                                           dims->in_dtype == DR_BF16, stream)

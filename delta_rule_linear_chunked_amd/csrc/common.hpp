@@ -69,6 +69,11 @@ struct Params {
   // count steps (cu offsets stay in tokens and are scaled on read), q and alpha rows
   // are per token, k, v and the gates per step, and o is written after a token's last step.
   int32_t lgnh;
+  // element strides of q, k and v: between consecutive tokens of a batch row (_ts) and between
+  // batch rows (_bs; decode: between sequences). Within a token the heads are d apart (k and v
+  // with two steps per token: a head's two steps are d apart, heads 2d apart). Dense inputs have
+  // _ts = H d (x2 for k, v with two steps per token) and _bs = tokens per row x _ts.
+  int64_t q_ts, q_bs, k_ts, k_bs, v_ts, v_bs;
 };
 
 // Row of step m (absolute step index) in the per-token arrays (q, alpha, o) and in the
@@ -78,6 +83,15 @@ __device__ __forceinline__ int64_t tok_row(const Params& p, int64_t m, int h) {
 }
 __device__ __forceinline__ int64_t step_row(const Params& p, int64_t m, int h) {
   return (((m >> p.lgnh) * p.H + h) << p.lgnh) + (m & ((1 << p.lgnh) - 1));
+}
+// Element offsets of q (per token) and of k / v (per step) for step s of batch row b, counted
+// from the start of the row, head h, with d elements per row of the input.
+__device__ __forceinline__ int64_t q_elem(const Params& p, int64_t b, int64_t s, int h, int d) {
+  return b * p.q_bs + (s >> p.lgnh) * p.q_ts + (int64_t)h * d;
+}
+__device__ __forceinline__ int64_t kv_elem(int64_t ts, int64_t bs, const Params& p, int64_t b, int64_t s, int h,
+                                           int d) {
+  return b * bs + (s >> p.lgnh) * ts + ((((int64_t)h) << p.lgnh) + (s & ((1 << p.lgnh) - 1))) * d;
 }
 // Offset of sequence n in steps, from the packed token offsets.
 __device__ __forceinline__ int64_t cu_steps(const Params& p, int n) { return (int64_t)p.cu[n] << p.lgnh; }

@@ -72,9 +72,10 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode_kernel(const
   // The token's vectors first (one element per thread; they are small and the staging below
   // needs them), then the state: memory returns in issue order, so the staging does not wait
   // for the state to arrive.
-  const InT* q = static_cast<const InT*>(p.q) + nh * DK;
-  const InT* k = static_cast<const InT*>(p.k) + nh * DK;
-  const InT* v = static_cast<const InT*>(p.v) + nh * DV + col0;
+  const int64_t sn = nh / p.H, sh = nh - sn * p.H;  // sequence and head (inputs through their strides)
+  const InT* q = static_cast<const InT*>(p.q) + sn * p.q_bs + sh * DK;
+  const InT* k = static_cast<const InT*>(p.k) + sn * p.k_bs + sh * DK;
+  const InT* v = static_cast<const InT*>(p.v) + sn * p.v_bs + sh * DV + col0;
   static_assert(DK <= NT && DVS <= NT, "one token element per thread");
   const bool prep = p.a_act || p.g_act || p.a_bf16;  // fused activations (uniform)
   float qi = 0.f, ki = 0.f, az = 0.f, e = 0.f, vj = 0.f, wr = 0.f;
@@ -262,10 +263,11 @@ __global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) void decode2_kernel(cons
   float* S = p.S + srow * (int64_t)DK * DV + col0;
 
   // token vectors first, then the state (see decode_kernel)
-  const InT* q = static_cast<const InT*>(p.q) + nh * DK;
-  const InT* k1 = static_cast<const InT*>(p.k) + (2 * nh) * DK;
+  const int64_t sn = nh / p.H, sh = nh - sn * p.H;  // sequence and head (inputs through their strides)
+  const InT* q = static_cast<const InT*>(p.q) + sn * p.q_bs + sh * DK;
+  const InT* k1 = static_cast<const InT*>(p.k) + sn * p.k_bs + (2 * sh) * DK;
   const InT* k2 = k1 + DK;
-  const InT* v1 = static_cast<const InT*>(p.v) + (2 * nh) * DV + col0;
+  const InT* v1 = static_cast<const InT*>(p.v) + sn * p.v_bs + (2 * sh) * DV + col0;
   const InT* v2 = v1 + DV;
   static_assert(DK <= NT && DVS <= NT, "one token element per thread");
   const bool prep = p.a_act || p.g_act || p.a_bf16;  // fused activations (uniform)

@@ -208,8 +208,8 @@ __device__ __forceinline__ void load_alpha(const Params& p, int64_t i, float (&a
 // A block with a gate at or extremely near zero (rare): k . g from exact suffix products and
 // the diagonal tiles of A and P from running products of the gates, exact for any gate value.
 template <int DKR, int DK, typename InT, bool VEC, int AM, int ACT>
-__device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, int64_t thq, int64_t thk, bool unit_a,
-                                         bool valid, float esc,
+__device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, int64_t thq, int64_t thk, int64_t qo,
+                                         int64_t ko, bool unit_a, bool valid, float esc,
                                          float rq, float rk, int w, int r, int g) {
   constexpr int KS = DK / 32;
   const int row = 16 * w + r;
@@ -226,7 +226,7 @@ __device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, i
     const bool live = valid && ch0 < DKR;
     float a8[8], k8[8];
     alpha8(thq * DKR + (live ? ch0 : 0), a8);
-    load8(kp + thk * DKR + (live ? ch0 : 0), k8);
+    load8(kp + ko + (live ? ch0 : 0), k8);
     float kgv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) kgv[j] = (live ? k8[j] * rk : 0.f) * row_suffix_prod_excl(live && !unit_a ? a8[j] : 1.f);
@@ -241,8 +241,8 @@ __device__ __forceinline__ void exact_block(const Params& p, PrepSmem<DK>& sm, i
       const bool live = valid && ch0 < DKR;
       float a2[8], k2[8], q2[8], b2[8];
       load_alpha<AM == 0 ? 0 : AM == 2 ? 3 : 4>(p, thq * DKR + (live ? ch0 : 0), a2);  // raw
-      load8(kp + thk * DKR + (live ? ch0 : 0), k2);
-      load8(qp + thq * DKR + (live ? ch0 : 0), q2);
+      load8(kp + ko + (live ? ch0 : 0), k2);
+      load8(qp + qo + (live ? ch0 : 0), q2);
       if constexpr (VEC) load8(p.erase + thk * DKR + (live ? ch0 : 0), b2);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -309,6 +309,9 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   // decay acts on the first step of a token only
   const int64_t mstep = bos + c0 + (valid ? row : 0);
   const int64_t thq = tok_row(p, mstep, h), thk = step_row(p, mstep, h);
+  // q and k through their strides (alpha and the gates are dense: rows thq, thk)
+  const int64_t brow = p.cu ? 0 : n, srow = p.cu ? mstep : mstep - bos;
+  const int64_t qo = q_elem(p, brow, srow, h, DKR), ko = kv_elem(p.k_ts, p.k_bs, p, brow, srow, h, DKR);
   const bool unit_a = (mstep & ((1 << p.lgnh) - 1)) != 0;
 
   // ---------------------------------------------------------------- input preparation
@@ -332,8 +335,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       const int ch0 = 32 * ks + 8 * g;
       if (valid && ch0 < DKR) {
         float k8[8], q8[8];
-        load8(kp + thk * DKR + ch0, k8);
-        load8(qp + thq * DKR + ch0, q8);
+        load8(kp + ko + ch0, k8);
+        load8(qp + qo + ch0, q8);
 #pragma unroll
         for (int j = 0; j < 8; ++j) { sq = fmaf(q8[j], q8[j], sq); sk = fmaf(k8[j], k8[j], sk); }
       }
@@ -365,8 +368,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       const bool live = valid && ch0 < DKR;
       float a8[8], k8[8], q8[8], b8[8];
       if (live) {
-        load8(kp + thk * DKR + ch0, k8);
-        load8(qp + thq * DKR + ch0, q8);
+        load8(kp + ko + ch0, k8);
+        load8(qp + qo + ch0, q8);
         if constexpr (AM != 0) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) a8[j] = av[ks][j];
@@ -423,7 +426,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       }
     } else {
       // Some gate of this block is zero or nearly so: exact block path (out of line).
-      exact_block<DKR, DK, InT, VEC, AM, ACT>(p, sm, thq, thk, unit_a, valid, esc, rq, rk, w, r, g);
+      exact_block<DKR, DK, InT, VEC, AM, ACT>(p, sm, thq, thk, qo, ko, unit_a, valid, esc, rq, rk, w, r, g);
     }
   }
   wave_lds_sync();

@@ -184,7 +184,8 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     int64_t tv = bos + (int64_t)cc * CH + 16 * w + lr;
     tv = tv > last ? last : tv;
     const int64_t thv = step_row(p, tv, h);
-    op.pv = *reinterpret_cast<const RowV*>(vp + thv * DV + dv0 + lc);
+    const int64_t vo = kv_elem(p.v_ts, p.v_bs, p, p.cu ? 0 : n, p.cu ? tv : tv - bos, h, DV);
+    op.pv = *reinterpret_cast<const RowV*>(vp + vo + dv0 + lc);
     if constexpr (VEC) op.pw = *reinterpret_cast<const RowF*>(p.write + thv * DV + dv0 + lc);
     else op.pw = p.write[thv];
   };

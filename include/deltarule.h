@@ -99,6 +99,8 @@ typedef enum dr_status {
  *   head_dim_k d_k, head_dim_v d_v: each one of 16, 32, 64, 128
  *   num_seqs   N: number of sequences (= B without cu_seqlens, len(cu_seqlens) - 1 with it)
  *   in_dtype   element type of q, k, v (dr_dtype)
+ *   version    0: q, k, v are dense as the entry points describe them; DR_DIMS_V2: the struct is
+ *              the first member of a dr_dims_v2, whose strides place q, k and v
  */
 typedef struct dr_dims {
   int64_t batch;
@@ -108,8 +110,29 @@ typedef struct dr_dims {
   int64_t head_dim_v;
   int64_t num_seqs;
   int32_t in_dtype;
-  int32_t reserved; /* must be 0 */
+  int32_t version; /* 0 or DR_DIMS_V2 */
 } dr_dims;
+
+/* Strided q, k, v (a pointer to `base` is passed where a dr_dims is expected, with
+ * base.version = DR_DIMS_V2), e.g. views of one fused [B, T, 3, H, d] projection. Each input
+ * keeps its last dimension contiguous and its heads d apart within a token (d_k for q and k, d_v
+ * for v; for DR_PRODUCT2, k and v keep a token's two steps d apart and heads 2 d apart), and gives
+ * two element strides: between consecutive tokens of a batch row, and between batch rows (for
+ * the decode step, between sequences; its token stride is unused). Dense inputs have token
+ * stride H d (2 H d for DR_PRODUCT2's k and v) and batch stride T times that. Strides must be
+ * non-negative and, times the element size, multiples of 16 bytes; every element the strides
+ * address must lie inside the caller's buffer (not checked). alpha, the gates, the states and
+ * the output stay dense. dr_chunk_fwd, dr_chunk_fwd_ex, dr_chunk_fwd_noalloc, dr_decode_step and
+ * dr_decode_step_ex take strided inputs; dr_chunk_bwd and dr_chunk_bwd_ex return
+ * DR_ERR_UNSUPPORTED for strides other than the dense ones.
+ */
+#define DR_DIMS_V2 2
+typedef struct dr_dims_v2 {
+  dr_dims base;
+  int64_t q_token_stride, q_batch_stride;
+  int64_t k_token_stride, k_batch_stride;
+  int64_t v_token_stride, v_batch_stride;
+} dr_dims_v2;
 
 /*
  * Chunkwise-parallel prefill (the "scan/chunked" form of the recurrence that the
