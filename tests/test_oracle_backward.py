@@ -164,3 +164,27 @@ def test_reverse_chain_is_a_time_reversed_forward_run(signed):
     for t in range(T):
         dR = o_r[0, 2 * (T - 1 - t)]                         # d(delta)_t = dL/dm_t
         np.testing.assert_allclose(w[0, t][:, None] * dR, g["dv"][0, t], rtol=1e-10, atol=1e-10)
+
+
+@pytest.mark.parametrize("signed", [False, True])
+def test_gate_gradient_is_a_reverse_cumulative_sum(signed):
+    """Every decay factor of the recurrence unrolled over a sequence is a product of consecutive
+    gates alpha_{s+1} ... alpha_r, and alpha_t times its derivative in alpha_t is the product itself
+    when s < t <= r. Grouping the products by their last index r (terms in q_r . dq_r and
+    u_r . du_r), by their first index s + 1 (terms in k_s . dk_s, k as the key only) and by the
+    end state: alpha_t . dalpha_t = sum_{j >= t} (q_j . dq_j + u_j . du_j - k_j . dk_j) +
+    rowsum(dS_T . S_T), per channel. With GDN-2's u = b . k, u . du = b . derase and the key-only
+    k . dk is k . dk - b . derase. The identity is what a chunked backward can compute the gate
+    gradient from (a reverse scan, then a division by alpha); here the oracle's gradients, from
+    the reverse walk, must satisfy it."""
+    a, S0 = _inputs("gdn2", B=2, T=9, H=2, dk=4, dv=3, signed=signed)
+    a[3][np.abs(a[3]) < 0.05] = 0.5  # away from zero: the identity divides by alpha
+    q, k, v, alpha, erase, write = a
+    do = RNG.standard_normal(v.shape)
+    dS_T = RNG.standard_normal(S0.shape)
+    g = backward.step_recurrence_grads(q, k, v, alpha, erase, write, "gdn2", do, dS_T=dS_T, S0=S0)
+    _, S_T = oracle.step_recurrence(q, k, v, alpha, erase, write, "gdn2", S0=S0)
+    per_token = q * g["dq"] + 2 * erase * g["derase"] - k * g["dk"]        # [B, T, H, d_k]
+    rhs = np.flip(np.cumsum(np.flip(per_token, axis=1), axis=1), axis=1)   # sum over j >= t
+    rhs = rhs + np.sum(dS_T * S_T, axis=-1)[:, None]                       # end state, per channel
+    np.testing.assert_allclose(alpha * g["dalpha"], rhs, rtol=1e-10, atol=1e-12)
