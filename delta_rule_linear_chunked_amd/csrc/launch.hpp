@@ -29,15 +29,18 @@ struct PrefillPlan {
   int64_t workspace;   // bytes of workspace (records of one window + packed-sequence tables + carry)
 };
 // Operand records of one window are kept to about this many bytes, which bounds the workspace of
-// any fixed-length prefill. Measured on the KDA prefill (4 x 4096 tokens, 16 heads, d = 128),
-// windows small enough for the 256 MB Infinity Cache (four of 16 chunks) halve the time the state
-// pass needs to read its records, but the pass is then bound by its per-chunk chain and the two
-// passes take 2-4 % longer in all (more, shorter launches), so the default budget is set high
-// enough that such problems run as one window.
+// any fixed-length prefill. The default depends on the state pass's value-column block. With
+// 32-column blocks (e.g. the KDA prefill, 4 x 4096 tokens, 16 heads, d = 128) one window is
+// fastest: smaller windows keep the records in the 256 MB Infinity Cache, but the pass is then
+// bound by its per-chunk chain and the extra launches cost 2-4 %. With 16-column blocks (few
+// (sequence, head) pairs, e.g. 2 x 16384 tokens x 16 heads) every workgroup reads a whole record
+// for half the matrix work, the pass is bound by those reads, and windows of about 130-170 MB of
+// records measured 6.5 % faster than one or two large windows (budgets of 96 to 384 MiB tried).
 constexpr int64_t PREFILL_WINDOW_BYTES = (int64_t)1 << 30;
+constexpr int64_t PREFILL_WINDOW_BYTES_NARROW = (int64_t)144 << 20;  // 16-column value blocks
 PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int64_t seqlen,
                          int64_t heads, int dk, int dv, bool packed,
-                         int64_t window_bytes = PREFILL_WINDOW_BYTES);
+                         int64_t window_bytes = 0);  // 0: the default for the plan's value block
 
 // Prefill: chunk preparation over every (chunk, head), then the state pass over every
 // (sequence, head, value block). `ws` is a workspace of plan.workspace bytes.

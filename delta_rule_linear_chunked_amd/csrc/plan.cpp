@@ -42,6 +42,7 @@ PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int
   } else {
     // windows of equal numbers of chunks, as few as keep one window's records within the budget
     // (DR_WINDOW_BYTES overrides the budget, for tests)
+    if (window_bytes <= 0) window_bytes = pl.dv_block <= 16 ? PREFILL_WINDOW_BYTES_NARROW : PREFILL_WINDOW_BYTES;
     if (const char* e = getenv("DR_WINDOW_BYTES")) {
       const long long b = atoll(e);
       if (b > 0) window_bytes = b;

@@ -353,9 +353,11 @@ int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t*
  * The prefill's launch plan for `dims` in full (for tests, profiling and callers that size their
  * memory): the fixed-length prefill runs its two passes over windows of chunk positions (a few
  * chunks of every sequence at a time, the state carried between windows), so that one window's
- * operand records (about 128.5 KiB per chunk and head at d_k = 128) stay within 1 GiB: the
- * workspace of a fixed-length prefill is at most about 1 GiB plus the carried state (num_seqs *
- * heads * d_k * d_v * 4 bytes) whatever its length. Packed sequences run as one window.
+ * operand records (about 128.5 KiB per chunk and head at d_k = 128) stay within 1 GiB, or
+ * within 144 MiB when the state pass uses 16-column value blocks (dv_block = 16, where windows
+ * that fit the Infinity Cache are faster): the workspace of a fixed-length prefill is at most
+ * about 1 GiB plus the carried state (num_seqs * heads * d_k * d_v * 4 bytes) whatever its
+ * length. Packed sequences run as one window.
  * DR_WINDOW_BYTES in the environment sets another budget (in bytes). With noalloc != 0 the plan is the one dr_chunk_fwd_noalloc
  * uses (windows small enough for its static scratch). Sequences are taken as packed when batch is 1
  * and num_seqs is not.
