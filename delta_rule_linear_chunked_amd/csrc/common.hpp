@@ -41,6 +41,7 @@ struct Params {
   // sequence (a window), whose records sit at slot n * win_k + (c - win_c0); the state passes from
   // one window to the next through `carry` [N, H, d_k, d_v] (read when carry_in, written instead of
   // the final state when carry_out). Packed sequences run as one window of all their chunks.
+  int32_t rec_nt;       // records written with non-temporal stores (one window: read back from HBM)
   int32_t win_c0;
   int32_t win_nc;
   int32_t win_k;

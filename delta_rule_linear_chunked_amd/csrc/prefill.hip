@@ -488,8 +488,8 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       float ut[8], qt[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) { ut[j] = uf[ks][j] * run[j]; qt[j] = qf[ks][j] * run[j]; }
-      st_frag(rs, R::UT, wu * KS + ks, l, Pol::make(ut));
-      st_frag(rs, R::QT, wu * KS + ks, l, Pol::make(qt));
+      st_frag(rs, R::UT, wu * KS + ks, l, Pol::make(ut), p.rec_nt);
+      st_frag(rs, R::QT, wu * KS + ks, l, Pol::make(qt), p.rec_nt);
     }
 #pragma unroll
     for (int J = 0; J < NBLK - 1; ++J) {
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
     if (st == 0 || w >= 2) {
       float a8[8];
       load8(&sm.u1.P[16 * w + r][32 * st + 8 * g], a8);
-      st_frag(rs, R::PP, wu * 2 + st, l, Pol::make(a8));
+      st_frag(rs, R::PP, wu * 2 + st, l, Pol::make(a8), p.rec_nt);
     }
   }
   for (int rt = wu; rt < DK / 16; rt += 4) {
@@ -529,7 +529,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
       float x[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) x[j] = sm.u2.kg[k0 + j][chA] * suf;
-      st_frag(rs, R::KB, rt * 2 + st, l, Pol::make(x));
+      st_frag(rs, R::KB, rt * 2 + st, l, Pol::make(x), p.rec_nt);
     }
   }
   if (tid < DK) {
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
     if (st == 0 || w >= 2) {
       float a8[8];
       load8(&sm.u2.T[16 * w + r][32 * st + 8 * g], a8);
-      st_frag(rs, R::TT, wu * 2 + st, l, Pol::make(a8));
+      st_frag(rs, R::TT, wu * 2 + st, l, Pol::make(a8), p.rec_nt);
     }
   }
 }
@@ -677,6 +677,11 @@ static void set_workspace(Params& p, const PrefillPlan& pl, void* ws) {
   p.win_k = (int32_t)pl.win_k;
   p.carry = prefill_carry(ws, pl, p.H);
   p.carry_in = p.carry_out = 0;
+  // Records of one window larger than the 256 MB Infinity Cache come back from HBM whatever
+  // the store policy: non-temporal stores then make the preparation faster (KDA prefill,
+  // 4 x 4096 tokens x 16 heads: 0.395 -> 0.376 ms per call). Smaller records, and windows sized
+  // for the cache, keep the default policy, under which they are still cached when read.
+  p.rec_nt = (pl.windows == 1 && pl.slots * p.H * pl.rec_size > ((int64_t)256 << 20)) ? 1 : 0;
   if (p.cu) {
     int32_t* tables = reinterpret_cast<int32_t*>(p.rec + pl.slots * p.H * pl.rec_size);
     p.chunk_seq = tables;

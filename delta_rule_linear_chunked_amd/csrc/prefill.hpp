@@ -38,12 +38,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rec_rsrc(const unsigned char* 
 // (Stores put the whole offset in the per-lane field and keep the scalar offset at zero:
 // the compiler protects the data registers of a wide buffer store from being
 // overwritten too early only in that form.)
+// `nt` (uniform): non-temporal stores, for records that the state pass will read back from HBM
+// anyway (one window); windows small enough for the Infinity Cache keep the default policy so
+// that the records stay there until they are read.
 template <class Frag>
-__device__ __forceinline__ void st_frag(__amdgpu_buffer_rsrc_t rs, int off, int idx, int lane, const Frag& f) {
+__device__ __forceinline__ void st_frag(__amdgpu_buffer_rsrc_t rs, int off, int idx, int lane, const Frag& f,
+                                        bool nt) {
   static_assert(sizeof(Frag) == 32, "fragment size");
   const u32x4* h = reinterpret_cast<const u32x4*>(&f);
-  __builtin_amdgcn_raw_buffer_store_b128(h[0], rs, lane * 16 + off + idx * 2048, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b128(h[1], rs, lane * 16 + 1024 + off + idx * 2048, 0, 0);
+  if (nt) {
+    __builtin_amdgcn_raw_buffer_store_b128(h[0], rs, lane * 16 + off + idx * 2048, 0, 2);
+    __builtin_amdgcn_raw_buffer_store_b128(h[1], rs, lane * 16 + 1024 + off + idx * 2048, 0, 2);
+  } else {
+    __builtin_amdgcn_raw_buffer_store_b128(h[0], rs, lane * 16 + off + idx * 2048, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(h[1], rs, lane * 16 + 1024 + off + idx * 2048, 0, 0);
+  }
 }
 template <class Frag>
 __device__ __forceinline__ Frag ld_frag(__amdgpu_buffer_rsrc_t rs, int off, int idx, int lane) {
