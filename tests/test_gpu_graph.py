@@ -100,3 +100,47 @@ def test_prefill_replays_from_a_graph(packed):
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_e) and torch.equal(S_g, S_e), f"replay {r} differs from the eager call"
     print(f"[graph prefill packed={packed}] 4 replays bit-identical to eager calls", flush=True)
+
+
+def test_noalloc_strided_windowed_prefill_replays_from_a_graph(monkeypatch):
+    # the allocation-free prefill (its workspace the library's static scratch: no memory nodes),
+    # on q, k, v given as views of one fused projection, in windows of two chunks; eager calls
+    # of the same entry point share the scratch between the replays
+    from gpu_util import prefill_inputs
+    monkeypatch.setenv("DR_WINDOW_BYTES", str(2 * 2 * 2 * 132 * 1024))  # two chunks of 2 rows x 2 heads
+    wl = synth.make_prefill("kda", 2, 300, 2, 128, 128, in_dtype="bf16", seed=seed_of("graph noalloc"))
+    a = prefill_inputs(wl)
+    plan = drl.chunk_fwd_plan_ex(2, 300, 2, 128, 128, noalloc=True)
+    assert plan["windows"] == 3 and plan["window_chunks"] == 2, plan
+    fused = torch.stack([a["q"], a["k"], a["v"]], dim=2).contiguous()
+    q, k, v = fused[:, :, 0], fused[:, :, 1], fused[:, :, 2]
+    B, T, H, _ = wl.q.shape
+    o_g = torch.empty((B, T, H, 128), device=q.device)
+    S_g = torch.empty((B, H, 128, 128), device=q.device)
+
+    def call(o, S):
+        drl.dr_chunk_fwd_noalloc(q, k, v, a["alpha"], a["erase"], None, "kda", a["S0"], None, o, S)
+
+    o_ref, S_ref = torch.empty_like(o_g), torch.empty_like(S_g)
+    drl.dr_chunk_fwd_ex(a["q"], a["k"], a["v"], a["alpha"], a["erase"], None, "kda", a["S0"], None, o_ref, S_ref)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(torch.empty_like(o_g), torch.empty_like(S_g))
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(o_g, S_g)
+    torch.cuda.synchronize()
+    for r in range(4):
+        o_g.zero_()
+        S_g.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o_g, o_ref) and torch.equal(S_g, S_ref), f"replay {r} differs from the pooled call"
+        o_e, S_e = torch.empty_like(o_g), torch.empty_like(S_g)
+        call(o_e, S_e)  # eager, on the same scratch, between the replays
+        torch.cuda.synchronize()
+        assert torch.equal(o_e, o_ref) and torch.equal(S_e, S_ref)
+    print("[graph noalloc strided windows] 4 replays bit-identical to the pooled dense call", flush=True)
