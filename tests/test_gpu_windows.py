@@ -86,3 +86,39 @@ def test_backward_with_windowed_checkpointing_forward(monkeypatch):
     for key in g1:
         if g1[key] is not None:
             assert torch.equal(g1[key], g2[key]), key
+
+
+def test_million_token_sequence_in_a_fixed_workspace(monkeypatch):
+    """One sequence of 2^20 tokens (2 heads, d = 64, bf16): the prefill runs in windows within a
+    workspace of about 150 MB whatever the length. Its first 16384 outputs match the oracle run
+    on those tokens alone (a prefix does not depend on what follows), and the whole run equals,
+    bit for bit, the same tokens in two calls split at a chunk boundary, the second resuming from
+    the first's final state."""
+    monkeypatch.delenv("DR_WINDOW_BYTES", raising=False)
+    T, H, d = 1 << 20, 2, 64
+    plan = drl.chunk_fwd_plan_ex(1, T, H, d, d)
+    print(f"[windows 1M] plan {plan}", flush=True)
+    assert plan["windows"] > 10 and plan["workspace"] < 160 * 2 ** 20, plan
+    wl = synth.make_prefill("kda", 1, T, H, d, d, in_dtype="bf16", seed=seed_of("million"))
+    a = prefill_inputs(wl)
+    o, S = drl.chunk_fwd(**a)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(o).all()) and bool(torch.isfinite(S).all())
+    n = 16384
+    oo, _ = oracle.step_recurrence(wl.q[:, :n], wl.k[:, :n], wl.v[:, :n], wl.alpha[:, :n], wl.erase[:, :n], None,
+                                   "kda", S0=wl.S0)
+    e = oracle.rel_err(o[:, :n].cpu().numpy(), oo)
+    print(f"[windows 1M] first {n} tokens against the oracle: err o={e:.3e}", flush=True)
+    assert e <= TOL["bf16"]
+    h = T // 2
+    sl = lambda x, lo, hi: None if x is None else x[:, lo:hi].contiguous()  # noqa: E731
+    first = {key: (sl(val, 0, h) if key in ("q", "k", "v", "alpha", "erase", "write") else val)
+             for key, val in a.items()}
+    o1, S1 = drl.chunk_fwd(**first)
+    second = {key: (sl(val, h, T) if key in ("q", "k", "v", "alpha", "erase", "write") else val)
+              for key, val in a.items()}
+    second["S0"] = S1
+    o2, S2 = drl.chunk_fwd(**second)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([o1, o2], dim=1), o) and torch.equal(S2, S)
+    print("[windows 1M] split run identical bit for bit", flush=True)
