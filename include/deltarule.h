@@ -343,7 +343,9 @@ int dr_version(void);
  * Launch shape the prefill would use for `dims` (for tests and profiling):
  * chunk length, value columns per workgroup of the sequential state pass, and
  * that pass's number of workgroups (taking the sequences as packed when batch
- * is 1 and num_seqs is not).
+ * is 1 and num_seqs is not). The value-column block is 32 when that gives at least 256
+ * workgroups, else 16; DR_DV_BLOCK in the environment (16, 32 or 64, at most d_v) overrides it,
+ * for tuning and tests (results do not depend on it beyond rounding order).
  * Returns DR_OK or an argument error.
  */
 int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t* dv_block,
@@ -357,10 +359,10 @@ int dr_chunk_fwd_plan(const dr_dims* dims, int variant, int32_t* chunk, int32_t*
  * within 144 MiB when the state pass uses 16-column value blocks (dv_block = 16, where windows
  * that fit the Infinity Cache are faster): the workspace of a fixed-length prefill is at most
  * about 1 GiB plus the carried state (num_seqs * heads * d_k * d_v * 4 bytes) whatever its
- * length. Packed sequences run as one window.
- * DR_WINDOW_BYTES in the environment sets another budget (in bytes). With noalloc != 0 the plan is the one dr_chunk_fwd_noalloc
- * uses (windows small enough for its static scratch). Sequences are taken as packed when batch is 1
- * and num_seqs is not.
+ * length. Packed sequences run as one window. DR_WINDOW_BYTES in the environment sets another
+ * budget (in bytes; windows change no arithmetic, the results stay identical bit for bit). With
+ * noalloc != 0 the plan is the one dr_chunk_fwd_noalloc uses (windows small enough for its static
+ * scratch). Sequences are taken as packed when batch is 1 and num_seqs is not.
  */
 typedef struct dr_plan {
   int32_t chunk;          /* steps per chunk */
