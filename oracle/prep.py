@@ -55,7 +55,9 @@ def alpha_from(z, act: str, scale: float = 1.0):
     gives exp(-scale * softplus(z)) in (0, 1]; ``tanh`` gives tanh(z) in [-1, 1].
 
     Pinned by: softplus(0) = log 2, so z = 0 gives 2^-scale; z = -inf gives exactly 1;
-    tanh(+-inf) = +-1 and tanh is odd."""
+    exp(-softplus(z)) = sigmoid(-z) at scale 1; tanh(+-inf) = +-1, tanh is odd, the exact
+    values tanh(ln x) = (x^2 - 1) / (x^2 + 1) (e.g. tanh(ln 2) = 3/5), its series near zero
+    and 1 - tanh z = 2 e^{-2z} / (1 + e^{-2z})."""
     z = _f64(z)
     if act == "none":
         return z
@@ -70,7 +72,8 @@ def gate_from(z, act: str, scale: float = 1.0):
     """Erase or write gate from its pre-activation: ``none`` passes z through,
     ``sigmoid`` gives scale * sigmoid(z) (scale 2 gives Complex KDA's beta in [0, 2]).
 
-    Pinned by sigmoid's values at 0 and +-inf and its symmetry."""
+    Pinned by sigmoid's values at 0 and +-inf, its symmetry and the exact values
+    sigmoid(+-ln x) = x / (x + 1), 1 / (x + 1) (e.g. sigmoid(ln 3) = 3/4)."""
     z = _f64(z)
     if z is None:
         return None

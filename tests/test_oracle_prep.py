@@ -82,6 +82,17 @@ def test_gate_scale_two_spans_zero_to_two():
     np.testing.assert_array_equal(prep.gate_from(z, "sigmoid", 2.0), [0.0, 1.0, 2.0])
 
 
+@pytest.mark.parametrize("x,scale", [(3.0, 1.0), (7.0, 1.0), (1.5, 2.0), (99.0, 0.5)])
+def test_sigmoid_gate_hand_values(x, scale):
+    # sigmoid z = 1 / (1 + e^{-z}); at z = ln x that is x / (x + 1), at z = -ln x 1 / (x + 1):
+    # sigmoid(ln 3) = 3/4, sigmoid(ln 7) = 7/8, sigmoid(ln 1.5) = 3/5, sigmoid(ln 99) = 99/100.
+    # A rescaled argument (sigmoid(1.01 z)) keeps the values at 0 and +-inf and the symmetry, and
+    # fails here.
+    assert prep.sigmoid(np.log(x)) == pytest.approx(x / (x + 1), abs=2e-16)
+    assert prep.gate_from(np.log(x), "sigmoid", scale) == pytest.approx(scale * x / (x + 1), abs=4e-16)
+    assert prep.gate_from(-np.log(x), "sigmoid", scale) == pytest.approx(scale / (x + 1), abs=4e-16)
+
+
 def test_prepare_with_everything_off_is_the_identity():
     q, k, a, e, w = (RNG.standard_normal((2, 3, 4)) for _ in range(5))
     out = prep.prepare(q, k, a, e, w, l2norm_qk=False, alpha_act="none", alpha_scale=1.0,
