@@ -97,7 +97,7 @@ int check_dims_common(const dr_dims* d) {
     for (int i = 0; i < 6; ++i) {
       if (st[i] < 0) return fail(DR_ERR_SHAPE, "%s stride %lld is negative", names[i], (long long)st[i]);
       if (st[i] > ((int64_t)1 << 40) || (st[i] * esz) % 16 != 0)
-        return fail(DR_ERR_ALIGN, "%s stride %lld is not a multiple of 16 bytes (or is beyond 2^40)", names[i],
+        return fail(DR_ERR_LAYOUT, "%s stride %lld is not a multiple of 16 bytes (or is beyond 2^40)", names[i],
                     (long long)st[i]);
     }
   }
@@ -119,11 +119,11 @@ int check_ptrs(std::initializer_list<std::pair<const void*, const char*>> req,
                std::initializer_list<std::pair<const void*, const char*>> opt) {
   for (auto& pr : req) {
     if (pr.first == nullptr) return fail(DR_ERR_NULL, "`%s` is NULL", pr.second);
-    if (!aligned16(pr.first)) return fail(DR_ERR_ALIGN, "`%s` is not 16-byte aligned", pr.second);
+    if (!aligned16(pr.first)) return fail(DR_ERR_LAYOUT, "`%s` is not 16-byte aligned", pr.second);
   }
   for (auto& pr : opt)
     if (pr.first != nullptr && !aligned16(pr.first))
-      return fail(DR_ERR_ALIGN, "`%s` is not 16-byte aligned", pr.second);
+      return fail(DR_ERR_LAYOUT, "`%s` is not 16-byte aligned", pr.second);
   return DR_OK;
 }
 
@@ -191,7 +191,7 @@ const char* dr_status_string(int status) {
     case DR_ERR_NULL: return "DR_ERR_NULL: a required pointer is NULL";
     case DR_ERR_SHAPE: return "DR_ERR_SHAPE: negative or inconsistent sizes";
     case DR_ERR_DTYPE: return "DR_ERR_DTYPE: unsupported input dtype";
-    case DR_ERR_ALIGN: return "DR_ERR_ALIGN: pointer not 16-byte aligned";
+    case DR_ERR_LAYOUT: return "DR_ERR_LAYOUT: pointer not 16-byte aligned, or strides the call does not take";
     case DR_ERR_UNSUPPORTED: return "DR_ERR_UNSUPPORTED: head size not in {16, 32, 64, 128}";
     case DR_ERR_VARIANT: return "DR_ERR_VARIANT: unknown variant or gates that do not fit it";
     case DR_ERR_HIP: return "DR_ERR_HIP: HIP runtime or launch failure";
@@ -286,13 +286,13 @@ static int opts_checks(const dr_opts* opts, bool prefill, int lg = 0) {
   if (opts->l2norm_qk != 0 && opts->l2norm_qk != 1)
     return fail(DR_ERR_UNSUPPORTED, "l2norm_qk must be 0 or 1");
   if (opts->state_idx) {
-    if (!aligned16(opts->state_idx)) return fail(DR_ERR_ALIGN, "state_idx must be 16-byte aligned");
+    if (!aligned16(opts->state_idx)) return fail(DR_ERR_LAYOUT, "state_idx must be 16-byte aligned");
     if (opts->num_slots < 0) return fail(DR_ERR_SHAPE, "num_slots (%lld) is negative", (long long)opts->num_slots);
     if (opts->num_slots > INT32_MAX) return fail(DR_ERR_UNSUPPORTED, "num_slots above 2^31 - 1");
   }
   if (opts->snapshots) {
     if (!prefill) return fail(DR_ERR_SHAPE, "snapshots are a prefill option");
-    if (!aligned16(opts->snapshots)) return fail(DR_ERR_ALIGN, "snapshots must be 16-byte aligned");
+    if (!aligned16(opts->snapshots)) return fail(DR_ERR_LAYOUT, "snapshots must be 16-byte aligned");
     if (opts->snapshot_every <= 0 || (opts->snapshot_every << lg) % 64 != 0)
       return fail(DR_ERR_SHAPE, "snapshot_every (%lld) must be a positive multiple of %d",
                   (long long)opts->snapshot_every, 64 >> lg);
@@ -468,7 +468,7 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
     input_strides(&dense, lg, dims->seqlen, b);
     for (int j = 0; j < 6; ++j)
       if (a[j] != b[j] && !(j % 2 == 1 && dims->batch <= 1))
-        return fail(DR_ERR_UNSUPPORTED, "the backward pass takes dense q, k, v (strides other than the dense ones)");
+        return fail(DR_ERR_LAYOUT, "the backward pass takes dense q, k, v (strides other than the dense ones)");
   }
   // the states after every 64 steps: the caller's (a prefill's snapshots), or a forward pass
   // with no output

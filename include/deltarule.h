@@ -86,7 +86,8 @@ typedef enum dr_status {
   DR_ERR_NULL = -1,        /* a required pointer is NULL */
   DR_ERR_SHAPE = -2,       /* negative or inconsistent sizes */
   DR_ERR_DTYPE = -3,       /* in_dtype is not DR_F32 / DR_BF16 */
-  DR_ERR_ALIGN = -4,       /* a pointer is not 16-byte aligned */
+  DR_ERR_LAYOUT = -4,      /* a pointer not 16-byte aligned, or strides the call does not take */
+  DR_ERR_ALIGN = -4,       /* the same code under its earlier name */
   DR_ERR_UNSUPPORTED = -5, /* head size outside {16, 32, 64, 128}, or a size beyond the limits */
   DR_ERR_VARIANT = -6,     /* unknown variant, or gate pointers that do not fit it */
   DR_ERR_HIP = -7          /* a HIP runtime call or kernel launch failed */
@@ -124,7 +125,8 @@ typedef struct dr_dims {
  * address must lie inside the caller's buffer (not checked). alpha, the gates, the states and
  * the output stay dense. dr_chunk_fwd, dr_chunk_fwd_ex, dr_chunk_fwd_noalloc, dr_decode_step and
  * dr_decode_step_ex take strided inputs; dr_chunk_bwd and dr_chunk_bwd_ex return
- * DR_ERR_UNSUPPORTED for strides other than the dense ones.
+ * DR_ERR_LAYOUT for strides other than the dense ones (as for strides that are not multiples of
+ * 16 bytes).
  */
 #define DR_DIMS_V2 2
 typedef struct dr_dims_v2 {

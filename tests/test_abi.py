@@ -40,6 +40,7 @@ def test_every_declared_symbol_is_exported(lib):
 def test_status_strings(lib):
     for code in range(0, -8, -1):
         assert lib.dr_status_string(code).decode().startswith("DR_")
+    assert lib.dr_status_string(-4).decode().startswith("DR_ERR_LAYOUT")
     assert lib.dr_version() >= 100
 
 
@@ -273,7 +274,7 @@ def test_backward_takes_only_dense_strides(lib):
     # dense strides given as a dr_dims_v2 are accepted (B = 0 below would launch nothing; with
     # tokens the call would launch, so only the rejection is exercised here)
     st = lib.dr_chunk_bwd(*args, _v2_ptr(strided), None)
-    assert st == -5 and "dense" in lib.dr_last_error().decode()
+    assert st == -4 and "dense" in lib.dr_last_error().decode()  # DR_ERR_LAYOUT
     dense.base.batch = 0
     dense.base.num_seqs = 0
     assert lib.dr_chunk_bwd(*args, _v2_ptr(dense), None) == 0
