@@ -282,3 +282,27 @@ def test_backward_takes_only_dense_strides(lib):
 
 def test_unknown_dims_version_is_rejected(lib):
     assert chunk(lib, dims(version=3)) == -2
+
+
+def test_last_error_is_per_thread(lib):
+    # dr_last_error() is thread-local: threads making failing calls at the same time (ctypes
+    # releases the GIL around each call) each read back the message of their own call
+    import threading
+
+    errors = []
+
+    def worker(i):
+        dk = 17 + i                                   # unsupported, and different in every thread
+        for _ in range(300):
+            st = chunk(lib, dims(dk=dk))
+            msg = lib.dr_last_error().decode()
+            if st != -5 or f"d_k={dk} " not in msg:
+                errors.append((i, st, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors[:3]
