@@ -452,9 +452,11 @@ def dr_chunk_bwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, dO,
     if q.dtype not in _DT:
         raise ValueError(f"q dtype {q.dtype} is not float32 or bfloat16")
     nt = (2,) if variant == "product2" else ()  # the transition axis of k and v
-    _need(q, "q", (B, T, H, dk_), q.dtype, dev)
-    _need(k, "k", (B, T, H) + nt + (dk_,), q.dtype, dev)
-    _need(v, "v", (B, T, H) + nt + (dv_,), q.dtype, dev)
+    # q, k, v may be views, as for the forward: batch and token strides are free
+    sq = _need_rows(q, "q", (B, T, H, dk_), 2, q.dtype, dev)
+    sk = _need_rows(k, "k", (B, T, H) + nt + (dk_,), 2, q.dtype, dev)
+    sv = _need_rows(v, "v", (B, T, H) + nt + (dv_,), 2, q.dtype, dev)
+    strides = None if all(x.is_contiguous() for x in (q, k, v)) else (sq[1], sq[0], sk[1], sk[0], sv[1], sv[0])
     _need(alpha, "alpha", (B, T, H, dk_), torch.float32, dev)
     es, ws = _gate_shapes(variant, (B, T, H), dk_, dv_)
     _need(erase, "erase", es, torch.float32, dev)
@@ -486,12 +488,12 @@ def dr_chunk_bwd(q, k, v, alpha, erase, write, variant: str, S0, cu_seqlens, dO,
         else:
             rows = checkpoints.shape[0]
         _need(checkpoints, "checkpoints", (rows, H, dk_, dv_), torch.float32, dev)
-    d = _Dims(B, T, H, dk_, dv_, N, _DT[q.dtype], 0)
+    d = _dims_for(B, T, H, dk_, dv_, N, q.dtype, strides)
     with torch.cuda.device(dev):
         st = lib.dr_chunk_bwd_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(erase), _ptr(write), VARIANTS[variant],
                                  _ptr(S0), _ptr(cu_seqlens), _ptr(dO), _ptr(dS_T), _ptr(dq), _ptr(dk), _ptr(dv),
                                  _ptr(dalpha), _ptr(derase), _ptr(dwrite), _ptr(dS0), _ptr(checkpoints),
-                                 ctypes.byref(d), _stream(dev))
+                                 _dims_arg(d), _stream(dev))
     _check(lib, st, "dr_chunk_bwd")
 
 
@@ -534,11 +536,9 @@ class _DeltaRule(torch.autograd.Function):
     @staticmethod
     def backward(ctx, dO, dS_T):
         q, k, v, alpha, erase, write, S0, cu_seqlens, ck = ctx.saved_tensors
-        # the backward kernels take dense q, k, v (the forward also reads strided views)
-        qc, kc, vc = (x.contiguous() for x in (q, k, v))
         if dO is None:
             dO = torch.zeros(q.shape[:3] + (v.shape[-1],), dtype=torch.float32, device=q.device)
-        g = chunk_bwd(qc, kc, vc, alpha, erase, write, ctx.variant, S0, cu_seqlens, dO=dO.contiguous(),
+        g = chunk_bwd(q, k, v, alpha, erase, write, ctx.variant, S0, cu_seqlens, dO=dO.contiguous(),
                       dS_T=None if dS_T is None else dS_T.contiguous(),
                       need_dS0=S0 is not None and ctx.needs_input_grad[6], checkpoints=ck)
         cast = lambda grad, x: None if grad is None else grad.to(x.dtype)

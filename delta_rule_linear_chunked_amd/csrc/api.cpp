@@ -460,16 +460,6 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
   const int dkh = (int)dims->head_dim_k, dvh = (int)dims->head_dim_v;
   const int64_t H = dims->num_heads, pairs = dims->num_seqs * H;
 
-  if (dims->version == DR_DIMS_V2) {
-    dr_dims dense = *dims;
-    dense.version = 0;
-    int64_t a[6], b[6];
-    input_strides(dims, lg, dims->seqlen, a);
-    input_strides(&dense, lg, dims->seqlen, b);
-    for (int j = 0; j < 6; ++j)
-      if (a[j] != b[j] && !(j % 2 == 1 && dims->batch <= 1))
-        return fail(DR_ERR_LAYOUT, "the backward pass takes dense q, k, v (strides other than the dense ones)");
-  }
   // the states after every 64 steps: the caller's (a prefill's snapshots), or a forward pass
   // with no output
   dr::Params p{};
@@ -478,7 +468,7 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
   p.write = has_write ? write : erase;
   p.S0 = S0; p.cu = cu_seqlens; p.o = nullptr; p.S = nullptr;
   p.lgnh = lg;
-  set_strides(p, dims, lg, dims->seqlen);  // dense (checked above)
+  set_strides(p, dims, lg, dims->seqlen);
   p.T = dims->seqlen << lg;
   p.H = (int32_t)H;
   p.DV = (int32_t)dvh;
@@ -542,6 +532,16 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
     b.DV = dvh;
     b.nseq = (int32_t)dims->num_seqs;
     b.variant = variant;
+    b.q_ts = p.q_ts; b.q_bs = p.q_bs; b.k_ts = p.k_ts; b.k_bs = p.k_bs; b.v_ts = p.v_ts; b.v_bs = p.v_bs;
+    if (dims->version == DR_DIMS_V2) {  // dense strides given as a dr_dims_v2 take the dense instance
+      dr_dims dense = *dims;
+      dense.version = 0;
+      int64_t a[6], d[6];
+      input_strides(dims, lg, dims->seqlen, a);
+      input_strides(&dense, lg, dims->seqlen, d);
+      for (int j = 0; j < 6; ++j)
+        if (a[j] != d[j] && !(j % 2 == 1 && dims->batch <= 1)) b.strided = 1;
+    }
     e = dr::launch_backward(b, pairs, dkh, dvh, dims->in_dtype == DR_BF16, vec, stream);
   }
   hipError_t ef = hipFreeAsync(ws, stream);

@@ -121,7 +121,9 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
-template <int DK, int DVB, typename InT, bool VEC>
+// STR: q, k, v read through the strides of p (an instance of its own: the dense one has no
+// scalar registers to spare for them)
+template <int DK, int DVB, typename InT, bool VEC, bool STR>
 __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
   using Sh = BwdShape<DK, DVB>;
   constexpr int RG = Sh::RG, CPL = Sh::CPL, RPL = Sh::RPL, NV = Sh::NV, NVR = Sh::NVR;
@@ -172,6 +174,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
     tq = (m >> p.lgnh) * H + h;
     tk = (tq << p.lgnh) + (m & lastm);
   };
+  // q, k and v through their strides: this (sequence, head)'s rows start at qh, kh, vh; step s of
+  // the batch row is (s >> lgnh) token strides further (k, v: plus (s & lastm) d for the step)
+  const int64_t brow = p.cu ? 0 : n, srow0 = p.cu ? bos : 0;
+  const InT* qh = STR ? qp + brow * p.q_bs + (int64_t)h * DK : qp;
+  const InT* kh = STR ? kp + brow * p.k_bs + ((int64_t)h << p.lgnh) * DK : kp;
+  const InT* vh = STR ? vp + brow * p.v_bs + ((int64_t)h << p.lgnh) * DV + dv0 : vp;
   constexpr int SK = (BW_SB * DK + 255) / 256, SV = (BW_SB * DVB + 255) / 256;
   static_assert(SK <= 16 && SV <= 16, "flag bits");
   // Raw values as loaded, and per element bit flags (bit x: element x is inside the sequence;
@@ -195,8 +203,14 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
       const int64_t t = t0 + j < len ? t0 + j : len - 1;
       int64_t tq, tk;
       rows(bos + t, tq, tk);
-      r.k[x] = kp[tk * DK + i];
-      r.q[x] = qp[tq * DK + i];
+      if constexpr (STR) {
+        const int64_t sr = srow0 + t;
+        r.k[x] = kh[(sr >> p.lgnh) * p.k_ts + (sr & lastm) * DK + i];
+        r.q[x] = qh[(sr >> p.lgnh) * p.q_ts + i];
+      } else {
+        r.k[x] = kp[tk * DK + i];
+        r.q[x] = qp[tq * DK + i];
+      }
       r.a[x] = p.alpha[tq * DK + i];
       r.ug[x] = VEC ? p.erase[tk * DK + i] : p.erase[tk];
       const bool first = ((bos + t) & lastm) == 0;
@@ -211,7 +225,12 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
       const int64_t t = t0 + j < len ? t0 + j : len - 1;
       int64_t tq, tk;
       rows(bos + t, tq, tk);
-      r.v[x] = vp[tk * DV + dv0 + cc];
+      if constexpr (STR) {
+        const int64_t sr = srow0 + t;
+        r.v[x] = vh[(sr >> p.lgnh) * p.v_ts + (sr & lastm) * DV + cc];
+      } else {
+        r.v[x] = vp[tk * DV + dv0 + cc];
+      }
       r.g[x] = VEC ? p.write[tk * DV + dv0 + cc] : p.write[tk];
       r.dO[x] = p.dO[tq * DV + dv0 + cc];
       const bool last = ((bos + t) & lastm) == lastm;
@@ -466,6 +485,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdParams p) {
   const int64_t tq = (m >> p.lgnh) * p.H + hh, tk = (tq << p.lgnh) + (m & lastm);
   const bool first = (m & lastm) == 0, last = (m & lastm) == lastm;
   const InT* kp = static_cast<const InT*>(p.k);
+  // k of this step through its strides (fixed length: batch row m / T, step m % T)
+  const int64_t brow = p.cu ? 0 : m / p.T;
+  const int64_t ko = kv_elem(p.k_ts, p.k_bs, p, brow, m - brow * p.T, (int)hh, DK);
   float kdu = 0.f;
   for (int i = lw; i < DK; i += 64) {
     float s[4] = {0.f, 0.f, 0.f, 0.f};
@@ -473,7 +495,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdParams p) {
 #pragma unroll
       for (int qn = 0; qn < 4; ++qn) s[qn] += p.part[(((int64_t)b * p.TH + th) * 4 + qn) * DK + i];
     }
-    const float kk = ld_f32(kp + tk * DK + i);
+    const float kk = ld_f32(kp + ko + i);
     const float ug = VEC ? p.erase[tk * DK + i] : p.erase[tk];
     if (last) p.dq[tq * DK + i] = s[0];
     p.dk[tk * DK + i] = fmaf(ug, s[2], s[1]);
@@ -500,7 +522,10 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdParams p) {
 template <int DK, int DVB, typename InT, bool VEC>
 static hipError_t launch_bwd_t(const BwdParams& p, int64_t pairs, hipStream_t s) {
   if (pairs > 0) {
-    hipLaunchKernelGGL((bwd_kernel<DK, DVB, InT, VEC>), dim3((unsigned)(pairs * p.ndvb)), dim3(256), 0, s, p);
+    if (p.strided)
+      hipLaunchKernelGGL((bwd_kernel<DK, DVB, InT, VEC, true>), dim3((unsigned)(pairs * p.ndvb)), dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL((bwd_kernel<DK, DVB, InT, VEC, false>), dim3((unsigned)(pairs * p.ndvb)), dim3(256), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -87,10 +87,13 @@ __device__ __forceinline__ int64_t step_row(const Params& p, int64_t m, int h) {
 }
 // Element offsets of q (per token) and of k / v (per step) for step s of batch row b, counted
 // from the start of the row, head h, with d elements per row of the input.
-__device__ __forceinline__ int64_t q_elem(const Params& p, int64_t b, int64_t s, int h, int d) {
+// (P: the prefill / decode parameters or the backward's, which carry the same stride fields)
+template <class P>
+__device__ __forceinline__ int64_t q_elem(const P& p, int64_t b, int64_t s, int h, int d) {
   return b * p.q_bs + (s >> p.lgnh) * p.q_ts + (int64_t)h * d;
 }
-__device__ __forceinline__ int64_t kv_elem(int64_t ts, int64_t bs, const Params& p, int64_t b, int64_t s, int h,
+template <class P>
+__device__ __forceinline__ int64_t kv_elem(int64_t ts, int64_t bs, const P& p, int64_t b, int64_t s, int h,
                                            int d) {
   return b * bs + (s >> p.lgnh) * ts + ((((int64_t)h) << p.lgnh) + (s & ((1 << p.lgnh) - 1))) * d;
 }
@@ -130,6 +133,8 @@ struct BwdParams {
   int32_t variant;      // 0 KDA, 1 RDA, 2 GDN-2, 3 CKDA, 4 two KDA transitions per token
   int32_t lgnh;         // transitions per token, as a power of two (see Params); T, TH and the
                         // partial sums count steps
+  int64_t q_ts, q_bs, k_ts, k_bs, v_ts, v_bs;  // element strides of q, k, v (as in Params)
+  int32_t strided;      // the strides are not those of dense inputs
 };
 
 __device__ __forceinline__ float ld_f32(const float* p) { return *p; }

@@ -123,10 +123,9 @@ typedef struct dr_dims {
  * stride H d (2 H d for DR_PRODUCT2's k and v) and batch stride T times that. Strides must be
  * non-negative and, times the element size, multiples of 16 bytes; every element the strides
  * address must lie inside the caller's buffer (not checked). alpha, the gates, the states and
- * the output stay dense. dr_chunk_fwd, dr_chunk_fwd_ex, dr_chunk_fwd_noalloc, dr_decode_step and
- * dr_decode_step_ex take strided inputs; dr_chunk_bwd and dr_chunk_bwd_ex return
- * DR_ERR_LAYOUT for strides other than the dense ones (as for strides that are not multiples of
- * 16 bytes).
+ * the output stay dense (so do the gradients of the backward). Every entry point that takes q, k
+ * and v takes them strided: dr_chunk_fwd, dr_chunk_fwd_ex, dr_chunk_fwd_noalloc, dr_decode_step,
+ * dr_decode_step_ex, dr_chunk_bwd and dr_chunk_bwd_ex.
  */
 #define DR_DIMS_V2 2
 typedef struct dr_dims_v2 {

@@ -1,6 +1,7 @@
 """GPU: q, k and v given through strides (a dr_dims_v2), e.g. as views of one fused projection.
-The kernels read them in place (no copy is made): the results must equal the same call on
-contiguous copies bit for bit (the same values reach the same instructions), and match the oracle."""
+The kernels read them in place (no copy is made): the results of the prefill, the decode step and
+the backward must equal the same call on contiguous copies bit for bit (the same values reach the
+same instructions), and match the oracle."""
 import numpy as np
 import pytest
 import torch
@@ -112,9 +113,31 @@ def test_decode_views(variant):
     assert torch.equal(o1, o2) and torch.equal(S1, S2)
 
 
-def test_backward_needs_dense_inputs():
-    wl = synth.make_prefill("kda", 1, 64, 2, 64, 64, in_dtype="bf16", seed=3)
+@pytest.mark.parametrize("case", ["kda", "gdn2_packed", "product2"])
+def test_backward_on_views(case):
+    # the backward reads q, k, v through their strides too: gradients equal those of the call on
+    # contiguous copies bit for bit (the gradients themselves are dense)
+    if case == "kda":
+        wl = synth.make_prefill("kda", 2, 150, 2, 128, 128, in_dtype="bf16", seed=seed_of("strided bwd", case))
+    elif case == "gdn2_packed":
+        wl = synth.make_prefill("gdn2", 1, 0, 2, 64, 64, in_dtype="bf16", seed=seed_of("strided bwd", case),
+                                lengths=[70, 0, 1, 129])
+    else:
+        wl = synth.make_product("kda", 2, 77, 2, 64, 64, in_dtype="bf16", seed=seed_of("strided bwd", case))
     a = prefill_inputs(wl)
-    big, (q, k, v) = _fused([a["q"], a["k"], a["v"]], a["q"].dtype)
-    with pytest.raises(ValueError, match="contiguous"):
-        drl.chunk_bwd(**dict(a, q=q, k=k, v=v), dO=torch.ones(a["q"].shape[:3] + (64,), device=q.device))
+    if case == "product2":  # k, v [B, T, H, 2, d] as views of [B, T, 2, H, 2, d] tensors
+        k = torch.stack([a["k"], torch.zeros_like(a["k"])], dim=2).contiguous()[:, :, 0]
+        v = torch.stack([torch.zeros_like(a["v"]), a["v"]], dim=2).contiguous()[:, :, 1]
+        q = torch.stack([a["q"], a["q"]], dim=2).contiguous()[:, :, 1]
+    else:
+        big, (q, k, v) = _fused([a["q"], a["k"], a["v"]], a["q"].dtype)
+    assert not (q.is_contiguous() or k.is_contiguous() or v.is_contiguous())
+    gen = torch.Generator(device="cuda").manual_seed(seed_of("strided bwd do", case))
+    dO = torch.randn(a["q"].shape[:3] + (a["v"].shape[-1],), device="cuda", generator=gen)
+    N = wl.S0.shape[0]
+    dS_T = torch.randn((N,) + tuple(wl.S0.shape[1:]), device="cuda", generator=gen)
+    g_ref = drl.chunk_bwd(**a, dO=dO, dS_T=dS_T)
+    g = drl.chunk_bwd(**dict(a, q=q, k=k, v=v), dO=dO, dS_T=dS_T)
+    torch.cuda.synchronize()
+    for name, ref in g_ref.items():
+        assert (ref is None and g[name] is None) or torch.equal(g[name], ref), name
