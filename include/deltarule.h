@@ -301,7 +301,8 @@ int dr_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void
  *   dwrite        RDA d(w) [B, T, H], GDN-2 d(w) [B, T, H, d_v]; must be NULL for KDA / CKDA
  *   dS0           [N, H, d_k, d_v], or NULL when not wanted
  * The inputs are those of the forward call (plain inputs: the fused preparation and the
- * stored-state options are forward-only). The call reruns the forward to keep the state after
+ * stored-state options are forward-only; q, k, v may be strided through a dr_dims_v2, the
+ * gradients are always dense). The call reruns the forward to keep the state after
  * every 64 tokens, then walks each sequence backwards, recomputing states between those
  * checkpoints; its workspace (about 4 * d_k * 4 bytes per token-head and value block of 32
  * columns, plus the checkpoints) comes from the library's pool like the prefill's.
