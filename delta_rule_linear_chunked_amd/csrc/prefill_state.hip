@@ -137,9 +137,11 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     }
   }
 
-  // ---- operands of a chunk, in registers. Two sets alternate: while chunk c is computed
-  // from one, the loads of chunk c + 1 stream into the other, so the load path works in
-  // parallel with the MFMAs (past the last chunk the last record is reloaded and unused).
+  // ---- operands of a chunk, in registers: one set, each group of fragments loaded again for
+  // chunk c + 1 right after its last use in chunk c, so every load has most of a chunk to
+  // arrive and the load path works in parallel with the MFMAs (past the last chunk the last
+  // record is reloaded and unused). A second, alternating set measured no faster and took 160
+  // more registers.
   // v and the write gate move as row segments: lane l holds token 16w + l/4 of the wave's
   // block, value columns (l % 4) * E .. + E - 1 of the block, with 16-byte accesses.
   constexpr int E = DVB / 4;
@@ -189,9 +191,9 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     if constexpr (VEC) op.pw = *reinterpret_cast<const RowF*>(p.write + thv * DV + dv0 + lc);
     else op.pw = p.write[thv];
   };
-  // Same issue order as the loads spread over a chunk below (v and write gate first), so
-  // that the waits at the top of the chunk loop, which serve both the first chunk and the
-  // later ones, count the same loads in flight on both paths into the loop.
+  // The first chunk's operands, in the order a chunk reloads them (v and write gate first), so
+  // that the waits in the chunk loop, which serve both the first chunk and the later ones,
+  // count the same loads in flight on both paths into the loop.
   auto load_ops = [&](Ops& op, int c) {
     const __amdgpu_buffer_rsrc_t rc = rec_ptr(c);
     load_vw(op, c);
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     }
   };
 
-  auto chunk = [&](int c, Ops& cur, Ops& nxt) {
+  auto chunk = [&](int c, Ops& cur) {
     const int64_t c0 = (int64_t)c * CH;
     // write values m = w . v (zero past the sequence end), row layout -> LDS -> rows 4g+i of
     // the accumulator layout
@@ -251,10 +253,8 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) mv[ct][i] = sm.X[w][4 * g + i][16 * ct + r];
     }
-    // the next chunk's operands stream into `nxt` in small groups placed between the
-    // MFMA groups below, so the load path and the matrix cores work at the same time
     const __amdgpu_buffer_rsrc_t rn = rec_ptr(c + 1);
-    load_vw(nxt, c + 1);
+    load_vw(cur, c + 1);
 
     // ================= X = Utilde S0, Y = Qtilde S0, R = M - X   (block row w)
     f32x4 accY[NCT];
@@ -264,15 +264,13 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
       for (int ct = 0; ct < NCT; ++ct) { accX[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; accY[ct] = accX[ct]; }
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        load_uq(nxt, rn, ks);
 #pragma unroll
         for (int ct = 0; ct < NCT; ++ct) {
           const Frag B = sm.S.get8(16 * ct + r, 32 * ks + 8 * g);
           Pol::mma(accX[ct], cur.fU[ks], B);
           if constexpr (OUT) Pol::mma(accY[ct], cur.fQ[ks], B);
         }
-        __builtin_amdgcn_sched_group_barrier(0x020, OUT ? 4 : 2, 0);          // the slice's global loads
-        __builtin_amdgcn_sched_group_barrier(0x008, (OUT ? 6 : 3) * NCT, 0);  // then its MFMAs
+        load_uq(cur, rn, ks);
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -286,7 +284,6 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 
     // ================= delta = T R   (block row w)
     const int nst = (w + 2) / 2;
-    load_tp(nxt, rn);
     {
       f32x4 accD[NCT];
 #pragma unroll
@@ -300,6 +297,9 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) sm.D.put4(16 * ct + r, 16 * w + 4 * g, accD[ct]);
+      // T of the next chunk (P is reloaded after its last use below)
+      cur.fT[0] = ld_frag<Frag>(rn, R::TT, wu * 2, l);
+      if (w >= 2) cur.fT[1] = ld_frag<Frag>(rn, R::TT, wu * 2 + 1, l);
     }
     __syncthreads();
 
@@ -320,9 +320,10 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
           }
         }
       }
-      // the next chunk's Kbar and Gamma_C loads
-#pragma unroll
-      for (int m = 0; m < NRT; ++m) load_k(nxt, rn, m);
+      if constexpr (OUT) {
+        cur.fP[0] = ld_frag<Frag>(rn, R::PP, wu * 2, l);
+        if (w >= 2) cur.fP[1] = ld_frag<Frag>(rn, R::PP, wu * 2 + 1, l);
+      }
       // S <- Diag(Gamma_C) S0 + Kbar^T delta (the sequential chain) issued first ...
       f32x4 accS[NRT][NCT];
 #pragma unroll
@@ -338,6 +339,9 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
           }
         }
       }
+      // the next chunk's Kbar and Gamma_C, after their last use
+#pragma unroll
+      for (int m = 0; m < NRT; ++m) load_k(cur, rn, m);
       // ... and O written while those MFMAs run: accumulator layout -> LDS -> row segments
       if constexpr (OUT) {
 #pragma unroll
@@ -377,13 +381,10 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
     __syncthreads();
   };
 
-  Ops opA, opB;
-  if (cend > cbeg) load_ops(opA, cbeg);
+  Ops op;
+  if (cend > cbeg) load_ops(op, cbeg);
   __syncthreads();
-  for (int c = cbeg; c < cend; c += 2) {
-    chunk(c, opA, opB);
-    if (c + 1 < cend) chunk(c + 1, opB, opA);
-  }
+  for (int c = cbeg; c < cend; ++c) chunk(c, op);
 
   // ---- the state for the next window, or the final state
   if (p.carry_out) store_state(p.carry + ((int64_t)n * H + h) * DKR * DV);
