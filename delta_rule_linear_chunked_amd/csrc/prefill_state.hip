@@ -51,8 +51,10 @@ struct StateSmem {
 
 // OUT = false (no output requested): the Qtilde S0 and P delta products and the Qtilde / P loads
 // are left out, and only the states are produced.
-template <int DKR, int DVB, typename InT, bool VEC, bool OUT>
-__global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
+// OCC: workgroups per CU the registers are sized for (2 only for launches with more workgroups
+// than CUs, where a second resident workgroup's chain fills the first one's waits).
+template <int DKR, int DVB, typename InT, bool VEC, bool OUT, int OCC = 1>
+__global__ __launch_bounds__(256, OCC) void chunk_state_kernel(const Params p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
   constexpr int DK = DKR < 32 ? 32 : DKR;
@@ -394,6 +396,20 @@ __global__ __launch_bounds__(256, 1) void chunk_state_kernel(const Params p) {
 // ============================================================================ host
 template <int DKR, int DVB, typename InT, bool VEC>
 static hipError_t launch_state_t(const Params& p, int64_t workgroups, hipStream_t s) {
+  // d_k = 128 with 32-column blocks and more workgroups than the 256 CUs of an MI355X (e.g. packed
+  // sequences x heads x blocks): two resident workgroups per CU (RDA / GDN-2 varlen 2.5% faster;
+  // with one workgroup per CU the one-per-CU instance is faster)
+  if constexpr (DKR == 128 && DVB == 32) {
+    if (workgroups > 256) {
+      if (p.o)
+        hipLaunchKernelGGL((chunk_state_kernel<DKR, DVB, InT, VEC, true, 2>), dim3((unsigned)workgroups), dim3(256), 0,
+                           s, p);
+      else
+        hipLaunchKernelGGL((chunk_state_kernel<DKR, DVB, InT, VEC, false, 2>), dim3((unsigned)workgroups), dim3(256), 0,
+                           s, p);
+      return hipGetLastError();
+    }
+  }
   if (p.o)
     hipLaunchKernelGGL((chunk_state_kernel<DKR, DVB, InT, VEC, true>), dim3((unsigned)workgroups), dim3(256), 0, s, p);
   else  // states (and snapshots) only
