@@ -92,6 +92,32 @@ def test_many_packed_sequences(nseq):
     check(wl, f"nseq={nseq}")
 
 
+@pytest.mark.parametrize("variant,in_dtype", [("kda", "bf16"), ("gdn2", "bf16"), ("rda", "f32")])
+def test_more_workgroups_than_cus(variant, in_dtype):
+    # d_k = d_v = 128 with 40 packed sequences x 8 heads: 1280 state workgroups of 32 columns, more
+    # than the 256 CUs, so the state pass runs its instance with two resident workgroups per CU;
+    # full compare with the oracle, the states-only instance and snapshots as well
+    from oracle import states
+    rng = np.random.default_rng(seed_of("more wgs", variant))
+    lens = rng.integers(0, 150, size=40)
+    lens[::9] = 0
+    lens[4::7] = 128
+    wl = synth.make_prefill(variant, 1, 0, 8, 128, 128, in_dtype=in_dtype, seed=seed_of("more wgs wl", variant),
+                            lengths=lens)
+    assert drl.chunk_fwd_plan(1, wl.q.shape[1], 8, 128, 128, num_seqs=40)[2] > 256  # (chunk, dv_block, workgroups)
+    check(wl, "more workgroups than CUs")
+    a = prefill_inputs(wl)
+    o, S_T, snaps = drl.chunk_fwd(**a, snapshot_every=64)
+    _, S_only, snaps_only = drl.chunk_fwd(**a, snapshot_every=64, output=False)
+    torch.cuda.synchronize()
+    assert torch.equal(S_T, S_only) and torch.equal(snaps, snaps_only)
+    ref = states.snapshots(wl.q, wl.k, wl.v, wl.alpha, wl.erase, wl.write, wl.variant, 64, S0=wl.S0,
+                           cu_seqlens=wl.cu_seqlens)
+    err = oracle.rel_err(snaps.cpu().numpy(), ref)
+    print(f"[more workgroups than CUs {variant}] snapshots err={err:.3e}", flush=True)
+    assert err <= TOL[in_dtype]
+
+
 def test_exact_zero_and_unit_gates():
     """alpha = 0 exactly, alpha = +-1 and beta = 2 (Complex KDA ranges); zeros force the
     exact running-product path for the block's diagonal tile."""
