@@ -255,6 +255,7 @@ __global__ __launch_bounds__(256, OCC) void chunk_state_kernel(const Params p) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) mv[ct][i] = sm.X[w][4 * g + i][16 * ct + r];
     }
+    // from here on each operand group is reloaded for chunk c + 1 as soon as chunk c is done with it
     const __amdgpu_buffer_rsrc_t rn = rec_ptr(c + 1);
     load_vw(cur, c + 1);
 
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(256, OCC) void chunk_state_kernel(const Params p) {
           Pol::mma(accX[ct], cur.fU[ks], B);
           if constexpr (OUT) Pol::mma(accY[ct], cur.fQ[ks], B);
         }
-        load_uq(cur, rn, ks);
+        load_uq(cur, rn, ks);  // this slice's Utilde / Qtilde of the next chunk
       }
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
