@@ -20,7 +20,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libdeltarule.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "plan.cpp", "scratch.hip", "decode.hip", "prefill.hip", "prefill_state.hip", "backward.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "scratch.hip", "decode.hip", "prefill.hip", "prefill_state.hip", "backward.hip",
+           "backward_chunked.hip"]
 
 # Packed-fp32 instructions are disabled for every device compile; hipcc's host
 # pass does not know the feature and says so, which is harmless.

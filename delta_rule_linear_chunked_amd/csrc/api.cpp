@@ -165,6 +165,13 @@ bool debug_validate() {
   return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
 }
 
+// DR_BWD_WALK set (and not "0"): the backward takes the exact per-token walk for every call (the
+// chunked path is the default where it applies).
+bool walk_forced() {
+  const char* e = getenv("DR_BWD_WALK");
+  return e != nullptr && e[0] != '\0' && !(e[0] == '0' && e[1] == '\0');
+}
+
 // cu_seqlens [nseq + 1] (device) must start at 0, never decrease and end at most at `tokens`.
 // A synchronising copy on `stream`.
 int check_offsets(const int32_t* cu, int64_t nseq, int64_t tokens, hipStream_t stream) {
@@ -492,10 +499,25 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
     plw.workspace -= pl.slots * H * pl.rec_size;
     plw.rec_size = 0;
   }
+  // The chunked MFMA path (fixed length, one transition per token, d_k 64 or 128, d_v a multiple
+  // of 32 up to 128) runs first; the walk's kernels then run only if it flagged a chunk whose gates
+  // it does not take. Its records and chunk-end gradients share the walk's partial-sum buffers
+  // (the walk writes them only when it runs, after the chunked passes are done with them); the
+  // flag sits apart.
+  const bool chunked = lg == 0 && cu_seqlens == nullptr && (dkh == 64 || dkh == 128) && dvh % 32 == 0 &&
+                       dvh <= 128 && dims->seqlen > 0 && !walk_forced();
+  const int64_t ncpb = (dims->seqlen + 63) / 64;
+  const int64_t cslots = dims->batch * ncpb * H;
+  const int64_t crec = chunked ? dr::cbwd_record_bytes(dkh, dvh) : 0;
+  const int64_t chunk_bytes = chunked ? round256(cslots * crec) + round256(cslots * dkh * dvh * 4) : 0;
+  if (chunked && cslots > INT32_MAX)
+    return fail(DR_ERR_UNSUPPORTED, "problem too large: more than 2^31 - 1 workgroups per kernel");
   const int64_t off_snap = round256(plw.workspace);
   const int64_t off_part = off_snap + (checkpoints ? 0 : round256(nsnap * H * dkh * dvh * 4));
   const int64_t off_parts = off_part + round256((int64_t)ndvb * TH * 4 * dkh * 4);
-  const int64_t total = off_parts + round256((int64_t)ndvb * TH * 4);
+  const int64_t walk_end = off_parts + round256((int64_t)ndvb * TH * 4);
+  const int64_t off_flag = walk_end > off_part + chunk_bytes ? walk_end : off_part + chunk_bytes;
+  const int64_t total = off_flag + 256;
   void* ws = nullptr;
   hipError_t e = workspace_alloc((size_t)total, stream, &ws);
   if (e != hipSuccess)
@@ -542,7 +564,30 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
       for (int j = 0; j < 6; ++j)
         if (a[j] != d[j] && !(j % 2 == 1 && dims->batch <= 1)) b.strided = 1;
     }
-    e = dr::launch_backward(b, pairs, dkh, dvh, dims->in_dtype == DR_BF16, vec, stream);
+    if (chunked) {
+      dr::CbParams cb{};
+      cb.q = q; cb.k = k; cb.v = v; cb.alpha = alpha;
+      cb.erase = erase;
+      cb.write = p.write;
+      cb.S0 = S0; cb.dO = dO; cb.dST = dS_T; cb.snap = p.snap;
+      cb.dq = dq; cb.dk = dk; cb.dv = dv; cb.dalpha = dalpha; cb.derase = derase; cb.dwrite = dwrite;
+      cb.dS0 = dS0;
+      cb.rec = wsb + off_part;
+      cb.rec_size = crec;
+      cb.dsc = reinterpret_cast<float*>(wsb + off_part + round256(cslots * crec));
+      cb.flag = reinterpret_cast<int32_t*>(wsb + off_flag);
+      cb.T = dims->seqlen;
+      cb.H = (int32_t)H;
+      cb.DV = dvh;
+      cb.B = (int32_t)dims->batch;
+      cb.nc = (int32_t)ncpb;
+      cb.variant = variant;
+      cb.lgnh = 0;
+      cb.q_ts = p.q_ts; cb.q_bs = p.q_bs; cb.k_ts = p.k_ts; cb.k_bs = p.k_bs; cb.v_ts = p.v_ts; cb.v_bs = p.v_bs;
+      e = dr::launch_chunked_backward(cb, dkh, dims->in_dtype == DR_BF16, vec, stream);
+      b.run_flag = cb.flag;
+    }
+    if (e == hipSuccess) e = dr::launch_backward(b, pairs, dkh, dvh, dims->in_dtype == DR_BF16, vec, stream);
   }
   hipError_t ef = hipFreeAsync(ws, stream);
   if (e != hipSuccess) return fail(DR_ERR_HIP, "backward launch failed: %s", hipGetErrorString(e));

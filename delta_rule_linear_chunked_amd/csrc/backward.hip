@@ -125,6 +125,7 @@ __device__ __forceinline__ float group_sum(float x) {
 // scalar registers to spare for them)
 template <int DK, int DVB, typename InT, bool VEC, bool STR>
 __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
+  if (p.run_flag && *p.run_flag == 0) return;
   using Sh = BwdShape<DK, DVB>;
   constexpr int RG = Sh::RG, CPL = Sh::CPL, RPL = Sh::RPL, NV = Sh::NV, NVR = Sh::NVR;
   __shared__ __align__(16) BwdSmem<DK, DVB> sm;
@@ -477,6 +478,7 @@ __global__ __launch_bounds__(256, 1) void bwd_kernel(const BwdParams p) {
 // and dalpha from its first.
 template <int DK, typename InT, bool VEC>
 __global__ __launch_bounds__(256) void bwd_reduce_kernel(const BwdParams p) {
+  if (p.run_flag && *p.run_flag == 0) return;
   const int64_t th = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // step-major row
   const int lw = threadIdx.x & 63;
   if (th >= p.TH) return;

@@ -1,0 +1,946 @@
+// Chunked backward of the gated delta-rule prefill on gfx950: the gradients of a prefill for
+// fixed-length sequences with one transition per token, in three MFMA passes after the
+// checkpointing forward (the course page "GDN, KDA và Mamba-2 · cập nhật state trong hybrid",
+// section 3: training keeps checkpoints and the chunked form's intermediates).
+//
+// Inside a chunk with start state S0, end-state gradient dS (the gradient reaching the state
+// after the chunk's last token from later tokens) and output gradient dO, with Gamma_r the
+// running product of the decays and the chunk algebra of prefill.hip (T = (I + A)^-1,
+// Utilde = Gamma . u, Qtilde = Gamma . q, Kbar_s = Gamma_C / Gamma_s . k_s, P, delta):
+//
+//   eps    = T^T (P^T dO + Kbar dS)                  the gradient of delta (= dm)
+//   dS0    = Diag(Gamma_C) dS + Qtilde^T dO - Utilde^T eps
+//          = M dS + N,  M = Diag(Gamma_C) - W^T Kbar,  N = Z^T dO,  W = T Utilde,  Z = Qtilde - P W
+//   dQtilde = dO S0^T,  dUtilde = -eps S0^T,  dKbar = delta dS^T,
+//   dP = tril(dO delta^T),  dA = -strict_tril(eps delta^T)
+//
+// and, with the decay ratios written through the chunk's running product (Kd_s = k_s / Gamma_s),
+//   dq = Gamma . (dQtilde + dP Kd),  du = Gamma . (dUtilde + dA Kd),
+//   dk (as the key) = (Gamma_C . dKbar + dP^T Qtilde + dA^T Utilde) / Gamma.
+// Every decay product in a chunk runs over a token range, and alpha_t times its derivative is that
+// product, so alpha_t dL/dalpha_t (per channel) is the reverse cumulative sum over the chunk of
+// q . dq + u . du - k . dk plus the end state's term rowsum(dS . S_C); dividing by alpha_t gives
+// the gate gradient.
+//
+// The division by Gamma_s and by alpha_t is what limits this form: a chunk in which some gate has
+// magnitude below 2^-10, or a running product leaves [2^-100, 2^100], or a value is not finite,
+// raises a flag, and the whole call then takes the exact per-token reverse walk (backward.hip),
+// which divides by nothing. (KDA, RDA and GDN-2 decays exp(-c softplus(z)) close to 1 never
+// raise it; Complex KDA gates near zero do.)
+//
+// Passes (fixed length B x T, chunks of 64 tokens, nc per sequence):
+//   cbwd_prep_kernel   one workgroup per (batch row, chunk, head): M as MFMA operand fragments
+//                      and N in fp32 into the chunk's record;
+//   cbwd_state_kernel  one workgroup per (batch row, head, 32 value columns): walks the chunks in
+//                      reverse with dS in registers, stores dS at every chunk end, dS <- M dS + N;
+//   cbwd_grad_kernel   one workgroup per (batch row, chunk, head): recomputes the chunk algebra,
+//                      loops over 32-column value blocks for delta, eps and the tile gradients,
+//                      then forms dq, dk, dv, dalpha and the gate gradients.
+#include "prefill.hpp"
+
+namespace dr {
+
+namespace {
+
+constexpr float CB_TAU = 0x1p-10f;   // smallest gate magnitude the chunked form takes
+constexpr float CB_LO = 0x1p-100f;   // range of the running products it takes
+constexpr float CB_HI = 0x1p100f;
+constexpr int L68 = CH + 4;          // row stride of 64-column fp32 tiles
+constexpr int L36 = 36;              // row stride of 32-column fp32 tiles
+
+// Record of one (batch row, chunk, head): M's fragments as A operands (row tiles of output
+// channels x 32-deep steps over input channels), then N [d_k][d_v] in fp32.
+template <int DK>
+struct CRec {
+  static constexpr int KS = DK / 32;
+  static constexpr int64_t MF = 0;
+  static constexpr int64_t NN = (int64_t)(DK / 16) * KS * 2048;
+  static int64_t size(int dv) { return (NN + (int64_t)DK * dv * 4 + 255) / 256 * 256; }
+};
+
+// LDS of the two per-chunk kernels. r0: Gamma (then, by pass, Utilde / Qtilde / Z, or dP and dA);
+// r1: Kd (then dO in the preparation); r2: A, At, P, T of the chunk algebra, then the value-block
+// buffers of the gradient kernel, then Qtilde / Utilde and the gate-gradient sums, or W and M in the
+// preparation.
+template <int DK>
+struct CbSmem {
+  static constexpr int LG = DK + 4;
+  static constexpr int R0 = (CH * LG > 2 * CH * L68) ? CH * LG : 2 * CH * L68;
+  static constexpr int R1 = CH * (128 + 4);
+  static constexpr int RB = 2 * DK * L36 + 3 * CH * L36 + 2 * 32 * L68;  // value-block buffers
+  static constexpr int RM = DK * LG;                                   // M in the preparation
+  static constexpr int R2a = RB > 4 * CH * L68 ? RB : 4 * CH * L68;
+  static constexpr int R2b = 2 * CH * LG > RM ? 2 * CH * LG : RM;
+  static constexpr int R2 = R2a > R2b ? R2a : R2b;
+  float r0[R0];
+  float r1[R1];
+  float r2[R2];
+  float gc[DK];     // Gamma_C
+  float ddp[256];   // per-thread partial sums of rowsum(S0 . dS)
+  float ecs[4][DK]; // per-wave column sums of Kbar . dKbar
+};
+// offsets in r2 during the chunk algebra
+constexpr int OA = 0, OAT = CH * L68, OP = 2 * CH * L68, OT = 3 * CH * L68;
+
+template <class Pol>
+__device__ __forceinline__ typename Pol::Frag frag_c(const float* p) {
+  float x[8];
+  load8(p, x);
+  return Pol::make(x);
+}
+template <class Pol>
+__device__ __forceinline__ typename Pol::Frag frag_s(const float* p, int stride) {
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = p[j * stride];
+  return Pol::make(x);
+}
+
+// Row of token t of chunk c, batch row b, head h in the dense per-token arrays.
+__device__ __forceinline__ int64_t cb_row(const CbParams& p, int b, int64_t m, int h) {
+  return ((int64_t)b * p.T + m) * p.H + h;
+}
+
+// The chunk algebra shared by the preparation and the gradient kernel: Gamma in r0, Kd in r1,
+// A, P and T in r2, Gamma_C in gc; ut / qt receive this thread's row of Utilde / Qtilde (token
+// 16 w + lane % 16, channels 32 ks + 8 (lane / 16) + j). With set_flag, a chunk outside the
+// chunked form's range sets *p.flag.
+template <int DK, typename InT, bool VEC>
+__device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm, int b, int c, int h, int nvalid,
+                                              float (&ut)[DK / 32][8], float (&qt)[DK / 32][8], bool set_flag) {
+  using Pol = typename PolicyFor<InT>::type;
+  using Frag = typename Pol::Frag;
+  constexpr int KS = DK / 32, LG = CbSmem<DK>::LG;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  const int64_t m0 = (int64_t)c * CH;
+
+  // Gamma: a running product down the chunk, one thread per channel (tokens past the sequence
+  // end take decay 1)
+  if (tid < DK) {
+    float a[CH];
+#pragma unroll
+    for (int t = 0; t < CH; ++t) a[t] = t < nvalid ? p.alpha[cb_row(p, b, m0 + t, h) * DK + tid] : 1.f;
+    float gm = 1.f;
+    bool bad = false;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      bad = bad || !(fabsf(a[t]) >= CB_TAU);  // (also true for NaN)
+      gm *= a[t];
+      bad = bad || !(fabsf(gm) >= CB_LO && fabsf(gm) <= CB_HI);
+      sm.r0[t * LG + tid] = gm;
+    }
+    sm.gc[tid] = gm;
+    if (set_flag && bad) atomicOr(p.flag, 1);
+  }
+  __syncthreads();
+
+  // this thread's row: Utilde, Qtilde (registers) and Kd (LDS)
+  {
+    const int row = 16 * w + r;
+    const bool valid = row < nvalid;
+    const int64_t m = m0 + (valid ? row : 0);
+    const int64_t th = cb_row(p, b, m, h);
+    const InT* qp = static_cast<const InT*>(p.q);
+    const InT* kp = static_cast<const InT*>(p.k);
+    const int64_t qo = q_elem(p, b, m, h, DK), ko = kv_elem(p.k_ts, p.k_bs, p, b, m, h, DK);
+    const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * g;
+      float q8[8], k8[8], b8[8], g8[8];
+      if (valid) {
+        load8(qp + qo + ch0, q8);
+        load8(kp + ko + ch0, k8);
+        if constexpr (VEC) load8(p.erase + th * DK + ch0, b8);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { q8[j] = 0.f; k8[j] = 0.f; b8[j] = 0.f; }
+      }
+      load8(&sm.r0[row * LG + ch0], g8);
+      float kd[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        qt[ks][j] = q8[j] * g8[j];
+        ut[ks][j] = (VEC ? b8[j] : esc) * k8[j] * g8[j];
+        kd[j] = k8[j] / g8[j];
+      }
+      store4(&sm.r1[row * LG + ch0], f32x4{kd[0], kd[1], kd[2], kd[3]});
+      store4(&sm.r1[row * LG + ch0 + 4], f32x4{kd[4], kd[5], kd[6], kd[7]});
+    }
+  }
+  __syncthreads();
+
+  // A = strict_tril(Utilde Kd^T), P = tril(Qtilde Kd^T) for row block w; T zeroed in row block w
+  {
+    f32x4 accA[NBLK], accP[NBLK];
+#pragma unroll
+    for (int J = 0; J < NBLK; ++J) { accA[J] = f32x4{0.f, 0.f, 0.f, 0.f}; accP[J] = accA[J]; }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const Frag UF = Pol::make(ut[ks]);
+      const Frag QF = Pol::make(qt[ks]);
+#pragma unroll
+      for (int J = 0; J < NBLK; ++J) {
+        if (J <= w) {
+          const Frag KF = frag_c<Pol>(&sm.r1[(16 * J + r) * LG + 32 * ks + 8 * g]);
+          Pol::mma(accA[J], UF, KF);
+          Pol::mma(accP[J], QF, KF);
+        }
+      }
+    }
+#pragma unroll
+    for (int J = 0; J < NBLK; ++J) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g + i, col = 16 * J + r;
+        sm.r2[OA + row * L68 + col] = (J <= w && col < row) ? accA[J][i] : 0.f;
+        sm.r2[OP + row * L68 + col] = (J <= w && col <= row) ? accP[J][i] : 0.f;
+        sm.r2[OT + row * L68 + col] = 0.f;
+      }
+    }
+  }
+  __syncthreads();
+  float* A = sm.r2 + OA;
+  float* At = sm.r2 + OAT;
+  float* Tm = sm.r2 + OT;
+  // diagonal blocks of T = (I + A)^-1 by forward substitution, one lane per column of block w
+  if (l < 16) {
+    float t[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      float acc = (rr == l) ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < rr; ++s) acc = fmaf(-A[(16 * w + rr) * L68 + 16 * w + s], t[s], acc);
+      t[rr] = acc;
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) Tm[(16 * w + rr) * L68 + 16 * w + l] = t[rr];
+  }
+  __syncthreads();
+  // At_wK = T_ww A_wK for K < w (16-deep products, the upper half of the 32-deep slice zero)
+  {
+    float x[8];
+    if (g < 2) {
+      load8(&Tm[(16 * w + r) * L68 + 16 * w + 8 * g], x);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = 0.f;
+    }
+    const Frag Tww = Pol::make(x);
+#pragma unroll
+    for (int K = 0; K < NBLK - 1; ++K) {
+      if (K < w) {
+        float y[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) y[j] = g < 2 ? A[(16 * w + 8 * g + j) * L68 + 16 * K + r] : 0.f;
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        Pol::mma(acc, Tww, Pol::make(y));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) At[(16 * w + 4 * g + i) * L68 + 16 * K + r] = acc[i];
+      }
+    }
+  }
+  __syncthreads();
+  // T_wJ = -sum_{K = J}^{w - 1} At_wK T_KJ, by increasing distance d = w - J
+#pragma unroll
+  for (int d = 1; d < NBLK; ++d) {
+    if (w >= d) {
+      const int J = w - d;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        if (st < (d + 1) / 2) {
+          const int k0 = 16 * J + 32 * st + 8 * g;
+          float a8[8], b8[8];
+          if (k0 < 16 * w) {
+            load8(&At[(16 * w + r) * L68 + k0], a8);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b8[j] = Tm[(k0 + j) * L68 + 16 * J + r];
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) { a8[j] = 0.f; b8[j] = 0.f; }
+          }
+          Pol::mma(acc, Pol::make(a8), Pol::make(b8));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Tm[(16 * w + 4 * g + i) * L68 + 16 * J + r] = -acc[i];
+    }
+    __syncthreads();
+  }
+}
+
+__device__ __forceinline__ void cb_slot(const CbParams& p, int slot, int& b, int& c, int& h, int& nvalid) {
+  h = slot % p.H;
+  c = (slot / p.H) % p.nc;
+  b = slot / (p.H * p.nc);
+  const int64_t left = p.T - (int64_t)c * CH;
+  nvalid = left < CH ? (int)left : CH;
+}
+
+}  // namespace
+
+// ============================================================================ pass 1
+__global__ void cbwd_flag_clear_kernel(int32_t* flag) {
+  if (threadIdx.x == 0) *flag = 0;
+}
+
+template <int DK, typename InT, bool VEC>
+__global__ __launch_bounds__(256, 1) void cbwd_prep_kernel(const CbParams p) {
+  using Pol = typename PolicyFor<InT>::type;
+  using Frag = typename Pol::Frag;
+  constexpr int KS = DK / 32, LG = CbSmem<DK>::LG, NRT = DK / 64, NCT = DK / 16;
+  using R = CRec<DK>;
+  __shared__ __align__(16) CbSmem<DK> sm;
+  int b, c, h, nvalid;
+  cb_slot(p, blockIdx.x, b, c, h, nvalid);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  float ut[KS][8], qt[KS][8];
+  chunk_algebra<DK, InT, VEC>(p, sm, b, c, h, nvalid, ut, qt, true);
+  const float* Tm = sm.r2 + OT;
+  const float* Pm = sm.r2 + OP;
+  float* Wm = sm.r2;  // W over A and At (no longer read)
+
+  // Utilde -> r0 (Gamma is not read past the chunk algebra)
+  {
+    const int row = 16 * w + r;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * g;
+      store4(&sm.r0[row * LG + ch0], f32x4{ut[ks][0], ut[ks][1], ut[ks][2], ut[ks][3]});
+      store4(&sm.r0[row * LG + ch0 + 4], f32x4{ut[ks][4], ut[ks][5], ut[ks][6], ut[ks][7]});
+    }
+  }
+  __syncthreads();
+  // W = T Utilde, row block w
+  {
+    f32x4 acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (st == 0 || w >= 2) {
+        const Frag TF = frag_c<Pol>(&Tm[(16 * w + r) * L68 + 32 * st + 8 * g]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          Pol::mma(acc[ct], TF, frag_s<Pol>(&sm.r0[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Wm[(16 * w + 4 * g + i) * LG + 16 * ct + r] = acc[ct][i];
+    }
+  }
+  __syncthreads();
+  // Qtilde -> r0, then Z = Qtilde - P W in place (row block w)
+  {
+    const int row = 16 * w + r;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * g;
+      store4(&sm.r0[row * LG + ch0], f32x4{qt[ks][0], qt[ks][1], qt[ks][2], qt[ks][3]});
+      store4(&sm.r0[row * LG + ch0 + 4], f32x4{qt[ks][4], qt[ks][5], qt[ks][6], qt[ks][7]});
+    }
+  }
+  __syncthreads();
+  {
+    f32x4 acc[NCT];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      if (st == 0 || w >= 2) {
+        const Frag PF = frag_c<Pol>(&Pm[(16 * w + r) * L68 + 32 * st + 8 * g]);
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct)
+          Pol::mma(acc[ct], PF, frag_s<Pol>(&Wm[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float* z = &sm.r0[(16 * w + 4 * g + i) * LG + 16 * ct + r];
+        *z = *z - acc[ct][i];
+      }
+    }
+  }
+  __syncthreads();
+  // M = Diag(Gamma_C) - W^T Kbar, output-channel tiles w + 4 m
+  {
+    f32x4 acc[NRT][NCT];
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) acc[m][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      Frag AF[NRT];
+#pragma unroll
+      for (int m = 0; m < NRT; ++m) AF[m] = frag_s<Pol>(&Wm[(32 * st + 8 * g) * LG + 16 * (w + 4 * m) + r], LG);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const float gcc = sm.gc[16 * ct + r];
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = sm.r1[(32 * st + 8 * g + j) * LG + 16 * ct + r] * gcc;
+        const Frag BF = Pol::make(x);
+#pragma unroll
+        for (int m = 0; m < NRT; ++m) Pol::mma(acc[m][ct], AF[m], BF);
+      }
+    }
+    __syncthreads();  // W and Kd read by every wave
+    float* Mm = sm.r2;
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ra = 16 * (w + 4 * m) + 4 * g + i, cb = 16 * ct + r;
+          Mm[ra * LG + cb] = (ra == cb ? sm.gc[cb] : 0.f) - acc[m][ct][i];
+        }
+      }
+    }
+  }
+  // dO of the chunk -> r1 [64][d_v + 4] (zero past the sequence end)
+  const int DV = p.DV, LV = DV + 4;
+  for (int idx = tid; idx < CH * (DV / 4); idx += 256) {
+    const int t = idx / (DV / 4), v4 = idx % (DV / 4);
+    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (t < nvalid) x = *reinterpret_cast<const f32x4*>(p.dO + cb_row(p, b, (int64_t)c * CH + t, h) * DV + 4 * v4);
+    store4(&sm.r1[t * LV + 4 * v4], x);
+  }
+  __syncthreads();
+  const int64_t slot = blockIdx.x;
+  unsigned char* rec = p.rec + slot * p.rec_size;
+  const __amdgpu_buffer_rsrc_t rs = rec_rsrc(rec, p.rec_size);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  // M's fragments: row tile rt, step kb: row 16 rt + lane % 16, columns 32 kb + 8 (lane / 16) + j
+  for (int rt = wu; rt < DK / 16; rt += 4) {
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) {
+      float x[8];
+      load8(&sm.r2[(16 * rt + r) * LG + 32 * kb + 8 * g], x);
+      st_frag(rs, (int)R::MF, rt * KS + kb, l, Pol::make(x), true);
+    }
+  }
+  // N = Z^T dO, output-channel tiles w + 4 m, stored row-major in fp32
+  float* Nrec = reinterpret_cast<float*>(rec + R::NN);
+  for (int ct0 = 0; ct0 < DV / 16; ct0 += 4) {
+    f32x4 acc[NRT][4];
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc[m][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      Frag AF[NRT];
+#pragma unroll
+      for (int m = 0; m < NRT; ++m) AF[m] = frag_s<Pol>(&sm.r0[(32 * st + 8 * g) * LG + 16 * (w + 4 * m) + r], LG);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (ct0 + u < DV / 16) {
+          const Frag BF = frag_s<Pol>(&sm.r1[(32 * st + 8 * g) * LV + 16 * (ct0 + u) + r], LV);
+#pragma unroll
+          for (int m = 0; m < NRT; ++m) Pol::mma(acc[m][u], AF[m], BF);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (ct0 + u < DV / 16) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            __builtin_nontemporal_store(acc[m][u][i], &Nrec[(16 * (w + 4 * m) + 4 * g + i) * DV + 16 * (ct0 + u) + r]);
+        }
+      }
+    }
+  }
+}
+
+// ============================================================================ pass 2
+// dS walks the chunks in reverse, one workgroup per (batch row, head, 32 value columns); wave w
+// holds output-channel tiles w + 4 m.
+template <int DK, typename InT>
+__global__ __launch_bounds__(256, 1) void cbwd_state_kernel(const CbParams p) {
+  using Pol = typename PolicyFor<InT>::type;
+  using Frag = typename Pol::Frag;
+  constexpr int KS = DK / 32, NRT = DK / 64, NCT = 2, DVB = 32;
+  using R = CRec<DK>;
+  __shared__ __align__(16) float Gf[DVB][DK + 4];  // dS, transposed: [value column][channel]
+  const int ndvb = p.DV / DVB;
+  const int logical = p.B * p.H * ndvb;
+  const int lid = (gridDim.x % 8 == 0) ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
+  if (lid >= logical) return;
+  const int pair = lid / ndvb, dv0 = (lid % ndvb) * DVB;
+  const int b = pair / p.H, h = pair % p.H;
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  const int DV = p.DV;
+  const int64_t SS = (int64_t)DK * DV;
+
+  f32x4 G[NRT][NCT];
+#pragma unroll
+  for (int m = 0; m < NRT; ++m) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ch = 16 * (w + 4 * m) + 4 * g + i;
+        G[m][ct][i] = p.dST ? p.dST[((int64_t)b * p.H + h) * SS + (int64_t)ch * DV + dv0 + 16 * ct + r] : 0.f;
+      }
+    }
+  }
+  for (int c = p.nc - 1; c >= 0; --c) {
+    const int64_t slot = ((int64_t)b * p.nc + c) * p.H + h;
+    float* dsc = p.dsc + slot * SS;
+    const unsigned char* rec = p.rec + slot * p.rec_size;
+    const __amdgpu_buffer_rsrc_t rs = rec_rsrc(rec, p.rec_size);
+    const float* Nrec = reinterpret_cast<const float*>(rec + R::NN);
+    f32x4 acc[NRT][NCT];
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 16 * (w + 4 * m) + 4 * g + i;
+          const int64_t o = (int64_t)ch * DV + dv0 + 16 * ct + r;
+          dsc[o] = G[m][ct][i];
+          Gf[16 * ct + r][ch] = G[m][ct][i];
+          acc[m][ct][i] = Nrec[o];
+        }
+      }
+    }
+    Frag MF[NRT][KS];
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb) MF[m][kb] = ld_frag<Frag>(rs, (int)R::MF, (w + 4 * m) * KS + kb, l);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < KS; ++kb) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const Frag BF = frag_c<Pol>(&Gf[16 * ct + r][32 * kb + 8 * g]);
+#pragma unroll
+        for (int m = 0; m < NRT; ++m) Pol::mma(acc[m][ct], MF[m][kb], BF);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) G[m][ct] = acc[m][ct];
+    }
+    __syncthreads();
+  }
+  if (p.dS0) {
+#pragma unroll
+    for (int m = 0; m < NRT; ++m) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ch = 16 * (w + 4 * m) + 4 * g + i;
+          p.dS0[((int64_t)b * p.H + h) * SS + (int64_t)ch * DV + dv0 + 16 * ct + r] = G[m][ct][i];
+        }
+      }
+    }
+  }
+}
+
+// ============================================================================ pass 3
+template <int DK, typename InT, bool VEC>
+__global__ __launch_bounds__(256, 1) void cbwd_grad_kernel(const CbParams p) {
+  using Pol = typename PolicyFor<InT>::type;
+  using Frag = typename Pol::Frag;
+  constexpr int KS = DK / 32, LG = CbSmem<DK>::LG, NCT = DK / 16;
+  constexpr int PARTS = 256 / DK, CPP = 32 / PARTS;  // rowsum partials: threads per channel, columns each
+  __shared__ __align__(16) CbSmem<DK> sm;
+  if (*p.flag) return;  // the exact walk takes the call
+  int b, c, h, nvalid;
+  cb_slot(p, blockIdx.x, b, c, h, nvalid);
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  const int64_t m0 = (int64_t)c * CH;
+  const int DV = p.DV;
+  const int64_t SS = (int64_t)DK * DV;
+  const bool kda = p.variant == 0 || p.variant == 3;
+  const InT* qp = static_cast<const InT*>(p.q);
+  const InT* kp = static_cast<const InT*>(p.k);
+  const InT* vp = static_cast<const InT*>(p.v);
+
+  Frag UF[KS], KbF[KS], TF[2], TtF[2], PtF[2];
+  {
+    float ut[KS][8], qt[KS][8];
+    chunk_algebra<DK, InT, VEC>(p, sm, b, c, h, nvalid, ut, qt, false);
+    const float* Tm = sm.r2 + OT;
+    const float* Pm = sm.r2 + OP;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      UF[ks] = Pol::make(ut[ks]);
+      float x[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) x[j] = sm.r1[(16 * w + r) * LG + 32 * ks + 8 * g + j] * sm.gc[32 * ks + 8 * g + j];
+      KbF[ks] = Pol::make(x);
+    }
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      TF[st] = frag_c<Pol>(&Tm[(16 * w + r) * L68 + 32 * st + 8 * g]);
+      TtF[st] = frag_s<Pol>(&Tm[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+      PtF[st] = frag_s<Pol>(&Pm[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+    }
+  }
+  __syncthreads();
+
+  // ---- value blocks of 32 columns: delta, eps, dv and the tile gradients
+  float* S0b = sm.r2;
+  float* dSb = S0b + DK * L36;
+  float* dOb = dSb + DK * L36;
+  float* Dl = dOb + CH * L36;
+  float* El = Dl + CH * L36;
+  float* Rt = El + CH * L36;
+  float* Yt = Rt + 32 * L68;
+  const float* S0p = c == 0 ? (p.S0 ? p.S0 + ((int64_t)b * p.H + h) * SS : nullptr)
+                            : p.snap + (((int64_t)b * (p.T / CH) + c - 1) * p.H + h) * SS;
+  const float* dSp = p.dsc + (((int64_t)b * p.nc + c) * p.H + h) * SS;
+  f32x4 dQt[NCT], dUt[NCT], dKb[NCT], dPa[NBLK], dAa[NBLK];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) { dQt[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; dUt[ct] = dQt[ct]; dKb[ct] = dQt[ct]; }
+#pragma unroll
+  for (int J = 0; J < NBLK; ++J) { dPa[J] = f32x4{0.f, 0.f, 0.f, 0.f}; dAa[J] = dPa[J]; }
+  float dpart = 0.f;
+  float vdm[4] = {0.f, 0.f, 0.f, 0.f};  // v . dm of rows 16 w + 4 g + i over this lane's columns
+  for (int dv0 = 0; dv0 < DV; dv0 += 32) {
+    for (int idx = tid; idx < DK * 8; idx += 256) {
+      const int row = idx >> 3, q4 = idx & 7;
+      const int64_t o = (int64_t)row * DV + dv0 + 4 * q4;
+      store4(&S0b[row * L36 + 4 * q4], S0p ? *reinterpret_cast<const f32x4*>(S0p + o) : f32x4{0.f, 0.f, 0.f, 0.f});
+      store4(&dSb[row * L36 + 4 * q4], *reinterpret_cast<const f32x4*>(dSp + o));
+    }
+    for (int idx = tid; idx < CH * 8; idx += 256) {
+      const int t = idx >> 3, q4 = idx & 7;
+      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (t < nvalid) x = *reinterpret_cast<const f32x4*>(p.dO + cb_row(p, b, m0 + t, h) * DV + dv0 + 4 * q4);
+      store4(&dOb[t * L36 + 4 * q4], x);
+    }
+    // m = write . v at rows 16 w + 4 g + i, columns 16 ct + r of the block
+    float mv[2][4], vv[2][4], wv[2][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * w + 4 * g + i;
+      const bool ok = t < nvalid;
+      const int64_t m = m0 + (ok ? t : 0);
+      const int64_t th = cb_row(p, b, m, h);
+      const int64_t vo = kv_elem(p.v_ts, p.v_bs, p, b, m, h, DV);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int col = dv0 + 16 * ct + r;
+        const float vx = ok ? ld_f32(vp + vo + col) : 0.f;
+        const float wg = ok ? (VEC ? p.write[th * DV + col] : p.write[th]) : 0.f;
+        vv[ct][i] = vx;
+        wv[ct][i] = wg;
+        mv[ct][i] = wg * vx;
+      }
+    }
+    __syncthreads();
+    {  // rowsum(S0 . dS) partials: channel tid % DK, columns CPP * (tid / DK) ..
+      const int ch = tid % DK, c0 = CPP * (tid / DK);
+#pragma unroll
+      for (int j = 0; j < CPP; ++j) dpart = fmaf(S0b[ch * L36 + c0 + j], dSb[ch * L36 + c0 + j], dpart);
+    }
+    // X = Utilde S0 -> R = M - X (transposed into Rt); Y = Kbar dS + P^T dO (transposed into Yt)
+    {
+      f32x4 accX[2], accY[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) { accX[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; accY[ct] = accX[ct]; }
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          Pol::mma(accX[ct], UF[ks], frag_s<Pol>(&S0b[(32 * ks + 8 * g) * L36 + 16 * ct + r], L36));
+          Pol::mma(accY[ct], KbF[ks], frag_s<Pol>(&dSb[(32 * ks + 8 * g) * L36 + 16 * ct + r], L36));
+        }
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          Pol::mma(accY[ct], PtF[st], frag_s<Pol>(&dOb[(32 * st + 8 * g) * L36 + 16 * ct + r], L36));
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Rt[(16 * ct + r) * L68 + 16 * w + 4 * g + i] = mv[ct][i] - accX[ct][i];
+          Yt[(16 * ct + r) * L68 + 16 * w + 4 * g + i] = accY[ct][i];
+        }
+      }
+    }
+    __syncthreads();
+    // delta = T R, eps = T^T Y; dm = eps goes to dv and to the write gate's gradient
+    {
+      f32x4 accD[2], accE[2];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) { accD[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; accE[ct] = accD[ct]; }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          Pol::mma(accD[ct], TF[st], frag_c<Pol>(&Rt[(16 * ct + r) * L68 + 32 * st + 8 * g]));
+          Pol::mma(accE[ct], TtF[st], frag_c<Pol>(&Yt[(16 * ct + r) * L68 + 32 * st + 8 * g]));
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * w + 4 * g + i;
+          Dl[t * L36 + 16 * ct + r] = accD[ct][i];
+          El[t * L36 + 16 * ct + r] = accE[ct][i];
+          if (t < nvalid) {
+            const int64_t th = cb_row(p, b, m0 + t, h);
+            const int col = dv0 + 16 * ct + r;
+            const float e = accE[ct][i];
+            p.dv[th * DV + col] = wv[ct][i] * e;
+            if constexpr (VEC) p.dwrite[th * DV + col] = vv[ct][i] * e;
+            else vdm[i] = fmaf(vv[ct][i], e, vdm[i]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // tile gradients: dQtilde += dO S0^T, dUtilde -= eps S0^T, dKbar += delta dS^T,
+    // dP += dO delta^T, dA -= eps delta^T (row block w)
+    {
+      const Frag AO = frag_c<Pol>(&dOb[(16 * w + r) * L36 + 8 * g]);
+      float xe[8];
+      load8(&El[(16 * w + r) * L36 + 8 * g], xe);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xe[j] = -xe[j];
+      const Frag AE = Pol::make(xe);
+      const Frag AD = frag_c<Pol>(&Dl[(16 * w + r) * L36 + 8 * g]);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const Frag BS = frag_c<Pol>(&S0b[(16 * ct + r) * L36 + 8 * g]);
+        Pol::mma(dQt[ct], AO, BS);
+        Pol::mma(dUt[ct], AE, BS);
+        Pol::mma(dKb[ct], AD, frag_c<Pol>(&dSb[(16 * ct + r) * L36 + 8 * g]));
+      }
+#pragma unroll
+      for (int J = 0; J < NBLK; ++J) {
+        if (J <= w) {
+          const Frag BD = frag_c<Pol>(&Dl[(16 * J + r) * L36 + 8 * g]);
+          Pol::mma(dPa[J], AO, BD);
+          Pol::mma(dAa[J], AE, BD);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  sm.ddp[tid] = dpart;
+
+  // ---- Qtilde and Utilde -> r2 (recomputed from Gamma), this thread's Gamma values
+  float* Ql = sm.r2;
+  float* Ul = sm.r2 + CH * LG;
+  {
+    const int row = 16 * w + r;
+    const bool valid = row < nvalid;
+    const int64_t m = m0 + (valid ? row : 0);
+    const int64_t th = cb_row(p, b, m, h);
+    const int64_t qo = q_elem(p, b, m, h, DK), ko = kv_elem(p.k_ts, p.k_bs, p, b, m, h, DK);
+    const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * g;
+      float q8[8], k8[8], b8[8], g8[8];
+      if (valid) {
+        load8(qp + qo + ch0, q8);
+        load8(kp + ko + ch0, k8);
+        if constexpr (VEC) load8(p.erase + th * DK + ch0, b8);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) { q8[j] = 0.f; k8[j] = 0.f; b8[j] = 0.f; }
+      }
+      load8(&sm.r0[row * LG + ch0], g8);
+      float a[8], u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) { a[j] = q8[j] * g8[j]; u[j] = (VEC ? b8[j] : esc) * k8[j] * g8[j]; }
+      store4(&Ql[row * LG + ch0], f32x4{a[0], a[1], a[2], a[3]});
+      store4(&Ql[row * LG + ch0 + 4], f32x4{a[4], a[5], a[6], a[7]});
+      store4(&Ul[row * LG + ch0], f32x4{u[0], u[1], u[2], u[3]});
+      store4(&Ul[row * LG + ch0 + 4], f32x4{u[4], u[5], u[6], u[7]});
+    }
+  }
+  float gam[NCT][4];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) gam[ct][i] = sm.r0[(16 * w + 4 * g + i) * LG + 16 * ct + r];
+  }
+  __syncthreads();
+  // dP (lower triangle) and dA (strict lower triangle) -> r0
+  float* dPl = sm.r0;
+  float* dAl = sm.r0 + CH * L68;
+#pragma unroll
+  for (int J = 0; J < NBLK; ++J) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * w + 4 * g + i, col = 16 * J + r;
+      dPl[row * L68 + col] = (J <= w && col <= row) ? dPa[J][i] : 0.f;
+      dAl[row * L68 + col] = (J <= w && col < row) ? dAa[J][i] : 0.f;
+    }
+  }
+  // Gamma_C . dKbar, and the column sums of Kbar . dKbar (= Kd . (Gamma_C . dKbar))
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const float gcc = sm.gc[16 * ct + r];
+    float e = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      dKb[ct][i] *= gcc;
+      e = fmaf(sm.r1[(16 * w + 4 * g + i) * LG + 16 * ct + r], dKb[ct][i], e);
+    }
+    e += __shfl_xor(e, 16);
+    e += __shfl_xor(e, 32);
+    if (g == 0) sm.ecs[w][16 * ct + r] = e;
+  }
+  __syncthreads();
+  // dq' = dQtilde + dP Kd, du' = dUtilde + dA Kd, dk' = Gamma_C . dKbar + dP^T Qtilde + dA^T Utilde
+#pragma unroll
+  for (int st = 0; st < 2; ++st) {
+    if (st == 0 || w >= 2) {
+      const Frag AP = frag_c<Pol>(&dPl[(16 * w + r) * L68 + 32 * st + 8 * g]);
+      const Frag AA = frag_c<Pol>(&dAl[(16 * w + r) * L68 + 32 * st + 8 * g]);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const Frag BK = frag_s<Pol>(&sm.r1[(32 * st + 8 * g) * LG + 16 * ct + r], LG);
+        Pol::mma(dQt[ct], AP, BK);
+        Pol::mma(dUt[ct], AA, BK);
+      }
+    }
+    const Frag APt = frag_s<Pol>(&dPl[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+    const Frag AAt = frag_s<Pol>(&dAl[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      Pol::mma(dKb[ct], APt, frag_s<Pol>(&Ql[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
+      Pol::mma(dKb[ct], AAt, frag_s<Pol>(&Ul[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
+    }
+  }
+  __syncthreads();
+  // final values per (token 16 w + 4 g + i, channel 16 ct + r); x = q dq + u du - k dk -> r2
+  float* X = sm.r2;
+  float kdu[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 16 * w + 4 * g + i;
+    const bool ok = t < nvalid;
+    const int64_t m = m0 + (ok ? t : 0);
+    const int64_t th = cb_row(p, b, m, h);
+    const int64_t qo = q_elem(p, b, m, h, DK), ko = kv_elem(p.k_ts, p.k_bs, p, b, m, h, DK);
+    const float esc = VEC ? 0.f : p.erase[th];
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int ch = 16 * ct + r;
+      const float gm = gam[ct][i];
+      const float dqv = gm * dQt[ct][i];
+      const float duv = gm * dUt[ct][i];
+      const float dkk = dKb[ct][i] / gm;
+      const float qv = ld_f32(qp + qo + ch), kv = ld_f32(kp + ko + ch);
+      const float ev = VEC ? p.erase[th * DK + ch] : esc;
+      const float uv = ev * kv;
+      X[t * LG + ch] = ok ? (qv * dqv + uv * duv - kv * dkk) : 0.f;
+      if (ok) {
+        p.dq[th * DK + ch] = dqv;
+        p.dk[th * DK + ch] = fmaf(ev, duv, dkk);
+        if constexpr (VEC) p.derase[th * DK + ch] = kv * duv;
+      }
+      kdu[i] = fmaf(kv, duv, kdu[i]);
+    }
+  }
+  if constexpr (!VEC) {
+    // per token: k . du over the channels and v . dm over the value columns (lanes r of a row group)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float a = kdu[i], v = vdm[i];
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) { a += __shfl_xor(a, d); v += __shfl_xor(v, d); }
+      const int t = 16 * w + 4 * g + i;
+      if (r == 0 && t < nvalid) {
+        const int64_t th = cb_row(p, b, m0 + t, h);
+        if (kda) {
+          p.derase[th] = a + v;
+        } else {
+          p.derase[th] = a;
+          p.dwrite[th] = v;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  // alpha_t dalpha_t = reverse cumulative sum of x + Gamma_C rowsum(S0 . dS) + sum_s Kbar . dKbar
+  if (tid < DK) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < PARTS; ++q) s += sm.ddp[q * DK + tid];
+    s *= sm.gc[tid];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) s += sm.ecs[q][tid];
+    for (int t = CH - 1; t >= 0; --t) {
+      s += X[t * LG + tid];
+      X[t * LG + tid] = s;
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 16 * w + 4 * g + i;
+    if (t < nvalid) {
+      const int64_t th = cb_row(p, b, m0 + t, h);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int ch = 16 * ct + r;
+        p.dalpha[th * DK + ch] = X[t * LG + ch] / p.alpha[th * DK + ch];
+      }
+    }
+  }
+}
+
+// ============================================================================ host
+int64_t cbwd_record_bytes(int dk, int dv) { return dk == 64 ? CRec<64>::size(dv) : CRec<128>::size(dv); }
+
+template <int DK, typename InT, bool VEC>
+static hipError_t launch_cb_t(const CbParams& p, hipStream_t s) {
+  const int64_t slots = (int64_t)p.B * p.nc * p.H;
+  hipLaunchKernelGGL(cbwd_flag_clear_kernel, dim3(1), dim3(64), 0, s, p.flag);
+  hipLaunchKernelGGL((cbwd_prep_kernel<DK, InT, VEC>), dim3((unsigned)slots), dim3(256), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  int64_t wg = (int64_t)p.B * p.H * (p.DV / 32);
+  wg = (wg + 7) / 8 * 8;
+  hipLaunchKernelGGL((cbwd_state_kernel<DK, InT>), dim3((unsigned)wg), dim3(256), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((cbwd_grad_kernel<DK, InT, VEC>), dim3((unsigned)slots), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DK>
+static hipError_t launch_cb_dk(const CbParams& p, bool bf16, bool vec, hipStream_t s) {
+  if (bf16) return vec ? launch_cb_t<DK, __bf16, true>(p, s) : launch_cb_t<DK, __bf16, false>(p, s);
+  return vec ? launch_cb_t<DK, float, true>(p, s) : launch_cb_t<DK, float, false>(p, s);
+}
+
+hipError_t launch_chunked_backward(const CbParams& p, int dk, bool bf16, bool vec, hipStream_t s) {
+  if (p.B == 0 || p.T == 0 || p.H == 0) return hipSuccess;
+  if (dk == 64) return launch_cb_dk<64>(p, bf16, vec, s);
+  if (dk == 128) return launch_cb_dk<128>(p, bf16, vec, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace dr

@@ -135,6 +135,41 @@ struct BwdParams {
                         // partial sums count steps
   int64_t q_ts, q_bs, k_ts, k_bs, v_ts, v_bs;  // element strides of q, k, v (as in Params)
   int32_t strided;      // the strides are not those of dense inputs
+  const int32_t* run_flag;  // when set, the kernels run only if *run_flag is non-zero (the chunked
+                            // backward hands its call over to this exact walk that way)
+};
+
+// Parameter block of the chunked backward (fixed-length sequences, one transition per token).
+struct CbParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* alpha;
+  const float* erase;   // beta (KDA/CKDA), e (RDA) or b (GDN-2)
+  const float* write;   // == erase for KDA/CKDA, w (RDA) or w (GDN-2)
+  const float* S0;      // initial states (may be null)
+  const float* dO;
+  const float* dST;     // may be null
+  const float* snap;    // forward states after every 64 tokens: [B * (T / 64), H, d_k, d_v]
+  float* dq;
+  float* dk;
+  float* dv;
+  float* dalpha;
+  float* derase;
+  float* dwrite;
+  float* dS0;           // may be null
+  unsigned char* rec;   // per (batch row, chunk, head): the chunk's map of the state gradient
+  int64_t rec_size;
+  float* dsc;           // [B, chunks, H, d_k, d_v]: gradient reaching the state at each chunk's end
+  int32_t* flag;        // set when some chunk's gates are outside the chunked form's range
+  int64_t T;
+  int32_t H;
+  int32_t DV;
+  int32_t B;
+  int32_t nc;           // chunks per sequence
+  int32_t variant;      // 0 KDA, 1 RDA, 2 GDN-2, 3 CKDA
+  int32_t lgnh;         // 0 (one transition per token); read by q_elem / kv_elem
+  int64_t q_ts, q_bs, k_ts, k_bs, v_ts, v_bs;
 };
 
 __device__ __forceinline__ float ld_f32(const float* p) { return *p; }

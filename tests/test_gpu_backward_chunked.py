@@ -1,0 +1,110 @@
+"""GPU parity of the chunked MFMA backward (fixed-length sequences, one transition per token,
+d_k 64 or 128, d_v a multiple of 32 up to 128) against the fp64 oracle's reverse recurrence and
+against the exact per-token walk on the same inputs (the walk forced with DR_BWD_WALK=1).
+
+Tolerance per gradient tensor, max |err| / RMS(ref): 1e-4 for fp32 inputs and 1e-2 for bf16
+inputs, as for the walk. A chunk whose gates the chunked form does not take (a gate below 2^-10
+in magnitude) hands the whole call to the walk, whose results are then reproduced bit for bit."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import delta_rule_linear_chunked_amd as drl
+from oracle import backward, rel_err
+import synth
+from gpu_util import TOL, prefill_inputs, seed_of, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ("dq", "dk", "dv", "dalpha", "derase", "dwrite", "dS0")
+
+
+def _grads(a, dO, dS_T, walk=False):
+    old = os.environ.get("DR_BWD_WALK")
+    os.environ["DR_BWD_WALK"] = "1" if walk else "0"
+    try:
+        g = drl.chunk_bwd(**a, dO=dO, dS_T=dS_T)
+        torch.cuda.synchronize()
+    finally:
+        if old is None:
+            del os.environ["DR_BWD_WALK"]
+        else:
+            os.environ["DR_BWD_WALK"] = old
+    return {k: (None if v is None else v.cpu().numpy().astype(np.float64)) for k, v in g.items()}
+
+
+def _inputs(wl, seed):
+    rng = np.random.default_rng(seed)
+    dO = rng.standard_normal(wl.v.shape).astype(np.float32)
+    dS_T = rng.standard_normal(wl.S0.shape).astype(np.float32)
+    return dO, dS_T
+
+
+def _oracle(wl, dO, dS_T):
+    return backward.step_recurrence_grads(wl.q, wl.k, wl.v, wl.alpha, wl.erase, wl.write, wl.variant, dO,
+                                          dS_T=dS_T, S0=wl.S0)
+
+
+def _check(tag, g, ref, tol):
+    errs = {n: rel_err(g[n], ref[n]) for n in NAMES if ref[n] is not None}
+    print(f"[chunked backward {tag}] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["kda", "rda", "gdn2"])
+@pytest.mark.parametrize("dk,dv,T", [(128, 128, 150), (64, 32, 129), (128, 64, 40), (64, 128, 64)])
+def test_chunked_matches_oracle_and_walk(variant, dk, dv, T, in_dtype):
+    wl = synth.make_prefill(variant, 2, T, 2, dk, dv, in_dtype=in_dtype, seed=seed_of("cbwd", variant, dk, dv, T))
+    dO, dS_T = _inputs(wl, seed_of("cbwd do", variant, dk, dv, T))
+    a = prefill_inputs(wl)
+    g = _grads(a, to_dev(dO), to_dev(dS_T))
+    gw = _grads(a, to_dev(dO), to_dev(dS_T), walk=True)
+    ref = _oracle(wl, dO, dS_T)
+    _check(f"{variant} dk={dk} dv={dv} T={T} {in_dtype}", g, ref, TOL[in_dtype])
+    _check(f"{variant} dk={dk} dv={dv} T={T} {in_dtype} walk", gw, ref, TOL[in_dtype])
+    # the chunked path ran: its rounding differs from the walk's
+    assert any(not np.array_equal(g[n], gw[n]) for n in NAMES if g[n] is not None)
+
+
+def test_small_gate_hands_the_call_to_the_walk():
+    wl = synth.make_prefill("kda", 2, 200, 2, 128, 64, in_dtype="bf16", seed=seed_of("cbwd flag"))
+    wl.alpha[1, 150, 0, 7] = 1e-4   # one gate below 2^-10 in one chunk
+    dO, dS_T = _inputs(wl, 77)
+    a = prefill_inputs(wl)
+    g = _grads(a, to_dev(dO), to_dev(dS_T))
+    gw = _grads(a, to_dev(dO), to_dev(dS_T), walk=True)
+    for n in NAMES:
+        if g[n] is not None:
+            assert np.array_equal(g[n], gw[n]), n
+    _check("flagged chunk", g, _oracle(wl, dO, dS_T), TOL["bf16"])
+
+
+def test_ckda_without_small_gates_stays_chunked():
+    # Complex KDA gates with no magnitude below 2^-10 and products inside the range: chunked
+    wl = synth.make_prefill("ckda", 1, 128, 2, 64, 64, in_dtype="f32", seed=seed_of("cbwd ckda"))
+    a8 = np.abs(wl.alpha)
+    wl.alpha = np.where(a8 < 0.7, np.sign(wl.alpha + 1e-30) * 0.7, wl.alpha).astype(np.float32)
+    dO, dS_T = _inputs(wl, 5)
+    a = prefill_inputs(wl)
+    g = _grads(a, to_dev(dO), to_dev(dS_T))
+    gw = _grads(a, to_dev(dO), to_dev(dS_T), walk=True)
+    _check("ckda signed gates", g, _oracle(wl, dO, dS_T), TOL["f32"])
+    assert any(not np.array_equal(g[n], gw[n]) for n in NAMES if g[n] is not None)
+
+
+def test_chunked_equals_walk_at_full_size():
+    # the KDA prefill workload (B=4, T=4096, H=16, d=128, bf16): every gradient of the chunked path
+    # against the exact walk's, whole tensors
+    wl = synth.preset("kda_prefill")
+    dO, dS_T = _inputs(wl, 1003)
+    a = prefill_inputs(wl)
+    g = _grads(a, to_dev(dO), to_dev(dS_T))
+    gw = _grads(a, to_dev(dO), to_dev(dS_T), walk=True)
+    errs = {n: rel_err(g[n], gw[n]) for n in NAMES if g[n] is not None}
+    print("[chunked backward kda_prefill vs walk] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= TOL["bf16"], (n, e)
