@@ -76,8 +76,9 @@ struct CbSmem {
   float r1[R1];
   float r2[R2];
   float gc[DK];     // Gamma_C
-  float ddp[256];   // per-thread partial sums of rowsum(S0 . dS)
-  float ecs[4][DK]; // per-wave column sums of Kbar . dKbar
+  float ddp[512];   // per-thread partial sums of rowsum(S0 . dS)
+  float ecs[4][DK]; // per-row-block column sums of Kbar . dKbar
+  float red[2][2][CH];  // per-half token sums: k . du, v . dm
 };
 // offsets in r2 during the chunk algebra
 constexpr int OA = 0, OAT = CH * L68, OP = 2 * CH * L68, OT = 3 * CH * L68;
@@ -111,26 +112,51 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
   constexpr int KS = DK / 32, LG = CbSmem<DK>::LG;
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  // (with 512 threads, waves w and w + 4 share row block w; the second half only builds its ut / qt)
+  const int tid = threadIdx.x, w = (tid >> 6) & 3, hf = tid >> 8, l = tid & 63, r = l & 15, g = l >> 4;
   const int64_t m0 = (int64_t)c * CH;
 
-  // Gamma: a running product down the chunk, one thread per channel (tokens past the sequence
-  // end take decay 1)
-  if (tid < DK) {
-    float a[CH];
+  // Gamma: running products down the chunk per channel (tokens past the sequence end take decay
+  // 1), in segments of SEG tokens: every thread loads its segment, multiplies it out, and the
+  // segments' totals are chained through LDS
+  {
+    constexpr int NSEG = 4, SEG = CH / NSEG;
+    const int nthr = blockDim.x;
+    for (int it = tid; it < DK * NSEG; it += nthr) {
+      const int ch = it % DK, sg = it / DK;
+      float a[SEG];
 #pragma unroll
-    for (int t = 0; t < CH; ++t) a[t] = t < nvalid ? p.alpha[cb_row(p, b, m0 + t, h) * DK + tid] : 1.f;
-    float gm = 1.f;
-    bool bad = false;
+      for (int t = 0; t < SEG; ++t) {
+        const int tt = sg * SEG + t;
+        a[t] = tt < nvalid ? p.alpha[cb_row(p, b, m0 + tt, h) * DK + ch] : 1.f;
+      }
+      float gm = 1.f;
+      bool bad = false;
 #pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      bad = bad || !(fabsf(a[t]) >= CB_TAU);  // (also true for NaN)
-      gm *= a[t];
-      bad = bad || !(fabsf(gm) >= CB_LO && fabsf(gm) <= CB_HI);
-      sm.r0[t * LG + tid] = gm;
+      for (int t = 0; t < SEG; ++t) {
+        bad = bad || !(fabsf(a[t]) >= CB_TAU);  // (also true for NaN)
+        gm *= a[t];
+        sm.r0[(sg * SEG + t) * LG + ch] = gm;
+      }
+      sm.ddp[sg * DK + ch] = gm;  // the segment's total
+      if (set_flag && bad) atomicOr(p.flag, 1);
     }
-    sm.gc[tid] = gm;
-    if (set_flag && bad) atomicOr(p.flag, 1);
+    __syncthreads();
+    for (int it = tid; it < DK * NSEG; it += nthr) {
+      const int ch = it % DK, sg = it / DK;
+      float pre = 1.f;
+      for (int q = 0; q < sg; ++q) pre *= sm.ddp[q * DK + ch];
+      bool bad = false;
+#pragma unroll
+      for (int t = 0; t < SEG; ++t) {
+        float* x = &sm.r0[(sg * SEG + t) * LG + ch];
+        const float gm = pre * *x;
+        bad = bad || !(fabsf(gm) >= CB_LO && fabsf(gm) <= CB_HI);
+        *x = gm;
+      }
+      if (sg == NSEG - 1) sm.gc[ch] = pre * sm.ddp[sg * DK + ch];
+      if (set_flag && bad) atomicOr(p.flag, 1);
+    }
   }
   __syncthreads();
 
@@ -164,14 +190,16 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
         ut[ks][j] = (VEC ? b8[j] : esc) * k8[j] * g8[j];
         kd[j] = k8[j] / g8[j];
       }
-      store4(&sm.r1[row * LG + ch0], f32x4{kd[0], kd[1], kd[2], kd[3]});
-      store4(&sm.r1[row * LG + ch0 + 4], f32x4{kd[4], kd[5], kd[6], kd[7]});
+      if (hf == 0) {
+        store4(&sm.r1[row * LG + ch0], f32x4{kd[0], kd[1], kd[2], kd[3]});
+        store4(&sm.r1[row * LG + ch0 + 4], f32x4{kd[4], kd[5], kd[6], kd[7]});
+      }
     }
   }
   __syncthreads();
 
   // A = strict_tril(Utilde Kd^T), P = tril(Qtilde Kd^T) for row block w; T zeroed in row block w
-  {
+  if (hf == 0) {
     f32x4 accA[NBLK], accP[NBLK];
 #pragma unroll
     for (int J = 0; J < NBLK; ++J) { accA[J] = f32x4{0.f, 0.f, 0.f, 0.f}; accP[J] = accA[J]; }
@@ -204,7 +232,7 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
   float* At = sm.r2 + OAT;
   float* Tm = sm.r2 + OT;
   // diagonal blocks of T = (I + A)^-1 by forward substitution, one lane per column of block w
-  if (l < 16) {
+  if (hf == 0 && l < 16) {
     float t[16];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -218,7 +246,7 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
   }
   __syncthreads();
   // At_wK = T_ww A_wK for K < w (16-deep products, the upper half of the 32-deep slice zero)
-  {
+  if (hf == 0) {
     float x[8];
     if (g < 2) {
       load8(&Tm[(16 * w + r) * L68 + 16 * w + 8 * g], x);
@@ -244,7 +272,7 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
   // T_wJ = -sum_{K = J}^{w - 1} At_wK T_KJ, by increasing distance d = w - J
 #pragma unroll
   for (int d = 1; d < NBLK; ++d) {
-    if (w >= d) {
+    if (hf == 0 && w >= d) {
       const int J = w - d;
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -285,16 +313,21 @@ __global__ void cbwd_flag_clear_kernel(int32_t* flag) {
   if (threadIdx.x == 0) *flag = 0;
 }
 
+// Eight waves: waves w and w + 4 share row block w of the 64-token products (W, Z) and take half of
+// the channel tiles each; in the products over channels (M, N) wave v takes output-channel tile
+// v % (d_k / 16) and, for d_k = 64, every second column tile.
 template <int DK, typename InT, bool VEC>
-__global__ __launch_bounds__(256, 1) void cbwd_prep_kernel(const CbParams p) {
+__global__ __launch_bounds__(512, 1) void cbwd_prep_kernel(const CbParams p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
-  constexpr int KS = DK / 32, LG = CbSmem<DK>::LG, NRT = DK / 64, NCT = DK / 16;
+  constexpr int KS = DK / 32, LG = CbSmem<DK>::LG, NCT = DK / 16, NCH = NCT / 2;
+  constexpr int RT = DK / 16, WPR = 8 / RT;  // output-channel tiles; waves per tile
   using R = CRec<DK>;
   __shared__ __align__(16) CbSmem<DK> sm;
   int b, c, h, nvalid;
   cb_slot(p, blockIdx.x, b, c, h, nvalid);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, w8 = tid >> 6, w = w8 & 3, hf = w8 >> 2, l = tid & 63, r = l & 15, g = l >> 4;
+  const int rt = w8 % RT, part = w8 / RT;
   float ut[KS][8], qt[KS][8];
   chunk_algebra<DK, InT, VEC>(p, sm, b, c, h, nvalid, ut, qt, true);
   const float* Tm = sm.r2 + OT;
@@ -302,112 +335,99 @@ __global__ __launch_bounds__(256, 1) void cbwd_prep_kernel(const CbParams p) {
   float* Wm = sm.r2;  // W over A and At (no longer read)
 
   // Utilde -> r0 (Gamma is not read past the chunk algebra)
-  {
-    const int row = 16 * w + r;
+  auto put_rows = [&](const float (&x)[KS][8]) {
+    if (hf == 0) {
+      const int row = 16 * w + r;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch0 = 32 * ks + 8 * g;
-      store4(&sm.r0[row * LG + ch0], f32x4{ut[ks][0], ut[ks][1], ut[ks][2], ut[ks][3]});
-      store4(&sm.r0[row * LG + ch0 + 4], f32x4{ut[ks][4], ut[ks][5], ut[ks][6], ut[ks][7]});
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch0 = 32 * ks + 8 * g;
+        store4(&sm.r0[row * LG + ch0], f32x4{x[ks][0], x[ks][1], x[ks][2], x[ks][3]});
+        store4(&sm.r0[row * LG + ch0 + 4], f32x4{x[ks][4], x[ks][5], x[ks][6], x[ks][7]});
+      }
     }
-  }
+  };
+  put_rows(ut);
   __syncthreads();
-  // W = T Utilde, row block w
+  // W = T Utilde, row block w, this half's channel tiles
   {
-    f32x4 acc[NCT];
+    f32x4 acc[NCH];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cc = 0; cc < NCH; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       if (st == 0 || w >= 2) {
         const Frag TF = frag_c<Pol>(&Tm[(16 * w + r) * L68 + 32 * st + 8 * g]);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          Pol::mma(acc[ct], TF, frag_s<Pol>(&sm.r0[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
+        for (int cc = 0; cc < NCH; ++cc)
+          Pol::mma(acc[cc], TF, frag_s<Pol>(&sm.r0[(32 * st + 8 * g) * LG + 16 * (hf * NCH + cc) + r], LG));
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
+    for (int cc = 0; cc < NCH; ++cc) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Wm[(16 * w + 4 * g + i) * LG + 16 * ct + r] = acc[ct][i];
+      for (int i = 0; i < 4; ++i) Wm[(16 * w + 4 * g + i) * LG + 16 * (hf * NCH + cc) + r] = acc[cc][i];
     }
   }
   __syncthreads();
-  // Qtilde -> r0, then Z = Qtilde - P W in place (row block w)
-  {
-    const int row = 16 * w + r;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch0 = 32 * ks + 8 * g;
-      store4(&sm.r0[row * LG + ch0], f32x4{qt[ks][0], qt[ks][1], qt[ks][2], qt[ks][3]});
-      store4(&sm.r0[row * LG + ch0 + 4], f32x4{qt[ks][4], qt[ks][5], qt[ks][6], qt[ks][7]});
-    }
-  }
+  // Qtilde -> r0, then Z = Qtilde - P W in place (row block w, this half's channel tiles)
+  put_rows(qt);
   __syncthreads();
   {
-    f32x4 acc[NCT];
+    f32x4 acc[NCH];
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int cc = 0; cc < NCH; ++cc) acc[cc] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
       if (st == 0 || w >= 2) {
         const Frag PF = frag_c<Pol>(&Pm[(16 * w + r) * L68 + 32 * st + 8 * g]);
 #pragma unroll
-        for (int ct = 0; ct < NCT; ++ct)
-          Pol::mma(acc[ct], PF, frag_s<Pol>(&Wm[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
+        for (int cc = 0; cc < NCH; ++cc)
+          Pol::mma(acc[cc], PF, frag_s<Pol>(&Wm[(32 * st + 8 * g) * LG + 16 * (hf * NCH + cc) + r], LG));
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
+    for (int cc = 0; cc < NCH; ++cc) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float* z = &sm.r0[(16 * w + 4 * g + i) * LG + 16 * ct + r];
-        *z = *z - acc[ct][i];
+        float* z = &sm.r0[(16 * w + 4 * g + i) * LG + 16 * (hf * NCH + cc) + r];
+        *z = *z - acc[cc][i];
       }
     }
   }
   __syncthreads();
-  // M = Diag(Gamma_C) - W^T Kbar, output-channel tiles w + 4 m
+  // M = Diag(Gamma_C) - W^T Kbar: output-channel tile rt, column tiles part, part + WPR, ...
   {
-    f32x4 acc[NRT][NCT];
+    constexpr int NM = NCT / WPR;
+    f32x4 acc[NM];
 #pragma unroll
-    for (int m = 0; m < NRT; ++m) {
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) acc[m][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int u = 0; u < NM; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      Frag AF[NRT];
+      const Frag AF = frag_s<Pol>(&Wm[(32 * st + 8 * g) * LG + 16 * rt + r], LG);
 #pragma unroll
-      for (int m = 0; m < NRT; ++m) AF[m] = frag_s<Pol>(&Wm[(32 * st + 8 * g) * LG + 16 * (w + 4 * m) + r], LG);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
+      for (int u = 0; u < NM; ++u) {
+        const int ct = part + WPR * u;
         const float gcc = sm.gc[16 * ct + r];
         float x[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) x[j] = sm.r1[(32 * st + 8 * g + j) * LG + 16 * ct + r] * gcc;
-        const Frag BF = Pol::make(x);
-#pragma unroll
-        for (int m = 0; m < NRT; ++m) Pol::mma(acc[m][ct], AF[m], BF);
+        Pol::mma(acc[u], AF, Pol::make(x));
       }
     }
     __syncthreads();  // W and Kd read by every wave
     float* Mm = sm.r2;
 #pragma unroll
-    for (int m = 0; m < NRT; ++m) {
+    for (int u = 0; u < NM; ++u) {
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ra = 16 * (w + 4 * m) + 4 * g + i, cb = 16 * ct + r;
-          Mm[ra * LG + cb] = (ra == cb ? sm.gc[cb] : 0.f) - acc[m][ct][i];
-        }
+      for (int i = 0; i < 4; ++i) {
+        const int ra = 16 * rt + 4 * g + i, cb = 16 * (part + WPR * u) + r;
+        Mm[ra * LG + cb] = (ra == cb ? sm.gc[cb] : 0.f) - acc[u][i];
       }
     }
   }
   // dO of the chunk -> r1 [64][d_v + 4] (zero past the sequence end)
   const int DV = p.DV, LV = DV + 4;
-  for (int idx = tid; idx < CH * (DV / 4); idx += 256) {
+  for (int idx = tid; idx < CH * (DV / 4); idx += 512) {
     const int t = idx / (DV / 4), v4 = idx % (DV / 4);
     f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
     if (t < nvalid) x = *reinterpret_cast<const f32x4*>(p.dO + cb_row(p, b, (int64_t)c * CH + t, h) * DV + 4 * v4);
@@ -417,9 +437,8 @@ __global__ __launch_bounds__(256, 1) void cbwd_prep_kernel(const CbParams p) {
   const int64_t slot = blockIdx.x;
   unsigned char* rec = p.rec + slot * p.rec_size;
   const __amdgpu_buffer_rsrc_t rs = rec_rsrc(rec, p.rec_size);
-  const int wu = __builtin_amdgcn_readfirstlane(w);
   // M's fragments: row tile rt, step kb: row 16 rt + lane % 16, columns 32 kb + 8 (lane / 16) + j
-  for (int rt = wu; rt < DK / 16; rt += 4) {
+  if (part == 0) {
 #pragma unroll
     for (int kb = 0; kb < KS; ++kb) {
       float x[8];
@@ -427,38 +446,31 @@ __global__ __launch_bounds__(256, 1) void cbwd_prep_kernel(const CbParams p) {
       st_frag(rs, (int)R::MF, rt * KS + kb, l, Pol::make(x), true);
     }
   }
-  // N = Z^T dO, output-channel tiles w + 4 m, stored row-major in fp32
+  // N = Z^T dO: output-channel tile rt, column tiles part, part + WPR, ..., stored row-major in fp32
   float* Nrec = reinterpret_cast<float*>(rec + R::NN);
-  for (int ct0 = 0; ct0 < DV / 16; ct0 += 4) {
-    f32x4 acc[NRT][4];
+  const int NV = DV / 16;
+  Frag AZ[2];
 #pragma unroll
-    for (int m = 0; m < NRT; ++m) {
+  for (int st = 0; st < 2; ++st) AZ[st] = frag_s<Pol>(&sm.r0[(32 * st + 8 * g) * LG + 16 * rt + r], LG);
+  for (int ct0 = part; ct0 < NV; ct0 += 4 * WPR) {
+    f32x4 acc[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) acc[m][u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int u = 0; u < 4; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      Frag AF[NRT];
-#pragma unroll
-      for (int m = 0; m < NRT; ++m) AF[m] = frag_s<Pol>(&sm.r0[(32 * st + 8 * g) * LG + 16 * (w + 4 * m) + r], LG);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        if (ct0 + u < DV / 16) {
-          const Frag BF = frag_s<Pol>(&sm.r1[(32 * st + 8 * g) * LV + 16 * (ct0 + u) + r], LV);
-#pragma unroll
-          for (int m = 0; m < NRT; ++m) Pol::mma(acc[m][u], AF[m], BF);
-        }
+        const int ct = ct0 + WPR * u;
+        if (ct < NV) Pol::mma(acc[u], AZ[st], frag_s<Pol>(&sm.r1[(32 * st + 8 * g) * LV + 16 * ct + r], LV));
       }
     }
 #pragma unroll
-    for (int m = 0; m < NRT; ++m) {
+    for (int u = 0; u < 4; ++u) {
+      const int ct = ct0 + WPR * u;
+      if (ct < NV) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (ct0 + u < DV / 16) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            __builtin_nontemporal_store(acc[m][u][i], &Nrec[(16 * (w + 4 * m) + 4 * g + i) * DV + 16 * (ct0 + u) + r]);
-        }
+        for (int i = 0; i < 4; ++i)
+          __builtin_nontemporal_store(acc[u][i], &Nrec[(16 * rt + 4 * g + i) * DV + 16 * ct + r]);
       }
     }
   }
@@ -556,17 +568,22 @@ __global__ __launch_bounds__(256, 1) void cbwd_state_kernel(const CbParams p) {
 }
 
 // ============================================================================ pass 3
+// Eight waves, two per SIMD so that each covers the other's LDS and memory waits. Waves w and w + 4
+// share the 16-token row block w and split the products by role: the first half (waves 0-3) those
+// with S0 (X = Utilde S0, delta = T R, dQtilde, dUtilde, then dq and du), the second half those with
+// dS (Y = Kbar dS + P^T dO, eps = T^T Y, dKbar, dP, dA, then dk).
 template <int DK, typename InT, bool VEC>
-__global__ __launch_bounds__(256, 1) void cbwd_grad_kernel(const CbParams p) {
+__global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
-  constexpr int KS = DK / 32, LG = CbSmem<DK>::LG, NCT = DK / 16;
-  constexpr int PARTS = 256 / DK, CPP = 32 / PARTS;  // rowsum partials: threads per channel, columns each
+  constexpr int KS = DK / 32, LG = CbSmem<DK>::LG, NCT = DK / 16, KH = KS / 2;
+  constexpr int NA2 = NCT > 8 ? NCT : 8;
+  constexpr int PARTS = 512 / DK, CPP = 32 / PARTS;  // rowsum partials: threads per channel, columns each
   __shared__ __align__(16) CbSmem<DK> sm;
   if (*p.flag) return;  // the exact walk takes the call
   int b, c, h, nvalid;
   cb_slot(p, blockIdx.x, b, c, h, nvalid);
-  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  const int tid = threadIdx.x, w = (tid >> 6) & 3, hf = tid >> 8, l = tid & 63, r = l & 15, g = l >> 4;
   const int64_t m0 = (int64_t)c * CH;
   const int DV = p.DV;
   const int64_t SS = (int64_t)DK * DV;
@@ -575,25 +592,32 @@ __global__ __launch_bounds__(256, 1) void cbwd_grad_kernel(const CbParams p) {
   const InT* kp = static_cast<const InT*>(p.k);
   const InT* vp = static_cast<const InT*>(p.v);
 
-  Frag UF[KS], KbF[KS], TF[2], TtF[2], PtF[2];
+  // A operands of row block w: first half Utilde (F1) and T (F2); second half Kbar (F1), T^T (F2)
+  // and P^T (F3)
+  Frag F1[KS], F2[2], F3[2];
   {
     float ut[KS][8], qt[KS][8];
     chunk_algebra<DK, InT, VEC>(p, sm, b, c, h, nvalid, ut, qt, false);
     const float* Tm = sm.r2 + OT;
     const float* Pm = sm.r2 + OP;
+    if (hf == 0) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      UF[ks] = Pol::make(ut[ks]);
-      float x[8];
+      for (int ks = 0; ks < KS; ++ks) F1[ks] = Pol::make(ut[ks]);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) x[j] = sm.r1[(16 * w + r) * LG + 32 * ks + 8 * g + j] * sm.gc[32 * ks + 8 * g + j];
-      KbF[ks] = Pol::make(x);
-    }
+      for (int st = 0; st < 2; ++st) F2[st] = frag_c<Pol>(&Tm[(16 * w + r) * L68 + 32 * st + 8 * g]);
+    } else {
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      TF[st] = frag_c<Pol>(&Tm[(16 * w + r) * L68 + 32 * st + 8 * g]);
-      TtF[st] = frag_s<Pol>(&Tm[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
-      PtF[st] = frag_s<Pol>(&Pm[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+      for (int ks = 0; ks < KS; ++ks) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = sm.r1[(16 * w + r) * LG + 32 * ks + 8 * g + j] * sm.gc[32 * ks + 8 * g + j];
+        F1[ks] = Pol::make(x);
+      }
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        F2[st] = frag_s<Pol>(&Tm[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+        F3[st] = frag_s<Pol>(&Pm[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+      }
     }
   }
   __syncthreads();
@@ -609,28 +633,31 @@ __global__ __launch_bounds__(256, 1) void cbwd_grad_kernel(const CbParams p) {
   const float* S0p = c == 0 ? (p.S0 ? p.S0 + ((int64_t)b * p.H + h) * SS : nullptr)
                             : p.snap + (((int64_t)b * (p.T / CH) + c - 1) * p.H + h) * SS;
   const float* dSp = p.dsc + (((int64_t)b * p.nc + c) * p.H + h) * SS;
-  f32x4 dQt[NCT], dUt[NCT], dKb[NCT], dPa[NBLK], dAa[NBLK];
+  // accumulators: first half dQtilde (A1) and dUtilde (A2) over the channel tiles; second half
+  // dKbar (A1), dP over the token blocks (A2[0..3]) and dA (A2[4..7])
+  f32x4 A1[NCT], A2[NA2];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) { dQt[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; dUt[ct] = dQt[ct]; dKb[ct] = dQt[ct]; }
+  for (int ct = 0; ct < NCT; ++ct) A1[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int J = 0; J < NBLK; ++J) { dPa[J] = f32x4{0.f, 0.f, 0.f, 0.f}; dAa[J] = dPa[J]; }
+  for (int ct = 0; ct < NA2; ++ct) A2[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
   float dpart = 0.f;
-  float vdm[4] = {0.f, 0.f, 0.f, 0.f};  // v . dm of rows 16 w + 4 g + i over this lane's columns
+  float vdm[4] = {0.f, 0.f, 0.f, 0.f};  // second half: v . dm of rows 16 w + 4 g + i, this lane's columns
   for (int dv0 = 0; dv0 < DV; dv0 += 32) {
-    for (int idx = tid; idx < DK * 8; idx += 256) {
+    for (int idx = tid; idx < DK * 8; idx += 512) {
       const int row = idx >> 3, q4 = idx & 7;
       const int64_t o = (int64_t)row * DV + dv0 + 4 * q4;
       store4(&S0b[row * L36 + 4 * q4], S0p ? *reinterpret_cast<const f32x4*>(S0p + o) : f32x4{0.f, 0.f, 0.f, 0.f});
       store4(&dSb[row * L36 + 4 * q4], *reinterpret_cast<const f32x4*>(dSp + o));
     }
-    for (int idx = tid; idx < CH * 8; idx += 256) {
+    for (int idx = tid; idx < CH * 8; idx += 512) {
       const int t = idx >> 3, q4 = idx & 7;
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
       if (t < nvalid) x = *reinterpret_cast<const f32x4*>(p.dO + cb_row(p, b, m0 + t, h) * DV + dv0 + 4 * q4);
       store4(&dOb[t * L36 + 4 * q4], x);
     }
-    // m = write . v at rows 16 w + 4 g + i, columns 16 ct + r of the block
-    float mv[2][4], vv[2][4], wv[2][4];
+    // rows 16 w + 4 g + i, columns 16 ct + r of the block: first half m = write . v, second half v
+    // (ev) and the write gate (wv)
+    float ev[2][4], wv[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * w + 4 * g + i;
@@ -643,9 +670,8 @@ __global__ __launch_bounds__(256, 1) void cbwd_grad_kernel(const CbParams p) {
         const int col = dv0 + 16 * ct + r;
         const float vx = ok ? ld_f32(vp + vo + col) : 0.f;
         const float wg = ok ? (VEC ? p.write[th * DV + col] : p.write[th]) : 0.f;
-        vv[ct][i] = vx;
+        ev[ct][i] = hf == 0 ? wg * vx : vx;
         wv[ct][i] = wg;
-        mv[ct][i] = wg * vx;
       }
     }
     __syncthreads();
@@ -654,69 +680,73 @@ __global__ __launch_bounds__(256, 1) void cbwd_grad_kernel(const CbParams p) {
 #pragma unroll
       for (int j = 0; j < CPP; ++j) dpart = fmaf(S0b[ch * L36 + c0 + j], dSb[ch * L36 + c0 + j], dpart);
     }
-    // X = Utilde S0 -> R = M - X (transposed into Rt); Y = Kbar dS + P^T dO (transposed into Yt)
     {
-      f32x4 accX[2], accY[2];
+      f32x4 acc[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) { accX[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; accY[ct] = accX[ct]; }
+      for (int ct = 0; ct < 2; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (hf == 0) {  // X = Utilde S0 -> R = M - X, transposed into Rt
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct)
+            Pol::mma(acc[ct], F1[ks], frag_s<Pol>(&S0b[(32 * ks + 8 * g) * L36 + 16 * ct + r], L36));
+        }
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          Pol::mma(accX[ct], UF[ks], frag_s<Pol>(&S0b[(32 * ks + 8 * g) * L36 + 16 * ct + r], L36));
-          Pol::mma(accY[ct], KbF[ks], frag_s<Pol>(&dSb[(32 * ks + 8 * g) * L36 + 16 * ct + r], L36));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Rt[(16 * ct + r) * L68 + 16 * w + 4 * g + i] = ev[ct][i] - acc[ct][i];
         }
-      }
+      } else {  // Y = Kbar dS + P^T dO, transposed into Yt
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+        for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-          Pol::mma(accY[ct], PtF[st], frag_s<Pol>(&dOb[(32 * st + 8 * g) * L36 + 16 * ct + r], L36));
-      }
+          for (int ct = 0; ct < 2; ++ct)
+            Pol::mma(acc[ct], F1[ks], frag_s<Pol>(&dSb[(32 * ks + 8 * g) * L36 + 16 * ct + r], L36));
+        }
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
+        for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          Rt[(16 * ct + r) * L68 + 16 * w + 4 * g + i] = mv[ct][i] - accX[ct][i];
-          Yt[(16 * ct + r) * L68 + 16 * w + 4 * g + i] = accY[ct][i];
+          for (int ct = 0; ct < 2; ++ct)
+            Pol::mma(acc[ct], F3[st], frag_s<Pol>(&dOb[(32 * st + 8 * g) * L36 + 16 * ct + r], L36));
+        }
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Yt[(16 * ct + r) * L68 + 16 * w + 4 * g + i] = acc[ct][i];
         }
       }
     }
     __syncthreads();
-    // delta = T R, eps = T^T Y; dm = eps goes to dv and to the write gate's gradient
-    {
-      f32x4 accD[2], accE[2];
+    {  // delta = T R (first half), eps = T^T Y (second half; dm = eps goes to dv and the write gate)
+      f32x4 acc[2];
 #pragma unroll
-      for (int ct = 0; ct < 2; ++ct) { accD[ct] = f32x4{0.f, 0.f, 0.f, 0.f}; accE[ct] = accD[ct]; }
+      for (int ct = 0; ct < 2; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const float* src = hf == 0 ? Rt : Yt;
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) {
-          Pol::mma(accD[ct], TF[st], frag_c<Pol>(&Rt[(16 * ct + r) * L68 + 32 * st + 8 * g]));
-          Pol::mma(accE[ct], TtF[st], frag_c<Pol>(&Yt[(16 * ct + r) * L68 + 32 * st + 8 * g]));
-        }
+        for (int ct = 0; ct < 2; ++ct) Pol::mma(acc[ct], F2[st], frag_c<Pol>(&src[(16 * ct + r) * L68 + 32 * st + 8 * g]));
       }
+      float* dst = hf == 0 ? Dl : El;
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * w + 4 * g + i;
-          Dl[t * L36 + 16 * ct + r] = accD[ct][i];
-          El[t * L36 + 16 * ct + r] = accE[ct][i];
-          if (t < nvalid) {
+          dst[t * L36 + 16 * ct + r] = acc[ct][i];
+          if (hf == 1 && t < nvalid) {
             const int64_t th = cb_row(p, b, m0 + t, h);
             const int col = dv0 + 16 * ct + r;
-            const float e = accE[ct][i];
+            const float e = acc[ct][i];
             p.dv[th * DV + col] = wv[ct][i] * e;
-            if constexpr (VEC) p.dwrite[th * DV + col] = vv[ct][i] * e;
-            else vdm[i] = fmaf(vv[ct][i], e, vdm[i]);
+            if constexpr (VEC) p.dwrite[th * DV + col] = ev[ct][i] * e;
+            else vdm[i] = fmaf(ev[ct][i], e, vdm[i]);
           }
         }
       }
     }
     __syncthreads();
-    // tile gradients: dQtilde += dO S0^T, dUtilde -= eps S0^T, dKbar += delta dS^T,
-    // dP += dO delta^T, dA -= eps delta^T (row block w)
+    // tile gradients of row block w
     {
       const Frag AO = frag_c<Pol>(&dOb[(16 * w + r) * L36 + 8 * g]);
       float xe[8];
@@ -724,28 +754,51 @@ __global__ __launch_bounds__(256, 1) void cbwd_grad_kernel(const CbParams p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) xe[j] = -xe[j];
       const Frag AE = Pol::make(xe);
-      const Frag AD = frag_c<Pol>(&Dl[(16 * w + r) * L36 + 8 * g]);
+      if (hf == 0) {  // dQtilde += dO S0^T, dUtilde -= eps S0^T
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const Frag BS = frag_c<Pol>(&S0b[(16 * ct + r) * L36 + 8 * g]);
-        Pol::mma(dQt[ct], AO, BS);
-        Pol::mma(dUt[ct], AE, BS);
-        Pol::mma(dKb[ct], AD, frag_c<Pol>(&dSb[(16 * ct + r) * L36 + 8 * g]));
-      }
+        for (int ct = 0; ct < NCT; ++ct) {
+          const Frag BS = frag_c<Pol>(&S0b[(16 * ct + r) * L36 + 8 * g]);
+          Pol::mma(A1[ct], AO, BS);
+          Pol::mma(A2[ct], AE, BS);
+        }
+      } else {  // dKbar += delta dS^T, dP += dO delta^T, dA -= eps delta^T
+        const Frag AD = frag_c<Pol>(&Dl[(16 * w + r) * L36 + 8 * g]);
 #pragma unroll
-      for (int J = 0; J < NBLK; ++J) {
-        if (J <= w) {
-          const Frag BD = frag_c<Pol>(&Dl[(16 * J + r) * L36 + 8 * g]);
-          Pol::mma(dPa[J], AO, BD);
-          Pol::mma(dAa[J], AE, BD);
+        for (int ct = 0; ct < NCT; ++ct) Pol::mma(A1[ct], AD, frag_c<Pol>(&dSb[(16 * ct + r) * L36 + 8 * g]));
+#pragma unroll
+        for (int J = 0; J < NBLK; ++J) {
+          if (J <= w) {
+            const Frag BD = frag_c<Pol>(&Dl[(16 * J + r) * L36 + 8 * g]);
+            Pol::mma(A2[J], AO, BD);
+            Pol::mma(A2[NBLK + J], AE, BD);
+          }
         }
       }
     }
     __syncthreads();
   }
   sm.ddp[tid] = dpart;
+  // values read back at the end (loaded before any of this phase's stores, so that their loads
+  // overlap the work in between): the decay at the positions whose gate gradient this lane writes,
+  // and the erase gate
+  float al[4][NCT / 2], esr[4], evr[VEC ? NCT : 1][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = 16 * w + 4 * g + i;
+    const int64_t th = cb_row(p, b, m0 + (t < nvalid ? t : 0), h);
+#pragma unroll
+    for (int cc = 0; cc < NCT / 2; ++cc) al[i][cc] = p.alpha[th * DK + 16 * (hf * (NCT / 2) + cc) + r];
+    if constexpr (VEC) {
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) evr[ct][i] = hf == 0 ? p.erase[th * DK + 16 * ct + r] : 0.f;
+      esr[i] = 0.f;
+    } else {
+      esr[i] = p.erase[th];
+    }
+  }
 
-  // ---- Qtilde and Utilde -> r2 (recomputed from Gamma), this thread's Gamma values
+  // ---- Qtilde and Utilde -> r2 (recomputed from Gamma; each half takes half the channels),
+  // Gamma at this lane's positions
   float* Ql = sm.r2;
   float* Ul = sm.r2 + CH * LG;
   {
@@ -756,8 +809,8 @@ __global__ __launch_bounds__(256, 1) void cbwd_grad_kernel(const CbParams p) {
     const int64_t qo = q_elem(p, b, m, h, DK), ko = kv_elem(p.k_ts, p.k_bs, p, b, m, h, DK);
     const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const int ch0 = 32 * ks + 8 * g;
+    for (int kh = 0; kh < KH; ++kh) {
+      const int ch0 = 32 * (hf * KH + kh) + 8 * g;
       float q8[8], k8[8], b8[8], g8[8];
       if (valid) {
         load8(qp + qo + ch0, q8);
@@ -784,105 +837,134 @@ __global__ __launch_bounds__(256, 1) void cbwd_grad_kernel(const CbParams p) {
     for (int i = 0; i < 4; ++i) gam[ct][i] = sm.r0[(16 * w + 4 * g + i) * LG + 16 * ct + r];
   }
   __syncthreads();
-  // dP (lower triangle) and dA (strict lower triangle) -> r0
   float* dPl = sm.r0;
   float* dAl = sm.r0 + CH * L68;
+  if (hf == 1) {
+    // dP (lower triangle) and dA (strict lower triangle) -> r0
 #pragma unroll
-  for (int J = 0; J < NBLK; ++J) {
+    for (int J = 0; J < NBLK; ++J) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * w + 4 * g + i, col = 16 * J + r;
-      dPl[row * L68 + col] = (J <= w && col <= row) ? dPa[J][i] : 0.f;
-      dAl[row * L68 + col] = (J <= w && col < row) ? dAa[J][i] : 0.f;
-    }
-  }
-  // Gamma_C . dKbar, and the column sums of Kbar . dKbar (= Kd . (Gamma_C . dKbar))
-#pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    const float gcc = sm.gc[16 * ct + r];
-    float e = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      dKb[ct][i] *= gcc;
-      e = fmaf(sm.r1[(16 * w + 4 * g + i) * LG + 16 * ct + r], dKb[ct][i], e);
-    }
-    e += __shfl_xor(e, 16);
-    e += __shfl_xor(e, 32);
-    if (g == 0) sm.ecs[w][16 * ct + r] = e;
-  }
-  __syncthreads();
-  // dq' = dQtilde + dP Kd, du' = dUtilde + dA Kd, dk' = Gamma_C . dKbar + dP^T Qtilde + dA^T Utilde
-#pragma unroll
-  for (int st = 0; st < 2; ++st) {
-    if (st == 0 || w >= 2) {
-      const Frag AP = frag_c<Pol>(&dPl[(16 * w + r) * L68 + 32 * st + 8 * g]);
-      const Frag AA = frag_c<Pol>(&dAl[(16 * w + r) * L68 + 32 * st + 8 * g]);
-#pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const Frag BK = frag_s<Pol>(&sm.r1[(32 * st + 8 * g) * LG + 16 * ct + r], LG);
-        Pol::mma(dQt[ct], AP, BK);
-        Pol::mma(dUt[ct], AA, BK);
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * w + 4 * g + i, col = 16 * J + r;
+        dPl[row * L68 + col] = (J <= w && col <= row) ? A2[J][i] : 0.f;
+        dAl[row * L68 + col] = (J <= w && col < row) ? A2[NBLK + J][i] : 0.f;
       }
     }
-    const Frag APt = frag_s<Pol>(&dPl[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
-    const Frag AAt = frag_s<Pol>(&dAl[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
-#pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      Pol::mma(dKb[ct], APt, frag_s<Pol>(&Ql[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
-      Pol::mma(dKb[ct], AAt, frag_s<Pol>(&Ul[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
-    }
-  }
-  __syncthreads();
-  // final values per (token 16 w + 4 g + i, channel 16 ct + r); x = q dq + u du - k dk -> r2
-  float* X = sm.r2;
-  float kdu[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = 16 * w + 4 * g + i;
-    const bool ok = t < nvalid;
-    const int64_t m = m0 + (ok ? t : 0);
-    const int64_t th = cb_row(p, b, m, h);
-    const int64_t qo = q_elem(p, b, m, h, DK), ko = kv_elem(p.k_ts, p.k_bs, p, b, m, h, DK);
-    const float esc = VEC ? 0.f : p.erase[th];
+    // Gamma_C . dKbar, and the column sums of Kbar . dKbar (= Kd . (Gamma_C . dKbar))
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       const int ch = 16 * ct + r;
-      const float gm = gam[ct][i];
-      const float dqv = gm * dQt[ct][i];
-      const float duv = gm * dUt[ct][i];
-      const float dkk = dKb[ct][i] / gm;
-      const float qv = ld_f32(qp + qo + ch), kv = ld_f32(kp + ko + ch);
-      const float ev = VEC ? p.erase[th * DK + ch] : esc;
-      const float uv = ev * kv;
-      X[t * LG + ch] = ok ? (qv * dqv + uv * duv - kv * dkk) : 0.f;
-      if (ok) {
-        p.dq[th * DK + ch] = dqv;
-        p.dk[th * DK + ch] = fmaf(ev, duv, dkk);
-        if constexpr (VEC) p.derase[th * DK + ch] = kv * duv;
+      const float gcc = sm.gc[ch];
+      float e = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        A1[ct][i] *= gcc;
+        e = fmaf(sm.r1[(16 * w + 4 * g + i) * LG + ch], A1[ct][i], e);
       }
-      kdu[i] = fmaf(kv, duv, kdu[i]);
+      e += __shfl_xor(e, 16);
+      e += __shfl_xor(e, 32);
+      if (g == 0) sm.ecs[w][ch] = e;
     }
   }
-  if constexpr (!VEC) {
-    // per token: k . du over the channels and v . dm over the value columns (lanes r of a row group)
+  __syncthreads();
+  if (hf == 0) {  // dq' = dQtilde + dP Kd, du' = dUtilde + dA Kd
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float a = kdu[i], v = vdm[i];
+    for (int st = 0; st < 2; ++st) {
+      if (st == 0 || w >= 2) {
+        const Frag AP = frag_c<Pol>(&dPl[(16 * w + r) * L68 + 32 * st + 8 * g]);
+        const Frag AA = frag_c<Pol>(&dAl[(16 * w + r) * L68 + 32 * st + 8 * g]);
 #pragma unroll
-      for (int d = 1; d < 16; d <<= 1) { a += __shfl_xor(a, d); v += __shfl_xor(v, d); }
-      const int t = 16 * w + 4 * g + i;
-      if (r == 0 && t < nvalid) {
-        const int64_t th = cb_row(p, b, m0 + t, h);
-        if (kda) {
-          p.derase[th] = a + v;
-        } else {
-          p.derase[th] = a;
-          p.dwrite[th] = v;
+        for (int ct = 0; ct < NCT; ++ct) {
+          const Frag BK = frag_s<Pol>(&sm.r1[(32 * st + 8 * g) * LG + 16 * ct + r], LG);
+          Pol::mma(A1[ct], AP, BK);
+          Pol::mma(A2[ct], AA, BK);
         }
+      }
+    }
+  } else {  // dk' = Gamma_C . dKbar + dP^T Qtilde + dA^T Utilde
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const Frag APt = frag_s<Pol>(&dPl[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+      const Frag AAt = frag_s<Pol>(&dAl[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        Pol::mma(A1[ct], APt, frag_s<Pol>(&Ql[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
+        Pol::mma(A1[ct], AAt, frag_s<Pol>(&Ul[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
       }
     }
   }
   __syncthreads();
+  // dk as the key (second half) -> r0 (dP and dA are no longer read); then the first half forms
+  // everything per (token 16 w + 4 g + i, channel 16 ct + r) from the LDS copies of Qtilde, Utilde
+  // and Kd (q dq = Qtilde dq', u du = Utilde du', k = Gamma Kd), with x = q dq + u du - k dk -> X
+  // in Qtilde's place
+  float* X = sm.r2;
+  float* Kk = sm.r0;
+  if (hf == 1) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Kk[(16 * w + 4 * g + i) * LG + 16 * ct + r] = A1[ct][i] / gam[ct][i];
+    }
+  }
+  __syncthreads();
+  if (hf == 0) {
+    float kdu[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * w + 4 * g + i;
+      const bool ok = t < nvalid;
+      const int64_t th = cb_row(p, b, m0 + (ok ? t : 0), h);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        const int ch = 16 * ct + r, o = t * LG + ch;
+        const float gm = gam[ct][i];
+        const float dqv = gm * A1[ct][i];
+        const float duv = gm * A2[ct][i];
+        const float dkk = Kk[o];
+        const float kv = sm.r1[o] * gm;
+        const float evv = VEC ? evr[ct][i] : esr[i];
+        X[o] = Ql[o] * A1[ct][i] + Ul[o] * A2[ct][i] - kv * dkk;
+        if (ok) {
+          p.dq[th * DK + ch] = dqv;
+          p.dk[th * DK + ch] = fmaf(evv, duv, dkk);
+          if constexpr (VEC) p.derase[th * DK + ch] = kv * duv;
+        }
+        kdu[i] = fmaf(kv, duv, kdu[i]);
+      }
+    }
+    if constexpr (!VEC) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float a = kdu[i];
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) a += __shfl_xor(a, d);
+        if (r == 0) sm.red[0][0][16 * w + 4 * g + i] = a;
+      }
+    }
+  } else if constexpr (!VEC) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v = vdm[i];
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) v += __shfl_xor(v, d);
+      if (r == 0) sm.red[0][1][16 * w + 4 * g + i] = v;
+    }
+  }
+  __syncthreads();
+  if constexpr (!VEC) {
+    // per token: k . du over the channels, v . dm over the value columns
+    if (tid < nvalid) {
+      const int64_t th = cb_row(p, b, m0 + tid, h);
+      const float a = sm.red[0][0][tid], v = sm.red[0][1][tid];
+      if (kda) {
+        p.derase[th] = a + v;
+      } else {
+        p.derase[th] = a;
+        p.dwrite[th] = v;
+      }
+    }
+  }
   // alpha_t dalpha_t = reverse cumulative sum of x + Gamma_C rowsum(S0 . dS) + sum_s Kbar . dKbar
   if (tid < DK) {
     float s = 0.f;
@@ -897,15 +979,16 @@ __global__ __launch_bounds__(256, 1) void cbwd_grad_kernel(const CbParams p) {
     }
   }
   __syncthreads();
+  // each half writes half of the channel tiles
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = 16 * w + 4 * g + i;
     if (t < nvalid) {
       const int64_t th = cb_row(p, b, m0 + t, h);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        const int ch = 16 * ct + r;
-        p.dalpha[th * DK + ch] = X[t * LG + ch] / p.alpha[th * DK + ch];
+      for (int cc = 0; cc < NCT / 2; ++cc) {
+        const int ch = 16 * (hf * (NCT / 2) + cc) + r;
+        p.dalpha[th * DK + ch] = X[t * LG + ch] / al[i][cc];
       }
     }
   }
@@ -918,7 +1001,7 @@ template <int DK, typename InT, bool VEC>
 static hipError_t launch_cb_t(const CbParams& p, hipStream_t s) {
   const int64_t slots = (int64_t)p.B * p.nc * p.H;
   hipLaunchKernelGGL(cbwd_flag_clear_kernel, dim3(1), dim3(64), 0, s, p.flag);
-  hipLaunchKernelGGL((cbwd_prep_kernel<DK, InT, VEC>), dim3((unsigned)slots), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((cbwd_prep_kernel<DK, InT, VEC>), dim3((unsigned)slots), dim3(512), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   int64_t wg = (int64_t)p.B * p.H * (p.DV / 32);
@@ -926,7 +1009,7 @@ static hipError_t launch_cb_t(const CbParams& p, hipStream_t s) {
   hipLaunchKernelGGL((cbwd_state_kernel<DK, InT>), dim3((unsigned)wg), dim3(256), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((cbwd_grad_kernel<DK, InT, VEC>), dim3((unsigned)slots), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((cbwd_grad_kernel<DK, InT, VEC>), dim3((unsigned)slots), dim3(512), 0, s, p);
   return hipGetLastError();
 }
 
