@@ -498,7 +498,9 @@ def main():
                  "achieved_GBps": pbytes / (pms * 1e-3) / 1e9}
         del psets
 
-    # backward (gradients of the same prefill, dO and dS_T random): checkpointing forward + reverse walk
+    # backward (gradients of the same prefill, dO and dS_T random): checkpointing forward, then the
+    # chunked MFMA path (these gates never hand the call to the walk); the exact walk alone is timed
+    # beside it (DR_BWD_WALK=1)
     bwd = None
     if not args.no_backward:
         gdO = torch.randn((B, T, H, D), device=dev)
@@ -545,10 +547,28 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         cms = e0.elapsed_time(e1) / bsteps
+        old_walk = os.environ.get("DR_BWD_WALK")
+        os.environ["DR_BWD_WALK"] = "1"
+        try:
+            bstep(0)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(bsteps):
+                bstep(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wms = e0.elapsed_time(e1) / bsteps
+        finally:
+            if old_walk is None:
+                del os.environ["DR_BWD_WALK"]
+            else:
+                os.environ["DR_BWD_WALK"] = old_walk
         bwd = {"workload": "gradients of the KDA prefill (dq, dk, dv, dalpha, dbeta, dS0) for random dO and dS_T",
+               "path": "checkpointing forward, then the chunked MFMA backward",
                "ms_per_step": bms, "tokens_per_s": tokens / (bms * 1e-3), "steps": bsteps,
                "vs_forward": bms / ms_step,
-               "ms_per_step_given_checkpoints": cms}
+               "ms_per_step_given_checkpoints": cms,
+               "walk_ms_per_step": wms}
         del gdO, gdS, grads, ckpts
 
     # two KDA transitions per token (PRODUCT2) on the same shape: 4 x 4096 tokens, 2 x 4096 steps

@@ -303,10 +303,18 @@ int dr_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void
  * The inputs are those of the forward call (plain inputs: the fused preparation and the
  * stored-state options are forward-only; q, k, v may be strided through a dr_dims_v2, the
  * gradients are always dense). The call reruns the forward to keep the state after
- * every 64 tokens, then walks each sequence backwards, recomputing states between those
- * checkpoints; its workspace (about 4 * d_k * 4 bytes per token-head and value block of 32
- * columns, plus the checkpoints) comes from the library's pool like the prefill's.
- * Deterministic: no atomics.
+ * every 64 tokens. Fixed-length calls with one transition per token, d_k 64 or 128 and d_v a
+ * multiple of 32 up to 128 then take the chunked form: per 64-token chunk an affine map of the
+ * state gradient, a reverse pass over the chunks, and the chunk's gradients from its tile
+ * products, all on MFMA. That form divides by the decays' running products and by the decays
+ * themselves, so a chunk with a gate of magnitude below 2^-10, a running product outside
+ * [2^-100, 2^100] or a value that is not finite hands the whole call, on the device and without a
+ * host synchronisation, to the exact per-token walk, which every other call takes directly: it
+ * walks each sequence backwards, recomputing states between the checkpoints. DR_BWD_WALK set (and
+ * not "0") in the environment sends every call to the walk. The workspace (about 4 * d_k * 4
+ * bytes per token-head and value block of 32 columns, plus the checkpoints; the chunked form's
+ * records and chunk-end gradients, 4 * d_k * (d_k + 2 d_v) bytes per chunk-head, share it) comes from the
+ * library's pool like the prefill's. Deterministic on both paths: no atomics on the results.
  */
 int dr_chunk_bwd(const void* q, const void* k, const void* v, const float* alpha,
                  const float* erase, const float* write, int variant,
