@@ -499,15 +499,16 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
     plw.workspace -= pl.slots * H * pl.rec_size;
     plw.rec_size = 0;
   }
-  // The chunked MFMA path (fixed length, one transition per token, d_k 64 or 128, d_v a multiple
-  // of 32 up to 128) runs first; the walk's kernels then run only if it flagged a chunk whose gates
+  // The chunked MFMA path (one transition per token, d_k 64 or 128, d_v a multiple of 32 up to
+  // 128) runs first; the walk's kernels then run only if it flagged a chunk whose gates
   // it does not take. Its records and chunk-end gradients share the walk's partial-sum buffers
   // (the walk writes them only when it runs, after the chunked passes are done with them); the
   // flag sits apart.
-  const bool chunked = lg == 0 && cu_seqlens == nullptr && (dkh == 64 || dkh == 128) && dvh % 32 == 0 &&
-                       dvh <= 128 && dims->seqlen > 0 && !walk_forced();
+  const bool chunked = lg == 0 && (dkh == 64 || dkh == 128) && dvh % 32 == 0 && dvh <= 128 &&
+                       dims->seqlen > 0 && !walk_forced();
   const int64_t ncpb = (dims->seqlen + 63) / 64;
-  const int64_t cslots = dims->batch * ncpb * H;
+  // chunk slots x heads: fixed length B x chunks per sequence, packed the plan's upper bound
+  const int64_t cslots = (cu_seqlens ? pl.slots : dims->batch * ncpb) * H;
   const int64_t crec = chunked ? dr::cbwd_record_bytes(dkh, dvh) : 0;
   const int64_t chunk_bytes = chunked ? round256(cslots * crec) + round256(cslots * dkh * dvh * 4) : 0;
   if (chunked && cslots > INT32_MAX)
@@ -581,6 +582,17 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
       cb.DV = dvh;
       cb.B = (int32_t)dims->batch;
       cb.nc = (int32_t)ncpb;
+      cb.nseq = (int32_t)dims->num_seqs;
+      cb.slots = (int32_t)(cslots / H);
+      if (cu_seqlens) {  // the plan pass's tables (written by the forward or by launch_plan_only above)
+        int32_t* tab = dr::prefill_chunk_tables(ws, plw, H);
+        cb.cu = b.cu;
+        cb.chunk_seq = tab;
+        cb.chunk_c0 = tab + plw.slots;
+        cb.seq_first = tab + 2 * plw.slots;
+        cb.snap_first = b.snap_first;
+        cb.seq_order = b.seq_order;
+      }
       cb.variant = variant;
       cb.lgnh = 0;
       cb.q_ts = p.q_ts; cb.q_bs = p.q_bs; cb.k_ts = p.k_ts; cb.k_bs = p.k_bs; cb.v_ts = p.v_ts; cb.v_bs = p.v_bs;

@@ -1,5 +1,5 @@
-// Chunked backward of the gated delta-rule prefill on gfx950: the gradients of a prefill for
-// fixed-length sequences with one transition per token, in three MFMA passes after the
+// Chunked backward of the gated delta-rule prefill on gfx950: the gradients of a prefill with one
+// transition per token (fixed-length or packed sequences), in three MFMA passes after the
 // checkpointing forward (the course page "GDN, KDA và Mamba-2 · cập nhật state trong hybrid",
 // section 3: training keeps checkpoints and the chunked form's intermediates).
 //
@@ -28,12 +28,13 @@
 // which divides by nothing. (KDA, RDA and GDN-2 decays exp(-c softplus(z)) close to 1 never
 // raise it; Complex KDA gates near zero do.)
 //
-// Passes (fixed length B x T, chunks of 64 tokens, nc per sequence):
-//   cbwd_prep_kernel   one workgroup per (batch row, chunk, head): M as MFMA operand fragments
+// Passes (chunks of 64 tokens from each sequence's start; packed sequences take their chunk slots
+// from the prefill's plan pass):
+//   cbwd_prep_kernel   one workgroup per (chunk, head): M as MFMA operand fragments
 //                      and N in fp32 into the chunk's record;
-//   cbwd_state_kernel  one workgroup per (batch row, head, 32 value columns): walks the chunks in
+//   cbwd_state_kernel  one workgroup per (sequence, head, 32 value columns): walks the chunks in
 //                      reverse with dS in registers, stores dS at every chunk end, dS <- M dS + N;
-//   cbwd_grad_kernel   one workgroup per (batch row, chunk, head): recomputes the chunk algebra,
+//   cbwd_grad_kernel   one workgroup per (chunk, head): recomputes the chunk algebra,
 //                      loops over 32-column value blocks for delta, eps and the tile gradients,
 //                      then forms dq, dk, dv, dalpha and the gate gradients.
 #include "prefill.hpp"
@@ -102,19 +103,19 @@ __device__ __forceinline__ int64_t cb_row(const CbParams& p, int b, int64_t m, i
   return ((int64_t)b * p.T + m) * p.H + h;
 }
 
-// The chunk algebra shared by the preparation and the gradient kernel: Gamma in r0, Kd in r1,
+// The chunk algebra shared by the preparation and the gradient kernel (the chunk's rows are tokens
+// m0 .. m0 + 63 of batch row b): Gamma in r0, Kd in r1,
 // A, P and T in r2, Gamma_C in gc; ut / qt receive this thread's row of Utilde / Qtilde (token
 // 16 w + lane % 16, channels 32 ks + 8 (lane / 16) + j). With set_flag, a chunk outside the
 // chunked form's range sets *p.flag.
 template <int DK, typename InT, bool VEC>
-__device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm, int b, int c, int h, int nvalid,
+__device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm, int b, int64_t m0, int h, int nvalid,
                                               float (&ut)[DK / 32][8], float (&qt)[DK / 32][8], bool set_flag) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
   constexpr int KS = DK / 32, LG = CbSmem<DK>::LG;
   // (with 512 threads, waves w and w + 4 share row block w; the second half only builds its ut / qt)
   const int tid = threadIdx.x, w = (tid >> 6) & 3, hf = tid >> 8, l = tid & 63, r = l & 15, g = l >> 4;
-  const int64_t m0 = (int64_t)c * CH;
 
   // Gamma: running products down the chunk per channel (tokens past the sequence end take decay
   // 1), in segments of SEG tokens: every thread loads its segment, multiplies it out, and the
@@ -298,12 +299,41 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
   }
 }
 
-__device__ __forceinline__ void cb_slot(const CbParams& p, int slot, int& b, int& c, int& h, int& nvalid) {
-  h = slot % p.H;
-  c = (slot / p.H) % p.nc;
-  b = slot / (p.H * p.nc);
-  const int64_t left = p.T - (int64_t)c * CH;
-  nvalid = left < CH ? (int)left : CH;
+// The chunk a workgroup of the per-chunk kernels takes (blockIdx.x = chunk slot * H + head): its
+// sequence n and chunk index c within it, the batch row b and first token m0 through which its
+// rows are addressed, and its valid tokens. False for an unused slot of packed sequences.
+struct CbChunk {
+  int n, c, h, b, nvalid;
+  int64_t m0;
+};
+__device__ __forceinline__ bool cb_chunk(const CbParams& p, CbChunk& k) {
+  const int slot = blockIdx.x / p.H;
+  k.h = blockIdx.x % p.H;
+  if (p.cu) {
+    k.n = p.chunk_seq[slot];
+    if (k.n < 0) return false;
+    const int64_t bos = p.cu[k.n], len = p.cu[k.n + 1] - bos, c0 = p.chunk_c0[slot];
+    k.c = (int)(c0 / CH);
+    k.b = 0;
+    k.m0 = bos + c0;
+    k.nvalid = len - c0 < CH ? (int)(len - c0) : CH;
+  } else {
+    k.n = slot / p.nc;
+    k.c = slot % p.nc;
+    k.b = k.n;
+    k.m0 = (int64_t)k.c * CH;
+    const int64_t left = p.T - k.m0;
+    k.nvalid = left < CH ? (int)left : CH;
+  }
+  return true;
+}
+
+// State at the start of chunk k (null: zero): the initial state, or the forward's snapshot after
+// the previous chunk.
+__device__ __forceinline__ const float* cb_start_state(const CbParams& p, const CbChunk& k, int64_t SS) {
+  if (k.c == 0) return p.S0 ? p.S0 + ((int64_t)k.n * p.H + k.h) * SS : nullptr;
+  const int64_t row = (p.cu ? (int64_t)p.snap_first[k.n] : (int64_t)k.n * (p.T / CH)) + k.c - 1;
+  return p.snap + (row * p.H + k.h) * SS;
 }
 
 }  // namespace
@@ -324,12 +354,14 @@ __global__ __launch_bounds__(512, 1) void cbwd_prep_kernel(const CbParams p) {
   constexpr int RT = DK / 16, WPR = 8 / RT;  // output-channel tiles; waves per tile
   using R = CRec<DK>;
   __shared__ __align__(16) CbSmem<DK> sm;
-  int b, c, h, nvalid;
-  cb_slot(p, blockIdx.x, b, c, h, nvalid);
+  CbChunk ck;
+  if (!cb_chunk(p, ck)) return;
+  const int b = ck.b, h = ck.h, nvalid = ck.nvalid;
+  const int64_t m0 = ck.m0;
   const int tid = threadIdx.x, w8 = tid >> 6, w = w8 & 3, hf = w8 >> 2, l = tid & 63, r = l & 15, g = l >> 4;
   const int rt = w8 % RT, part = w8 / RT;
   float ut[KS][8], qt[KS][8];
-  chunk_algebra<DK, InT, VEC>(p, sm, b, c, h, nvalid, ut, qt, true);
+  chunk_algebra<DK, InT, VEC>(p, sm, b, m0, h, nvalid, ut, qt, true);
   const float* Tm = sm.r2 + OT;
   const float* Pm = sm.r2 + OP;
   float* Wm = sm.r2;  // W over A and At (no longer read)
@@ -430,7 +462,7 @@ __global__ __launch_bounds__(512, 1) void cbwd_prep_kernel(const CbParams p) {
   for (int idx = tid; idx < CH * (DV / 4); idx += 512) {
     const int t = idx / (DV / 4), v4 = idx % (DV / 4);
     f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < nvalid) x = *reinterpret_cast<const f32x4*>(p.dO + cb_row(p, b, (int64_t)c * CH + t, h) * DV + 4 * v4);
+    if (t < nvalid) x = *reinterpret_cast<const f32x4*>(p.dO + cb_row(p, b, m0 + t, h) * DV + 4 * v4);
     store4(&sm.r1[t * LV + 4 * v4], x);
   }
   __syncthreads();
@@ -487,11 +519,15 @@ __global__ __launch_bounds__(256, 1) void cbwd_state_kernel(const CbParams p) {
   using R = CRec<DK>;
   __shared__ __align__(16) float Gf[DVB][DK + 4];  // dS, transposed: [value column][channel]
   const int ndvb = p.DV / DVB;
-  const int logical = p.B * p.H * ndvb;
+  const int logical = p.nseq * p.H * ndvb;
   const int lid = (gridDim.x % 8 == 0) ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
   if (lid >= logical) return;
+  // (sequence, head) pairs, packed sequences longest first; a pair's value blocks are adjacent
   const int pair = lid / ndvb, dv0 = (lid % ndvb) * DVB;
-  const int b = pair / p.H, h = pair % p.H;
+  const int b = p.cu ? p.seq_order[pair / p.H] : pair / p.H, h = pair % p.H;
+  // the sequence's chunk slots: first .. first + nch - 1
+  const int first = p.cu ? p.seq_first[b] : b * p.nc;
+  const int nch = p.cu ? (int)((p.cu[b + 1] - p.cu[b] + CH - 1) / CH) : p.nc;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
   const int DV = p.DV;
   const int64_t SS = (int64_t)DK * DV;
@@ -508,8 +544,8 @@ __global__ __launch_bounds__(256, 1) void cbwd_state_kernel(const CbParams p) {
       }
     }
   }
-  for (int c = p.nc - 1; c >= 0; --c) {
-    const int64_t slot = ((int64_t)b * p.nc + c) * p.H + h;
+  for (int c = nch - 1; c >= 0; --c) {
+    const int64_t slot = ((int64_t)first + c) * p.H + h;
     float* dsc = p.dsc + slot * SS;
     const unsigned char* rec = p.rec + slot * p.rec_size;
     const __amdgpu_buffer_rsrc_t rs = rec_rsrc(rec, p.rec_size);
@@ -581,10 +617,11 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
   constexpr int PARTS = 512 / DK, CPP = 32 / PARTS;  // rowsum partials: threads per channel, columns each
   __shared__ __align__(16) CbSmem<DK> sm;
   if (*p.flag) return;  // the exact walk takes the call
-  int b, c, h, nvalid;
-  cb_slot(p, blockIdx.x, b, c, h, nvalid);
+  CbChunk ck;
+  if (!cb_chunk(p, ck)) return;
+  const int b = ck.b, h = ck.h, nvalid = ck.nvalid;
+  const int64_t m0 = ck.m0;
   const int tid = threadIdx.x, w = (tid >> 6) & 3, hf = tid >> 8, l = tid & 63, r = l & 15, g = l >> 4;
-  const int64_t m0 = (int64_t)c * CH;
   const int DV = p.DV;
   const int64_t SS = (int64_t)DK * DV;
   const bool kda = p.variant == 0 || p.variant == 3;
@@ -597,7 +634,7 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
   Frag F1[KS], F2[2], F3[2];
   {
     float ut[KS][8], qt[KS][8];
-    chunk_algebra<DK, InT, VEC>(p, sm, b, c, h, nvalid, ut, qt, false);
+    chunk_algebra<DK, InT, VEC>(p, sm, b, m0, h, nvalid, ut, qt, false);
     const float* Tm = sm.r2 + OT;
     const float* Pm = sm.r2 + OP;
     if (hf == 0) {
@@ -630,9 +667,8 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
   float* El = Dl + CH * L36;
   float* Rt = El + CH * L36;
   float* Yt = Rt + 32 * L68;
-  const float* S0p = c == 0 ? (p.S0 ? p.S0 + ((int64_t)b * p.H + h) * SS : nullptr)
-                            : p.snap + (((int64_t)b * (p.T / CH) + c - 1) * p.H + h) * SS;
-  const float* dSp = p.dsc + (((int64_t)b * p.nc + c) * p.H + h) * SS;
+  const float* S0p = cb_start_state(p, ck, SS);
+  const float* dSp = p.dsc + (int64_t)blockIdx.x * SS;
   // accumulators: first half dQtilde (A1) and dUtilde (A2) over the channel tiles; second half
   // dKbar (A1), dP over the token blocks (A2[0..3]) and dA (A2[4..7])
   f32x4 A1[NCT], A2[NA2];
@@ -999,12 +1035,12 @@ int64_t cbwd_record_bytes(int dk, int dv) { return dk == 64 ? CRec<64>::size(dv)
 
 template <int DK, typename InT, bool VEC>
 static hipError_t launch_cb_t(const CbParams& p, hipStream_t s) {
-  const int64_t slots = (int64_t)p.B * p.nc * p.H;
+  const int64_t slots = (int64_t)p.slots * p.H;
   hipLaunchKernelGGL(cbwd_flag_clear_kernel, dim3(1), dim3(64), 0, s, p.flag);
   hipLaunchKernelGGL((cbwd_prep_kernel<DK, InT, VEC>), dim3((unsigned)slots), dim3(512), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  int64_t wg = (int64_t)p.B * p.H * (p.DV / 32);
+  int64_t wg = (int64_t)p.nseq * p.H * (p.DV / 32);
   wg = (wg + 7) / 8 * 8;
   hipLaunchKernelGGL((cbwd_state_kernel<DK, InT>), dim3((unsigned)wg), dim3(256), 0, s, p);
   e = hipGetLastError();
@@ -1020,7 +1056,7 @@ static hipError_t launch_cb_dk(const CbParams& p, bool bf16, bool vec, hipStream
 }
 
 hipError_t launch_chunked_backward(const CbParams& p, int dk, bool bf16, bool vec, hipStream_t s) {
-  if (p.B == 0 || p.T == 0 || p.H == 0) return hipSuccess;
+  if (p.nseq == 0 || p.H == 0) return hipSuccess;
   if (dk == 64) return launch_cb_dk<64>(p, bf16, vec, s);
   if (dk == 128) return launch_cb_dk<128>(p, bf16, vec, s);
   return hipErrorInvalidValue;

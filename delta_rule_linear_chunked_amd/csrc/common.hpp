@@ -139,7 +139,7 @@ struct BwdParams {
                             // backward hands its call over to this exact walk that way)
 };
 
-// Parameter block of the chunked backward (fixed-length sequences, one transition per token).
+// Parameter block of the chunked backward (one transition per token).
 struct CbParams {
   const void* q;
   const void* k;
@@ -150,7 +150,17 @@ struct CbParams {
   const float* S0;      // initial states (may be null)
   const float* dO;
   const float* dST;     // may be null
-  const float* snap;    // forward states after every 64 tokens: [B * (T / 64), H, d_k, d_v]
+  const float* snap;    // forward states after every 64 tokens of each sequence (rows as in the prefill's
+                        // snapshots: fixed length b * (T / 64) + c, packed snap_first[n] + c)
+  // packed sequences (cu non-null, B == 1): the prefill plan pass's clamped offsets and tables
+  const int32_t* cu;
+  const int32_t* chunk_seq;
+  const int32_t* chunk_c0;
+  const int32_t* seq_first;
+  const int32_t* snap_first;
+  const int32_t* seq_order;
+  int32_t nseq;         // sequences (fixed length: B)
+  int32_t slots;        // chunk slots (fixed length: B * nc)
   float* dq;
   float* dk;
   float* dv;
@@ -158,15 +168,15 @@ struct CbParams {
   float* derase;
   float* dwrite;
   float* dS0;           // may be null
-  unsigned char* rec;   // per (batch row, chunk, head): the chunk's map of the state gradient
+  unsigned char* rec;   // per (chunk slot, head): the chunk's map of the state gradient
   int64_t rec_size;
-  float* dsc;           // [B, chunks, H, d_k, d_v]: gradient reaching the state at each chunk's end
+  float* dsc;           // [slots, H, d_k, d_v]: gradient reaching the state at each chunk's end
   int32_t* flag;        // set when some chunk's gates are outside the chunked form's range
   int64_t T;
   int32_t H;
   int32_t DV;
   int32_t B;
-  int32_t nc;           // chunks per sequence
+  int32_t nc;           // fixed length: chunks per sequence (chunk slot b * nc + c)
   int32_t variant;      // 0 KDA, 1 RDA, 2 GDN-2, 3 CKDA
   int32_t lgnh;         // 0 (one transition per token); read by q_elem / kv_elem
   int64_t q_ts, q_bs, k_ts, k_bs, v_ts, v_bs;

@@ -50,6 +50,9 @@ hipError_t launch_prefill(Params p, const PrefillPlan& plan, void* ws, int dk, b
 // Packed sequences: where the prefill's workspace keeps the first snapshot row of each sequence
 // (filled by the prefill when snapshots are taken), followed by the sequences' longest-first order.
 int32_t* prefill_snap_first(void* ws, const PrefillPlan& plan, int64_t heads, int64_t nseq);
+// Packed sequences: the plan pass's chunk tables: the sequence of each chunk slot (-1: unused) [slots],
+// the slot's first token within its sequence [slots], each sequence's first slot [nseq + 1].
+int32_t* prefill_chunk_tables(void* ws, const PrefillPlan& plan, int64_t heads);
 // Packed sequences: the plan pass's clamped, non-decreasing copy of the offsets [nseq + 1], from which
 // every later pass (the backward's included) takes its sequence spans.
 int32_t* prefill_cu_table(void* ws, const PrefillPlan& plan, int64_t heads, int64_t nseq);
@@ -70,7 +73,7 @@ hipError_t scratch_buffer(void** ptr);
 int bwd_dv_block(int dv);
 hipError_t launch_backward(BwdParams p, int64_t pairs, int dk, int dv, bool bf16, bool vec, hipStream_t s);
 
-// Chunked backward (backward_chunked.hip): fixed-length sequences, one transition per token,
+// Chunked backward (backward_chunked.hip): fixed-length or packed sequences, one transition per token,
 // d_k in {64, 128}, d_v a multiple of 32 up to 128. Bytes of one chunk record, then the launches:
 // the flag is cleared, every (batch row, chunk, head) builds its record, the state-gradient pass
 // runs over the chunks in reverse and the gradient kernel writes every output except dS0 (which

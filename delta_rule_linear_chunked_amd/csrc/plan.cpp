@@ -62,6 +62,10 @@ PrefillPlan plan_prefill(int64_t num_pairs, int64_t num_seqs, int64_t batch, int
 }
 
 
+int32_t* prefill_chunk_tables(void* ws, const PrefillPlan& pl, int64_t heads) {
+  return reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + pl.slots * heads * pl.rec_size);
+}
+
 int32_t* prefill_snap_first(void* ws, const PrefillPlan& pl, int64_t heads, int64_t nseq) {
   return reinterpret_cast<int32_t*>(static_cast<unsigned char*>(ws) + pl.slots * heads * pl.rec_size) + 2 * pl.slots +
          nseq + 1;

@@ -108,3 +108,38 @@ def test_chunked_equals_walk_at_full_size():
     print("[chunked backward kda_prefill vs walk] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
     for n, e in errs.items():
         assert e <= TOL["bf16"], (n, e)
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["kda", "rda", "gdn2"])
+@pytest.mark.parametrize("dk,dv", [(128, 64), (64, 128)])
+def test_packed_sequences_chunked(variant, dk, dv, in_dtype):
+    # packed sequences (empty, length 1, exact and partial chunks) take the chunked path through
+    # the prefill plan pass's chunk slots
+    lens = [70, 0, 1, 64, 129, 8, 0, 200]
+    wl = synth.make_prefill(variant, 1, 0, 2, dk, dv, in_dtype=in_dtype, seed=seed_of("cbwd packed", variant, dk, dv),
+                            lengths=lens)
+    dO, dS_T = _inputs(wl, seed_of("cbwd packed do", variant, dk, dv))
+    a = prefill_inputs(wl)
+    g = _grads(a, to_dev(dO), to_dev(dS_T))
+    gw = _grads(a, to_dev(dO), to_dev(dS_T), walk=True)
+    ref = backward.step_recurrence_grads(wl.q, wl.k, wl.v, wl.alpha, wl.erase, wl.write, wl.variant, dO,
+                                         dS_T=dS_T, S0=wl.S0, cu_seqlens=wl.cu_seqlens)
+    _check(f"packed {variant} dk={dk} dv={dv} {in_dtype}", g, ref, TOL[in_dtype])
+    assert any(not np.array_equal(g[n], gw[n]) for n in NAMES if g[n] is not None)
+    # an empty sequence passes dS_T through to dS0
+    assert np.array_equal(g["dS0"][1], dS_T[1].astype(np.float64))
+
+
+def test_packed_varlen_workload_against_walk():
+    # the RDA varlen workload (12 sequences, 32768 tokens, H=16, d=128, bf16), whole tensors
+    wl = synth.preset("rda_varlen")
+    dO, dS_T = _inputs(wl, 1004)
+    a = prefill_inputs(wl)
+    g = _grads(a, to_dev(dO), to_dev(dS_T))
+    gw = _grads(a, to_dev(dO), to_dev(dS_T), walk=True)
+    errs = {n: rel_err(g[n], gw[n]) for n in NAMES if g[n] is not None}
+    print("[chunked backward rda_varlen vs walk] " + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= TOL["bf16"], (n, e)
+    assert any(not np.array_equal(g[n], gw[n]) for n in NAMES if g[n] is not None)
