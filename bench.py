@@ -655,6 +655,40 @@ def main():
                             "tokens": Bw * Tw, "alg_bytes_per_launch": ob,
                             "achieved_GBps": ob / (oms * 1e-3) / 1e9,
                             "hbm_frac": ob / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+            if not args.no_backward and name != "ckda_long":
+                # the backward of the packed workloads: chunked path, and the exact walk beside it
+                gdO = torch.randn((Bw, Tw, H, D), device=dev)
+                gdS = torch.randn((N, H, D, D), device=dev)
+                gshape = (Bw, Tw, H, D) if variant == "gdn2" else (Bw, Tw, H)
+                gg = [torch.empty((Bw, Tw, H, D), device=dev) for _ in range(4)]
+                ge, gw = torch.empty(gshape, device=dev), torch.empty(gshape, device=dev)
+                gS0 = torch.empty((N, H, D, D), device=dev)
+
+                def gstep():
+                    drl.dr_chunk_bwd(a["q"], a["k"], a["v"], a["alpha"], a["erase"], a["write"], variant, a["S0"],
+                                     a["cu"], gdO, gdS, gg[0], gg[1], gg[2], gg[3], ge, gw, gS0)
+
+                def gtime():
+                    gstep()
+                    torch.cuda.synchronize()
+                    e0.record(stream)
+                    for i in range(5):
+                        gstep()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    return e0.elapsed_time(e1) / 5
+
+                others[name]["backward_ms_per_step"] = gtime()
+                old_walk = os.environ.get("DR_BWD_WALK")
+                os.environ["DR_BWD_WALK"] = "1"
+                try:
+                    others[name]["backward_walk_ms_per_step"] = gtime()
+                finally:
+                    if old_walk is None:
+                        del os.environ["DR_BWD_WALK"]
+                    else:
+                        os.environ["DR_BWD_WALK"] = old_walk
+                del gdO, gdS, gg, ge, gw, gS0
             del a, ow, Sw
 
     traffic, kernel_traffic = None, None
