@@ -741,9 +741,11 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
         }
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
+          if (st == 1 || w < 2) {  // P^T's rows of block w are zero before token 16 w
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct)
-            Pol::mma(acc[ct], F3[st], frag_s<Pol>(&dOb[(32 * st + 8 * g) * L36 + 16 * ct + r], L36));
+            for (int ct = 0; ct < 2; ++ct)
+              Pol::mma(acc[ct], F3[st], frag_s<Pol>(&dOb[(32 * st + 8 * g) * L36 + 16 * ct + r], L36));
+          }
         }
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
@@ -758,10 +760,14 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) acc[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
       const float* src = hf == 0 ? Rt : Yt;
+      // T's rows of block w are zero past token 16 w + 15, T^T's before token 16 w: skip the
+      // 32-token step that is all zero
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
+        if (hf == 0 ? (st == 0 || w >= 2) : (st == 1 || w < 2)) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct) Pol::mma(acc[ct], F2[st], frag_c<Pol>(&src[(16 * ct + r) * L68 + 32 * st + 8 * g]));
+          for (int ct = 0; ct < 2; ++ct) Pol::mma(acc[ct], F2[st], frag_c<Pol>(&src[(16 * ct + r) * L68 + 32 * st + 8 * g]));
+        }
       }
       float* dst = hf == 0 ? Dl : El;
 #pragma unroll
@@ -920,12 +926,14 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
   } else {  // dk' = Gamma_C . dKbar + dP^T Qtilde + dA^T Utilde
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const Frag APt = frag_s<Pol>(&dPl[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
-      const Frag AAt = frag_s<Pol>(&dAl[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+      if (st == 1 || w < 2) {  // dP^T's and dA^T's rows of block w are zero before token 16 w
+        const Frag APt = frag_s<Pol>(&dPl[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
+        const Frag AAt = frag_s<Pol>(&dAl[(32 * st + 8 * g) * L68 + 16 * w + r], L68);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct) {
-        Pol::mma(A1[ct], APt, frag_s<Pol>(&Ql[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
-        Pol::mma(A1[ct], AAt, frag_s<Pol>(&Ul[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
+        for (int ct = 0; ct < NCT; ++ct) {
+          Pol::mma(A1[ct], APt, frag_s<Pol>(&Ql[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
+          Pol::mma(A1[ct], AAt, frag_s<Pol>(&Ul[(32 * st + 8 * g) * LG + 16 * ct + r], LG));
+        }
       }
     }
   }
