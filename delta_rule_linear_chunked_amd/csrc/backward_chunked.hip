@@ -509,15 +509,45 @@ __global__ __launch_bounds__(512, 1) void cbwd_prep_kernel(const CbParams p) {
 }
 
 // ============================================================================ pass 2
-// dS walks the chunks in reverse, one workgroup per (batch row, head, 32 value columns); wave w
-// holds output-channel tiles w + 4 m.
+// dS, transposed ([value column][channel]), as split MFMA B operands: hi / lo bf16 planes (bf16
+// inputs) or fp32, written four channels at a time from the accumulators
+template <class Pol, int DK> struct GTile;
+template <int DK> struct GTile<PolBF3, DK> {
+  __bf16 hi[32][DK + 8], lo[32][DK + 8];
+  __device__ __forceinline__ void put4(int v, int ch, const f32x4& x) {
+    uint32_t hh[2], ll[2];
+    split2(x[0], x[1], hh[0], ll[0]);
+    split2(x[2], x[3], hh[1], ll[1]);
+    *reinterpret_cast<bf16x4*>(&hi[v][ch]) = __builtin_bit_cast(bf16x4, hh);
+    *reinterpret_cast<bf16x4*>(&lo[v][ch]) = __builtin_bit_cast(bf16x4, ll);
+  }
+  __device__ __forceinline__ PolBF3::Frag get8(int v, int ch) const {
+    PolBF3::Frag f;
+    f.hi = *reinterpret_cast<const bf16x8*>(&hi[v][ch]);
+    f.lo = *reinterpret_cast<const bf16x8*>(&lo[v][ch]);
+    return f;
+  }
+};
+template <int DK> struct GTile<PolF32, DK> {
+  float x[32][DK + 4];
+  __device__ __forceinline__ void put4(int v, int ch, const f32x4& a) { store4(&x[v][ch], a); }
+  __device__ __forceinline__ PolF32::Frag get8(int v, int ch) const {
+    PolF32::Frag f;
+    load8(&x[v][ch], f.v);
+    return f;
+  }
+};
+
+// dS walks the chunks in reverse, one workgroup per (sequence, head, 32 value columns); wave w
+// holds output-channel tiles w + 4 m. The next chunk's M_c fragments and N_c values are loaded a
+// chunk ahead, and dS alternates between two LDS tiles, so each chunk takes one barrier.
 template <int DK, typename InT>
 __global__ __launch_bounds__(256, 1) void cbwd_state_kernel(const CbParams p) {
   using Pol = typename PolicyFor<InT>::type;
   using Frag = typename Pol::Frag;
   constexpr int KS = DK / 32, NRT = DK / 64, NCT = 2, DVB = 32;
   using R = CRec<DK>;
-  __shared__ __align__(16) float Gf[DVB][DK + 4];  // dS, transposed: [value column][channel]
+  __shared__ __align__(16) GTile<Pol, DK> Gt[2];
   const int ndvb = p.DV / DVB;
   const int logical = p.nseq * p.H * ndvb;
   const int lid = (gridDim.x % 8 == 0) ? xcd_remap(blockIdx.x, gridDim.x) : blockIdx.x;
@@ -529,6 +559,7 @@ __global__ __launch_bounds__(256, 1) void cbwd_state_kernel(const CbParams p) {
   const int first = p.cu ? p.seq_first[b] : b * p.nc;
   const int nch = p.cu ? (int)((p.cu[b + 1] - p.cu[b] + CH - 1) / CH) : p.nc;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int DV = p.DV;
   const int64_t SS = (int64_t)DK * DV;
 
@@ -544,41 +575,53 @@ __global__ __launch_bounds__(256, 1) void cbwd_state_kernel(const CbParams p) {
       }
     }
   }
-  for (int c = nch - 1; c >= 0; --c) {
+  Frag MF[NRT][KS];
+  f32x4 NV[NRT][NCT];
+  auto load_chunk = [&](int c) {
     const int64_t slot = ((int64_t)first + c) * p.H + h;
-    float* dsc = p.dsc + slot * SS;
     const unsigned char* rec = p.rec + slot * p.rec_size;
     const __amdgpu_buffer_rsrc_t rs = rec_rsrc(rec, p.rec_size);
     const float* Nrec = reinterpret_cast<const float*>(rec + R::NN);
-    f32x4 acc[NRT][NCT];
 #pragma unroll
     for (int m = 0; m < NRT; ++m) {
+#pragma unroll
+      for (int kb = 0; kb < KS; ++kb) MF[m][kb] = ld_frag<Frag>(rs, (int)R::MF, (wu + 4 * m) * KS + kb, l);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int ch = 16 * (w + 4 * m) + 4 * g + i;
-          const int64_t o = (int64_t)ch * DV + dv0 + 16 * ct + r;
-          dsc[o] = G[m][ct][i];
-          Gf[16 * ct + r][ch] = G[m][ct][i];
-          acc[m][ct][i] = Nrec[o];
-        }
+        for (int i = 0; i < 4; ++i)
+          NV[m][ct][i] = Nrec[(int64_t)(16 * (w + 4 * m) + 4 * g + i) * DV + dv0 + 16 * ct + r];
       }
     }
-    Frag MF[NRT][KS];
+  };
+  if (nch > 0) load_chunk(nch - 1);
+  for (int c = nch - 1; c >= 0; --c) {
+    GTile<Pol, DK>& T = Gt[c & 1];
+    float* dsc = p.dsc + (((int64_t)first + c) * p.H + h) * SS;
+    f32x4 acc[NRT][NCT];
+    Frag A[NRT][KS];
 #pragma unroll
     for (int m = 0; m < NRT; ++m) {
 #pragma unroll
-      for (int kb = 0; kb < KS; ++kb) MF[m][kb] = ld_frag<Frag>(rs, (int)R::MF, (w + 4 * m) * KS + kb, l);
+      for (int kb = 0; kb < KS; ++kb) A[m][kb] = MF[m][kb];
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        acc[m][ct] = NV[m][ct];
+        const int ch0 = 16 * (w + 4 * m) + 4 * g;
+        T.put4(16 * ct + r, ch0, G[m][ct]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dsc[(int64_t)(ch0 + i) * DV + dv0 + 16 * ct + r] = G[m][ct][i];
+      }
     }
+    if (c > 0) load_chunk(c - 1);
     __syncthreads();
 #pragma unroll
     for (int kb = 0; kb < KS; ++kb) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
-        const Frag BF = frag_c<Pol>(&Gf[16 * ct + r][32 * kb + 8 * g]);
+        const Frag BF = T.get8(16 * ct + r, 32 * kb + 8 * g);
 #pragma unroll
-        for (int m = 0; m < NRT; ++m) Pol::mma(acc[m][ct], MF[m][kb], BF);
+        for (int m = 0; m < NRT; ++m) Pol::mma(acc[m][ct], A[m][kb], BF);
       }
     }
 #pragma unroll
@@ -586,7 +629,6 @@ __global__ __launch_bounds__(256, 1) void cbwd_state_kernel(const CbParams p) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) G[m][ct] = acc[m][ct];
     }
-    __syncthreads();
   }
   if (p.dS0) {
 #pragma unroll
