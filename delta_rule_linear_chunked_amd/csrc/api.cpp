@@ -499,14 +499,14 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
     plw.workspace -= pl.slots * H * pl.rec_size;
     plw.rec_size = 0;
   }
-  // The chunked MFMA path (one transition per token, d_k 64 or 128, d_v a multiple of 32 up to
-  // 128) runs first; the walk's kernels then run only if it flagged a chunk whose gates
+  // The chunked MFMA path (one or two transitions per token, d_k 64 or 128, d_v a multiple of 32
+  // up to 128) runs first; the walk's kernels then run only if it flagged a chunk whose gates
   // it does not take. Its records and chunk-end gradients share the walk's partial-sum buffers
   // (the walk writes them only when it runs, after the chunked passes are done with them); the
   // flag sits apart.
-  const bool chunked = lg == 0 && (dkh == 64 || dkh == 128) && dvh % 32 == 0 && dvh <= 128 &&
-                       dims->seqlen > 0 && !walk_forced();
-  const int64_t ncpb = (dims->seqlen + 63) / 64;
+  const bool chunked = (dkh == 64 || dkh == 128) && dvh % 32 == 0 && dvh <= 128 && dims->seqlen > 0 &&
+                       !walk_forced();
+  const int64_t ncpb = ((dims->seqlen << lg) + 63) / 64;  // 64-step chunks per sequence
   // chunk slots x heads: fixed length B x chunks per sequence, packed the plan's upper bound
   const int64_t cslots = (cu_seqlens ? pl.slots : dims->batch * ncpb) * H;
   const int64_t crec = chunked ? dr::cbwd_record_bytes(dkh, dvh) : 0;
@@ -577,7 +577,7 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
       cb.rec_size = crec;
       cb.dsc = reinterpret_cast<float*>(wsb + off_part + round256(cslots * crec));
       cb.flag = reinterpret_cast<int32_t*>(wsb + off_flag);
-      cb.T = dims->seqlen;
+      cb.T = dims->seqlen << lg;
       cb.H = (int32_t)H;
       cb.DV = dvh;
       cb.B = (int32_t)dims->batch;
@@ -594,7 +594,7 @@ int dr_chunk_bwd_ex(const void* q, const void* k, const void* v, const float* al
         cb.seq_order = b.seq_order;
       }
       cb.variant = variant;
-      cb.lgnh = 0;
+      cb.lgnh = lg;
       cb.q_ts = p.q_ts; cb.q_bs = p.q_bs; cb.k_ts = p.k_ts; cb.k_bs = p.k_bs; cb.v_ts = p.v_ts; cb.v_bs = p.v_bs;
       e = dr::launch_chunked_backward(cb, dkh, dims->in_dtype == DR_BF16, vec, stream);
       b.run_flag = cb.flag;

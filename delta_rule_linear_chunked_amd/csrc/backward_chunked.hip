@@ -98,9 +98,20 @@ __device__ __forceinline__ typename Pol::Frag frag_s(const float* p, int stride)
   return Pol::make(x);
 }
 
-// Row of token t of chunk c, batch row b, head h in the dense per-token arrays.
-__device__ __forceinline__ int64_t cb_row(const CbParams& p, int b, int64_t m, int h) {
-  return ((int64_t)b * p.T + m) * p.H + h;
+// Step m of batch row b (fixed length; packed sequences: b = 0 and m the absolute step), head h:
+// its row in the per-token arrays (q, alpha, dO, dq, dalpha) and in the per-step arrays (k, v, the
+// gates and their gradients), and whether it is a token's first or last step. With one transition
+// per token both rows are (b T + m) H + h; with two (lgnh = 1) a token's steps are consecutive.
+__device__ __forceinline__ int64_t cb_tok(const CbParams& p, int b, int64_t m, int h) {
+  return ((((int64_t)b * p.T + m) >> p.lgnh) * p.H + h);
+}
+__device__ __forceinline__ int64_t cb_step(const CbParams& p, int b, int64_t m, int h) {
+  const int64_t a = (int64_t)b * p.T + m;
+  return ((((a >> p.lgnh) * p.H + h) << p.lgnh) + (a & ((1 << p.lgnh) - 1)));
+}
+__device__ __forceinline__ bool cb_first(const CbParams& p, int64_t m) { return (m & ((1 << p.lgnh) - 1)) == 0; }
+__device__ __forceinline__ bool cb_last(const CbParams& p, int64_t m) {
+  return (m & ((1 << p.lgnh) - 1)) == (1 << p.lgnh) - 1;
 }
 
 // The chunk algebra shared by the preparation and the gradient kernel (the chunk's rows are tokens
@@ -129,7 +140,7 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
 #pragma unroll
       for (int t = 0; t < SEG; ++t) {
         const int tt = sg * SEG + t;
-        a[t] = tt < nvalid ? p.alpha[cb_row(p, b, m0 + tt, h) * DK + ch] : 1.f;
+        a[t] = tt < nvalid && cb_first(p, m0 + tt) ? p.alpha[cb_tok(p, b, m0 + tt, h) * DK + ch] : 1.f;
       }
       float gm = 1.f;
       bool bad = false;
@@ -166,7 +177,7 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
     const int row = 16 * w + r;
     const bool valid = row < nvalid;
     const int64_t m = m0 + (valid ? row : 0);
-    const int64_t th = cb_row(p, b, m, h);
+    const int64_t th = cb_step(p, b, m, h);
     const InT* qp = static_cast<const InT*>(p.q);
     const InT* kp = static_cast<const InT*>(p.k);
     const int64_t qo = q_elem(p, b, m, h, DK), ko = kv_elem(p.k_ts, p.k_bs, p, b, m, h, DK);
@@ -312,7 +323,8 @@ __device__ __forceinline__ bool cb_chunk(const CbParams& p, CbChunk& k) {
   if (p.cu) {
     k.n = p.chunk_seq[slot];
     if (k.n < 0) return false;
-    const int64_t bos = p.cu[k.n], len = p.cu[k.n + 1] - bos, c0 = p.chunk_c0[slot];
+    const int64_t bos = (int64_t)p.cu[k.n] << p.lgnh, len = ((int64_t)p.cu[k.n + 1] << p.lgnh) - bos;
+    const int64_t c0 = p.chunk_c0[slot];
     k.c = (int)(c0 / CH);
     k.b = 0;
     k.m0 = bos + c0;
@@ -462,7 +474,7 @@ __global__ __launch_bounds__(512, 1) void cbwd_prep_kernel(const CbParams p) {
   for (int idx = tid; idx < CH * (DV / 4); idx += 512) {
     const int t = idx / (DV / 4), v4 = idx % (DV / 4);
     f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < nvalid) x = *reinterpret_cast<const f32x4*>(p.dO + cb_row(p, b, m0 + t, h) * DV + 4 * v4);
+    if (t < nvalid && cb_last(p, m0 + t)) x = *reinterpret_cast<const f32x4*>(p.dO + cb_tok(p, b, m0 + t, h) * DV + 4 * v4);
     store4(&sm.r1[t * LV + 4 * v4], x);
   }
   __syncthreads();
@@ -557,7 +569,7 @@ __global__ __launch_bounds__(256, 1) void cbwd_state_kernel(const CbParams p) {
   const int b = p.cu ? p.seq_order[pair / p.H] : pair / p.H, h = pair % p.H;
   // the sequence's chunk slots: first .. first + nch - 1
   const int first = p.cu ? p.seq_first[b] : b * p.nc;
-  const int nch = p.cu ? (int)((p.cu[b + 1] - p.cu[b] + CH - 1) / CH) : p.nc;
+  const int nch = p.cu ? (int)(((((int64_t)p.cu[b + 1] - p.cu[b]) << p.lgnh) + CH - 1) / CH) : p.nc;
   const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, g = l >> 4;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int DV = p.DV;
@@ -666,7 +678,7 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
   const int tid = threadIdx.x, w = (tid >> 6) & 3, hf = tid >> 8, l = tid & 63, r = l & 15, g = l >> 4;
   const int DV = p.DV;
   const int64_t SS = (int64_t)DK * DV;
-  const bool kda = p.variant == 0 || p.variant == 3;
+  const bool kda = p.variant == 0 || p.variant == 3 || p.variant == 4;  // beta for both uses
   const InT* qp = static_cast<const InT*>(p.q);
   const InT* kp = static_cast<const InT*>(p.k);
   const InT* vp = static_cast<const InT*>(p.v);
@@ -730,7 +742,8 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
     for (int idx = tid; idx < CH * 8; idx += 512) {
       const int t = idx >> 3, q4 = idx & 7;
       f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (t < nvalid) x = *reinterpret_cast<const f32x4*>(p.dO + cb_row(p, b, m0 + t, h) * DV + dv0 + 4 * q4);
+      if (t < nvalid && cb_last(p, m0 + t))
+        x = *reinterpret_cast<const f32x4*>(p.dO + cb_tok(p, b, m0 + t, h) * DV + dv0 + 4 * q4);
       store4(&dOb[t * L36 + 4 * q4], x);
     }
     // rows 16 w + 4 g + i, columns 16 ct + r of the block: first half m = write . v, second half v
@@ -741,7 +754,7 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
       const int t = 16 * w + 4 * g + i;
       const bool ok = t < nvalid;
       const int64_t m = m0 + (ok ? t : 0);
-      const int64_t th = cb_row(p, b, m, h);
+      const int64_t th = cb_step(p, b, m, h);
       const int64_t vo = kv_elem(p.v_ts, p.v_bs, p, b, m, h, DV);
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
@@ -819,7 +832,7 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
           const int t = 16 * w + 4 * g + i;
           dst[t * L36 + 16 * ct + r] = acc[ct][i];
           if (hf == 1 && t < nvalid) {
-            const int64_t th = cb_row(p, b, m0 + t, h);
+            const int64_t th = cb_step(p, b, m0 + t, h);
             const int col = dv0 + 16 * ct + r;
             const float e = acc[ct][i];
             p.dv[th * DV + col] = wv[ct][i] * e;
@@ -869,9 +882,10 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = 16 * w + 4 * g + i;
-    const int64_t th = cb_row(p, b, m0 + (t < nvalid ? t : 0), h);
+    const int64_t mt = m0 + (t < nvalid ? t : 0);
+    const int64_t th = cb_step(p, b, mt, h), tq = cb_tok(p, b, mt, h);
 #pragma unroll
-    for (int cc = 0; cc < NCT / 2; ++cc) al[i][cc] = p.alpha[th * DK + 16 * (hf * (NCT / 2) + cc) + r];
+    for (int cc = 0; cc < NCT / 2; ++cc) al[i][cc] = p.alpha[tq * DK + 16 * (hf * (NCT / 2) + cc) + r];
     if constexpr (VEC) {
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) evr[ct][i] = hf == 0 ? p.erase[th * DK + 16 * ct + r] : 0.f;
@@ -889,7 +903,7 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
     const int row = 16 * w + r;
     const bool valid = row < nvalid;
     const int64_t m = m0 + (valid ? row : 0);
-    const int64_t th = cb_row(p, b, m, h);
+    const int64_t th = cb_step(p, b, m, h);
     const int64_t qo = q_elem(p, b, m, h, DK), ko = kv_elem(p.k_ts, p.k_bs, p, b, m, h, DK);
     const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
 #pragma unroll
@@ -1000,7 +1014,9 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
     for (int i = 0; i < 4; ++i) {
       const int t = 16 * w + 4 * g + i;
       const bool ok = t < nvalid;
-      const int64_t th = cb_row(p, b, m0 + (ok ? t : 0), h);
+      const int64_t mt = m0 + (ok ? t : 0);
+      const int64_t th = cb_step(p, b, mt, h), tq = cb_tok(p, b, mt, h);
+      const bool lastq = cb_last(p, mt);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
         const int ch = 16 * ct + r, o = t * LG + ch;
@@ -1012,7 +1028,7 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
         const float evv = VEC ? evr[ct][i] : esr[i];
         X[o] = Ql[o] * A1[ct][i] + Ul[o] * A2[ct][i] - kv * dkk;
         if (ok) {
-          p.dq[th * DK + ch] = dqv;
+          if (lastq) p.dq[tq * DK + ch] = dqv;
           p.dk[th * DK + ch] = fmaf(evv, duv, dkk);
           if constexpr (VEC) p.derase[th * DK + ch] = kv * duv;
         }
@@ -1041,7 +1057,7 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
   if constexpr (!VEC) {
     // per token: k . du over the channels, v . dm over the value columns
     if (tid < nvalid) {
-      const int64_t th = cb_row(p, b, m0 + tid, h);
+      const int64_t th = cb_step(p, b, m0 + tid, h);
       const float a = sm.red[0][0][tid], v = sm.red[0][1][tid];
       if (kda) {
         p.derase[th] = a + v;
@@ -1069,12 +1085,12 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int t = 16 * w + 4 * g + i;
-    if (t < nvalid) {
-      const int64_t th = cb_row(p, b, m0 + t, h);
+    if (t < nvalid && cb_first(p, m0 + t)) {  // the decay acts on a token's first step
+      const int64_t tq = cb_tok(p, b, m0 + t, h);
 #pragma unroll
       for (int cc = 0; cc < NCT / 2; ++cc) {
         const int ch = 16 * (hf * (NCT / 2) + cc) + r;
-        p.dalpha[th * DK + ch] = X[t * LG + ch] / al[i][cc];
+        p.dalpha[tq * DK + ch] = X[t * LG + ch] / al[i][cc];
       }
     }
   }

@@ -172,13 +172,13 @@ struct CbParams {
   int64_t rec_size;
   float* dsc;           // [slots, H, d_k, d_v]: gradient reaching the state at each chunk's end
   int32_t* flag;        // set when some chunk's gates are outside the chunked form's range
-  int64_t T;
+  int64_t T;            // steps per batch row
   int32_t H;
   int32_t DV;
   int32_t B;
-  int32_t nc;           // fixed length: chunks per sequence (chunk slot b * nc + c)
-  int32_t variant;      // 0 KDA, 1 RDA, 2 GDN-2, 3 CKDA
-  int32_t lgnh;         // 0 (one transition per token); read by q_elem / kv_elem
+  int32_t nc;           // fixed length: 64-step chunks per sequence (chunk slot b * nc + c)
+  int32_t variant;      // 0 KDA, 1 RDA, 2 GDN-2, 3 CKDA, 4 two KDA transitions per token
+  int32_t lgnh;         // transitions per token, as a power of two (see Params)
   int64_t q_ts, q_bs, k_ts, k_bs, v_ts, v_bs;
 };
 

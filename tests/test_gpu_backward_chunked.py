@@ -143,3 +143,33 @@ def test_packed_varlen_workload_against_walk():
     for n, e in errs.items():
         assert e <= TOL["bf16"], (n, e)
     assert any(not np.array_equal(g[n], gw[n]) for n in NAMES if g[n] is not None)
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("lengths", [None, [40, 0, 1, 33, 70]])
+def test_two_transitions_per_token_chunked(in_dtype, lengths):
+    # DR_PRODUCT2: a token's two KDA steps are consecutive 64-step chunk rows; dq comes from a
+    # token's second step, dalpha from its first
+    from oracle import product
+    seed = seed_of("cbwd p2", in_dtype, lengths is None)
+    if lengths is None:
+        wl = synth.make_product("kda", 2, 75, 2, 128, 64, in_dtype=in_dtype, seed=seed)
+    else:
+        wl = synth.make_product("kda", 1, 0, 2, 128, 64, in_dtype=in_dtype, seed=seed, lengths=lengths)
+    rng = np.random.default_rng(seed)
+    dO = rng.standard_normal(wl.q.shape[:3] + (wl.v.shape[-1],)).astype(np.float32)
+    dS_T = rng.standard_normal((wl.num_seqs,) + wl.S0.shape[1:]).astype(np.float32)
+    a = dict(q=to_dev(wl.q, wl.in_dtype), k=to_dev(wl.k, wl.in_dtype), v=to_dev(wl.v, wl.in_dtype),
+             alpha=to_dev(wl.alpha), erase=to_dev(wl.erase), write=None, variant="product2", S0=to_dev(wl.S0),
+             cu_seqlens=None if wl.cu_seqlens is None else to_dev(wl.cu_seqlens))
+    g = _grads(a, to_dev(dO), to_dev(dS_T))
+    gw = _grads(a, to_dev(dO), to_dev(dS_T), walk=True)
+    ref = product.product_grads(wl.q, wl.k, wl.v, wl.alpha, wl.erase, dO, dS_T=dS_T, S0=wl.S0,
+                                cu_seqlens=wl.cu_seqlens)
+    pairs = {"dq": "dq", "dk": "dk", "dv": "dv", "dalpha": "dalpha", "derase": "dbeta", "dS0": "dS0"}
+    errs = {n: rel_err(g[n], ref[m]) for n, m in pairs.items()}
+    print(f"[chunked backward product2 {in_dtype} {'packed' if lengths else 'fixed'}] "
+          + " ".join(f"{k}={v:.2e}" for k, v in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= TOL[in_dtype], (n, e)
+    assert any(not np.array_equal(g[n], gw[n]) for n in pairs)
