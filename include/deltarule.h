@@ -303,8 +303,8 @@ int dr_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void
  * The inputs are those of the forward call (plain inputs: the fused preparation and the
  * stored-state options are forward-only; q, k, v may be strided through a dr_dims_v2, the
  * gradients are always dense). The call reruns the forward to keep the state after
- * every 64 tokens. Calls with one transition per token (fixed-length or packed), d_k 64 or 128
- * and d_v a multiple of 32 up to 128 then take the chunked form: per 64-token chunk an affine map of the
+ * every 64 steps (32 tokens for DR_PRODUCT2). Calls with d_k 64 or 128 and d_v a multiple of 32
+ * up to 128 (fixed-length or packed, one or two transitions per token) then take the chunked form: per 64-token chunk an affine map of the
  * state gradient, a reverse pass over the chunks, and the chunk's gradients from its tile
  * products, all on MFMA. That form divides by the decays' running products and by the decays
  * themselves, so a chunk with a gate of magnitude below 2^-10, a running product outside
