@@ -22,11 +22,12 @@
 // q . dq + u . du - k . dk plus the end state's term rowsum(dS . S_C); dividing by alpha_t gives
 // the gate gradient.
 //
-// The division by Gamma_s and by alpha_t is what limits this form: a chunk in which some gate has
-// magnitude below 2^-10, or a running product leaves [2^-100, 2^100], or a value is not finite,
-// raises a flag, and the whole call then takes the exact per-token reverse walk (backward.hip),
-// which divides by nothing. (KDA, RDA and GDN-2 decays exp(-c softplus(z)) close to 1 never
-// raise it; Complex KDA gates near zero do.)
+// The divisions by Gamma_s and by alpha_t are what limit this form. A gate of magnitude below 2^-4
+// takes its gate gradient from an exact inner product instead (up to 12 such gates per chunk);
+// a chunk with more of them, a zero or non-finite gate, or a running product outside
+// [2^-110, 2^100] raises a flag, and the whole call then takes the exact per-token reverse walk
+// (backward.hip), which divides by nothing. (KDA, RDA and GDN-2 decays exp(-c softplus(z)) close
+// to 1 never raise it; Complex KDA gates, a few percent of them near zero, do.)
 //
 // Passes (chunks of 64 tokens from each sequence's start; packed sequences take their chunk slots
 // from the prefill's plan pass):
@@ -43,8 +44,12 @@ namespace dr {
 
 namespace {
 
-constexpr float CB_TAU = 0x1p-10f;   // smallest gate magnitude the chunked form takes
-constexpr float CB_LO = 0x1p-100f;   // range of the running products it takes
+// Gates of magnitude below CB_TAU take the exact gate gradient: the cumulative sum's rounding,
+// divided by alpha, measured up to 2.5e-5 (split bf16) and 2e-6 (fp32) of the gradient's RMS over
+// |alpha| with Complex KDA gates, so below 2^-4 the division would exceed the parity bars' margin.
+constexpr float CB_TAU = 0x1p-4f;
+constexpr int CB_NE = 12;            // at most this many such (token, channel) entries per chunk
+constexpr float CB_LO = 0x1p-110f;   // range of the running products the chunked form takes
 constexpr float CB_HI = 0x1p100f;
 constexpr int L68 = CH + 4;          // row stride of 64-column fp32 tiles
 constexpr int L36 = 36;              // row stride of 32-column fp32 tiles
@@ -80,6 +85,12 @@ struct CbSmem {
   float ddp[512];   // per-thread partial sums of rowsum(S0 . dS)
   float ecs[4][DK]; // per-row-block column sums of Kbar . dKbar
   float red[2][2][CH];  // per-half token sums: k . du, v . dm
+  // gates of magnitude below CB_TAU: their count, (token, channel), and for the gradient kernel
+  // Qtilde and Utilde down the entry's channel and the entry's inner product
+  int ne;
+  int ent[CB_NE];
+  float eq[CB_NE][CH], eu[CB_NE][CH];
+  float eacc[CB_NE];
 };
 // offsets in r2 during the chunk algebra
 constexpr int OA = 0, OAT = CH * L68, OP = 2 * CH * L68, OT = 3 * CH * L68;
@@ -130,7 +141,9 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
 
   // Gamma: running products down the chunk per channel (tokens past the sequence end take decay
   // 1), in segments of SEG tokens: every thread loads its segment, multiplies it out, and the
-  // segments' totals are chained through LDS
+  // segments' totals are chained through LDS. Gates of magnitude below CB_TAU are listed.
+  if (tid == 0) sm.ne = 0;
+  __syncthreads();
   {
     constexpr int NSEG = 4, SEG = CH / NSEG;
     const int nthr = blockDim.x;
@@ -146,7 +159,12 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
       bool bad = false;
 #pragma unroll
       for (int t = 0; t < SEG; ++t) {
-        bad = bad || !(fabsf(a[t]) >= CB_TAU);  // (also true for NaN)
+        const float aa = fabsf(a[t]);
+        bad = bad || !(aa > 0.f && aa <= CB_HI);  // zero, not finite (NaN included) or too large
+        if (aa < CB_TAU && aa > 0.f) {
+          const int e = atomicAdd(&sm.ne, 1);
+          if (e < CB_NE) sm.ent[e] = (sg * SEG + t) * DK + ch;
+        }
         gm *= a[t];
         sm.r0[(sg * SEG + t) * LG + ch] = gm;
       }
@@ -171,6 +189,7 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
     }
   }
   __syncthreads();
+  if (set_flag && tid == 0 && sm.ne > CB_NE) atomicOr(p.flag, 1);
 
   // this thread's row: Utilde, Qtilde (registers) and Kd (LDS)
   {
@@ -349,6 +368,31 @@ __device__ __forceinline__ const float* cb_start_state(const CbParams& p, const 
 }
 
 }  // namespace
+
+// The entries' <L, R> over one value block's columns, for wave w8's entries w8, w8 + 8, ...: lane
+// (c, half) takes column c and every second token of the sums, the halves meet by a lane swap.
+// Out of line, so that the gradient kernel's registers are not sized for it on the path without
+// such entries.
+template <int DK>
+__device__ __attribute__((noinline)) void cb_entries(CbSmem<DK>& sm, int ne, int w8, int l, const float* S0b,
+                                                      const float* dSb, const float* dOb, const float* Dl,
+                                                      const float* El) {
+  constexpr int LG = CbSmem<DK>::LG;
+  for (int e = w8; e < ne; e += 8) {
+    const int te = sm.ent[e] / DK, ie = sm.ent[e] % DK, c = l & 31, hv = l >> 5;
+    float Lv = hv == 0 ? S0b[ie * L36 + c] : 0.f;
+    for (int s2 = hv; s2 < te; s2 += 2) Lv = fmaf(sm.r1[s2 * LG + ie], Dl[s2 * L36 + c], Lv);
+    float Rv = hv == 0 ? sm.gc[ie] * dSb[ie * L36 + c] : 0.f;
+    for (int r2 = te + ((te ^ hv) & 1); r2 < CH; r2 += 2)
+      Rv = fmaf(sm.eq[e][r2], dOb[r2 * L36 + c], fmaf(-sm.eu[e][r2], El[r2 * L36 + c], Rv));
+    Lv += __shfl_xor(Lv, 32);
+    Rv += __shfl_xor(Rv, 32);
+    float prod = hv == 0 ? Lv * Rv : 0.f;
+#pragma unroll
+    for (int d = 1; d < 32; d <<= 1) prod += __shfl_xor(prod, d);
+    if (l == 0) sm.eacc[e] += prod;
+  }
+}
 
 // ============================================================================ pass 1
 __global__ void cbwd_flag_clear_kernel(int32_t* flag) {
@@ -711,6 +755,30 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
       }
     }
   }
+  // Gates of magnitude below CB_TAU (at most CB_NE; more hand the call to the walk): their gate
+  // gradient is formed exactly, without the cumulative sum's cancelling terms, as
+  // alpha_t dalpha_t = <L, R> with L = S0_i + sum_{s<t} Kd_si delta_s (S_{t-1}'s row i over Gamma_{t-1})
+  // and R = Gamma_C,i dS_i + sum_{r>=t} (Qtilde_ri dO_r - Utilde_ri eps_r) (Gamma_t times the
+  // gradient reaching X_t's row i): every term of R holds alpha_t as a factor, so the division by
+  // alpha_t at the end loses nothing. Wave w8 takes entries w8, w8 + 8, ...; here Qtilde and
+  // Utilde down each entry's channel.
+  const int ne = sm.ne < CB_NE ? sm.ne : CB_NE;
+  const int w8 = tid >> 6;
+  for (int idx = tid; idx < ne * CH; idx += 512) {
+    const int e = idx / CH, rr = idx % CH;
+    const int te = sm.ent[e] / DK, ie = sm.ent[e] % DK;
+    float qv = 0.f, uv = 0.f;
+    if (rr >= te && rr < nvalid) {
+      const int64_t m = m0 + rr;
+      const float gm = sm.r0[rr * LG + ie];
+      const int64_t th = cb_step(p, b, m, h);
+      qv = gm * ld_f32(qp + q_elem(p, b, m, h, DK) + ie);
+      uv = gm * (VEC ? p.erase[th * DK + ie] : p.erase[th]) * ld_f32(kp + kv_elem(p.k_ts, p.k_bs, p, b, m, h, DK) + ie);
+    }
+    sm.eq[e][rr] = qv;
+    sm.eu[e][rr] = uv;
+    if (rr == 0) sm.eacc[e] = 0.f;
+  }
   __syncthreads();
 
   // ---- value blocks of 32 columns: delta, eps, dv and the tile gradients
@@ -843,6 +911,7 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
       }
     }
     __syncthreads();
+    if (w8 < ne) cb_entries<DK>(sm, ne, w8, l, S0b, dSb, dOb, Dl, El);
     // tile gradients of row block w
     {
       const Frag AO = frag_c<Pol>(&dOb[(16 * w + r) * L36 + 8 * g]);
@@ -1080,6 +1149,8 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
       X[t * LG + tid] = s;
     }
   }
+  __syncthreads();
+  if (tid < ne) X[(sm.ent[tid] / DK) * LG + sm.ent[tid] % DK] = sm.eacc[tid];  // the entries' exact values
   __syncthreads();
   // each half writes half of the channel tiles
 #pragma unroll

@@ -77,9 +77,10 @@ hipError_t launch_backward(BwdParams p, int64_t pairs, int dk, int dv, bool bf16
 // d_k in {64, 128}, d_v a multiple of 32 up to 128. Bytes of one chunk record, then the launches:
 // the flag is cleared, every (batch row, chunk, head) builds its record, the state-gradient pass
 // runs over the chunks in reverse and the gradient kernel writes every output except dS0 (which
-// the state-gradient pass writes). A chunk whose gates the chunked form does not take (a gate of
-// magnitude below 2^-10, a running product outside [2^-100, 2^100], or a value that is not finite)
-// sets *flag; the gradient kernel then writes nothing and the caller runs the exact walk.
+// the state-gradient pass writes). A chunk whose gates the chunked form does not take (more than 12
+// gates of magnitude below 2^-4, a zero or non-finite gate, a running product outside
+// [2^-110, 2^100]) sets *flag; the gradient kernel then writes nothing and the caller runs the
+// exact walk.
 struct CbParams;
 int64_t cbwd_record_bytes(int dk, int dv);
 hipError_t launch_chunked_backward(const CbParams& p, int dk, bool bf16, bool vec, hipStream_t s);

@@ -307,9 +307,10 @@ int dr_chunk_fwd_noalloc(const void* q, const void* k, const void* v, const void
  * up to 128 (fixed-length or packed, one or two transitions per token) then take the chunked form: per 64-token chunk an affine map of the
  * state gradient, a reverse pass over the chunks, and the chunk's gradients from its tile
  * products, all on MFMA. That form divides by the decays' running products and by the decays
- * themselves, so a chunk with a gate of magnitude below 2^-10, a running product outside
- * [2^-100, 2^100] or a value that is not finite hands the whole call, on the device and without a
- * host synchronisation, to the exact per-token walk, which every other call takes directly: it
+ * themselves: up to 12 gates per chunk of magnitude below 2^-4 take their gradient from an exact
+ * inner product instead, and a chunk with more of them, a zero or non-finite gate, or a running
+ * product outside [2^-110, 2^100] hands the whole call, on the device and without a host
+ * synchronisation, to the exact per-token walk, which every other call takes directly: it
  * walks each sequence backwards, recomputing states between the checkpoints. DR_BWD_WALK set (and
  * not "0") in the environment sends every call to the walk. The workspace (about 4 * d_k * 4
  * bytes per token-head and value block of 32 columns, plus the checkpoints; the chunked form's

@@ -3,8 +3,9 @@ d_k 64 or 128, d_v a multiple of 32 up to 128) against the fp64 oracle's reverse
 against the exact per-token walk on the same inputs (the walk forced with DR_BWD_WALK=1).
 
 Tolerance per gradient tensor, max |err| / RMS(ref): 1e-4 for fp32 inputs and 1e-2 for bf16
-inputs, as for the walk. A chunk whose gates the chunked form does not take (a gate below 2^-10
-in magnitude) hands the whole call to the walk, whose results are then reproduced bit for bit."""
+inputs, as for the walk. A chunk whose gates the chunked form does not take (a zero or non-finite
+gate, more than 12 gates below 2^-4 in magnitude, a running product below 2^-110) hands the whole
+call to the walk, whose results are then reproduced bit for bit."""
 import os
 
 import numpy as np
@@ -70,9 +71,16 @@ def test_chunked_matches_oracle_and_walk(variant, dk, dv, T, in_dtype):
     assert any(not np.array_equal(g[n], gw[n]) for n in NAMES if g[n] is not None)
 
 
-def test_small_gate_hands_the_call_to_the_walk():
-    wl = synth.make_prefill("kda", 2, 200, 2, 128, 64, in_dtype="bf16", seed=seed_of("cbwd flag"))
-    wl.alpha[1, 150, 0, 7] = 1e-4   # one gate below 2^-10 in one chunk
+@pytest.mark.parametrize("case", ["zero gate", "13 small gates in a chunk", "product below 2^-110"])
+def test_hand_over_to_the_walk(case):
+    # gates the chunked form does not take hand the whole call to the exact walk, bit for bit
+    wl = synth.make_prefill("kda", 2, 200, 2, 128, 64, in_dtype="bf16", seed=seed_of("cbwd flag", case))
+    if case == "zero gate":
+        wl.alpha[1, 150, 0, 7] = 0.0
+    elif case == "13 small gates in a chunk":
+        wl.alpha[1, 150, 0, :13] = 0.01
+    else:
+        wl.alpha[0, 64:128, 1, 5] = 0.3      # 0.3^64 < 2^-110 over one chunk
     dO, dS_T = _inputs(wl, 77)
     a = prefill_inputs(wl)
     g = _grads(a, to_dev(dO), to_dev(dS_T))
@@ -80,11 +88,23 @@ def test_small_gate_hands_the_call_to_the_walk():
     for n in NAMES:
         if g[n] is not None:
             assert np.array_equal(g[n], gw[n]), n
-    _check("flagged chunk", g, _oracle(wl, dO, dS_T), TOL["bf16"])
+    _check(f"flagged: {case}", g, _oracle(wl, dO, dS_T), TOL["bf16"])
+
+
+def test_twelve_small_gates_stay_chunked():
+    wl = synth.make_prefill("kda", 2, 200, 2, 128, 64, in_dtype="bf16", seed=seed_of("cbwd 12 small"))
+    wl.alpha[1, 150, 0, :6] = 1e-4
+    wl.alpha[1, 150, 0, 6:12] = 0.03
+    dO, dS_T = _inputs(wl, 78)
+    a = prefill_inputs(wl)
+    g = _grads(a, to_dev(dO), to_dev(dS_T))
+    gw = _grads(a, to_dev(dO), to_dev(dS_T), walk=True)
+    _check("12 small gates", g, _oracle(wl, dO, dS_T), TOL["bf16"])
+    assert any(not np.array_equal(g[n], gw[n]) for n in NAMES if g[n] is not None)
 
 
 def test_ckda_without_small_gates_stays_chunked():
-    # Complex KDA gates with no magnitude below 2^-10 and products inside the range: chunked
+    # Complex KDA gates with no magnitude below 2^-4 and products inside the range: chunked
     wl = synth.make_prefill("ckda", 1, 128, 2, 64, 64, in_dtype="f32", seed=seed_of("cbwd ckda"))
     a8 = np.abs(wl.alpha)
     wl.alpha = np.where(a8 < 0.7, np.sign(wl.alpha + 1e-30) * 0.7, wl.alpha).astype(np.float32)
@@ -173,3 +193,38 @@ def test_two_transitions_per_token_chunked(in_dtype, lengths):
     for n, e in errs.items():
         assert e <= TOL[in_dtype], (n, e)
     assert any(not np.array_equal(g[n], gw[n]) for n in pairs)
+
+
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+def test_complex_kda_small_gates_stay_chunked(in_dtype):
+    # signed Complex KDA gates kept at magnitude 2^-4 or more, plus planted gates below 2^-4 (at most
+    # 12 per chunk): those take the exact gate gradient, the chunk stays on the chunked form
+    wl = synth.make_prefill("ckda", 2, 150, 2, 128, 64, in_dtype=in_dtype, seed=seed_of("cbwd ckda small", in_dtype))
+    wl.alpha = np.where(np.abs(wl.alpha) < 0.07, np.where(wl.alpha < 0, -0.07, 0.07), wl.alpha).astype(np.float32)
+    planted = ((0, 10, 0, 3, 1e-5), (1, 70, 1, 100, -3e-7), (1, 71, 1, 100, 2e-4), (0, 130, 1, 7, 0.05),
+               (1, 5, 0, 64, -0.03))
+    for b, t, h, i, x in planted:
+        wl.alpha[b, t, h, i] = x
+    dO, dS_T = _inputs(wl, seed_of("cbwd ckda small do", in_dtype))
+    a = prefill_inputs(wl)
+    g = _grads(a, to_dev(dO), to_dev(dS_T))
+    gw = _grads(a, to_dev(dO), to_dev(dS_T), walk=True)
+    ref = _oracle(wl, dO, dS_T)
+    _check(f"ckda small gates {in_dtype}", g, ref, TOL[in_dtype])
+    assert any(not np.array_equal(g[n], gw[n]) for n in NAMES if g[n] is not None)
+    rms = np.sqrt(np.mean(ref["dalpha"] ** 2))
+    for b, t, h, i, _ in planted:
+        assert abs(g["dalpha"][b, t, h, i] - ref["dalpha"][b, t, h, i]) <= TOL[in_dtype] * rms, (b, t, h, i)
+
+
+def test_complex_kda_long_context_hands_over_to_the_walk():
+    # the Complex KDA long-context workload (2 x 16384 tokens, H=16, d=128, bf16): a few percent of
+    # its gates lie below 2^-4, far more than 12 in most chunks, so the call takes the walk, bit for bit
+    wl = synth.preset("ckda_long")
+    dO, dS_T = _inputs(wl, 1005)
+    a = prefill_inputs(wl)
+    g = _grads(a, to_dev(dO), to_dev(dS_T))
+    gw = _grads(a, to_dev(dO), to_dev(dS_T), walk=True)
+    for n in NAMES:
+        if g[n] is not None:
+            assert np.array_equal(g[n], gw[n]), n
