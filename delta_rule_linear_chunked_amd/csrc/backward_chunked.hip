@@ -819,7 +819,11 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
     float ev[2][4], wv[2][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int t = 16 * w + 4 * g + i;
+      // the row index is made opaque so that its 64-bit offsets are formed again in each value
+      // block instead of being hoisted out of the loop: held across it they pushed accumulators
+      // to scratch (91 spilled registers; 10 now, none reloaded inside the loop's tile phase)
+      int t = 16 * w + 4 * g + i;
+      asm volatile("" : "+v"(t));
       const bool ok = t < nvalid;
       const int64_t m = m0 + (ok ? t : 0);
       const int64_t th = cb_step(p, b, m, h);
@@ -900,7 +904,9 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
           const int t = 16 * w + 4 * g + i;
           dst[t * L36 + 16 * ct + r] = acc[ct][i];
           if (hf == 1 && t < nvalid) {
-            const int64_t th = cb_step(p, b, m0 + t, h);
+            int to = t;  // opaque, as above
+            asm volatile("" : "+v"(to));
+            const int64_t th = cb_step(p, b, m0 + to, h);
             const int col = dv0 + 16 * ct + r;
             const float e = acc[ct][i];
             p.dv[th * DV + col] = wv[ct][i] * e;
@@ -1136,17 +1142,36 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
       }
     }
   }
-  // alpha_t dalpha_t = reverse cumulative sum of x + Gamma_C rowsum(S0 . dS) + sum_s Kbar . dKbar
-  if (tid < DK) {
-    float s = 0.f;
+  // alpha_t dalpha_t = reverse cumulative sum of x + Gamma_C rowsum(S0 . dS) + sum_s Kbar . dKbar,
+  // over PARTS segments of SEG tokens per channel: segment sums, then each segment's scan from the
+  // sum of everything after it
+  {
+    constexpr int SEG = CH / PARTS;
+    const int ch = tid % DK, sg = tid / DK;
+    float xs[SEG], tot = 0.f;
 #pragma unroll
-    for (int q = 0; q < PARTS; ++q) s += sm.ddp[q * DK + tid];
-    s *= sm.gc[tid];
+    for (int j = 0; j < SEG; ++j) {
+      xs[j] = X[(SEG * sg + j) * LG + ch];
+      tot += xs[j];
+    }
+    float base = 0.f;
+    if (sg == 0) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) s += sm.ecs[q][tid];
-    for (int t = CH - 1; t >= 0; --t) {
-      s += X[t * LG + tid];
-      X[t * LG + tid] = s;
+      for (int q = 0; q < PARTS; ++q) base += sm.ddp[q * DK + ch];
+      base *= sm.gc[ch];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) base += sm.ecs[q][ch];
+    }
+    __syncthreads();
+    sm.ddp[sg * DK + ch] = tot;
+    if (sg == 0) sm.ecs[0][ch] = base;
+    __syncthreads();
+    float s = sm.ecs[0][ch];
+    for (int q = PARTS - 1; q > sg; --q) s += sm.ddp[q * DK + ch];
+#pragma unroll
+    for (int j = SEG - 1; j >= 0; --j) {
+      s += xs[j];
+      X[(SEG * sg + j) * LG + ch] = s;
     }
   }
   __syncthreads();
