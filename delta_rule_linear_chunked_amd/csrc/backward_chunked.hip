@@ -139,6 +139,26 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
   // (with 512 threads, waves w and w + 4 share row block w; the second half only builds its ut / qt)
   const int tid = threadIdx.x, w = (tid >> 6) & 3, hf = tid >> 8, l = tid & 63, r = l & 15, g = l >> 4;
 
+  // This thread's row of q, k (and the erase gates) is loaded first, so that these loads are in
+  // flight while Gamma is formed: every lane loads (rows past the sequence end read the chunk's
+  // first row) and the values are selected where used. Loads under that condition were each
+  // waited for inside it, one slice after the other.
+  const int row = 16 * w + r;
+  const bool valid = row < nvalid;
+  const int64_t mrow = m0 + (valid ? row : 0);
+  const int64_t th = cb_step(p, b, mrow, h);
+  const int64_t qo = q_elem(p, b, mrow, h, DK), ko = kv_elem(p.k_ts, p.k_bs, p, b, mrow, h, DK);
+  typename Raw8Of<InT>::type qr[KS], kr[KS];
+  float br[VEC ? KS : 1][8];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int ch0 = 32 * ks + 8 * g;
+    ld_raw8(static_cast<const InT*>(p.q) + qo + ch0, qr[ks]);
+    ld_raw8(static_cast<const InT*>(p.k) + ko + ch0, kr[ks]);
+    if constexpr (VEC) load8(p.erase + th * DK + ch0, br[ks]);
+  }
+  const float esr = VEC ? 0.f : p.erase[th];
+
   // Gamma: running products down the chunk per channel (tokens past the sequence end take decay
   // 1), in segments of SEG tokens: every thread loads its segment, multiplies it out, and the
   // segments' totals are chained through LDS. Gates of magnitude below CB_TAU are listed.
@@ -193,25 +213,17 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
 
   // this thread's row: Utilde, Qtilde (registers) and Kd (LDS)
   {
-    const int row = 16 * w + r;
-    const bool valid = row < nvalid;
-    const int64_t m = m0 + (valid ? row : 0);
-    const int64_t th = cb_step(p, b, m, h);
-    const InT* qp = static_cast<const InT*>(p.q);
-    const InT* kp = static_cast<const InT*>(p.k);
-    const int64_t qo = q_elem(p, b, m, h, DK), ko = kv_elem(p.k_ts, p.k_bs, p, b, m, h, DK);
-    const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
+    const float esc = valid ? esr : 0.f;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch0 = 32 * ks + 8 * g;
       float q8[8], k8[8], b8[8], g8[8];
-      if (valid) {
-        load8(qp + qo + ch0, q8);
-        load8(kp + ko + ch0, k8);
-        if constexpr (VEC) load8(p.erase + th * DK + ch0, b8);
-      } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { q8[j] = 0.f; k8[j] = 0.f; b8[j] = 0.f; }
+      for (int j = 0; j < 8; ++j) {
+        q8[j] = valid ? raw8_at(qr[ks], j) : 0.f;
+        k8[j] = valid ? raw8_at(kr[ks], j) : 0.f;
+        if constexpr (VEC) b8[j] = valid ? br[ks][j] : 0.f;
+        else b8[j] = 0.f;
       }
       load8(&sm.r0[row * LG + ch0], g8);
       float kd[8];
@@ -418,6 +430,20 @@ __global__ __launch_bounds__(512, 1) void cbwd_prep_kernel(const CbParams p) {
   const int rt = w8 % RT, part = w8 / RT;
   float ut[KS][8], qt[KS][8];
   chunk_algebra<DK, InT, VEC>(p, sm, b, m0, h, nvalid, ut, qt, true);
+  // dO of the chunk (zero past the sequence end), loaded here so that its latency overlaps W, Z
+  // and M, and put in LDS once M is done with Kd: DV / 32 16-byte pieces per thread (d_v <= 128).
+  // Every load is issued, pieces that do not count reading the chunk's first row, and zeroed at
+  // the store: loads under a condition each got a wait for their data right behind them.
+  const int DV = p.DV, LV = DV + 4, NQ = DV / 32;
+  f32x4 dOr[4];
+  unsigned dOk = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = tid + 512 * k, t = idx / (DV / 4), v4 = idx % (DV / 4);
+    const bool ok = k < NQ && t < nvalid && cb_last(p, m0 + t);
+    dOk |= ok ? 1u << k : 0u;
+    dOr[k] = *reinterpret_cast<const f32x4*>(p.dO + cb_tok(p, b, m0 + (ok ? t : 0), h) * DV + 4 * (ok ? v4 : 0));
+  }
   const float* Tm = sm.r2 + OT;
   const float* Pm = sm.r2 + OP;
   float* Wm = sm.r2;  // W over A and At (no longer read)
@@ -513,13 +539,12 @@ __global__ __launch_bounds__(512, 1) void cbwd_prep_kernel(const CbParams p) {
       }
     }
   }
-  // dO of the chunk -> r1 [64][d_v + 4] (zero past the sequence end)
-  const int DV = p.DV, LV = DV + 4;
-  for (int idx = tid; idx < CH * (DV / 4); idx += 512) {
-    const int t = idx / (DV / 4), v4 = idx % (DV / 4);
-    f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (t < nvalid && cb_last(p, m0 + t)) x = *reinterpret_cast<const f32x4*>(p.dO + cb_tok(p, b, m0 + t, h) * DV + 4 * v4);
-    store4(&sm.r1[t * LV + 4 * v4], x);
+  // dO -> r1 [64][d_v + 4]
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int idx = tid + 512 * k;
+    if (k < NQ)
+      store4(&sm.r1[(idx / (DV / 4)) * LV + 4 * (idx % (DV / 4))], (dOk >> k) & 1u ? dOr[k] : f32x4{0.f, 0.f, 0.f, 0.f});
   }
   __syncthreads();
   const int64_t slot = blockIdx.x;
@@ -801,19 +826,29 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
   float dpart = 0.f;
   float vdm[4] = {0.f, 0.f, 0.f, 0.f};  // second half: v . dm of rows 16 w + 4 g + i, this lane's columns
   for (int dv0 = 0; dv0 < DV; dv0 += 32) {
-    for (int idx = tid; idx < DK * 8; idx += 512) {
-      const int row = idx >> 3, q4 = idx & 7;
-      const int64_t o = (int64_t)row * DV + dv0 + 4 * q4;
-      store4(&S0b[row * L36 + 4 * q4], S0p ? *reinterpret_cast<const f32x4*>(S0p + o) : f32x4{0.f, 0.f, 0.f, 0.f});
-      store4(&dSb[row * L36 + 4 * q4], *reinterpret_cast<const f32x4*>(dSp + o));
+    // the block's S0, dS and dO, every load issued before the first store (a dO row that does not
+    // count reads the chunk's first row and is zeroed at the store; loads under a condition were
+    // each waited for inside it)
+    constexpr int NSR = DK * 8 / 512;  // 16-byte pieces of S0 and of dS per thread
+    f32x4 s0v[NSR], dsv[NSR];
+    const float* S0q = S0p ? S0p : dSp;
+#pragma unroll
+    for (int k = 0; k < NSR; ++k) {
+      const int idx = tid + 512 * k;
+      const int64_t o = (int64_t)(idx >> 3) * DV + dv0 + 4 * (idx & 7);
+      s0v[k] = *reinterpret_cast<const f32x4*>(S0q + o);
+      dsv[k] = *reinterpret_cast<const f32x4*>(dSp + o);
     }
-    for (int idx = tid; idx < CH * 8; idx += 512) {
-      const int t = idx >> 3, q4 = idx & 7;
-      f32x4 x = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (t < nvalid && cb_last(p, m0 + t))
-        x = *reinterpret_cast<const f32x4*>(p.dO + cb_tok(p, b, m0 + t, h) * DV + dv0 + 4 * q4);
-      store4(&dOb[t * L36 + 4 * q4], x);
+    const int td = tid >> 3, q4d = tid & 7;  // CH * 8 = 512 pieces of dO, one per thread
+    const bool dok = td < nvalid && cb_last(p, m0 + td);
+    const f32x4 dov = *reinterpret_cast<const f32x4*>(p.dO + cb_tok(p, b, m0 + (dok ? td : 0), h) * DV + dv0 + 4 * q4d);
+#pragma unroll
+    for (int k = 0; k < NSR; ++k) {
+      const int idx = tid + 512 * k, row = idx >> 3, q4 = idx & 7;
+      store4(&S0b[row * L36 + 4 * q4], S0p ? s0v[k] : f32x4{0.f, 0.f, 0.f, 0.f});
+      store4(&dSb[row * L36 + 4 * q4], dsv[k]);
     }
+    store4(&dOb[td * L36 + 4 * q4d], dok ? dov : f32x4{0.f, 0.f, 0.f, 0.f});
     // rows 16 w + 4 g + i, columns 16 ct + r of the block: first half m = write . v, second half v
     // (ev) and the write gate (wv)
     float ev[2][4], wv[2][4];
@@ -831,8 +866,11 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
         const int col = dv0 + 16 * ct + r;
-        const float vx = ok ? ld_f32(vp + vo + col) : 0.f;
-        const float wg = ok ? (VEC ? p.write[th * DV + col] : p.write[th]) : 0.f;
+        // loaded whatever ok (the row is clamped to the chunk's first) and selected after
+        const float vr = ld_f32(vp + vo + col);
+        const float wr = VEC ? p.write[th * DV + col] : p.write[th];
+        const float vx = ok ? vr : 0.f;
+        const float wg = ok ? wr : 0.f;
         ev[ct][i] = hf == 0 ? wg * vx : vx;
         wv[ct][i] = wg;
       }
@@ -980,18 +1018,28 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
     const int64_t m = m0 + (valid ? row : 0);
     const int64_t th = cb_step(p, b, m, h);
     const int64_t qo = q_elem(p, b, m, h, DK), ko = kv_elem(p.k_ts, p.k_bs, p, b, m, h, DK);
-    const float esc = (!VEC && valid) ? p.erase[th] : 0.f;
+    const float esr = VEC ? 0.f : p.erase[th];
+    const float esc = valid ? esr : 0.f;
+    // both slices' loads issued first, selected after (as in the chunk algebra)
+    typename Raw8Of<InT>::type qr[KH], kr[KH];
+    float br[VEC ? KH : 1][8];
+#pragma unroll
+    for (int kh = 0; kh < KH; ++kh) {
+      const int ch0 = 32 * (hf * KH + kh) + 8 * g;
+      ld_raw8(qp + qo + ch0, qr[kh]);
+      ld_raw8(kp + ko + ch0, kr[kh]);
+      if constexpr (VEC) load8(p.erase + th * DK + ch0, br[kh]);
+    }
 #pragma unroll
     for (int kh = 0; kh < KH; ++kh) {
       const int ch0 = 32 * (hf * KH + kh) + 8 * g;
       float q8[8], k8[8], b8[8], g8[8];
-      if (valid) {
-        load8(qp + qo + ch0, q8);
-        load8(kp + ko + ch0, k8);
-        if constexpr (VEC) load8(p.erase + th * DK + ch0, b8);
-      } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { q8[j] = 0.f; k8[j] = 0.f; b8[j] = 0.f; }
+      for (int j = 0; j < 8; ++j) {
+        q8[j] = valid ? raw8_at(qr[kh], j) : 0.f;
+        k8[j] = valid ? raw8_at(kr[kh], j) : 0.f;
+        if constexpr (VEC) b8[j] = valid ? br[kh][j] : 0.f;
+        else b8[j] = 0.f;
       }
       load8(&sm.r0[row * LG + ch0], g8);
       float a[8], u[8];

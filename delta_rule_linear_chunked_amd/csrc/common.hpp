@@ -258,6 +258,21 @@ __device__ __forceinline__ void load8(const __bf16* p, float (&x)[8]) {
   for (int j = 0; j < 8; ++j) x[j] = (float)a[j];
 }
 
+// Eight consecutive q / k elements as loaded (16-byte loads), converted to fp32 where used.
+struct F32x8 {
+  f32x4 a, b;
+};
+template <typename T> struct Raw8Of;
+template <> struct Raw8Of<float> { using type = F32x8; };
+template <> struct Raw8Of<__bf16> { using type = bf16x8; };
+__device__ __forceinline__ void ld_raw8(const float* p, F32x8& r) {
+  r.a = *reinterpret_cast<const f32x4*>(p);
+  r.b = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ __forceinline__ void ld_raw8(const __bf16* p, bf16x8& r) { r = *reinterpret_cast<const bf16x8*>(p); }
+__device__ __forceinline__ float raw8_at(const F32x8& r, int j) { return j < 4 ? r.a[j] : r.b[j - 4]; }
+__device__ __forceinline__ float raw8_at(const bf16x8& r, int j) { return (float)r[j]; }
+
 // ---------------------------------------------------------------------------
 // MFMA 16x16 tiles with a 32-deep reduction per call.
 //

@@ -330,15 +330,21 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   float rq = 1.f, rk = 1.f;
   if (AM != 0 && p.prep_l2) {
     float sq = 0.f, sk = 0.f;
+    typename Raw8Of<InT>::type kn[KS], qn[KS];  // every slice's loads issued first (see below)
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      const int ch0 = 32 * ks + 8 * g;
-      if (valid && ch0 < DKR) {
-        float k8[8], q8[8];
-        load8(kp + ko + ch0, k8);
-        load8(qp + qo + ch0, q8);
+      const int ch0 = 32 * ks + 8 * g, cl = ch0 < DKR ? ch0 : 0;
+      ld_raw8(kp + ko + cl, kn[ks]);
+      ld_raw8(qp + qo + cl, qn[ks]);
+    }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) { sq = fmaf(q8[j], q8[j], sq); sk = fmaf(k8[j], k8[j], sk); }
+    for (int ks = 0; ks < KS; ++ks) {
+      const bool live = valid && 32 * ks + 8 * g < DKR;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float qv = live ? raw8_at(qn[ks], j) : 0.f, kv = live ? raw8_at(kn[ks], j) : 0.f;
+        sq = fmaf(qv, qv, sq);
+        sk = fmaf(kv, kv, sk);
       }
     }
     sq += __shfl_xor(sq, 16);
@@ -362,34 +368,48 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
     bool ok = true;
     f32x4 ad = f32x4{0.f, 0.f, 0.f, 0.f}, pd = ad;
     const float esc = (!VEC && valid) ? gate(p.erase[thk]) : 0.f;
+    // All slices' loads are issued before any is used: every lane loads (rows past the sequence
+    // end read the chunk's first row, channels past d_k channel 0) and the values are selected
+    // afterwards. Loads under the condition, slice by slice, were each waited for before the next
+    // slice's were issued.
+    typename Raw8Of<InT>::type kr[KS], qr[KS];
+    float ar[AM != 0 ? 1 : KS][8], br[VEC ? KS : 1][8];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int ch0 = 32 * ks + 8 * g, cl = ch0 < DKR ? ch0 : 0;
+      ld_raw8(kp + ko + cl, kr[ks]);
+      ld_raw8(qp + qo + cl, qr[ks]);
+      if constexpr (AM == 0) alpha8(thq * DKR + cl, ar[ks]);
+      if constexpr (VEC) load8(p.erase + thk * DKR + cl, br[ks]);
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const int ch0 = 32 * ks + 8 * g;
       const bool live = valid && ch0 < DKR;
       float a8[8], k8[8], q8[8], b8[8];
-      if (live) {
-        load8(kp + ko + ch0, k8);
-        load8(qp + qo + ch0, q8);
-        if constexpr (AM != 0) {
 #pragma unroll
-          for (int j = 0; j < 8; ++j) a8[j] = av[ks][j];
+      for (int j = 0; j < 8; ++j) {
+        k8[j] = raw8_at(kr[ks], j);
+        q8[j] = raw8_at(qr[ks], j);
+        if constexpr (AM != 0) a8[j] = av[ks][j];
+        else a8[j] = ar[ks][j];
+        if constexpr (VEC) b8[j] = br[ks][j];
+        else b8[j] = 0.f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        if constexpr (AM != 0) {
+          k8[j] *= rk;
+          q8[j] *= rq;
+          if constexpr (VEC) b8[j] = gate(b8[j]);
         } else {
-          alpha8(thq * DKR + ch0, a8);
-#pragma unroll
-          for (int j = 0; j < 8; ++j) a8[j] = unit_a ? 1.f : a8[j];
+          a8[j] = unit_a ? 1.f : a8[j];
         }
-        if constexpr (VEC) load8(p.erase + thk * DKR + ch0, b8);
-        if constexpr (AM != 0) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            k8[j] *= rk;
-            q8[j] *= rq;
-            if constexpr (VEC) b8[j] = gate(b8[j]);
-          }
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) { k8[j] = 0.f; q8[j] = 0.f; a8[j] = 1.f; b8[j] = 0.f; }
+        k8[j] = live ? k8[j] : 0.f;
+        q8[j] = live ? q8[j] : 0.f;
+        a8[j] = live ? a8[j] : 1.f;
+        if constexpr (VEC) b8[j] = live ? b8[j] : 0.f;
+        else b8[j] = 0.f;
       }
       float f8[8], kd[8], kgv[8];
 #pragma unroll
