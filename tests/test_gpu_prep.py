@@ -51,6 +51,22 @@ def test_prepared_prefill(variant, in_dtype, alpha_dtype):
     assert eo <= TOL[in_dtype] and es <= TOL[in_dtype]
 
 
+@pytest.mark.parametrize("in_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("variant", ["kda", "gdn2"])
+def test_prepared_prefill_narrow_keys(variant, in_dtype):
+    """d_k = 16, below the 32-deep MFMA slice: lanes past d_k load channel 0 and must drop it from
+    the norms and the gates (a ragged tail of 150 tokens besides)."""
+    wl = synth.make_prefill(variant, 2, 150, 2, 16, 16, in_dtype=in_dtype, seed=seed_of("prep16", variant, in_dtype),
+                            preact=True, alpha_dtype="f32")
+    o, S_T = drl.chunk_fwd(**_inputs(wl), prep=_kw(wl))
+    torch.cuda.synchronize()
+    q, k, alpha, erase, write = _oracle(wl)
+    o_ref, S_ref = oracle.step_recurrence(q, k, wl.v, alpha, erase, write, wl.variant, S0=wl.S0)
+    eo, es = oracle.rel_err(_np(o), o_ref), oracle.rel_err(_np(S_T), S_ref)
+    print(f"[prep prefill d_k=16 {variant} {in_dtype}] err o={eo:.3e} S_T={es:.3e}", flush=True)
+    assert eo <= TOL[in_dtype] and es <= TOL[in_dtype]
+
+
 def test_prepared_prefill_d128_packed():
     lens = [130, 0, 64, 300, 1]
     wl = synth.make_prefill("gdn2", 1, 0, 3, 128, 128, in_dtype="bf16", seed=seed_of("prep", "packed"),
