@@ -231,7 +231,7 @@ __device__ __forceinline__ void chunk_algebra(const CbParams& p, CbSmem<DK>& sm,
       for (int j = 0; j < 8; ++j) {
         qt[ks][j] = q8[j] * g8[j];
         ut[ks][j] = (VEC ? b8[j] : esc) * k8[j] * g8[j];
-        kd[j] = k8[j] / g8[j];
+        kd[j] = k8[j] * __builtin_amdgcn_rcpf(g8[j]);  // Gamma lies in [2^-110, 2^100] here
       }
       if (hf == 0) {
         store4(&sm.r1[row * LG + ch0], f32x4{kd[0], kd[1], kd[2], kd[3]});
@@ -1127,7 +1127,8 @@ __global__ __launch_bounds__(512, 1) void cbwd_grad_kernel(const CbParams p) {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Kk[(16 * w + 4 * g + i) * LG + 16 * ct + r] = A1[ct][i] / gam[ct][i];
+      for (int i = 0; i < 4; ++i)  // Gamma in [2^-110, 2^100]: the reciprocal is exact to an ulp
+        Kk[(16 * w + 4 * g + i) * LG + 16 * ct + r] = A1[ct][i] * __builtin_amdgcn_rcpf(gam[ct][i]);
     }
   }
   __syncthreads();
