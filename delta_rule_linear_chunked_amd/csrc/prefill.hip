@@ -509,7 +509,9 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) { ut[j] = uf[ks][j] * run[j]; qt[j] = qf[ks][j] * run[j]; }
       st_frag(rs, R::UT, wu * KS + ks, l, Pol::make(ut), p.rec_nt);
-      st_frag(rs, R::QT, wu * KS + ks, l, Pol::make(qt), p.rec_nt);
+      // Qtilde and P serve the output only: a call without output (states and snapshots only)
+      // leaves them out of the record, and its state pass does not read them
+      if (p.o) st_frag(rs, R::QT, wu * KS + ks, l, Pol::make(qt), p.rec_nt);
     }
 #pragma unroll
     for (int J = 0; J < NBLK - 1; ++J) {
@@ -528,7 +530,7 @@ __global__ __launch_bounds__(256, 2) void chunk_prep_kernel(const Params p) {
   // (rows of blocks 0 and 1 are zero in tokens 32..63: that step is never read, nor written)
 #pragma unroll
   for (int st = 0; st < 2; ++st) {
-    if (st == 0 || w >= 2) {
+    if (p.o && (st == 0 || w >= 2)) {
       float a8[8];
       load8(&sm.u1.P[16 * w + r][32 * st + 8 * g], a8);
       st_frag(rs, R::PP, wu * 2 + st, l, Pol::make(a8), p.rec_nt);
